@@ -1,0 +1,195 @@
+"""CPU oracle for the K4V2 group-128 KV cache -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain C,
+``kvq_oracle.c``) with numpy marshalling and holds no arithmetic of its own.
+The GPU library never imports it and shares no code with it.
+
+Functions and the passages they follow (pages cited by title and section):
+
+* ``quantize_group`` / ``quantize_append`` -- the KVarN write path: Hadamard
+  rotation, variance normalisation, asymmetric round-to-nearest (dothoosh.com,
+  "KVarN vs TurboQuant: 5x more context with higher accuracy", the four-stage
+  pipeline list, stages 1-3; beyondheadline.xyz, "Huawei's KV-cache trick",
+  section "The claim that breaks the usual trade-off": 4-bit keys, 2-bit
+  values, cache blocks, preset kvarn_k4v2_g128).
+* ``decode_attention`` -- attention over the dequantised, un-rotated cache by
+  its plain definition (softmax(scale q.k) v), fp64.
+* ``decode_attention_folded`` -- the same result reached by scale folding on
+  read-back (same pipeline list, stage 4), fp64; pins the algebra.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+D = 128
+PAGE = 16
+REGION = 1664
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.kvqo_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.kvqo_half_to_double.restype = ctypes.c_double
+    lib.kvqo_float_to_half.argtypes = [ctypes.c_float]
+    lib.kvqo_float_to_half.restype = ctypes.c_uint16
+    lib.kvqo_hadamard_entry.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.kvqo_hadamard_entry.restype = ctypes.c_int
+    lib.kvqo_fwht_f32.argtypes = [P]
+    lib.kvqo_fwht_f32.restype = None
+    lib.kvqo_hadamard_matvec_f64.argtypes = [P, P]
+    lib.kvqo_hadamard_matvec_f64.restype = None
+    lib.kvqo_quantize_group.argtypes = [P, ctypes.c_int, P, P, P]
+    lib.kvqo_quantize_group.restype = None
+    lib.kvqo_store_token.argtypes = [P, ctypes.c_int, P, ctypes.c_uint16, ctypes.c_uint16,
+                                     P, ctypes.c_uint16, ctypes.c_uint16]
+    lib.kvqo_store_token.restype = None
+    lib.kvqo_load_token.argtypes = [P, ctypes.c_int, P, P, P, P, P, P]
+    lib.kvqo_load_token.restype = None
+    lib.kvqo_quantize_append.argtypes = [P, P, i64, i64, P, i64, i32, P, i64]
+    lib.kvqo_quantize_append.restype = ctypes.c_int
+    lib.kvqo_dequant_slot.argtypes = [P, ctypes.c_int, P, P]
+    lib.kvqo_dequant_slot.restype = None
+    lib.kvqo_decode_attention.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
+                                          ctypes.c_double, P, P]
+    lib.kvqo_decode_attention.restype = ctypes.c_int
+    lib.kvqo_decode_attention_folded.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
+                                                 ctypes.c_double, P]
+    lib.kvqo_decode_attention_folded.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def half_to_double(bits: int) -> float:
+    return _load().kvqo_half_to_double(int(bits) & 0xFFFF)
+
+
+def float_to_half(x: float) -> int:
+    return int(_load().kvqo_float_to_half(float(np.float32(x))))
+
+
+def hadamard_entry(i: int, j: int) -> int:
+    return _load().kvqo_hadamard_entry(i, j)
+
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    y = _c(x, np.float32).copy()
+    assert y.shape == (D,)
+    _load().kvqo_fwht_f32(_ptr(y))
+    return y
+
+
+def hadamard_matvec_f64(x: np.ndarray) -> np.ndarray:
+    xx = _c(x, np.float64)
+    y = np.empty(D, np.float64)
+    _load().kvqo_hadamard_matvec_f64(_ptr(xx), _ptr(y))
+    return y
+
+
+def quantize_group(x_f16: np.ndarray, bits: int):
+    """x_f16: 128 float16 values.  Returns (codes uint8[128], s_bits, z_bits)."""
+    x = _c(x_f16, np.float16).view(np.uint16)
+    assert x.shape == (D,)
+    codes = np.empty(D, np.uint8)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint16)
+    _load().kvqo_quantize_group(_ptr(x), int(bits), _ptr(codes), _ptr(s), _ptr(z))
+    return codes, int(s[0]), int(z[0])
+
+
+def store_token(region: np.ndarray, off: int, kc, ks, kz, vc, vs, vz):
+    assert region.dtype == np.uint8 and region.size == REGION and region.flags.c_contiguous
+    _load().kvqo_store_token(_ptr(region), int(off), _ptr(_c(kc, np.uint8)), int(ks), int(kz),
+                             _ptr(_c(vc, np.uint8)), int(vs), int(vz))
+
+
+def load_token(region: np.ndarray, off: int):
+    r = _c(region, np.uint8)
+    kc = np.empty(D, np.uint8)
+    vc = np.empty(D, np.uint8)
+    m = np.zeros(4, np.uint16)
+    _load().kvqo_load_token(_ptr(r), int(off), _ptr(kc), _ptr(m[0:1]), _ptr(m[1:2]),
+                            _ptr(vc), _ptr(m[2:3]), _ptr(m[3:4]))
+    return kc, int(m[0]), int(m[1]), vc, int(m[2]), int(m[3])
+
+
+def quantize_append(key_f16: np.ndarray, value_f16: np.ndarray, slot_mapping: np.ndarray,
+                    pool: np.ndarray) -> None:
+    """key/value: float16 [T][Hkv][128]; slot_mapping int64[T]; pool uint8
+    [num_pages][Hkv][1664], written in place."""
+    k = _c(key_f16, np.float16)
+    v = _c(value_f16, np.float16)
+    T, H, d = k.shape
+    assert d == D and v.shape == k.shape
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.shape[1:] == (H, REGION)
+    sm = _c(slot_mapping, np.int64)
+    rc = _load().kvqo_quantize_append(_ptr(k), _ptr(v), H * D, H * D, _ptr(sm), T, H,
+                                      _ptr(pool), pool.shape[0])
+    if rc != 0:
+        raise ValueError("oracle append: slot outside the pool")
+
+
+def dequant_slot(region: np.ndarray, off: int):
+    r = _c(region, np.uint8)
+    k = np.empty(D, np.float64)
+    v = np.empty(D, np.float64)
+    _load().kvqo_dequant_slot(_ptr(r), int(off), _ptr(k), _ptr(v))
+    return k, v
+
+
+def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=None):
+    """Plain-definition decode attention in fp64.  query: float16 [B][Hq][128].
+    Returns float64 [B][Hq][128] (NaN where head_mask excludes a head)."""
+    pool = _c(pool, np.uint8)
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    q = _c(query_f16, np.float16)
+    B, Hq, d = q.shape
+    Hkv = pool.shape[1]
+    out = np.full((B, Hq, D), np.nan, np.float64)
+    hm = None if head_mask is None else _c(head_mask, np.uint8)
+    rc = _load().kvqo_decode_attention(_ptr(pool), pool.shape[0], Hkv, _ptr(bt), bt.shape[1],
+                                       _ptr(sl), B, Hq, _ptr(q), float(scale),
+                                       None if hm is None else _ptr(hm), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle decode: invalid shape or page id")
+    return out
+
+
+def decode_attention_folded(pool, block_tables, seq_lens, query_f16, scale):
+    pool = _c(pool, np.uint8)
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    q = _c(query_f16, np.float16)
+    B, Hq, d = q.shape
+    out = np.empty((B, Hq, D), np.float64)
+    rc = _load().kvqo_decode_attention_folded(_ptr(pool), pool.shape[0], pool.shape[1], _ptr(bt),
+                                              bt.shape[1], _ptr(sl), B, Hq, _ptr(q),
+                                              float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle folded decode: invalid shape or page id")
+    return out

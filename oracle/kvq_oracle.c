@@ -1,0 +1,462 @@
+/*
+ * kvq oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU statement of what the K4V2 group-128
+ * quantized KV cache computes.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library) shares no code, header, table or helper with this file.
+ *
+ * Sources (web pages; cited by tag):
+ *   [KVARN-HN]  beyondheadline.xyz, "Huawei's KV-cache trick: FP16 accuracy, a
+ *               four-times-larger cache and higher throughput at once" -- the
+ *               lede and the section "The claim that breaks the usual
+ *               trade-off" (4-bit keys, 2-bit values, Hadamard rotation,
+ *               variance normalisation, asymmetric low-bit quantisation of cache
+ *               blocks, preset kvarn_k4v2_g128).
+ *   [KVARN-P]   dothoosh.com, "KVarN vs TurboQuant: 5x more context with higher
+ *               accuracy" -- the four-stage pipeline list: (1) Hadamard
+ *               rotation, (2) variance normalisation, (3) asymmetric
+ *               round-to-nearest quantisation, (4) scale folding on read-back.
+ *   [KV-INFRA]  encorp.ai, "KV cache compression is an infrastructure decision,
+ *               not a model debate" -- section on decode being bound by HBM,
+ *               not FLOPs.
+ *
+ * The pages give no formulas.  The readings fixed here (one 128-channel group
+ * per token per KV head, unnormalised Sylvester Hadamard in natural order,
+ * per-group RMS as the variance normalisation, min/max asymmetric RTN with
+ * ties to even, fp16 scale/zero, 16-token pages and the byte layout) are the
+ * format "kvq-k4v2-g128 v1"; each is listed with its reason in the design
+ * notes of the repository.
+ *
+ * Precision: the encoder decides integer codes, so it runs in IEEE fp32 with
+ * round-to-nearest-even, no fused multiply-add (build with -ffp-contract=off)
+ * and denormals kept -- the precision the GPU encoder uses.  Attention is
+ * computed in fp64 from its plain definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KVQO_D 128          /* head_dim == group size                     */
+#define KVQO_PAGE 16        /* tokens per page                            */
+#define KVQO_REGION 1664    /* bytes per (page, kv head)                  */
+#define KVQO_K_CODES 0      /* token o: 64 bytes at 64*o                  */
+#define KVQO_V_CODES 1024   /* quad g=o/4, slot i=o%4: u16 at 128g+8m+2i  */
+#define KVQO_K_META 1536    /* token o: fp16 s, fp16 z at 1536+4o         */
+#define KVQO_V_META 1600    /* token o: fp16 s, fp16 z at 1600+4o         */
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 <-> binary32/64, written from the format definition.        */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 bits -> exact real value (every binary16 is exact in double). */
+double kvqo_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* zero / subnormal */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) 2^(e-15) */
+    return sign ? -v : v;
+}
+
+float kvqo_half_to_float(uint16_t h) { return (float)kvqo_half_to_double(h); }
+
+/* Nearest binary16 to a binary32 value, ties to even.  |f| is scaled by the
+ * binary16 unit in the last place of its binade (a power of two, so exact in
+ * double) and rounded to an integer with the default rounding mode
+ * (nearest-even).  A carry out of the significand lands in the exponent field
+ * by itself, and a result beyond the largest finite value becomes infinity. */
+uint16_t kvqo_float_to_half(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    double a = fabs((double)f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00);
+    if (isinf(f)) return (uint16_t)(sign | 0x7c00);
+    if (a < 0x1p-14) {                             /* subnormal binade */
+        double n = nearbyint(a * 0x1p24);          /* units of 2^-24 */
+        return (uint16_t)(sign | (uint16_t)n);     /* n == 1024 is the min normal */
+    }
+    int ex;
+    frexp(a, &ex);                                 /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                                /* a in [2^e, 2^(e+1)) */
+    double n = nearbyint(ldexp(a, 10 - e));        /* in [1024, 2048] */
+    long bits = ((long)(e + 15) << 10) + ((long)n - 1024);
+    if (bits >= 0x7c00) return (uint16_t)(sign | 0x7c00);
+    return (uint16_t)(sign | (uint16_t)bits);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard matrix of order 128 (Sylvester construction, natural order).     */
+/* ------------------------------------------------------------------------ */
+
+/* Entry (i, j) of the unnormalised Sylvester Hadamard matrix: (-1)^popcount(i&j). */
+int kvqo_hadamard_entry(int i, int j)
+{
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+}
+
+/* Fast Walsh-Hadamard transform in fp32, in place, no scaling.  Butterfly
+ * stages h = 1, 2, 4, ..., 64; each butterfly replaces (a, b) = (y[i], y[i+h])
+ * with (a + b, a - b).  This stage order is part of the format: it fixes the
+ * fp32 rounding of the rotated values that the codes are taken from. */
+void kvqo_fwht_f32(float *y)
+{
+    for (int h = 1; h < KVQO_D; h <<= 1)
+        for (int i = 0; i < KVQO_D; i++)
+            if ((i & h) == 0) {
+                float a = y[i], b = y[i + h];
+                y[i] = a + b;
+                y[i + h] = a - b;
+            }
+}
+
+/* y = H x in fp64 as a dense matrix-vector product (used where rounding order
+ * does not matter: un-rotating the cache for attention). */
+void kvqo_hadamard_matvec_f64(const double *x, double *y)
+{
+    for (int i = 0; i < KVQO_D; i++) {
+        double acc = 0.0;
+        for (int j = 0; j < KVQO_D; j++)
+            acc += kvqo_hadamard_entry(i, j) * x[j];
+        y[i] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Encoder: one group = the 128 channels of one token of one KV head.        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Quantise one group of 128 fp16 values to `bits`-bit codes (4 for keys, 2
+ * for values) with an fp16 scale s and zero z, following the pipeline order
+ * of [KVARN-P] (stages 1-3) and [KVARN-HN]:
+ *
+ *   1. Hadamard rotation [KVARN-P stage 1]: y = H x by the fp32 FWHT above.
+ *   2. Variance normalisation [KVARN-P stage 2, KVARN-HN]: read here as the
+ *      group's RMS.  p_i = y_i^2, summed by the fixed pairwise tree
+ *      (h = 64, 32, ..., 1: p[i] += p[i+h] for i < h); sigma =
+ *      sqrt(ss / 128); r = 1 / sigma; yh_i = y_i * r.  An all-zero group
+ *      encodes as codes 0, s = 0, z = 0.
+ *   3. Asymmetric round-to-nearest [KVARN-P stage 3]: m = min yh, M = max yh,
+ *      L = 2^bits - 1.  If M == m every code is 0 and the step is 0.
+ *      Otherwise delta = (M - m) / L, inv = L / (M - m) and
+ *      c_i = min(L, rint((yh_i - m) * inv)), ties to even.
+ *   4. The normalisation is folded back into the stored metadata:
+ *      s = fp16(delta * sigma), z = fp16(m * sigma), so that the rotated
+ *      value is recovered as s * c + z.  A zero z is stored as +0.
+ */
+void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
+                         uint16_t *s_out, uint16_t *z_out)
+{
+    float y[KVQO_D], p[KVQO_D];
+    for (int i = 0; i < KVQO_D; i++)
+        y[i] = kvqo_half_to_float(x[i]);
+
+    /* 1. Hadamard rotation */
+    kvqo_fwht_f32(y);
+
+    /* 2. variance normalisation */
+    for (int i = 0; i < KVQO_D; i++)
+        p[i] = y[i] * y[i];
+    for (int h = KVQO_D / 2; h >= 1; h >>= 1)
+        for (int i = 0; i < h; i++)
+            p[i] = p[i] + p[i + h];
+    float ss = p[0];
+    if (ss == 0.0f) {
+        memset(codes, 0, KVQO_D);
+        *s_out = 0;
+        *z_out = 0;
+        return;
+    }
+    float sigma = sqrtf(ss * 0x1p-7f);
+    float r = 1.0f / sigma;
+    float yh[KVQO_D];
+    for (int i = 0; i < KVQO_D; i++)
+        yh[i] = y[i] * r;
+
+    /* 3. asymmetric round-to-nearest */
+    float m = yh[0], M = yh[0];
+    for (int i = 1; i < KVQO_D; i++) {
+        if (yh[i] < m) m = yh[i];
+        if (yh[i] > M) M = yh[i];
+    }
+    const int L = (1 << bits) - 1;
+    float delta;
+    if (M == m) {
+        delta = 0.0f;
+        memset(codes, 0, KVQO_D);
+    } else {
+        delta = (M - m) / (float)L;
+        float inv = (float)L / (M - m);
+        for (int i = 0; i < KVQO_D; i++) {
+            float c = rintf((yh[i] - m) * inv);
+            codes[i] = (uint8_t)(c > (float)L ? L : (int)c);
+        }
+    }
+
+    /* 4. metadata */
+    *s_out = kvqo_float_to_half(delta * sigma);
+    uint16_t z = kvqo_float_to_half(m * sigma);
+    *z_out = (z == 0x8000) ? 0 : z;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Byte layout of one (page, KV head) region.                                */
+/* ------------------------------------------------------------------------ */
+
+/* Write token slot `off` (0..15) of a region: 128 key codes (0..15), 128
+ * value codes (0..3) and the two (s, z) pairs.
+ *   key codes:   byte 64*off + b = code[2b] | code[2b+1] << 4
+ *   value codes: for quad g = off/4, slot i = off%4 and m = 0..15, the 16-bit
+ *                little-endian word at 1024 + 128g + 8m + 2i holds the code of
+ *                channel 16j + m in bits 2j..2j+1 (j = 0..7)
+ *   metadata:    fp16 s then fp16 z, little-endian, at 1536 + 4*off (keys)
+ *                and 1600 + 4*off (values). */
+void kvqo_store_token(uint8_t *region, int off,
+                      const uint8_t *kc, uint16_t ks, uint16_t kz,
+                      const uint8_t *vc, uint16_t vs, uint16_t vz)
+{
+    uint8_t *kb = region + KVQO_K_CODES + 64 * off;
+    for (int b = 0; b < 64; b++)
+        kb[b] = (uint8_t)((kc[2 * b] & 15) | ((kc[2 * b + 1] & 15) << 4));
+
+    int g = off / 4, i = off % 4;
+    for (int m = 0; m < 16; m++) {
+        unsigned w = 0;
+        for (int j = 0; j < 8; j++)
+            w |= (unsigned)(vc[16 * j + m] & 3) << (2 * j);
+        uint8_t *vb = region + KVQO_V_CODES + 128 * g + 8 * m + 2 * i;
+        vb[0] = (uint8_t)(w & 0xff);
+        vb[1] = (uint8_t)(w >> 8);
+    }
+
+    uint8_t *km = region + KVQO_K_META + 4 * off;
+    km[0] = (uint8_t)(ks & 0xff); km[1] = (uint8_t)(ks >> 8);
+    km[2] = (uint8_t)(kz & 0xff); km[3] = (uint8_t)(kz >> 8);
+    uint8_t *vm = region + KVQO_V_META + 4 * off;
+    vm[0] = (uint8_t)(vs & 0xff); vm[1] = (uint8_t)(vs >> 8);
+    vm[2] = (uint8_t)(vz & 0xff); vm[3] = (uint8_t)(vz >> 8);
+}
+
+/* Inverse of kvqo_store_token. */
+void kvqo_load_token(const uint8_t *region, int off,
+                     uint8_t *kc, uint16_t *ks, uint16_t *kz,
+                     uint8_t *vc, uint16_t *vs, uint16_t *vz)
+{
+    const uint8_t *kb = region + KVQO_K_CODES + 64 * off;
+    for (int b = 0; b < 64; b++) {
+        kc[2 * b] = kb[b] & 15;
+        kc[2 * b + 1] = kb[b] >> 4;
+    }
+    int g = off / 4, i = off % 4;
+    for (int m = 0; m < 16; m++) {
+        const uint8_t *vb = region + KVQO_V_CODES + 128 * g + 8 * m + 2 * i;
+        unsigned w = (unsigned)vb[0] | ((unsigned)vb[1] << 8);
+        for (int j = 0; j < 8; j++)
+            vc[16 * j + m] = (uint8_t)((w >> (2 * j)) & 3);
+    }
+    const uint8_t *km = region + KVQO_K_META + 4 * off;
+    *ks = (uint16_t)(km[0] | (km[1] << 8));
+    *kz = (uint16_t)(km[2] | (km[3] << 8));
+    const uint8_t *vm = region + KVQO_V_META + 4 * off;
+    *vs = (uint16_t)(vm[0] | (vm[1] << 8));
+    *vz = (uint16_t)(vm[2] | (vm[3] << 8));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantise-on-write of cache blocks [KVARN-HN].                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * key/value: fp16 [num_tokens][num_kv_heads][128] with the given token
+ * strides (in elements; the head stride is 128).  slot_mapping[t] = page*16 +
+ * offset, or < 0 to skip the token.  pool: u8 [num_pages][num_kv_heads][1664].
+ * Returns 0, or -1 on a slot outside the pool (nothing is written for it).
+ */
+int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
+                         int64_t key_token_stride, int64_t value_token_stride,
+                         const int64_t *slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+{
+    int rc = 0;
+    uint8_t kc[KVQO_D], vc[KVQO_D];
+    for (int64_t t = 0; t < num_tokens; t++) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        int64_t page = slot / KVQO_PAGE;
+        int off = (int)(slot % KVQO_PAGE);
+        if (page >= num_pages) { rc = -1; continue; }
+        for (int h = 0; h < num_kv_heads; h++) {
+            uint16_t ks, kz, vs, vz;
+            kvqo_quantize_group(key + t * key_token_stride + (int64_t)h * KVQO_D, 4, kc, &ks, &kz);
+            kvqo_quantize_group(value + t * value_token_stride + (int64_t)h * KVQO_D, 2, vc, &vs, &vz);
+            uint8_t *region = pool + (page * num_kv_heads + h) * (int64_t)KVQO_REGION;
+            kvqo_store_token(region, off, kc, ks, kz, vc, vs, vz);
+        }
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the quantised paged cache.                          */
+/* ------------------------------------------------------------------------ */
+
+/* Dequantise one cached token back to the original (un-rotated) domain:
+ * rotated value yt_i = s*c_i + z; original value = H yt / 128 (H H = 128 I). */
+static void dequant_unrotate(const uint8_t *codes, uint16_t s16, uint16_t z16, double *out)
+{
+    double yt[KVQO_D];
+    double s = kvqo_half_to_double(s16), z = kvqo_half_to_double(z16);
+    for (int i = 0; i < KVQO_D; i++)
+        yt[i] = s * codes[i] + z;
+    kvqo_hadamard_matvec_f64(yt, out);
+    for (int i = 0; i < KVQO_D; i++)
+        out[i] /= 128.0;
+}
+
+/* Public helper for tests: dequantised, un-rotated key and value of one slot. */
+void kvqo_dequant_slot(const uint8_t *region, int off, double *k_out, double *v_out)
+{
+    uint8_t kc[KVQO_D], vc[KVQO_D];
+    uint16_t ks, kz, vs, vz;
+    kvqo_load_token(region, off, kc, &ks, &kz, vc, &vs, &vz);
+    dequant_unrotate(kc, ks, kz, k_out);
+    dequant_unrotate(vc, vs, vz, v_out);
+}
+
+/*
+ * Plain definition of one decode step.  For sequence b, query head hq and its
+ * KV head kvh = hq / (num_q_heads / num_kv_heads), with n = seq_lens[b]
+ * cached tokens (token t lives in page block_tables[b][t / 16], slot t % 16):
+ *     k_t, v_t = dequantised, un-rotated key and value of token t
+ *     l_t      = scale * (q . k_t)
+ *     out      = sum_t softmax(l)_t v_t
+ * in fp64.  query: fp16 [num_seqs][num_q_heads][128].  out: fp64, same shape.
+ * head_mask (optional, [num_seqs][num_q_heads]): only heads with a non-zero
+ * entry are computed; the rest of `out` is left untouched.
+ * Returns 0, or -1 on an invalid shape or page id.
+ */
+int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                          const int32_t *block_tables, int32_t max_pages_per_seq,
+                          const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                          const uint16_t *query, double scale,
+                          const uint8_t *head_mask, double *out)
+{
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+    const int G = num_q_heads / num_kv_heads;
+    for (int b = 0; b < num_seqs; b++) {
+        const int64_t n = seq_lens[b];
+        if (n < 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        for (int kvh = 0; kvh < num_kv_heads; kvh++) {
+            int any = 0;
+            for (int g = 0; g < G; g++)
+                if (!head_mask || head_mask[b * num_q_heads + kvh * G + g]) any = 1;
+            if (!any || n == 0) continue;
+            double *K = malloc(sizeof(double) * KVQO_D * n);
+            double *V = malloc(sizeof(double) * KVQO_D * n);
+            double *lg = malloc(sizeof(double) * n);
+            if (!K || !V || !lg) { free(K); free(V); free(lg); return -1; }
+            for (int64_t t = 0; t < n; t++) {
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                if (page < 0 || page >= num_pages) { free(K); free(V); free(lg); return -1; }
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
+                kvqo_dequant_slot(region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+            }
+            for (int g = 0; g < G; g++) {
+                int hq = kvh * G + g;
+                if (head_mask && !head_mask[b * num_q_heads + hq]) continue;
+                const uint16_t *q16 = query + ((int64_t)b * num_q_heads + hq) * KVQO_D;
+                double q[KVQO_D];
+                for (int i = 0; i < KVQO_D; i++) q[i] = kvqo_half_to_double(q16[i]);
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < n; t++) {
+                    double d = 0.0;
+                    for (int i = 0; i < KVQO_D; i++) d += q[i] * K[t * KVQO_D + i];
+                    lg[t] = scale * d;
+                    if (lg[t] > mx) mx = lg[t];
+                }
+                double den = 0.0, o[KVQO_D] = {0};
+                for (int64_t t = 0; t < n; t++) {
+                    double e = exp(lg[t] - mx);
+                    den += e;
+                    for (int i = 0; i < KVQO_D; i++) o[i] += e * V[t * KVQO_D + i];
+                }
+                double *dst = out + ((int64_t)b * num_q_heads + hq) * KVQO_D;
+                for (int i = 0; i < KVQO_D; i++) dst[i] = o[i] / den;
+            }
+            free(K); free(V); free(lg);
+        }
+    }
+    return 0;
+}
+
+/*
+ * The same step reached by scale folding on read-back [KVARN-P stage 4], in
+ * fp64: never materialise k_t or v_t.  With q' = H q (H symmetric):
+ *     q . k_t   = (q' . (s c_t + z 1)) / 128 = (s (q' . c_t) + z sum(q')) / 128
+ *     sum_t p_t v_t = H (acc + zacc 1) / 128,  acc = sum_t p_t s_t c_t,
+ *                                            zacc = sum_t p_t z_t,
+ *     and H 1 = 128 e_0, so the value zero-points reach output channel 0 only.
+ * Exists to pin this algebra against the plain definition above.
+ */
+int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                                 const int32_t *block_tables, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 const uint16_t *query, double scale, double *out)
+{
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+    const int G = num_q_heads / num_kv_heads;
+    uint8_t kc[KVQO_D], vc[KVQO_D];
+    for (int b = 0; b < num_seqs; b++) {
+        const int64_t n = seq_lens[b];
+        if (n <= 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        double *lg = malloc(sizeof(double) * n);
+        if (!lg) return -1;
+        for (int hq = 0; hq < num_q_heads; hq++) {
+            int kvh = hq / G;
+            const uint16_t *q16 = query + ((int64_t)b * num_q_heads + hq) * KVQO_D;
+            double q[KVQO_D], qr[KVQO_D], qsum = 0.0;
+            for (int i = 0; i < KVQO_D; i++) q[i] = kvqo_half_to_double(q16[i]);
+            kvqo_hadamard_matvec_f64(q, qr);
+            for (int i = 0; i < KVQO_D; i++) qsum += qr[i];
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < n; t++) {
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                if (page < 0 || page >= num_pages) { free(lg); return -1; }
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
+                uint16_t ks, kz, vs, vz;
+                kvqo_load_token(region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
+                double dot = 0.0;
+                for (int i = 0; i < KVQO_D; i++) dot += qr[i] * kc[i];
+                lg[t] = scale * (kvqo_half_to_double(ks) * dot + kvqo_half_to_double(kz) * qsum) / 128.0;
+                if (lg[t] > mx) mx = lg[t];
+            }
+            double l = 0.0, zacc = 0.0, acc[KVQO_D] = {0};
+            for (int64_t t = 0; t < n; t++) {
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
+                uint16_t ks, kz, vs, vz;
+                kvqo_load_token(region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
+                double p = exp(lg[t] - mx);
+                double sv = kvqo_half_to_double(vs);
+                l += p;
+                zacc += p * kvqo_half_to_double(vz);
+                for (int i = 0; i < KVQO_D; i++) acc[i] += p * sv * vc[i];
+            }
+            double o[KVQO_D];
+            kvqo_hadamard_matvec_f64(acc, o);
+            double *dst = out + ((int64_t)b * num_q_heads + hq) * KVQO_D;
+            for (int i = 0; i < KVQO_D; i++) dst[i] = o[i] / (128.0 * l);
+            dst[0] += zacc / l;
+        }
+        free(lg);
+    }
+    return 0;
+}

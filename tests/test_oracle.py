@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Nothing here re-types the oracle's formulas: each check is a closed form, an
+invariant, a special case that reduces to a library routine (numpy's binary16
+conversion, torch's scaled-dot-product attention), brute force, or a
+hand-derived fixture under tests/golden/.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kvq_inputs as inp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 128
+
+
+def _read_fixture(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            k, v = [s.strip() for s in line.split("=", 1)]
+            out[k] = v
+    return out
+
+
+def sylvester(n=128):
+    h = np.array([[1]], dtype=np.int64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+H = sylvester()
+
+
+# --------------------------------------------------------------------------
+# binary16 conversions vs numpy
+# --------------------------------------------------------------------------
+
+def test_half_to_double_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.signbit(got[~np.isnan(ref)]), np.signbit(ref[~np.isnan(ref)]))
+
+
+def test_float_to_half_matches_numpy_rne():
+    rng = np.random.default_rng(7)
+    vals = [
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-5).astype(np.float32),      # subnormal range
+        (rng.standard_normal(2000) * 3e4).astype(np.float32),       # near overflow
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24,
+                  2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26, 6.1e-5, 1.0 + 2.0 ** -11,
+                  1.0 + 3 * 2.0 ** -11, np.inf, -np.inf], dtype=np.float32),
+    ]
+    # exact ties between neighbouring binary16 values
+    hb = np.arange(0x0001, 0x7bff, 97, dtype=np.uint16)
+    lo = hb.view(np.float16).astype(np.float64)
+    hi = (hb + 1).view(np.float16).astype(np.float64)
+    vals.append(((lo + hi) / 2).astype(np.float32))
+    x = np.concatenate(vals)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------
+# Hadamard rotation
+# --------------------------------------------------------------------------
+
+def test_hadamard_entries_closed_form():
+    Ho = np.array([[oracle.hadamard_entry(i, j) for j in range(D)] for i in range(D)])
+    assert np.array_equal(Ho, H)                       # Sylvester recursion
+    assert np.array_equal(Ho @ Ho.T, 128 * np.eye(D, dtype=np.int64))
+    assert np.array_equal(Ho, Ho.T)
+
+
+def test_fwht_columns_and_involution():
+    for j in range(D):
+        e = np.zeros(D, np.float32)
+        e[j] = 1.0
+        assert np.array_equal(oracle.fwht_f32(e), H[:, j].astype(np.float32))
+    rng = np.random.default_rng(1)
+    x = rng.integers(-8, 9, D).astype(np.float32)
+    assert np.array_equal(oracle.fwht_f32(oracle.fwht_f32(x)), 128 * x)
+
+
+def test_fwht_f32_close_to_exact_on_fp16_inputs():
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        x16 = (rng.standard_normal(D) * rng.choice([1e-3, 1, 30])).astype(np.float16)
+        exact = H @ (x16.astype(np.float64))          # exact: fp16 values sum in < 53 bits
+        got = oracle.fwht_f32(x16.astype(np.float32)).astype(np.float64)
+        bound = 7 * 2.0 ** -24 * np.abs(x16.astype(np.float64)).sum()
+        assert np.max(np.abs(got - exact)) <= bound
+
+
+def test_matvec_f64():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(D)
+    assert np.allclose(oracle.hadamard_matvec_f64(x), H @ x, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Encoder
+# --------------------------------------------------------------------------
+
+def _dequant(codes, s, z):
+    return oracle.half_to_double(s) * codes.astype(np.float64) + oracle.half_to_double(z)
+
+
+def test_zero_and_constant_groups():
+    codes, s, z = oracle.quantize_group(np.zeros(D, np.float16), 4)
+    assert not codes.any() and s == 0 and z == 0
+    e0 = np.zeros(D, np.float16)
+    e0[0] = 1
+    for bits in (4, 2):
+        codes, s, z = oracle.quantize_group(e0, bits)   # H e0 = all ones -> M == m
+        assert not codes.any() and s == 0 and z == 0x3C00
+
+
+def test_hand_derived_example():
+    f = _read_fixture("quantize_e0_e1.txt")
+    x = np.zeros(D, np.float16)
+    x[0] = x[1] = 1
+    for bits, pre in ((4, "key"), (2, "value")):
+        codes, s, z = oracle.quantize_group(x, bits)
+        assert np.all(codes[0::2] == int(f[pre + "_codes_even"]))
+        assert np.all(codes[1::2] == int(f[pre + "_codes_odd"]))
+        assert s == int(f[pre + "_s"], 16) and z == int(f[pre + "_z"], 16)
+
+
+def _on_grid(rng, L, delta=2.0 ** -4, zero=-0.5):
+    c = rng.integers(0, L + 1, D)
+    c[rng.integers(D)] = 0
+    c[rng.integers(D)] = L
+    while c.min() != 0 or c.max() != L:
+        c = rng.integers(0, L + 1, D)
+    y = zero + delta * c                               # rotated-domain values, on the grid
+    x = (H @ y) / 128.0                                # H^-1 = H / 128
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x)  # representable exactly
+    return x16, c, delta, zero
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_on_grid_round_trip_exact(bits):
+    rng = np.random.default_rng(10 + bits)
+    L = (1 << bits) - 1
+    for _ in range(40):
+        x16, c, delta, zero = _on_grid(rng, L)
+        codes, s, z = oracle.quantize_group(x16, bits)
+        assert np.array_equal(codes, c)
+        assert oracle.half_to_double(s) == delta and oracle.half_to_double(z) == zero
+        assert np.array_equal(_dequant(codes, s, z), zero + delta * c)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_error_bound_and_brute_force_nearest_level(bits):
+    rng = np.random.default_rng(20 + bits)
+    L = (1 << bits) - 1
+    levels = np.arange(L + 1, dtype=np.float64)
+    for trial in range(300):
+        scale = [1.0, 0.01, 50.0][trial % 3]
+        x = rng.standard_normal(D) * scale
+        if trial % 5 == 0:
+            x[rng.integers(0, D, 3)] *= 20                   # outlier channels
+        x16 = x.astype(np.float16)
+        y = H @ x16.astype(np.float64)                       # exact rotation
+        codes, s16, z16 = oracle.quantize_group(x16, bits)
+        s, z = oracle.half_to_double(s16), oracle.half_to_double(z16)
+        assert codes.max() <= L
+        rec = s * codes + z
+        slack = 2.0 ** -10 * (L * s + abs(z)) + 1e-6 * np.abs(y).max()
+        err = np.abs(y - rec)
+        assert np.all(err <= s / 2 + slack)
+        # brute force: the chosen level is (up to the rounding slack) the nearest
+        best = np.min(np.abs(y[:, None] - (s * levels[None, :] + z)), axis=1)
+        assert np.all(err <= best + slack)
+        assert codes[np.argmin(y)] == 0 and codes[np.argmax(y)] == L
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_scale_equivariance(bits):
+    """min/max RTN is equivariant to a power-of-two input scale: codes are
+    unchanged and (s, z) scale exactly (powers of two commute with every
+    rounding away from over/underflow)."""
+    rng = np.random.default_rng(30 + bits)
+    for _ in range(100):
+        # magnitudes in [0.01, 4]: every scaled copy stays a normal fp16
+        x16 = (rng.choice([-1, 1], D) * rng.uniform(0.01, 4, D)).astype(np.float16)
+        c0, s0, z0 = oracle.quantize_group(x16, bits)
+        for k in (-3, -1, 1, 4):
+            xk = (x16.astype(np.float64) * 2.0 ** k).astype(np.float16)
+            assert np.array_equal(xk.astype(np.float64), x16.astype(np.float64) * 2.0 ** k)
+            ck, sk, zk = oracle.quantize_group(xk, bits)
+            assert np.array_equal(ck, c0)
+            assert oracle.half_to_double(sk) == oracle.half_to_double(s0) * 2.0 ** k
+            assert oracle.half_to_double(zk) == oracle.half_to_double(z0) * 2.0 ** k
+
+
+def test_rotation_spreads_key_outliers():
+    """Tiny workload keys (4 channels x20): quantising in the rotated domain
+    gives a lower reconstruction error than plain min/max RTN of the raw
+    channels at the same bit width."""
+    w = inp.workload("tiny")
+    k, _ = inp.sequence_kv(w, 0, 0, 256)
+    k = k[:, 0, :].numpy()
+    err_rot, err_raw = 0.0, 0.0
+    for t in range(k.shape[0]):
+        x = k[t].astype(np.float64)
+        codes, s, z = oracle.quantize_group(k[t], 4)
+        xr = (H @ _dequant(codes, s, z)) / 128.0
+        err_rot += np.sum((xr - x) ** 2)
+        lo, hi = x.min(), x.max()
+        step = (hi - lo) / 15
+        xq = lo + step * np.clip(np.rint((x - lo) / step), 0, 15)
+        err_raw += np.sum((xq - x) ** 2)
+    assert err_rot < 0.5 * err_raw
+
+
+# --------------------------------------------------------------------------
+# Byte layout
+# --------------------------------------------------------------------------
+
+def test_layout_golden():
+    f = _read_fixture("layout_pattern.txt")
+    off = int(f["off"])
+    region = np.zeros(1664, np.uint8)
+    kc = np.arange(D) % 16
+    vc = np.arange(D) % 4
+    oracle.store_token(region, off, kc, 0x1234, 0x5678, vc, 0x9ABC, 0xDEF0)
+    expect = np.zeros(1664, np.uint8)
+    expect[320:384] = np.frombuffer(bytes.fromhex(f["key_bytes_at_320"]), np.uint8)
+    for w, o in zip(f["value_words"].split(), f["value_word_offsets"].split()):
+        v = int(w, 16)
+        expect[int(o)] = v & 0xFF
+        expect[int(o) + 1] = v >> 8
+    expect[1556:1560] = np.frombuffer(bytes.fromhex(f["key_meta_at_1556"]), np.uint8)
+    expect[1620:1624] = np.frombuffer(bytes.fromhex(f["value_meta_at_1620"]), np.uint8)
+    assert np.array_equal(region, expect)
+
+
+def test_layout_round_trip_and_isolation():
+    rng = np.random.default_rng(40)
+    region = np.full(1664, 0xA5, np.uint8)
+    tokens = {}
+    for off in rng.permutation(16):
+        kc = rng.integers(0, 16, D)
+        vc = rng.integers(0, 4, D)
+        meta = [int(v) for v in rng.integers(0, 65536, 4)]
+        before = region.copy()
+        oracle.store_token(region, int(off), kc, meta[0], meta[1], vc, meta[2], meta[3])
+        changed = np.nonzero(before != region)[0]
+        # a token owns 64 + 32 + 4 + 4 bytes; nothing outside them changes
+        own = set(range(64 * off, 64 * off + 64))
+        g, i = off // 4, off % 4
+        for m in range(16):
+            own |= {1024 + 128 * g + 8 * m + 2 * i, 1024 + 128 * g + 8 * m + 2 * i + 1}
+        own |= set(range(1536 + 4 * off, 1540 + 4 * off)) | set(range(1600 + 4 * off, 1604 + 4 * off))
+        assert set(changed.tolist()) <= own
+        tokens[int(off)] = (kc, meta, vc)
+    for off, (kc, meta, vc) in tokens.items():
+        kc2, ks, kz, vc2, vs, vz = oracle.load_token(region, off)
+        assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
+        assert [ks, kz, vs, vz] == meta
+
+
+# --------------------------------------------------------------------------
+# Append
+# --------------------------------------------------------------------------
+
+def test_append_is_per_token_and_idempotent():
+    w = inp.workload("tiny", context=64)
+    k, v = inp.sequence_kv(w, 0)
+    k, v = k.numpy(), v.numpy()
+    bt, npages = inp.page_table(w)
+    slots = inp.slot_mapping(bt, 0, 0, 64)
+    pool_a = np.full((npages, 1, 1664), 0x5A, np.uint8)
+    oracle.quantize_append(k, v, slots, pool_a)
+    # one token at a time, in reverse order, into a differently-filled pool
+    pool_b = np.full_like(pool_a, 0x00)
+    for t in reversed(range(64)):
+        oracle.quantize_append(k[t:t + 1], v[t:t + 1], slots[t:t + 1], pool_b)
+    assert np.array_equal(pool_a, pool_b)
+    # re-append is idempotent; skipped slots (-1) write nothing
+    snap = pool_a.copy()
+    oracle.quantize_append(k, v, slots, pool_a)
+    assert np.array_equal(pool_a, snap)
+    oracle.quantize_append(k, v, np.full(64, -1, np.int64), pool_a)
+    assert np.array_equal(pool_a, snap)
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+
+def _small_case(num_seqs=2, hq=4, hkv=2, lens=(37, 70), seed=5, on_grid=False, page_perm=None):
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int64)
+    pages = [int(np.ceil(n / 16)) for n in lens]
+    total = sum(pages)
+    perm = rng.permutation(total) if page_perm is None else page_perm
+    bt = np.full((num_seqs, max(pages)), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    pool = np.zeros((total, hkv, 1664), np.uint8)
+    ks, vs = [], []
+    for b in range(num_seqs):
+        n = int(lens[b])
+        if on_grid:
+            k = np.stack([[_on_grid(rng, 15)[0] for _ in range(hkv)] for _ in range(n)])
+            v = np.stack([[_on_grid(rng, 3)[0] for _ in range(hkv)] for _ in range(n)])
+        else:
+            k = rng.standard_normal((n, hkv, D)).astype(np.float16)
+            v = rng.standard_normal((n, hkv, D)).astype(np.float16)
+        oracle.quantize_append(k, v, inp.slot_mapping(bt, b, 0, n), pool)
+        ks.append(k)
+        vs.append(v)
+    q = rng.standard_normal((num_seqs, hq, D)).astype(np.float16)
+    return pool, bt, lens, q, ks, vs
+
+
+def test_attention_on_grid_equals_sdpa_on_originals():
+    """On-grid keys/values survive quantisation exactly, so attention over the
+    quantised cache must equal textbook attention (torch SDPA, fp64) over the
+    original fp16 tensors -- pins dequantisation, un-rotation, page walk and
+    the GQA head mapping."""
+    pool, bt, lens, q, ks, vs = _small_case(on_grid=True, seed=6)
+    scale = 1 / np.sqrt(D)
+    out = oracle.decode_attention(pool, bt, lens, q, scale)
+    G = q.shape[1] // pool.shape[1]
+    for b in range(len(lens)):
+        K = torch.from_numpy(ks[b].astype(np.float64)).permute(1, 0, 2)   # [Hkv][n][D]
+        V = torch.from_numpy(vs[b].astype(np.float64)).permute(1, 0, 2)
+        K = K.repeat_interleave(G, 0).contiguous()
+        V = V.repeat_interleave(G, 0).contiguous()
+        Q = torch.from_numpy(q[b].astype(np.float64))[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[:, 0, :]
+        assert np.max(np.abs(out[b] - ref.numpy())) < 1e-12
+
+
+def test_attention_folded_equals_plain():
+    pool, bt, lens, q, _, _ = _small_case(seed=7, lens=(1, 129))
+    scale = 1 / np.sqrt(D)
+    a = oracle.decode_attention(pool, bt, lens, q, scale)
+    b = oracle.decode_attention_folded(pool, bt, lens, q, scale)
+    assert np.max(np.abs(a - b)) < 1e-9
+
+
+def test_attention_special_cases():
+    pool, bt, lens, q, _, _ = _small_case(seed=8, lens=(1, 50))
+    scale = 1 / np.sqrt(D)
+    out = oracle.decode_attention(pool, bt, lens, q, scale)
+    # n = 1: the output is the single cached value, dequantised and un-rotated
+    _, v0 = oracle.dequant_slot(pool[bt[0, 0], 0], 0)
+    _, v0b = oracle.dequant_slot(pool[bt[0, 0], 1], 0)
+    assert np.allclose(out[0, 0], v0, atol=1e-12) and np.allclose(out[0, 1], v0, atol=1e-12)
+    assert np.allclose(out[0, 2], v0b, atol=1e-12)
+    # q = 0: uniform weights -> mean of the cached values
+    q0 = np.zeros_like(q)
+    out0 = oracle.decode_attention(pool, bt, lens, q0, scale)
+    vals = np.stack([oracle.dequant_slot(pool[bt[1, t // 16], 0], t % 16)[1] for t in range(50)])
+    assert np.allclose(out0[1, 0], vals.mean(0), atol=1e-12)
+    # output is a convex combination of the cached values
+    assert np.all(out[1, 0] <= vals.max(0) + 1e-12) and np.all(out[1, 0] >= vals.min(0) - 1e-12)
+    # a very large scale makes the softmax hard: output -> value of the best key
+    keys = np.stack([oracle.dequant_slot(pool[bt[1, t // 16], 0], t % 16)[0] for t in range(50)])
+    logits = keys @ q[1, 0].astype(np.float64)
+    best = np.argsort(logits)[-2:]
+    if logits[best[1]] - logits[best[0]] > 1e-3:
+        hard = oracle.decode_attention(pool, bt, lens, q, 1e5)
+        assert np.allclose(hard[1, 0], vals[best[1]], atol=1e-9)
+
+
+def test_attention_identical_tokens_give_that_value():
+    rng = np.random.default_rng(9)
+    n = 40
+    k1 = rng.standard_normal((1, 1, D)).astype(np.float16)
+    v1 = rng.standard_normal((1, 1, D)).astype(np.float16)
+    k = np.repeat(k1, n, 0)
+    v = np.repeat(v1, n, 0)
+    bt = np.array([[2, 0, 1]], np.int32)
+    pool = np.zeros((3, 1, 1664), np.uint8)
+    oracle.quantize_append(k, v, inp.slot_mapping(bt, 0, 0, n), pool)
+    q = rng.standard_normal((1, 1, D)).astype(np.float16)
+    out = oracle.decode_attention(pool, bt, np.array([n]), q, 0.1)
+    _, vd = oracle.dequant_slot(pool[2, 0], 0)
+    assert np.allclose(out[0, 0], vd, atol=1e-12)
+
+
+def test_attention_invariant_to_physical_page_placement():
+    a = _small_case(seed=11, page_perm=np.arange(8))
+    b = _small_case(seed=11, page_perm=np.array([5, 3, 7, 0, 6, 1, 4, 2]))
+    scale = 1 / np.sqrt(D)
+    oa = oracle.decode_attention(a[0], a[1], a[2], a[3], scale)
+    ob = oracle.decode_attention(b[0], b[1], b[2], b[3], scale)
+    assert np.array_equal(oa, ob)
