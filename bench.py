@@ -1,0 +1,252 @@
+"""Benchmark: K4V2 g128 quantize-append + scale-folded paged decode attention.
+
+One step = quantise-append of the new token of every sequence, then one decode
+step of attention over the packed cache (every row of the hot path), on the
+Qwen3-32B-shaped workload: 8 sequences x 16384 cached tokens (+1 appended),
+64 query / 8 KV heads, head_dim 128, 16-token pages in a random block table.
+Synthetic seeded inputs (kvq_inputs); no model weights or datasets.
+
+Timing: inputs resident in HBM; W untimed warm-up steps, then K timed steps
+bracketed by torch.cuda.synchronize().  Each step runs on the next of R
+copies of the pool (R x 109 MB, more than the 256 MB Infinity Cache), so
+every decode reads its 109 MB from HBM.  The decode kernel is timed with HIP
+events on the stream it runs on, inside the timed region.
+
+Prints one JSON line.  N > 1 GPUs is not supported: this build measures one
+GPU's share (see the design notes for how the path shards).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "K4V2 decode-attention KV GB/s and % of HBM peak; quantize-append tokens/s"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+KV_BYTES_PER_TOKEN_HEAD = 104
+APPEND_BYTES_PER_TOKEN_HEAD = 512 + 104
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=6, help="pool copies cycled to defeat the Infinity Cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=8, help="(sequence, KV head) groups in the CPU sample")
+    ap.add_argument("--no-append-bench", action="store_true")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    return ap.parse_args()
+
+
+class DecodeCall:
+    """Pre-marshalled C-ABI calls (one ctypes call per kernel launch)."""
+
+    def __init__(self, kvq, lib, fmt, stream_ptr):
+        self.kvq, self.lib, self.fmt, self.stream = kvq, lib, ctypes.byref(fmt), ctypes.c_void_p(stream_ptr)
+
+    def append_args(self, k, v, slots, cache):
+        P = ctypes.c_void_p
+        return (self.fmt, P(k.data_ptr()), P(v.data_ptr()), ctypes.c_int64(k.stride(0)),
+                ctypes.c_int64(v.stride(0)), P(slots.data_ptr()), ctypes.c_int64(k.shape[0]),
+                ctypes.c_int32(k.shape[1]), P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]), self.stream)
+
+    def decode_args(self, out, q, cache, bt, lens, max_len, ws, pps):
+        P = ctypes.c_void_p
+        return (self.fmt, P(out.data_ptr()), 0 if out.dtype.itemsize == 2 else 1, P(q.data_ptr()),
+                P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]), P(bt.data_ptr()),
+                ctypes.c_int32(bt.shape[1]), P(lens.data_ptr()), ctypes.c_int32(q.shape[0]),
+                ctypes.c_int32(q.shape[1]), ctypes.c_int32(cache.shape[1]), ctypes.c_int32(max_len),
+                ctypes.c_float(1.0 / math.sqrt(128)), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                ctypes.c_int32(pps), self.stream)
+
+
+def cpu_baseline(w, groups: int):
+    """The oracle (plain C, one thread) on a bounded sample of the same
+    workload: `groups` (sequence 0, KV head) groups, each the quantise-append
+    of 16385 tokens and the decode of its 8 query heads."""
+    import numpy as np
+    import kvq_inputs as inp
+    import oracle
+    n = int(inp.final_lens(w)[0])
+    pages = -(-n // 16)
+    k, v = inp.sequence_kv(w, 0, 0, n)
+    q = inp.queries(w).numpy()
+    t_app = t_dec = 0.0
+    for h in range(groups):
+        pool = np.zeros((pages, 1, 1664), np.uint8)
+        kh, vh = k[:, h:h + 1].numpy(), v[:, h:h + 1].numpy()
+        t0 = time.perf_counter()
+        oracle.quantize_append(kh, vh, np.arange(n, dtype=np.int64), pool)
+        t1 = time.perf_counter()
+        oracle.decode_attention(pool, np.arange(pages, dtype=np.int32)[None], np.array([n]),
+                                q[0:1, h * w.gqa:(h + 1) * w.gqa], 1 / math.sqrt(128))
+        t2 = time.perf_counter()
+        t_app += t1 - t0
+        t_dec += t2 - t1
+    kv_bytes = groups * n * KV_BYTES_PER_TOKEN_HEAD
+    return {
+        "value": kv_bytes / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{groups} (sequence, KV head) groups of qwen3_32b_16k: {n} tokens each, "
+                  f"decode of {w.gqa} query heads per group (fp64 plain definition)",
+        "seconds": round(t_app + t_dec, 2),
+        "append_tokens_per_s": groups * n / t_app / w.num_kv_heads,
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_threads_available": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path "
+              "shards by (sequence, KV head) with no exchange, see the design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import kvq_inputs as inp
+    import quantized_decode_attention_quantize_amd as kvq
+
+    dev = torch.device("cuda:0")
+    lib = kvq.load()
+    fmt = kvq.format_from_string("kvarn_k4v2_g128")
+    stream = torch.cuda.current_stream()
+    call = DecodeCall(kvq, lib, fmt, stream.cuda_stream)
+
+    w = inp.workload("qwen3_32b_16k")
+    B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    ctx = w.context
+    n = ctx + 1
+    bt_np, num_pages = inp.page_table(w)
+    bt = torch.from_numpy(bt_np).to(dev)
+    lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+
+    # fill one pool with the 16384 cached tokens of every sequence, then copy it
+    base = torch.zeros((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, 0, ctx, device=dev)
+        kvq.quantize_append(k, v, torch.from_numpy(inp.slot_mapping(bt_np, b, 0, ctx)).to(dev), base)
+    pools = [base] + [base.clone() for _ in range(args.replicas - 1)]
+    new_k, new_v, slots = [], [], []
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, ctx, 1, device=dev)
+        new_k.append(k)
+        new_v.append(v)
+        slots.append(inp.slot_mapping(bt_np, b, ctx, 1))
+    new_k = torch.cat(new_k).contiguous()
+    new_v = torch.cat(new_v).contiguous()
+    slots = torch.from_numpy(np.concatenate(slots)).to(dev)
+    q = inp.queries(w, 0, device=dev).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    pps = args.pages_per_split
+    ws = kvq.alloc_workspace(B, Hq, Hkv, n, pps)
+    torch.cuda.synchronize()
+
+    app_args = [call.append_args(new_k, new_v, slots, p) for p in pools]
+    dec_args = [call.decode_args(out, q, p, bt, lens, n, ws, pps) for p in pools]
+    append_fn, decode_fn = lib.kvq_quantize_append, lib.kvq_decode_attention_ex
+
+    def step(i, ev=None):
+        r = i % len(pools)
+        st = append_fn(*app_args[r])
+        if ev is not None:
+            ev[0].record(stream)
+        st |= decode_fn(*dec_args[r])
+        if ev is not None:
+            ev[1].record(stream)
+        return st
+
+    for i in range(args.warmup):
+        if step(i):
+            raise RuntimeError("kvq call failed during warm-up")
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    bad = 0
+    for i in range(args.steps):
+        bad |= step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if bad:
+        raise RuntimeError("kvq call failed in the timed region")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded kvq_inputs; no model weights)",
+        "config": {"workload": "qwen3_32b_16k", "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": 128, "context": n, "page": 16, "format": "kvq-k4v2-g128 v1",
+                   "step": "append 1 token/seq + decode", "pool_replicas": len(pools),
+                   "pages_per_split": pps or kvq.decode_pages_per_split(B, Hq, Hkv, n)},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_kernel_ms": round(dec_avg_ms, 5),
+        "decode_kernel_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 5),
+                                     round(float(np.percentile(dec_ms, 90)), 5)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "bytes_per_launch": kv_bytes},
+    }
+
+    if not args.no_append_bench:
+        result.update(append_bench(torch, inp, kvq, call, dev))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_groups)
+
+    print(json.dumps(result), flush=True)
+
+
+def append_bench(torch, inp, kvq, call, dev):
+    """Bulk quantise-append of the Llama-3.1-70B-shaped 131072-token prompt
+    (8 KV heads) in one call; tokens/s of the prompt, timed with HIP events."""
+    import numpy as np
+    w = inp.workload("llama31_70b_128k")
+    T = w.context
+    bt_np, num_pages = inp.page_table(w)
+    k, v = inp.sequence_kv(w, 0, 0, T, device=dev)
+    slots = torch.from_numpy(inp.slot_mapping(bt_np, 0, 0, T)).to(dev)
+    cache = torch.zeros((num_pages, w.num_kv_heads, 1664), dtype=torch.uint8, device=dev)
+    args = call.append_args(k, v, slots, cache)
+    fn = kvq.load().kvq_quantize_append
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn(*args)
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn(*args)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    moved = T * w.num_kv_heads * APPEND_BYTES_PER_TOKEN_HEAD
+    return {"append_tokens_per_s": round(T / (ms * 1e-3), 1),
+            "append_config": {"workload": "llama31_70b_128k prefill", "tokens": T,
+                              "num_kv_heads": w.num_kv_heads, "kernel_ms": round(ms, 5),
+                              "GBps": round(moved / (ms * 1e-3) / 1e9, 2),
+                              "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}}
+
+
+if __name__ == "__main__":
+    main()

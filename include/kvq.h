@@ -1,0 +1,192 @@
+/*
+ * kvq.h -- C ABI of libkvq: K4V2 group-128 quantised paged KV cache for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Two operations on a paged KV cache:
+ *   kvq_quantize_append   quantise-on-write of new key/value tokens
+ *   kvq_decode_attention  one decode step of attention over the packed cache
+ *
+ * The method is the KVarN write/read path described on these web pages:
+ *   [KVARN-HN] beyondheadline.xyz, "Huawei's KV-cache trick: FP16 accuracy, a
+ *              four-times-larger cache and higher throughput at once" -- lede
+ *              and section "The claim that breaks the usual trade-off"
+ *              (4-bit keys, 2-bit values, Hadamard rotation, variance
+ *              normalisation, asymmetric low-bit quantisation of cache blocks;
+ *              one preset flag, kvarn_k4v2_g128; no calibration, no model
+ *              edits).
+ *   [KVARN-P]  dothoosh.com, "KVarN vs TurboQuant: 5x more context with higher
+ *              accuracy" -- the four-stage pipeline list (Hadamard rotation;
+ *              variance normalisation; asymmetric round-to-nearest; scale
+ *              folding on read-back) and the preset kv_cache_dtype string.
+ *
+ * Cache format "kvq-k4v2-g128 v1" (the pages fix no numbers; this library
+ * fixes them):
+ *   - head_dim = group = 128: one group per token per KV head;
+ *   - rotation: unnormalised Sylvester Hadamard H (H_ij = (-1)^popcount(i&j)),
+ *     computed as an fp32 fast Walsh-Hadamard transform with butterfly stages
+ *     h = 1, 2, ..., 64;
+ *   - variance normalisation: divide by the group RMS sigma = sqrt(sum y^2 /
+ *     128) (pairwise sum, fixed tree), folded back into the stored metadata;
+ *   - asymmetric round-to-nearest-even on the group's [min, max]: keys to
+ *     4 bits (0..15), values to 2 bits (0..3); fp16 scale s and zero z, so
+ *     that a rotated value is s * code + z and the original is H (s c + z) / 128;
+ *   - pages of 16 tokens; the pool is u8 [num_pages][num_kv_heads][1664],
+ *     one 1664-byte region per (page, KV head):
+ *       [0, 1024)     key codes, token o at 64*o, byte b = c[2b] | c[2b+1] << 4
+ *       [1024, 1536)  value codes, token o (quad g = o/4, slot i = o%4): for
+ *                     m = 0..15 the little-endian u16 at 1024 + 128g + 8m + 2i
+ *                     holds the code of channel 16j + m in bits 2j..2j+1
+ *       [1536, 1600)  key (s, z) fp16 pairs, token o at 1536 + 4*o
+ *       [1600, 1664)  value (s, z) fp16 pairs, token o at 1600 + 4*o
+ *     104 bytes per token per KV head (fp16: 512 bytes).
+ *
+ * Conventions for every call:
+ *   - All buffers are owned by the caller.  The library never allocates,
+ *     frees or synchronises device memory and keeps no global mutable state
+ *     besides a thread-local last HIP error.
+ *   - Pointers marked (device) are device pointers; (host) are host pointers.
+ *     fp16 values are passed as their uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Work is enqueued
+ *     and the call returns without waiting.
+ *   - Host-visible arguments are validated before anything is launched; a
+ *     failed check returns a status and launches nothing.  Device-resident
+ *     data (slot mappings, block tables, sequence lengths) are preconditions
+ *     the host cannot read: slots and page ids outside the pool are skipped by
+ *     the kernels (never written or read), other violations give undefined
+ *     results.
+ *   - A launch failure returns KVQ_ERR_HIP; kvq_last_hip_error() gives the
+ *     hipError_t code.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = 1,         /* a required pointer is NULL                    */
+    KVQ_ERR_SHAPE = 2,        /* a size is out of range or inconsistent        */
+    KVQ_ERR_UNSUPPORTED = 3,  /* format/preset other than k4v2_g128 v1         */
+    KVQ_ERR_ALIGN = 4,        /* a device pointer is not suitably aligned      */
+    KVQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required    */
+    KVQ_ERR_HIP = 6           /* the HIP runtime reported an error             */
+} kvq_status;
+
+/* Format descriptor.  v1 supports exactly {128, 128, 4, 2, 16}. */
+typedef struct kvq_format {
+    int32_t head_dim;    /* channels per head                    */
+    int32_t group_size;  /* channels per quantisation group      */
+    int32_t k_bits;      /* key code width                       */
+    int32_t v_bits;      /* value code width                     */
+    int32_t block_size;  /* tokens per page                      */
+} kvq_format;
+
+typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
+
+/* Parse a preset name ([KVARN-HN] flag value; [KVARN-P] kv_cache_dtype string).
+ * Accepts "k4v2_g128" and "kvarn_k4v2_g128".  preset, out: (host).
+ * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
+kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
+
+/* Bytes of one (page, KV head) region: 1664 for v1; 0 for an unsupported
+ * format or NULL. */
+size_t kvq_page_bytes(const kvq_format *fmt);
+
+/* Bytes of a pool of num_pages pages and num_kv_heads heads; 0 on invalid input. */
+size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_heads);
+
+/*
+ * Quantise-on-write [KVARN-HN; KVARN-P stages 1-3].
+ *   key, value        (device) fp16 [num_tokens][num_kv_heads][128]; token
+ *                     strides in elements (>= num_kv_heads*128), head stride
+ *                     128; 16-byte aligned; token strides multiples of 8.
+ *   slot_mapping      (device) int64 [num_tokens]; slot = page*16 + offset.
+ *                     A negative slot skips the token; a slot whose page is
+ *                     >= num_pages is skipped.  Slots must be distinct.
+ *   cache             (device) u8 pool [num_pages][num_kv_heads][1664],
+ *                     16-byte aligned.  Only the addressed token slots change.
+ * The codes depend only on the token's own 128 values (no calibration), so
+ * appends are order-independent and idempotent.
+ * num_tokens == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_quantize_append(const kvq_format *fmt,
+                               const uint16_t *key, const uint16_t *value,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               const int64_t *slot_mapping, int64_t num_tokens,
+                               int32_t num_kv_heads, uint8_t *cache, int64_t num_pages,
+                               void *stream);
+
+/* Workspace bytes kvq_decode_attention needs for these sizes (0 on invalid
+ * input).  pages_per_split = 0 selects the library's split heuristic; a
+ * positive value forces that many pages per split (see _ex below). */
+size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t pages_per_split);
+
+/*
+ * One decode step of attention over the quantised cache, read with scale
+ * folding [KVARN-P stage 4]: the key rotation is moved onto the query
+ * (H is symmetric), (s, z) are applied inside the dot products, the softmax
+ * runs online in fp32 in base 2, and a single Hadamard transform restores the
+ * output.  Mathematically equal to
+ *     out[b][hq] = sum_t softmax_t(softmax_scale * q . k_t) v_t,
+ * with k_t, v_t the dequantised, un-rotated cache entries of tokens
+ * t < seq_lens[b] and KV head hq / (num_q_heads / num_kv_heads).
+ *   out             (device) [num_seqs][num_q_heads][128], fp16 or fp32.
+ *   query           (device) fp16 [num_seqs][num_q_heads][128], contiguous.
+ *   cache           (device) pool as above.
+ *   block_tables    (device) int32 [num_seqs][max_pages_per_seq]; entry i of
+ *                   row b is the page holding tokens 16i..16i+15 of sequence b.
+ *                   Only entries i < ceil(seq_lens[b]/16) are read; a page id
+ *                   outside [0, num_pages) is treated as an empty page.
+ *   seq_lens        (device) int32 [num_seqs], each in [1, max_seq_len]
+ *                   (a zero length yields a zero output row).
+ *   max_seq_len     host-side bound on seq_lens, <= max_pages_per_seq*16.
+ *   workspace       (device) >= kvq_decode_workspace_bytes(...) bytes,
+ *                   16-byte aligned, ZERO-FILLED before its first use; every
+ *                   call returns its counters to zero.  Calls that share a
+ *                   workspace must not overlap in time.
+ * Returns KVQ_ERR_SHAPE when num_q_heads % num_kv_heads != 0 or a size is
+ * non-positive, KVQ_ERR_WORKSPACE when workspace_bytes is too small.
+ */
+kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                const uint16_t *query, const uint8_t *cache, int64_t num_pages,
+                                const int32_t *block_tables, int32_t max_pages_per_seq,
+                                const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* As kvq_decode_attention, with the split-K granularity forced to
+ * pages_per_split pages (> 0, a multiple of 2) per work-group instead of the
+ * heuristic.  The workspace must be sized with the same pages_per_split. */
+kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                   const uint16_t *query, const uint8_t *cache, int64_t num_pages,
+                                   const int32_t *block_tables, int32_t max_pages_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                   void *workspace, size_t workspace_bytes,
+                                   int32_t pages_per_split, void *stream);
+
+/* Pages per split the heuristic picks for these sizes (0 on invalid input). */
+int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_seq_len);
+
+/* Static description of a status code (never NULL). */
+const char *kvq_status_string(kvq_status status);
+
+/* hipError_t of the last KVQ_ERR_HIP returned on this thread (0 if none). */
+int kvq_last_hip_error(void);
+
+/* Library version string, e.g. "kvq 1.0 (kvq-k4v2-g128 v1, gfx950)". */
+const char *kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

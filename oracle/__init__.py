@@ -66,6 +66,10 @@ def _load():
     lib.kvqo_quantize_append.restype = ctypes.c_int
     lib.kvqo_dequant_slot.argtypes = [P, ctypes.c_int, P, P]
     lib.kvqo_dequant_slot.restype = None
+    lib.kvqo_dequant_slot_rotated.argtypes = [P, ctypes.c_int, P, P]
+    lib.kvqo_dequant_slot_rotated.restype = None
+    lib.kvqo_quantize_group_mode.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
+    lib.kvqo_quantize_group_mode.restype = None
     lib.kvqo_decode_attention.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
                                           ctypes.c_double, P, P]
     lib.kvqo_decode_attention.restype = ctypes.c_int
@@ -110,15 +114,27 @@ def hadamard_matvec_f64(x: np.ndarray) -> np.ndarray:
     return y
 
 
-def quantize_group(x_f16: np.ndarray, bits: int):
-    """x_f16: 128 float16 values.  Returns (codes uint8[128], s_bits, z_bits)."""
+def quantize_group(x_f16: np.ndarray, bits: int, offset_mode: int | None = None):
+    """x_f16: 128 float16 values.  Returns (codes uint8[128], s_bits, offset_bits);
+    the offset is the zero z (keys, offset_mode 0) or the group mean mu
+    (values, offset_mode 1).  By default 4-bit groups are keys, 2-bit values."""
     x = _c(x_f16, np.float16).view(np.uint16)
     assert x.shape == (D,)
+    if offset_mode is None:
+        offset_mode = 1 if bits == 2 else 0
     codes = np.empty(D, np.uint8)
     s = np.zeros(1, np.uint16)
     z = np.zeros(1, np.uint16)
-    _load().kvqo_quantize_group(_ptr(x), int(bits), _ptr(codes), _ptr(s), _ptr(z))
+    _load().kvqo_quantize_group_mode(_ptr(x), int(bits), int(offset_mode), _ptr(codes), _ptr(s), _ptr(z))
     return codes, int(s[0]), int(z[0])
+
+
+def group_zero(codes: np.ndarray, s_bits: int, off_bits: int, is_value: bool) -> float:
+    """Rotated-domain zero-point of a group: z (keys) or mu - s*C/128 (values)."""
+    off = half_to_double(off_bits)
+    if not is_value:
+        return off
+    return off - half_to_double(s_bits) * int(np.sum(codes, dtype=np.int64)) / 128.0
 
 
 def store_token(region: np.ndarray, off: int, kc, ks, kz, vc, vs, vz):
@@ -158,6 +174,14 @@ def dequant_slot(region: np.ndarray, off: int):
     k = np.empty(D, np.float64)
     v = np.empty(D, np.float64)
     _load().kvqo_dequant_slot(_ptr(r), int(off), _ptr(k), _ptr(v))
+    return k, v
+
+
+def dequant_slot_rotated(region: np.ndarray, off: int):
+    r = _c(region, np.uint8)
+    k = np.empty(D, np.float64)
+    v = np.empty(D, np.float64)
+    _load().kvqo_dequant_slot_rotated(_ptr(r), int(off), _ptr(k), _ptr(v))
     return k, v
 
 

@@ -135,8 +135,8 @@ void kvqo_hadamard_matvec_f64(const double *x, double *y)
 
 /*
  * Quantise one group of 128 fp16 values to `bits`-bit codes (4 for keys, 2
- * for values) with an fp16 scale s and zero z, following the pipeline order
- * of [KVARN-P] (stages 1-3) and [KVARN-HN]:
+ * for values) with an fp16 scale s and an fp16 offset, following the pipeline
+ * order of [KVARN-P] (stages 1-3) and [KVARN-HN]:
  *
  *   1. Hadamard rotation [KVARN-P stage 1]: y = H x by the fp32 FWHT above.
  *   2. Variance normalisation [KVARN-P stage 2, KVARN-HN]: read here as the
@@ -148,12 +148,21 @@ void kvqo_hadamard_matvec_f64(const double *x, double *y)
  *      L = 2^bits - 1.  If M == m every code is 0 and the step is 0.
  *      Otherwise delta = (M - m) / L, inv = L / (M - m) and
  *      c_i = min(L, rint((yh_i - m) * inv)), ties to even.
- *   4. The normalisation is folded back into the stored metadata:
- *      s = fp16(delta * sigma), z = fp16(m * sigma), so that the rotated
- *      value is recovered as s * c + z.  A zero z is stored as +0.
+ *   4. The normalisation is folded back into the stored metadata, s =
+ *      fp16(delta * sigma), and one offset:
+ *        keys   (offset_mode 0): the zero z = fp16(m * sigma); the rotated
+ *               value is s * c + z;
+ *        values (offset_mode 1): the group mean mu = fp16(sigma * (m + delta
+ *               * C / 128)), C = sum of the 128 codes (the fp32 product delta*C
+ *               is scaled by the exact 2^-7, then m is added); the rotated
+ *               value is s * c + (mu - s * C / 128).
+ *      mu is the dequantised group's mean in the rotated domain, which is
+ *      the dequantised original channel 0 (H 1 = 128 e_0); storing it
+ *      instead of z keeps channel 0 free of the cancellation between s*C and
+ *      128*z.  A zero offset is stored as +0.
  */
-void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
-                         uint16_t *s_out, uint16_t *z_out)
+void kvqo_quantize_group_mode(const uint16_t *x, int bits, int offset_mode, uint8_t *codes,
+                              uint16_t *s_out, uint16_t *z_out)
 {
     float y[KVQO_D], p[KVQO_D];
     for (int i = 0; i < KVQO_D; i++)
@@ -203,8 +212,25 @@ void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
 
     /* 4. metadata */
     *s_out = kvqo_float_to_half(delta * sigma);
-    uint16_t z = kvqo_float_to_half(m * sigma);
+    uint16_t z;
+    if (offset_mode == 0) {
+        z = kvqo_float_to_half(m * sigma);
+    } else {
+        int csum = 0;
+        for (int i = 0; i < KVQO_D; i++) csum += codes[i];
+        float t = delta * (float)csum;
+        t = t * 0x1p-7f;
+        t = m + t;
+        z = kvqo_float_to_half(t * sigma);
+    }
     *z_out = (z == 0x8000) ? 0 : z;
+}
+
+/* Keys: offset_mode 0 (zero z); values: offset_mode 1 (group mean). */
+void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
+                         uint16_t *s_out, uint16_t *z_out)
+{
+    kvqo_quantize_group_mode(x, bits, bits == 2 ? 1 : 0, codes, s_out, z_out);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -308,12 +334,23 @@ int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
 /* Decode attention over the quantised paged cache.                          */
 /* ------------------------------------------------------------------------ */
 
+/* Zero-point of a group in the rotated domain: z itself for keys; for values
+ * z = mu - s * C / 128 (exact in double: C <= 384). */
+static double group_zero(const uint8_t *codes, uint16_t s16, uint16_t off16, int is_value)
+{
+    double off = kvqo_half_to_double(off16);
+    if (!is_value) return off;
+    int csum = 0;
+    for (int i = 0; i < KVQO_D; i++) csum += codes[i];
+    return off - kvqo_half_to_double(s16) * csum / 128.0;
+}
+
 /* Dequantise one cached token back to the original (un-rotated) domain:
  * rotated value yt_i = s*c_i + z; original value = H yt / 128 (H H = 128 I). */
-static void dequant_unrotate(const uint8_t *codes, uint16_t s16, uint16_t z16, double *out)
+static void dequant_unrotate(const uint8_t *codes, uint16_t s16, uint16_t z16, int is_value, double *out)
 {
     double yt[KVQO_D];
-    double s = kvqo_half_to_double(s16), z = kvqo_half_to_double(z16);
+    double s = kvqo_half_to_double(s16), z = group_zero(codes, s16, z16, is_value);
     for (int i = 0; i < KVQO_D; i++)
         yt[i] = s * codes[i] + z;
     kvqo_hadamard_matvec_f64(yt, out);
@@ -327,8 +364,21 @@ void kvqo_dequant_slot(const uint8_t *region, int off, double *k_out, double *v_
     uint8_t kc[KVQO_D], vc[KVQO_D];
     uint16_t ks, kz, vs, vz;
     kvqo_load_token(region, off, kc, &ks, &kz, vc, &vs, &vz);
-    dequant_unrotate(kc, ks, kz, k_out);
-    dequant_unrotate(vc, vs, vz, v_out);
+    dequant_unrotate(kc, ks, kz, 0, k_out);
+    dequant_unrotate(vc, vs, vz, 1, v_out);
+}
+
+/* Rotated-domain dequantised values of one slot (s*c + z per channel). */
+void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, double *v_out)
+{
+    uint8_t kc[KVQO_D], vc[KVQO_D];
+    uint16_t ks, kz, vs, vz;
+    kvqo_load_token(region, off, kc, &ks, &kz, vc, &vs, &vz);
+    double kzero = group_zero(kc, ks, kz, 0), vzero = group_zero(vc, vs, vz, 1);
+    for (int i = 0; i < KVQO_D; i++) {
+        k_out[i] = kvqo_half_to_double(ks) * kc[i] + kzero;
+        v_out[i] = kvqo_half_to_double(vs) * vc[i] + vzero;
+    }
 }
 
 /*
@@ -401,9 +451,10 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
  * The same step reached by scale folding on read-back [KVARN-P stage 4], in
  * fp64: never materialise k_t or v_t.  With q' = H q (H symmetric):
  *     q . k_t   = (q' . (s c_t + z 1)) / 128 = (s (q' . c_t) + z sum(q')) / 128
- *     sum_t p_t v_t = H (acc + zacc 1) / 128,  acc = sum_t p_t s_t c_t,
- *                                            zacc = sum_t p_t z_t,
- *     and H 1 = 128 e_0, so the value zero-points reach output channel 0 only.
+ *     sum_t p_t v_t = H (acc + zv 1) / 128,  acc = sum_t p_t s_t c_t,
+ *                                          zv = sum_t p_t z_t,
+ *     and H 1 = 128 e_0, so the value zero-points reach output channel 0
+ *     only; there (H acc)_0 + 128 zv = 128 sum_t p_t mu_t, the stored means.
  * Exists to pin this algebra against the plain definition above.
  */
 int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
@@ -447,14 +498,15 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
                 double p = exp(lg[t] - mx);
                 double sv = kvqo_half_to_double(vs);
                 l += p;
-                zacc += p * kvqo_half_to_double(vz);
+                zacc += p * kvqo_half_to_double(vz);      /* value mean mu */
                 for (int i = 0; i < KVQO_D; i++) acc[i] += p * sv * vc[i];
             }
             double o[KVQO_D];
             kvqo_hadamard_matvec_f64(acc, o);
             double *dst = out + ((int64_t)b * num_q_heads + hq) * KVQO_D;
             for (int i = 0; i < KVQO_D; i++) dst[i] = o[i] / (128.0 * l);
-            dst[0] += zacc / l;
+            /* channel 0: (H acc)_0 + 128 sum p z = sum p (s C + 128 (mu - s C/128)) */
+            dst[0] = zacc / l;
         }
         free(lg);
     }

@@ -1,0 +1,223 @@
+"""kvq: K4V2 group-128 quantised paged KV cache for AMD Instinct MI355X.
+
+A thin ctypes binding over ``libkvq.so`` (hand-written HIP kernels for gfx950,
+C ABI declared in ``include/kvq.h``).  The binding only marshals arguments:
+every step of quantise-append and decode attention runs in the library's
+kernels.  PyTorch provides device memory and streams.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+Names follow the C ABI: ``quantize_append`` and ``decode_attention``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "KvqError", "Format", "load", "library_path", "format_from_string", "page_bytes",
+    "cache_bytes", "alloc_cache", "quantize_append", "decode_workspace_bytes",
+    "decode_pages_per_split", "alloc_workspace", "decode_attention", "version",
+    "HEAD_DIM", "PAGE", "REGION_BYTES",
+]
+
+HEAD_DIM = 128
+PAGE = 16
+REGION_BYTES = 1664
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvq.so")
+_lib = None
+
+KVQ_OK = 0
+_STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_SHAPE", 3: "KVQ_ERR_UNSUPPORTED",
+           4: "KVQ_ERR_ALIGN", 5: "KVQ_ERR_WORKSPACE", 6: "KVQ_ERR_HIP"}
+OUT_F16, OUT_F32 = 0, 1
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {_STATUS.get(status, status)}"
+        if hip_error:
+            msg += f" (hipError {hip_error})"
+        super().__init__(msg)
+
+
+class Format(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkvq.so (built in-tree by ``build.py``).  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libkvq.so not found at {_LIB_PATH}; build it with "
+                           "`python -m quantized_decode_attention_quantize_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    FP = ctypes.POINTER(Format)
+    sigs = {
+        "kvq_format_from_string": (ctypes.c_int, [ctypes.c_char_p, FP]),
+        "kvq_page_bytes": (sz, [FP]),
+        "kvq_cache_bytes": (sz, [FP, i64, i32]),
+        "kvq_quantize_append": (ctypes.c_int, [FP, P, P, i64, i64, P, i64, i32, P, i64, P]),
+        "kvq_decode_workspace_bytes": (sz, [FP, i32, i32, i32, i32, i32]),
+        "kvq_decode_pages_per_split": (i32, [i32, i32, i32, i32]),
+        "kvq_decode_attention": (ctypes.c_int, [FP, P, ctypes.c_int, P, P, i64, P, i32, P, i32, i32,
+                                                i32, i32, ctypes.c_float, P, sz, P]),
+        "kvq_decode_attention_ex": (ctypes.c_int, [FP, P, ctypes.c_int, P, P, i64, P, i32, P, i32,
+                                                   i32, i32, i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvq_last_hip_error": (ctypes.c_int, []),
+        "kvq_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != KVQ_OK:
+        lib = load()
+        raise KvqError(status, what, lib.kvq_last_hip_error() if status == 6 else 0)
+
+
+def version() -> str:
+    return load().kvq_version().decode()
+
+
+def format_from_string(preset: str = "kvarn_k4v2_g128") -> Format:
+    f = Format()
+    _check(load().kvq_format_from_string(preset.encode(), ctypes.byref(f)), "format_from_string")
+    return f
+
+
+_V1 = None
+
+
+def _fmt(fmt: Format | None) -> Format:
+    global _V1
+    if fmt is not None:
+        return fmt
+    if _V1 is None:
+        _V1 = format_from_string("k4v2_g128")
+    return _V1
+
+
+def page_bytes(fmt: Format | None = None) -> int:
+    return int(load().kvq_page_bytes(ctypes.byref(_fmt(fmt))))
+
+
+def cache_bytes(num_pages: int, num_kv_heads: int, fmt: Format | None = None) -> int:
+    return int(load().kvq_cache_bytes(ctypes.byref(_fmt(fmt)), num_pages, num_kv_heads))
+
+
+def alloc_cache(num_pages: int, num_kv_heads: int, device="cuda") -> torch.Tensor:
+    """Uninitialised pool u8 [num_pages][num_kv_heads][1664]."""
+    return torch.empty((num_pages, num_kv_heads, REGION_BYTES), dtype=torch.uint8, device=device)
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def quantize_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                    cache: torch.Tensor, stream=None, fmt: Format | None = None) -> None:
+    """Quantise fp16 key/value [T][num_kv_heads][128] into the pool at the given
+    slots (int64 [T]; page*16 + offset; negative = skip)."""
+    if key.dtype != torch.float16 or value.dtype != torch.float16:
+        raise TypeError("key/value must be float16")
+    if slot_mapping.dtype != torch.int64 or cache.dtype != torch.uint8:
+        raise TypeError("slot_mapping must be int64 and cache uint8")
+    if key.dim() != 3 or key.shape != value.shape or key.shape[2] != HEAD_DIM:
+        raise ValueError("key/value must be [T][num_kv_heads][128] with equal shapes")
+    T, H, _ = key.shape
+    for t in (key, value):
+        if t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+            raise ValueError("key/value heads must be contiguous 128-element rows")
+    if cache.dim() != 3 or cache.shape[1] != H or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
+    if not slot_mapping.is_contiguous() or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be a contiguous int64 vector of length T")
+    st = load().kvq_quantize_append(ctypes.byref(_fmt(fmt)), _ptr(key), _ptr(value), key.stride(0),
+                                    value.stride(0), _ptr(slot_mapping), T, H, _ptr(cache),
+                                    cache.shape[0], _stream_ptr(stream))
+    _check(st, "kvq_quantize_append")
+
+
+def decode_pages_per_split(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int) -> int:
+    return int(load().kvq_decode_pages_per_split(num_seqs, num_q_heads, num_kv_heads, max_seq_len))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                           pages_per_split: int = 0, fmt: Format | None = None) -> int:
+    n = load().kvq_decode_workspace_bytes(ctypes.byref(_fmt(fmt)), num_seqs, num_q_heads,
+                                          num_kv_heads, max_seq_len, pages_per_split)
+    if n == 0:
+        raise KvqError(2, "kvq_decode_workspace_bytes")
+    return int(n)
+
+
+def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                    pages_per_split: int = 0, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace (the decode kernel requires zeroed counters on
+    first use and leaves them zero)."""
+    n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pages_per_split)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
+                     seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float | None = None,
+                     out: torch.Tensor | None = None, out_dtype=torch.float32,
+                     workspace: torch.Tensor | None = None, pages_per_split: int = 0,
+                     stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """One decode step: query fp16 [B][Hq][128] against the pool; returns
+    out [B][Hq][128] (fp32 or fp16)."""
+    if query.dtype != torch.float16 or query.dim() != 3 or query.shape[2] != HEAD_DIM:
+        raise ValueError("query must be float16 [B][Hq][128]")
+    if not query.is_contiguous():
+        raise ValueError("query must be contiguous")
+    B, Hq, _ = query.shape
+    if cache.dim() != 3 or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
+    Hkv = cache.shape[1]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B][max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=query.device)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device)
+    st = load().kvq_decode_attention_ex(
+        ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
+        _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
+        workspace.numel(), int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_decode_attention")
+    return out

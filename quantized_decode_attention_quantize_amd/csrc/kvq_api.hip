@@ -1,0 +1,212 @@
+// C ABI of libkvq: argument validation, sizing and dispatch to the kernels.
+// The declarations, argument meanings, layouts and error behaviour are in
+// include/kvq.h.
+#include <string.h>
+
+#include "../../include/kvq.h"
+#include "kvq_device.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool is_v1(const kvq_format *f) {
+    return f && f->head_dim == 128 && f->group_size == 128 && f->k_bits == 4 && f->v_bits == 2 &&
+           f->block_size == 16;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+kvq_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return KVQ_OK;
+    g_last_hip_error = (int)e;
+    return KVQ_ERR_HIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerGroup); }
+
+// Split heuristic: aim for about 1024 work-groups (4 per compute unit on a
+// 256-CU part) in total, at least 8 pages (one page pair per wave) per split.
+int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads);
+    const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
+    int64_t pps = ceil_div(units * max_pages, 1024);
+    pps = ceil_div(pps, 8) * 8;
+    if (pps < 8) pps = 8;
+    if (pps > max_pages) pps = ceil_div(max_pages, 2) * 2;
+    if (pps < 2) pps = 2;
+    return (int32_t)pps;
+}
+
+bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
+    return num_seqs > 0 && num_q_heads > 0 && num_kv_heads > 0 && max_seq_len > 0 &&
+           num_q_heads % num_kv_heads == 0 && num_seqs <= 65535 &&
+           (int64_t)num_kv_heads * head_groups(num_q_heads / num_kv_heads) <= 65535;
+}
+
+struct WorkspaceLayout {
+    int32_t splits;
+    size_t partial_bytes;
+    size_t counter_offset;
+    size_t total;
+};
+
+WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                       int32_t pps) {
+    WorkspaceLayout w;
+    const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
+    w.splits = (int32_t)ceil_div(max_pages, pps);
+    w.partial_bytes = (size_t)num_seqs * num_q_heads * w.splits * kvq::kPartialFloats * sizeof(float);
+    w.counter_offset = (w.partial_bytes + 255) & ~(size_t)255;
+    const size_t counters =
+        (size_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads) * sizeof(int32_t);
+    w.total = w.counter_offset + ((counters + 255) & ~(size_t)255);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
+    if (!preset || !out) return KVQ_ERR_NULL;
+    if (strcmp(preset, "k4v2_g128") != 0 && strcmp(preset, "kvarn_k4v2_g128") != 0)
+        return KVQ_ERR_UNSUPPORTED;
+    out->head_dim = 128;
+    out->group_size = 128;
+    out->k_bits = 4;
+    out->v_bits = 2;
+    out->block_size = 16;
+    return KVQ_OK;
+}
+
+size_t kvq_page_bytes(const kvq_format *fmt) { return is_v1(fmt) ? (size_t)kvq::kRegion : 0; }
+
+size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_heads) {
+    if (!is_v1(fmt) || num_pages < 0 || num_kv_heads <= 0) return 0;
+    return (size_t)num_pages * (size_t)num_kv_heads * (size_t)kvq::kRegion;
+}
+
+kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const uint16_t *value,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                               uint8_t *cache, int64_t num_pages, void *stream) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
+    if (num_tokens == 0) return KVQ_OK;
+    if (!key || !value || !slot_mapping || !cache) return KVQ_ERR_NULL;
+    const int64_t row = (int64_t)num_kv_heads * kvq::kHeadDim;
+    if (key_token_stride < row || value_token_stride < row) return KVQ_ERR_SHAPE;
+    if (num_tokens > ((int64_t)1 << 40) / num_kv_heads) return KVQ_ERR_SHAPE;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(cache) || ((uintptr_t)slot_mapping & 7u) ||
+        (key_token_stride % 8) || (value_token_stride % 8))
+        return KVQ_ERR_ALIGN;
+    kvq::AppendArgs a;
+    a.key = key;
+    a.value = value;
+    a.key_stride = key_token_stride;
+    a.value_stride = value_token_stride;
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    return hip_status(kvq::launch_append(a, (hipStream_t)stream));
+}
+
+int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t max_seq_len) {
+    if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
+    return heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split) {
+    if (!is_v1(fmt) || !decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
+    if (pages_per_split < 0 || (pages_per_split % 2)) return 0;
+    const int32_t pps = pages_per_split ? pages_per_split
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+    return layout(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pps).total;
+}
+
+kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                   const uint16_t *query, const uint8_t *cache, int64_t num_pages,
+                                   const int32_t *block_tables, int32_t max_pages_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                   void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                   void *stream) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32) return KVQ_ERR_UNSUPPORTED;
+    if (!out || !query || !cache || !block_tables || !seq_lens) return KVQ_ERR_NULL;
+    if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len) || num_pages <= 0 ||
+        max_pages_per_seq <= 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage ||
+        pages_per_split < 0 || (pages_per_split % 2))
+        return KVQ_ERR_SHAPE;
+    if (!(softmax_scale == softmax_scale)) return KVQ_ERR_SHAPE;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(cache) || ((uintptr_t)block_tables & 3u) ||
+        ((uintptr_t)seq_lens & 3u))
+        return KVQ_ERR_ALIGN;
+    const int32_t pps = pages_per_split ? pages_per_split
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pps);
+    if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+    if (w.splits > 65535) return KVQ_ERR_SHAPE;
+
+    kvq::DecodeArgs a;
+    a.out = out;
+    a.out_f32 = out_dtype == KVQ_OUT_F32;
+    a.query = query;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.block_tables = block_tables;
+    a.bt_stride = max_pages_per_seq;
+    a.max_seq_len = max_seq_len;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.gqa = num_q_heads / num_kv_heads;
+    a.head_groups = head_groups(a.gqa);
+    a.splits = w.splits;
+    a.pages_per_split = pps;
+    a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
+    a.partials = static_cast<float *>(workspace);
+    a.counters = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + w.counter_offset);
+    return hip_status(kvq::launch_decode(a, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                const uint16_t *query, const uint8_t *cache, int64_t num_pages,
+                                const int32_t *block_tables, int32_t max_pages_per_seq,
+                                const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    return kvq_decode_attention_ex(fmt, out, out_dtype, query, cache, num_pages, block_tables,
+                                   max_pages_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                                   max_seq_len, softmax_scale, workspace, workspace_bytes, 0, stream);
+}
+
+const char *kvq_status_string(kvq_status status) {
+    switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer";
+    case KVQ_ERR_SHAPE: return "invalid size or shape";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format";
+    case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int kvq_last_hip_error(void) { return g_last_hip_error; }
+
+const char *kvq_version(void) { return "kvq 1.0 (kvq-k4v2-g128 v1, gfx950)"; }
+
+}  // extern "C"

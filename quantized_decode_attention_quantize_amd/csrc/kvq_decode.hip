@@ -1,0 +1,547 @@
+// Split-K decode attention over the K4V2 g128 paged cache, read with scale
+// folding (dothoosh.com, "KVarN vs TurboQuant: 5x more context with higher
+// accuracy", pipeline list stage 4).  Decode streams the whole cache through
+// HBM once per token (encorp.ai, "KV cache compression is an infrastructure
+// decision, not a model debate", section on the HBM ceiling), so the kernel is
+// built to move 104 bytes per cached token per KV head and nothing more, and
+// never materialises dequantised keys or values (vLLM's TurboQuant test lost
+// 10-70% throughput to exactly that conversion: dzen.ru summary of the vLLM
+// TurboQuant post, section "Performance").
+//
+// Algebra (H = H^T, H H = 128 I, H 1 = 128 e_0; cached rotated value s c + z):
+//   q . k_t  = (s_t (q'.c_t) + z_t sum(q')) / 128,          q' = H q
+//   sum_t p_t v_t = (H acc + 128 zv e_0) / 128,  acc = sum p_t s_t c_t,
+//                                                zv = sum p_t z_t,
+// and since the value metadata stores the group mean mu_t = s_t C_t / 128 +
+// z_t (C_t = code sum), output channel 0 is simply sum p_t mu_t / sum p_t:
+// the large, nearly cancelling terms s_t C_t and 128 z_t never meet in fp32.
+//
+// Work decomposition.  Grid (split, kv head x head group, sequence); a
+// work-group of 4 waves owns `pages_per_split` consecutive pages of one
+// (sequence, KV head) and up to 8 query heads of that KV head.  Each wave
+// takes page pairs w, w+4, ... of the split.
+//
+// Per page pair, per wave (64 lanes; n = lane & 15, g = lane >> 4):
+//   Scores: v_mfma_f32_16x16x32_f16 x 4, A = key codes (row = token n, the
+//     16 bytes of the token's 64-byte code row at 16g, each nibble an fp16
+//     subnormal), B = the rotated query in fp16 with 16 columns: columns 0-7
+//     q_hi of heads 0-7, columns 8-15 the residual q_lo = q' - q_hi (the
+//     two-term query of the BitDecoding digest: rit.work, "BitDecoding-FP4
+//     ...", second paragraph).  Output lane (n, g) holds tokens 4g..4g+3 of
+//     column n; a DPP row rotation by 8 adds the partner column.
+//   Softmax: base 2, fp32, running max per head, rescaled lazily (only when a
+//     page's score exceeds the running max by more than 8, i.e. p <= 256).
+//   Values: v_mfma_f32_16x16x32_f16, A = value codes (row = channel 16j + m,
+//     k = 8 tokens: 4 of each page), B = w = p * s_v (k = the same 8 tokens):
+//     column n < 8 holds fp16(w) of head n, column n + 8 the residual
+//     w - fp16(w), so the two columns together carry w to ~2^-22 and the
+//     rounding cannot break the cancellation between s_v * sum(c) and the
+//     zero-point sum in output channel 0.  A 2-bit code at bits 2j'..2j'+1 of a 16-bit
+//     word is, bit for bit, the fp16 subnormal c * 2^(2j' - 24); MFMA takes
+//     fp16 subnormals exactly, so the value codes need one AND per pair of
+//     tokens and no conversion.  The power of two is removed per channel
+//     block in the epilogue.
+// Epilogue: merge the 4 waves in LDS; write one partial (m, l, zacc, acc) per
+// head (zacc = sum p mu); the last work-group of a (sequence, KV head) to
+// finish (device-scope atomic counter) merges the partials and writes
+// o_j = (H acc)_j / (128 l) for j >= 1 and o_0 = zacc / l, then resets the
+// counter to zero.
+#include <math.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kLazyThreshold = 8.0f;   // log2 of the largest unnormalised weight
+
+struct PageRegs {
+    uint4 k;    // key codes: token (lane & 15), bytes 16*(lane >> 4) .. +15
+    uint2 v;    // value codes: 8 bytes at 8*lane (quad lane>>4, channel lane&15)
+    uint4 km;   // key (s, z) of tokens 4g..4g+3
+    uint4 vm;   // value (s, z) of tokens 4g..4g+3
+};
+
+// Byte offsets of a lane's loads inside a page region (loop invariant).
+struct LaneOffsets {
+    uint32_t k, v, km, vm;
+    __device__ explicit LaneOffsets(int lane)
+        : k(kKCodes + (uint32_t)(lane & 15) * 64u + (uint32_t)(lane >> 4) * 16u),
+          v(kVCodes + (uint32_t)lane * 8u),
+          km(kKMeta + (uint32_t)(lane >> 4) * 16u),
+          vm(kVMeta + (uint32_t)(lane >> 4) * 16u) {}
+};
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// `region` is wave-uniform: it becomes a buffer resource in scalar registers
+// (1664-byte range, so the hardware bounds-checks every access) and the
+// per-lane 32-bit offsets are loop invariant, so a page costs four buffer
+// loads and no vector address arithmetic.
+__device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffsets &o, PageRegs &r) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(region), (short)0, kRegion, 0x00020000);
+    const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k, 0, 0);
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.v, 0, 0);
+    const v4u km = __builtin_amdgcn_raw_buffer_load_b128(rs, o.km, 0, 0);
+    const v4u vm = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vm, 0, 0);
+    r.k = make_uint4(k.x, k.y, k.z, k.w);
+    r.v = make_uint2(v.x, v.y);
+    r.km = make_uint4(km.x, km.y, km.z, km.w);
+    r.vm = make_uint4(vm.x, vm.y, vm.z, vm.w);
+}
+
+// Key-code A operand of one 8-channel dword w (channels 8d..8d+7 of the 32
+// this lane-group owns): four dwords of fp16 pairs.  A 4-bit code at bits
+// 4r'..4r'+3 of a 16-bit half is, bit for bit, the fp16 subnormal
+// c * 2^(4r' - 24); with r' in {0, 1} every code needs one AND per pair of
+// channels.  Slot e of the 8 holds channel perm[e] = {0,4,1,5,2,6,3,7}[e],
+// scaled by 2^-24 (e & 2 == 0) or 2^-20 (e & 2 != 0); the query operand
+// carries the matching channel order and the inverse 2^-4.
+__device__ __forceinline__ v8h key_codes(uint32_t w) {
+    const uint32_t t = w >> 8;
+    const uint4 u = {w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+    return __builtin_bit_cast(v8h, u);
+}
+
+// Folded base-2 scores of the lane's 4 tokens of one page:
+// v_mfma_f32_16x16x32_f16 x 4 (32 channels per instruction and lane-group),
+// columns n < 8 the fp16 query q_hi of head n, columns n >= 8 its residual
+// q_lo = q' - q_hi; adding the partner column (lane n ^ 8, one DPP move)
+// gives both lanes of a pair the same score for head n & 7.
+__device__ __forceinline__ void page_scores(const PageRegs &r, const v8h (&bq)[4],
+                                            float c1, float c2, float *lg) {
+    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.x), bq[0], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.y), bq[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.z), bq[2], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.w), bq[3], d, 0, 0, 0);
+    const uint32_t km[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float dot = d[i] + row_swap8(d[i]);     // q_hi . c + q_lo . c
+        const float ks = half_bits_to_float(km[i] & 0xffffu);
+        const float kz = half_bits_to_float(km[i] >> 16);
+        lg[i] = c1 * (ks * dot) + c2 * kz;
+    }
+}
+
+// Value-code A operands of one page for one lane: u = two 16-bit words
+// (token slots 4g+i, 4g+i+1 for i = 0 or 2), crumb j of a word at bits
+// 2j..2j+1.  Each output dword is a pair of fp16 subnormals holding crumb j
+// of both words at mantissa bits 6-7 (value c * 2^-18, j = 0, 2, 6) or 8-9
+// (c * 2^-16, j = 1, 3, 4, 5, 7).  The codes are moved that high because the
+// MFMA accumulates very small products with less than fp32 precision (codes
+// at bits 0-1 lost up to ~3e-5 relative, biased towards zero; at bits 6-9 the
+// sums stay at fp32 rounding).  Left shifts only spill low-word bits into
+// bits 16-21 and right shifts high-word bits into bits 10-15; both lie
+// outside the masks.
+__device__ __forceinline__ uint32_t value_code(uint32_t u, int j) {
+    constexpr uint32_t kBits67 = 0x00C000C0u, kBits89 = 0x03000300u;
+    switch (j) {
+    case 0: return (u << 6) & kBits67;
+    case 1: return (u << 6) & kBits89;
+    case 2: return (u << 2) & kBits67;
+    case 3: return (u << 2) & kBits89;
+    case 4: return u & kBits89;
+    case 5: return (u >> 2) & kBits89;
+    case 6: return (u >> 6) & kBits67;
+    default: return (u >> 6) & kBits89;
+    }
+}
+
+// log2 of the factor that removes the code scaling of channel block j
+__device__ __forceinline__ constexpr int value_unscale_log2(int j) {
+    return (j == 0 || j == 2 || j == 6) ? 18 : 16;
+}
+
+struct State {
+    float m;        // running max (base 2) of this lane's column
+    float l;        // partial sum of weights over this lane's tokens
+    float z;        // partial sum of weight * value zero-point
+    v4f acc[8];     // value accumulators, channel 16j + 4g + i, column n
+};
+
+struct LaneConsts {
+    float c1, c2;          // folded score constants of head n & 7
+    float res_k;           // 0 (lanes n < 8: weight) or -1 (lanes n >= 8: residual)
+};
+
+// One page pair.  kMasked: tokens at or beyond n_tokens (page A starts at
+// token tokA, page B at tokB; tokB = n_tokens marks an absent page B) take no
+// weight, whatever their (possibly never written) slots hold.
+template <bool kMasked>
+__device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &B, int tokA, int tokB,
+                                             int n_tokens, const v8h (&bq)[4], const LaneConsts &lc,
+                                             int g, State &st) {
+    float lg[8];
+    page_scores(A, bq, lc.c1, lc.c2, lg);
+    page_scores(B, bq, lc.c1, lc.c2, lg + 4);
+    bool valid[8];
+    if (kMasked) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            valid[i] = tokA + 4 * g + i < n_tokens;
+            valid[4 + i] = tokB + 4 * g + i < n_tokens;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++) lg[i] = valid[i] ? lg[i] : -INFINITY;
+    }
+    float lmax = lg[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) lmax = fmaxf(lmax, lg[i]);
+    if (__any(lmax > st.m + kLazyThreshold)) {
+        float cm = fmaxf(lmax, xor_lane(lmax, 16));
+        cm = fmaxf(cm, xor_lane(cm, 32));
+        const float m_new = fmaxf(st.m, cm);
+        const float f = (st.m == -INFINITY) ? 0.0f : fast_exp2(st.m - m_new);
+        st.l *= f;
+        st.z *= f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) st.acc[j] *= f;
+        st.m = m_new;
+    }
+    // Weights are exp2(l - m - 8) <= 1 (the lazy threshold is folded into the
+    // exponent), so w = p * s_v <= s_v stays inside fp16 for any value scale
+    // the format can store; l and zacc carry the same factor, which cancels.
+    const float mref = ((st.m == -INFINITY) ? 0.0f : st.m) + kLazyThreshold;
+    const uint32_t vm[8] = {A.vm.x, A.vm.y, A.vm.z, A.vm.w, B.vm.x, B.vm.y, B.vm.z, B.vm.w};
+    v8h bw;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float p = fast_exp2(lg[i] - mref);
+        const float vs = half_bits_to_float(vm[i] & 0xffffu);
+        const float vz = half_bits_to_float(vm[i] >> 16);
+        float w;
+        if (kMasked) {
+            st.l += p;
+            st.z += valid[i] ? p * vz : 0.0f;
+            w = valid[i] ? p * vs : 0.0f;
+        } else {
+            st.l += p;
+            st.z += p * vz;
+            w = p * vs;
+        }
+        // columns n < 8 take fp16(w), columns n >= 8 the exact residual
+        // w - fp16(w), so that the value sum is carried to ~2^-22
+        const _Float16 w_hi = (_Float16)w;
+        bw[i] = (_Float16)fmaf((float)w_hi, lc.res_k, w);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint4 packed = {value_code(A.v.x, j), value_code(A.v.y, j),
+                              value_code(B.v.x, j), value_code(B.v.y, j)};
+        const v8h av = __builtin_bit_cast(v8h, packed);
+        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, st.acc[j], 0, 0, 0);
+    }
+}
+
+// o_j = (H acc)_j / (128 l), j >= 1, and o_0 = zacc / l for one head: 32 lanes (lane & 31) hold
+// channels 4*(lane & 31) .. +3; the FWHT runs 2 stages in-lane and 5 across.
+__device__ __forceinline__ void finalize_head(float (&acc)[4], float l, float z, int lane32,
+                                              void *out, int out_f32, int64_t row) {
+    float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+    {
+        float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
+        p = y[2]; q = y[3]; y[2] = p + q; y[3] = p - q;
+        p = y[0]; q = y[2]; y[0] = p + q; y[2] = p - q;
+        p = y[1]; q = y[3]; y[1] = p + q; y[3] = p - q;
+    }
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) {
+        const bool upper = (lane32 & x) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float other = xor_lane(y[e], x);
+            y[e] = upper ? (other - y[e]) : (y[e] + other);
+        }
+    }
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+    const float sc = inv_l * (1.0f / 128.0f);
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) o[e] = y[e] * sc;
+    if (lane32 == 0) o[0] = z * inv_l;   // channel 0 is the weighted mean of the stored value means
+    const int64_t base = row * kHeadDim + 4 * lane32;
+    if (out_f32) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + base) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+        const uint32_t lo = (uint32_t)float_to_half_bits(o[0]) | ((uint32_t)float_to_half_bits(o[1]) << 16);
+        const uint32_t hi = (uint32_t)float_to_half_bits(o[2]) | ((uint32_t)float_to_half_bits(o[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + base) = make_uint2(lo, hi);
+    }
+}
+
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    const int split = blockIdx.x;
+    const int kvh = blockIdx.y / a.head_groups;
+    const int hg = blockIdx.y % a.head_groups;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int max_len = a.max_seq_len;
+    int n_tokens = a.seq_lens[b];
+    n_tokens = n_tokens < 0 ? 0 : (n_tokens > max_len ? max_len : n_tokens);
+    const int npages = (n_tokens + kPage - 1) / kPage;
+    const int pps = a.pages_per_split;
+    const int p_begin = split * pps;
+    const int hq0 = kvh * a.gqa + hg * kHeadsPerGroup;
+    const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
+
+    if (n_tokens == 0) {             // empty sequence: zero output rows
+        if (split == 0 && (tid >> 5) < nh) {
+            const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+            if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
+            else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
+        }
+        return;
+    }
+    if (p_begin >= npages) return;   // this split lies past the sequence end
+    const int p_end = min(p_begin + pps, npages);
+    const int nsplit = (npages + pps - 1) / pps;
+
+    __shared__ _Float16 s_qb[16][kHeadDim];   // [column][slot], slot = 32g + 8d + e
+    __shared__ float s_c1[kHeadsPerGroup], s_c2[kHeadsPerGroup];
+    __shared__ float s_m[kWaves][kHeadsPerGroup], s_l[kWaves][kHeadsPerGroup], s_z[kWaves][kHeadsPerGroup];
+    __shared__ float s_acc[kWaves][kHeadsPerGroup][kHeadDim];
+    __shared__ int s_last;
+
+    // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 ----
+    // q' = H q in fp32, scaled by a power of two so that max |q'| lies in
+    // [2^13, 2^14), then written as q_hi = fp16(q'), q_lo = fp16(q' - q_hi):
+    // the two-term query carries q' to about 2^-22 of each element.
+    {
+        const int hh = 2 * wave + (lane >> 5);
+        const int l32 = lane & 31;
+        const int c0 = 4 * l32;
+        float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (hh < nh) {
+            const uint2 raw = *reinterpret_cast<const uint2 *>(
+                a.query + ((int64_t)b * a.num_q_heads + hq0 + hh) * kHeadDim + c0);
+            q[0] = half_bits_to_float(raw.x & 0xffffu);
+            q[1] = half_bits_to_float(raw.x >> 16);
+            q[2] = half_bits_to_float(raw.y & 0xffffu);
+            q[3] = half_bits_to_float(raw.y >> 16);
+        }
+        {
+            float p = q[0], r = q[1]; q[0] = p + r; q[1] = p - r;
+            p = q[2]; r = q[3]; q[2] = p + r; q[3] = p - r;
+            p = q[0]; r = q[2]; q[0] = p + r; q[2] = p - r;
+            p = q[1]; r = q[3]; q[1] = p + r; q[3] = p - r;
+        }
+#pragma unroll
+        for (int x = 1; x < 32; x <<= 1) {
+            const bool upper = (l32 & x) != 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float other = xor_lane(q[e], x);
+                q[e] = upper ? (other - q[e]) : (q[e] + other);
+            }
+        }
+        float am = fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3])));
+        float qs = q[0] + q[1] + q[2] + q[3];
+#pragma unroll
+        for (int x = 1; x < 32; x <<= 1) {
+            am = fmaxf(am, xor_lane(am, x));
+            qs += xor_lane(qs, x);
+        }
+        int ex = 0;
+        if (am > 0.0f) (void)frexpf(am, &ex);          // am in [2^(ex-1), 2^ex)
+        const int shift = 14 - ex;                       // q' * 2^shift: max in [2^13, 2^14)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int ch = c0 + e;
+            const int r8 = ch & 7;
+            const int slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
+            const int hi_nibble = (slot >> 1) & 1;       // slots scaled by 2^-20 in the key operand
+            const float v = __builtin_ldexpf(q[e], shift - 4 * hi_nibble);
+            const _Float16 vh = (_Float16)v;
+            s_qb[hh][slot] = vh;
+            s_qb[8 + hh][slot] = (_Float16)(v - (float)vh);
+        }
+        if (l32 == 0) {
+            // dot(q', c) = D * 2^(24 - shift), D the MFMA sum with codes c * 2^-24
+            s_c1[hh] = a.alpha * __builtin_ldexpf(1.0f, 24 - shift);
+            s_c2[hh] = a.alpha * qs;
+        }
+    }
+    __syncthreads();
+
+    const int n16 = lane & 15;
+    const int g = lane >> 4;
+    v8h bq[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) bq[d] = *reinterpret_cast<const v8h *>(&s_qb[n16][32 * g + 8 * d]);
+    LaneConsts lc;
+    lc.c1 = s_c1[n16 & 7];
+    lc.c2 = s_c2[n16 & 7];
+    lc.res_k = n16 < 8 ? 0.0f : -1.0f;
+
+    State st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) st.acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- page-pair loop ----
+    const int npairs = (p_end - p_begin + 1) >> 1;
+    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
+    const int64_t head_off = (int64_t)kvh * kRegion;
+    const int64_t page_stride = (int64_t)a.num_kv_heads * kRegion;
+
+    // A page id outside the pool is read as page 0: never an out-of-bounds
+    // access (the output is unspecified under that precondition violation).
+    const LaneOffsets lo(lane);
+    const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
+    auto page_ptr = [&](int p) -> const uint8_t * {
+        uint32_t id = (uint32_t)bt[p];
+        if (id >= num_pages32) id = 0;           // also catches negative ids
+        return a.cache + (int64_t)id * page_stride + head_off;
+    };
+
+    // Pairs of this split: all but possibly the last are full (both pages
+    // inside the split and every token < n_tokens).  Wave w takes pairs
+    // w, w + 4, ...; full pairs run through a triple-buffered loop whose loads
+    // are always issued (past the end they repeat the wave's last pair), so
+    // two pairs are in flight while one is computed.  The partial pair, if
+    // any, is loaded and processed afterwards with per-token masking.
+    const int last_pa = p_begin + 2 * (npairs - 1);
+    const bool last_partial = (last_pa + 1 >= p_end) || (last_pa + 2) * kPage > n_tokens;
+    const int nfull = npairs - (last_partial ? 1 : 0);
+    const int nk = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+
+    // The scheduling barrier keeps the compiler from sinking the prefetch
+    // loads into the next pair's arithmetic (which it otherwise does to save
+    // registers, leaving the current pair's loads as the newest in flight).
+    auto issue = [&](PageRegs &A, PageRegs &B, int i) {
+        const int kk = wave + kWaves * (i < nk ? i : nk - 1);
+        const int pa = p_begin + 2 * kk;
+        load_page(page_ptr(pa), lo, A);
+        load_page(page_ptr(pa + 1), lo, B);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nk > 0) {
+        PageRegs r0A, r0B, r1A, r1B, r2A, r2B;
+        issue(r0A, r0B, 0);
+        issue(r1A, r1B, 1);
+        for (int i = 0;; i += 3) {
+            issue(r2A, r2B, i + 2);
+            process_pair<false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+            if (i + 1 >= nk) break;
+            issue(r0A, r0B, i + 3);
+            process_pair<false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
+            if (i + 2 >= nk) break;
+            issue(r1A, r1B, i + 4);
+            process_pair<false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
+            if (i + 3 >= nk) break;
+        }
+    }
+    if (last_partial && wave == (npairs - 1) % kWaves) {
+        PageRegs tA, tB;
+        const bool has_b = last_pa + 1 < p_end;
+        load_page(page_ptr(last_pa), lo, tA);
+        load_page(page_ptr(has_b ? last_pa + 1 : last_pa), lo, tB);
+        process_pair<true>(tA, tB, last_pa * kPage, has_b ? (last_pa + 1) * kPage : n_tokens,
+                           n_tokens, bq, lc, g, st);
+    }
+
+    // ---- merge the 4 waves ----
+    float lsum = st.l + xor_lane(st.l, 16);
+    lsum += xor_lane(lsum, 32);
+    float zsum = st.z + xor_lane(st.z, 16);
+    zsum += xor_lane(zsum, 32);
+    // value sums: column n holds the fp16 part, column n + 8 the residual
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) st.acc[j][i] += row_swap8(st.acc[j][i]);
+    if (n16 < kHeadsPerGroup) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float unscale = __builtin_ldexpf(1.0f, value_unscale_log2(j));
+#pragma unroll
+            for (int i = 0; i < 4; i++) s_acc[wave][n16][16 * j + 4 * g + i] = st.acc[j][i] * unscale;
+        }
+        if (g == 0) {
+            s_m[wave][n16] = st.m;
+            s_l[wave][n16] = lsum;
+            s_z[wave][n16] = zsum;
+        }
+    }
+    __syncthreads();
+
+    const int hh = tid >> 5;          // head of this thread in the merge
+    const int l32 = tid & 31;
+    const int c0 = 4 * l32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, s_m[w][hh]);
+    float lt = 0.0f, zt = 0.0f, acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const float mw = s_m[w][hh];
+        const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+        lt += f * s_l[w][hh];
+        zt += f * s_z[w][hh];
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc4[e] += f * s_acc[w][hh][c0 + e];
+    }
+
+    const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
+    if (nsplit == 1) {
+        if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row);
+        return;
+    }
+
+    float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
+    if (hh < nh) {
+        if (l32 == 0) {
+            mine[0] = M;
+            mine[1] = lt;
+            mine[2] = zt;
+        }
+        *reinterpret_cast<float4 *>(mine + 4 + c0) = make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
+    }
+    __threadfence();
+    __syncthreads();
+    int32_t *counter = a.counters + ((int64_t)b * a.num_kv_heads + kvh) * a.head_groups + hg;
+    if (tid == 0) s_last = (atomicAdd(counter, 1) == nsplit - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    if (hh < nh) {
+        const float *base = a.partials + row * a.splits * kPartialFloats;
+        float Mt = -INFINITY;
+        for (int s = 0; s < nsplit; s++) Mt = fmaxf(Mt, base[s * kPartialFloats]);
+        float l2 = 0.0f, z2 = 0.0f, o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = 0; s < nsplit; s++) {
+            const float *ps = base + s * kPartialFloats;
+            const float ms = ps[0];
+            const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - Mt);
+            l2 += f * ps[1];
+            z2 += f * ps[2];
+            const float4 v = *reinterpret_cast<const float4 *>(ps + 4 + c0);
+            o4[0] += f * v.x;
+            o4[1] += f * v.y;
+            o4[2] += f * v.z;
+            o4[3] += f * v.w;
+        }
+        finalize_head(o4, l2, z2, l32, a.out, a.out_f32, row);
+    }
+    if (tid == 0) *counter = 0;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
+    hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,100 @@
+// Internal definitions of libkvq (gfx950).  Not part of the public ABI.
+//
+// Cache format "kvq-k4v2-g128 v1": one 1664-byte region per (page, KV head);
+// 16 tokens per page; 128 channels per head; see include/kvq.h for the layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 16;
+constexpr int kRegion = 1664;
+constexpr int kKCodes = 0;      // token o: 64 bytes at 64*o
+constexpr int kVCodes = 1024;   // quad g, slot i, m: u16 at 1024 + 128g + 8m + 2i
+constexpr int kKMeta = 1536;    // token o: (s, z) fp16 at 1536 + 4o
+constexpr int kVMeta = 1600;    // token o: (s, z) fp16 at 1600 + 4o
+
+// Decode work decomposition.
+constexpr int kWaves = 4;           // waves per work-group
+constexpr int kHeadsPerGroup = 8;   // query heads per MFMA column block (hi + lo = 16 columns)
+constexpr int kPartialFloats = 132; // m, l, zacc, pad, acc[128]
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);   // v_cvt_f16_f32, nearest-even
+}
+
+// Lane exchange within a wave (ds_bpermute); `mask` < 64.
+__device__ __forceinline__ float xor_lane(float v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+__device__ __forceinline__ uint32_t xor_lane_u(uint32_t v, int mask) {
+    return (uint32_t)__shfl_xor((int)v, mask, 64);
+}
+
+// Value of lane (l ^ 8) within each row of 16 lanes, as one DPP move
+// (row_ror:8 rotates a row by half its width).
+__device__ __forceinline__ float row_swap8(float v) {
+    return __builtin_bit_cast(float,
+        __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+    return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
+}
+
+}  // namespace kvq
+
+// Launchers (host side), implemented next to their kernels.
+namespace kvq {
+
+struct AppendArgs {
+    const uint16_t *key;
+    const uint16_t *value;
+    int64_t key_stride;
+    int64_t value_stride;
+    const int64_t *slots;
+    int64_t num_tokens;
+    int32_t num_kv_heads;
+    uint8_t *cache;
+    int64_t num_pages;
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    void *out;
+    int out_f32;
+    const uint16_t *query;
+    const uint8_t *cache;
+    int64_t num_pages;
+    const int32_t *block_tables;
+    int32_t bt_stride;        // entries per block-table row (max_pages_per_seq)
+    int32_t max_seq_len;      // sequences are clamped to this many tokens
+    const int32_t *seq_lens;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t gqa;              // num_q_heads / num_kv_heads
+    int32_t head_groups;      // ceil(gqa / 8)
+    int32_t splits;           // work-groups per (seq, kv head, head group)
+    int32_t pages_per_split;
+    float alpha;              // softmax_scale * log2(e) / 128
+    float *partials;          // [num_seqs][num_q_heads][splits][132]
+    int32_t *counters;        // [num_seqs][num_kv_heads][head_groups]
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kvq

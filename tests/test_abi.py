@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+host-visible arguments without launching anything (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import quantized_decode_attention_quantize_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.load()
+    names = declared_functions()
+    assert "kvq_quantize_append" in names and "kvq_decode_attention" in names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_format_and_sizes():
+    lib = kvq.load()
+    f = kvq.Format()
+    assert lib.kvq_format_from_string(b"kvarn_k4v2_g128", ctypes.byref(f)) == 0
+    assert (f.head_dim, f.group_size, f.k_bits, f.v_bits, f.block_size) == (128, 128, 4, 2, 16)
+    assert lib.kvq_format_from_string(b"k4v2_g128", ctypes.byref(f)) == 0
+    assert lib.kvq_format_from_string(b"k8v4_g128", ctypes.byref(f)) == 3
+    assert lib.kvq_format_from_string(None, ctypes.byref(f)) == 1
+    assert kvq.page_bytes() == 1664 == 64 * 16 + 32 * 16 + 4 * 16 + 4 * 16
+    # 104 bytes per token per KV head against 512 for fp16: 4.92x, inside the
+    # 3-5x capacity range the KVarN pages report
+    ratio = 512 / (1664 / 16)
+    assert 3.0 <= ratio <= 5.0 and abs(ratio - 4.923) < 1e-3
+    assert kvq.cache_bytes(10, 8) == 10 * 8 * 1664
+    bad = kvq.Format(128, 128, 8, 4, 16)
+    assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
+    assert lib.kvq_cache_bytes(ctypes.byref(bad), 10, 8) == 0
+
+
+def test_kv_memory_closed_form():
+    """Sizing check of the bf16 cache figure on the HBM page (Llama-3.1-70B:
+    80 layers, 8 KV heads, head_dim 128): 2*80*8*128*2 bytes per token, about
+    0.31 MB, about 40 GiB at 128K tokens; the K4V2 pool is 4.92x smaller."""
+    per_token_bf16 = 2 * 80 * 8 * 128 * 2
+    assert per_token_bf16 == 327_680
+    assert abs(per_token_bf16 * 131072 / 2 ** 30 - 40.0) < 1e-9
+    k4v2 = kvq.cache_bytes(131072 // 16, 8) * 80
+    assert abs(per_token_bf16 * 131072 / k4v2 - 512 / 104) < 1e-12
+
+
+def test_workspace_sizing_and_heuristic():
+    pps = kvq.decode_pages_per_split(8, 64, 8, 16385)
+    assert pps > 0 and pps % 2 == 0
+    n = kvq.decode_workspace_bytes(8, 64, 8, 16385)
+    splits = -(-1025 // pps)
+    assert n >= 8 * 64 * splits * 132 * 4 + 8 * 8 * 4
+    assert kvq.decode_workspace_bytes(8, 64, 8, 16385, 16) >= 8 * 64 * 65 * 132 * 4
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_workspace_bytes(8, 60, 8, 16385)        # Hq % Hkv != 0
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_workspace_bytes(8, 64, 8, 16385, 3)     # odd split
+
+
+def _fmt():
+    return ctypes.byref(kvq.format_from_string())
+
+
+def test_append_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    good = P(0x10000)
+    # null format / unsupported format
+    assert lib.kvq_quantize_append(None, good, good, 1024, 1024, good, 4, 8, good, 10, None) == 1
+    bad = kvq.Format(128, 128, 8, 4, 16)
+    assert lib.kvq_quantize_append(ctypes.byref(bad), good, good, 1024, 1024, good, 4, 8, good, 10, None) == 3
+    # zero tokens: no-op success
+    assert lib.kvq_quantize_append(_fmt(), None, None, 1024, 1024, None, 0, 8, None, 10, None) == 0
+    assert lib.kvq_quantize_append(_fmt(), None, good, 1024, 1024, good, 4, 8, good, 10, None) == 1
+    assert lib.kvq_quantize_append(_fmt(), good, good, 100, 1024, good, 4, 8, good, 10, None) == 2
+    assert lib.kvq_quantize_append(_fmt(), good, good, 1024, 1024, good, -1, 8, good, 10, None) == 2
+    assert lib.kvq_quantize_append(_fmt(), P(0x10002), good, 1024, 1024, good, 4, 8, good, 10, None) == 4
+    assert lib.kvq_quantize_append(_fmt(), good, good, 1028, 1024, good, 4, 8, good, 10, None) == 2 or \
+        lib.kvq_quantize_append(_fmt(), good, good, 1028, 1024, good, 4, 8, good, 10, None) == 4
+
+
+def test_decode_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    ws = kvq.decode_workspace_bytes(2, 8, 2, 100)
+
+    def call(**kw):
+        a = dict(out=g, dt=1, q=g, cache=g, np=10, bt=g, mp=7, sl=g, B=2, Hq=8, Hkv=2, L=100,
+                 scale=0.088, ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        return lib.kvq_decode_attention_ex(_fmt(), a["out"], a["dt"], a["q"], a["cache"], a["np"], a["bt"],
+                                           a["mp"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["L"], a["scale"],
+                                           a["ws"], a["wsb"], a["pps"], None)
+
+    assert call(out=None) == 1
+    assert call(Hq=7) == 2                      # Hq % Hkv != 0
+    assert call(B=0) == 2
+    assert call(L=200) == 2                     # max_seq_len > max_pages * 16
+    assert call(pps=3) == 2
+    assert call(dt=5) == 3
+    assert call(q=P(0x10008)) == 4
+    assert call(wsb=ws - 1) == 5
+    assert call(ws=None) == 5
+    assert lib.kvq_decode_attention(None, g, 1, g, g, 10, g, 7, g, 2, 8, 2, 100, 0.1, g, ws, None) == 1
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the error path of a GPU-less host")
+def test_launch_without_gpu_reports_hip_error():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    st = lib.kvq_quantize_append(_fmt(), g, g, 1024, 1024, g, 4, 8, g, 10, None)
+    assert st == 6
+    assert lib.kvq_last_hip_error() != 0
+    assert lib.kvq_status_string(6) == b"HIP runtime error"
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    mod = importlib.reload(kvq)
+    monkeypatch.setattr(mod, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(RuntimeError):
+        mod.load()
+    importlib.reload(kvq)

@@ -1,0 +1,392 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed cache bytes bit-identical to the oracle's; attention max-abs error
+<= 2e-3 against the oracle's fp64 plain-definition attention (fp32 or fp16
+output).  Small cases are checked in full; the five workloads at full size in
+the launch configuration the benchmark uses, on sampled (sequence, KV head)
+groups that the oracle recomputes from the same seeded inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_inputs as inp
+import oracle
+import quantized_decode_attention_quantize_amd as kvq
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+TOL = 2e-3
+D = 128
+SCALE = 1.0 / math.sqrt(D)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvq.load()
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def valid_byte_mask(n_tokens_in_page: int) -> np.ndarray:
+    """Bytes of a region that hold data of the first r token slots."""
+    r = n_tokens_in_page
+    m = np.zeros(1664, bool)
+    m[:64 * r] = True
+    for o in range(r):
+        for mm in range(16):
+            off = 1024 + 128 * (o // 4) + 8 * mm + 2 * (o % 4)
+            m[off:off + 2] = True
+    m[1536:1536 + 4 * r] = True
+    m[1600:1600 + 4 * r] = True
+    return m
+
+
+def gpu_append(k, v, slots, cache):
+    kvq.quantize_append(k, v, slots, cache)
+
+
+# --------------------------------------------------------------------------
+# Quantise-append
+# --------------------------------------------------------------------------
+
+def test_append_tiny_workload_bit_exact(dev):
+    w = inp.workload("tiny")
+    n = int(inp.final_lens(w)[0])
+    bt, num_pages = inp.page_table(w)
+    k, v = inp.sequence_kv(w, 0)
+    slots = inp.slot_mapping(bt, 0, 0, n)
+    log(f"append tiny n={n} pages={num_pages}")
+    cache = torch.full((num_pages, 1, 1664), 0xA5, dtype=torch.uint8, device=dev)
+    gpu_append(k.to(dev), v.to(dev), torch.from_numpy(slots).to(dev), cache)
+    pool = np.full((num_pages, 1, 1664), 0xA5, np.uint8)
+    oracle.quantize_append(k.numpy(), v.numpy(), slots, pool)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+
+
+def _mixed_tokens(rng, T, H):
+    """fp16 [T][H][128] rows drawn from several regimes, including subnormal
+    inputs, large values, outlier channels, zero rows, rows whose rotation is
+    constant, and near-tie rows built on a half-step grid."""
+    Hm = np.array([[1]])
+    while Hm.shape[0] < D:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    x = np.empty((T, H, D), np.float64)
+    kinds = rng.integers(0, 8, (T, H))
+    for t in range(T):
+        for h in range(H):
+            kd = kinds[t, h]
+            if kd == 0:
+                r = rng.standard_normal(D)
+            elif kd == 1:
+                r = rng.standard_normal(D) * 1e-5               # fp16 subnormals
+            elif kd == 2:
+                r = rng.standard_normal(D) * 300.0
+            elif kd == 3:
+                r = rng.standard_normal(D)
+                r[rng.integers(0, D, 4)] *= 20.0
+            elif kd == 4:
+                r = np.zeros(D)
+            elif kd == 5:
+                r = np.zeros(D)
+                r[0] = rng.choice([-3.0, 0.5, 7.25])          # rotation is constant
+            elif kd == 6:                                     # half-step grid: ties
+                L = 15 if rng.random() < 0.5 else 3
+                hs = rng.integers(0, 2 * L + 1, D)
+                hs[0], hs[1] = 0, 2 * L
+                y = -0.5 + hs * (2.0 ** -5)
+                r = (Hm @ y) / 128.0
+            else:
+                r = rng.standard_t(3, D)
+            x[t, h] = r
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("H,T,num_pages,seed", [(1, 37, 8, 1), (3, 200, 20, 2), (8, 515, 40, 3)])
+def test_append_mixed_regimes_strided_and_skips(dev, H, T, num_pages, seed):
+    rng = np.random.default_rng(100 + seed)
+    log(f"append mixed H={H} T={T} pages={num_pages}")
+    k = _mixed_tokens(rng, T, H)
+    v = _mixed_tokens(rng, T, H)
+    slots = rng.permutation(num_pages * 16)[:T].astype(np.int64)
+    slots[rng.integers(0, T, 5)] = -1                          # skipped tokens
+    slots[0] = num_pages * 16 + 3                               # outside the pool: skipped
+    # strided inputs: token stride (H + 1) * 128
+    kb = torch.zeros((T, H + 1, D), dtype=torch.float16)
+    vb = torch.zeros((T, H + 1, D), dtype=torch.float16)
+    kb[:, :H] = torch.from_numpy(k)
+    vb[:, :H] = torch.from_numpy(v)
+    kd, vd = kb.to(dev)[:, :H], vb.to(dev)[:, :H]
+    cache = torch.full((num_pages, H, 1664), 0x3C, dtype=torch.uint8, device=dev)
+    gpu_append(kd, vd, torch.from_numpy(slots).to(dev), cache)
+    pool = np.full((num_pages, H, 1664), 0x3C, np.uint8)
+    ok = (slots >= 0) & (slots < num_pages * 16)
+    oracle.quantize_append(k[ok], v[ok], slots[ok], pool)
+    got = cache.cpu().numpy()
+    diff = np.argwhere(got != pool)
+    assert diff.size == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
+
+
+def test_append_one_token_at_a_time_matches_bulk(dev):
+    w = inp.workload("qwen3_32b_16k", context=64, new_tokens=0, num_seqs=2)
+    bt, num_pages = inp.page_table(w)
+    caches = []
+    for mode in ("bulk", "single"):
+        cache = torch.zeros((num_pages, w.num_kv_heads, 1664), dtype=torch.uint8, device=dev)
+        for b in range(w.num_seqs):
+            k, v = inp.sequence_kv(w, b, device=dev)
+            slots = torch.from_numpy(inp.slot_mapping(bt, b, 0, 64)).to(dev)
+            if mode == "bulk":
+                gpu_append(k, v, slots, cache)
+            else:
+                for t in range(64):
+                    gpu_append(k[t:t + 1], v[t:t + 1], slots[t:t + 1], cache)
+        caches.append(cache.cpu())
+    assert torch.equal(caches[0], caches[1])
+
+
+# --------------------------------------------------------------------------
+# Decode attention, small cases in full
+# --------------------------------------------------------------------------
+
+def _build_case(dev, B, Hq, Hkv, lens, seed, spare_pages=3):
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int64)
+    pages = [int(math.ceil(n / 16)) for n in lens]
+    num_pages = sum(pages) + spare_pages
+    perm = rng.permutation(num_pages)
+    max_pages = max(pages) + 2
+    bt = np.full((B, max_pages), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    cache = torch.full((num_pages, Hkv, 1664), 0xFF, dtype=torch.uint8, device=dev)  # NaN metadata in unused slots
+    pool = np.full((num_pages, Hkv, 1664), 0xFF, np.uint8)
+    for b in range(B):
+        n = int(lens[b])
+        k = (rng.standard_normal((n, Hkv, D)) * rng.choice([0.5, 1, 2])).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        k[:, :, rng.integers(0, D, 3)] *= 10
+        slots = inp.slot_mapping(bt, b, 0, n)
+        gpu_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                   torch.from_numpy(slots).to(dev), cache)
+        oracle.quantize_append(k, v, slots, pool)
+    q = (rng.standard_normal((B, Hq, D)) * rng.choice([0.5, 1, 3])).astype(np.float16)
+    return cache, pool, bt, lens, q
+
+
+SMALL = [
+    # B, Hq, Hkv, lens
+    (1, 1, 1, [1]),
+    (1, 1, 1, [15]),
+    (1, 2, 1, [16]),
+    (2, 4, 1, [17, 33]),
+    (2, 8, 2, [31, 32]),
+    (3, 8, 1, [100, 1, 257]),
+    (2, 16, 2, [1000, 999]),
+    (1, 32, 2, [700]),        # G = 16: two head groups
+    (4, 12, 4, [64, 65, 127, 300]),   # G = 3
+    (2, 64, 8, [513, 77]),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens", SMALL)
+def test_decode_small_matches_oracle(dev, B, Hq, Hkv, lens):
+    log(f"decode small B={B} Hq={Hq} Hkv={Hkv} lens={lens}")
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=B * 1000 + Hq + sum(lens))
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention(pool, bt, lens_np, q, SCALE)
+    qd = torch.from_numpy(q).to(dev)
+    btd = torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (0, 2, 6):
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps)
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+    out16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16)
+    err16 = np.max(np.abs(out16.float().cpu().numpy() - ref))
+    assert err16 <= TOL, f"fp16 out err={err16}"
+
+
+def test_decode_deterministic_split_invariant_and_page_placement(dev):
+    B, Hq, Hkv, lens = 3, 16, 2, [400, 1, 777]
+    log("decode determinism / split / placement")
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=77)
+    qd = torch.from_numpy(q).to(dev)
+    btd = torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    ws = kvq.alloc_workspace(B, Hq, Hkv, L)
+    a = kvq.decode_attention(qd, cache, btd, ld, L, workspace=ws).cpu()
+    b = kvq.decode_attention(qd, cache, btd, ld, L, workspace=ws).cpu()
+    assert torch.equal(a, b)                         # repeat: identical bits, workspace reused
+    c = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=2).cpu()
+    assert torch.max(torch.abs(a - c)).item() <= 1e-5
+    # move every page to another physical slot; same logical cache
+    num_pages = cache.shape[0]
+    rng = np.random.default_rng(5)
+    newpos = rng.permutation(num_pages)
+    cache2 = torch.empty_like(cache)
+    cache2[torch.from_numpy(newpos).to(dev)] = cache
+    bt2 = np.where(bt >= 0, newpos[np.maximum(bt, 0)], -1).astype(np.int32)
+    d = kvq.decode_attention(qd, cache2, torch.from_numpy(bt2).to(dev), ld, L, workspace=ws).cpu()
+    assert torch.equal(a, d)
+
+
+def test_decode_zero_query_gives_mean_value(dev):
+    B, Hq, Hkv, lens = 1, 4, 1, [123]
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=9)
+    q[:] = 0
+    out = kvq.decode_attention(torch.from_numpy(q).to(dev), cache, torch.from_numpy(bt).to(dev),
+                               torch.from_numpy(lens_np.astype(np.int32)).to(dev), 123).cpu().numpy()
+    vals = np.stack([oracle.dequant_slot(pool[bt[0, t // 16], 0], t % 16)[1] for t in range(123)])
+    assert np.max(np.abs(out[0] - vals.mean(0)[None, :])) <= TOL
+
+
+# --------------------------------------------------------------------------
+# The workloads at full size, sampled
+# --------------------------------------------------------------------------
+
+def _fill_cache(w, dev, keep=()):
+    """Append every sequence's cached tokens (positions [0, seq_lens)) on the GPU;
+    returns (cache, block_tables, kept host K/V of the sequences in `keep`)."""
+    bt, num_pages = inp.page_table(w)
+    lens = inp.seq_lens(w)
+    cache = torch.zeros((num_pages, w.num_kv_heads, 1664), dtype=torch.uint8, device=dev)
+    kept = {}
+    for b in range(w.num_seqs):
+        n = int(lens[b])
+        k, v = inp.sequence_kv(w, b, 0, n, device=dev)
+        slots = torch.from_numpy(inp.slot_mapping(bt, b, 0, n)).to(dev)
+        gpu_append(k, v, slots, cache)
+        if b in keep:
+            kept[b] = (k.cpu().numpy(), v.cpu().numpy())
+        del k, v
+    return cache, bt, kept
+
+
+def _check_group(cache, bt, b, kvh, n, k_seq, v_seq, q_b, G, out_b):
+    """Oracle check of (sequence b, KV head kvh): codes of all n tokens and the
+    attention of the G query heads."""
+    pages = int(math.ceil(n / 16))
+    pool = np.zeros((pages, 1, 1664), np.uint8)
+    oracle.quantize_append(k_seq[:n, kvh:kvh + 1], v_seq[:n, kvh:kvh + 1],
+                           np.arange(n, dtype=np.int64), pool)
+    ids = torch.from_numpy(bt[b, :pages].astype(np.int64)).to(cache.device)
+    got = cache[ids, kvh].cpu().numpy()
+    full = got[:-1] == pool[:-1, 0]
+    assert full.all(), f"codes differ in full pages of seq {b} head {kvh}"
+    r = n - 16 * (pages - 1)
+    m = valid_byte_mask(r)
+    assert np.array_equal(got[-1][m], pool[-1, 0][m]), f"codes differ in last page of seq {b} head {kvh}"
+    qh = q_b[kvh * G:(kvh + 1) * G][None]
+    ref = oracle.decode_attention(pool, np.arange(pages, dtype=np.int32)[None], np.array([n]), qh, SCALE)[0]
+    err = np.max(np.abs(out_b[kvh * G:(kvh + 1) * G].astype(np.float64) - ref))
+    assert err <= TOL, f"seq {b} kv head {kvh}: max-abs err {err}"
+    return err
+
+
+def _decode(w, dev, cache, bt, lens, q, out_dtype=torch.float32):
+    L = int(lens.max())
+    return kvq.decode_attention(q.to(dev), cache, torch.from_numpy(bt).to(dev),
+                                torch.from_numpy(lens.astype(np.int32)).to(dev), L,
+                                out_dtype=out_dtype)
+
+
+def test_workload_tiny(dev):
+    w = inp.workload("tiny")
+    log("workload tiny")
+    cache, bt, kept = _fill_cache(w, dev, keep=(0,))
+    lens = inp.seq_lens(w)
+    q = inp.queries(w)
+    out = _decode(w, dev, cache, bt, lens, q).cpu().numpy()
+    _check_group(cache, bt, 0, 0, int(lens[0]), *kept[0], q.numpy()[0], 1, out[0])
+
+
+def test_workload_qwen3_32b_16k(dev):
+    """8 x 16384 cached tokens, append one token per sequence, then decode
+    16385 tokens; 64 q / 8 KV heads.  Samples 2 sequences x 2 KV heads."""
+    w = inp.workload("qwen3_32b_16k")
+    log("workload qwen3_32b_16k: fill")
+    keep = (0, 5)
+    cache, bt, kept = _fill_cache(w, dev, keep=keep)
+    lens = inp.seq_lens(w)
+    # the step: append token `context` of every sequence, then attend
+    new_k, new_v, slots = [], [], []
+    for b in range(w.num_seqs):
+        k, v = inp.sequence_kv(w, b, w.context, 1)
+        new_k.append(k)
+        new_v.append(v)
+        slots.append(inp.slot_mapping(bt, b, w.context, 1))
+    kn, vn = torch.cat(new_k), torch.cat(new_v)
+    gpu_append(kn.to(dev), vn.to(dev), torch.from_numpy(np.concatenate(slots)).to(dev), cache)
+    lens1 = lens + 1
+    q = inp.queries(w)
+    log("workload qwen3_32b_16k: decode")
+    out = _decode(w, dev, cache, bt, lens1, q, out_dtype=torch.float16).float().cpu().numpy()
+    for b in keep:
+        k, v = kept[b]
+        k = np.concatenate([k, kn[b:b + 1].numpy()])
+        v = np.concatenate([v, vn[b:b + 1].numpy()])
+        for kvh in (0, 7):
+            e = _check_group(cache, bt, b, kvh, int(lens1[b]), k, v, q.numpy()[b], w.gqa, out[b])
+            log(f"  seq {b} kv {kvh}: err {e:.2e}")
+
+
+def test_workload_qwen3_4b_64k_ragged(dev):
+    w = inp.workload("qwen3_4b_64k")
+    log("workload qwen3_4b_64k: fill")
+    lens = inp.seq_lens(w)
+    keep = (int(np.argmin(lens)), int(np.argmax(lens)))
+    cache, bt, kept = _fill_cache(w, dev, keep=keep)
+    q = inp.queries(w)
+    out = _decode(w, dev, cache, bt, lens, q).cpu().numpy()
+    for b in keep:
+        e = _check_group(cache, bt, b, 3, int(lens[b]), *kept[b], q.numpy()[b], w.gqa, out[b])
+        log(f"  seq {b} (n={lens[b]}) kv 3: err {e:.2e}")
+
+
+def test_workload_qwen3_30b_a3b_128k(dev):
+    w = inp.workload("qwen3_30b_a3b_128k")
+    log("workload qwen3_30b_a3b_128k: fill")
+    cache, bt, kept = _fill_cache(w, dev, keep=(2,))
+    lens = inp.seq_lens(w)
+    q = inp.queries(w)
+    out = _decode(w, dev, cache, bt, lens, q).cpu().numpy()
+    e = _check_group(cache, bt, 2, 1, int(lens[2]), *kept[2], q.numpy()[2], w.gqa, out[2])
+    log(f"  seq 2 kv 1: err {e:.2e}")
+
+
+def test_workload_llama31_70b_prefill_then_decode(dev):
+    """Bulk quantise-append of a 131072-token prompt (one call), then decode
+    steps that each append one token; steps 0, 1 and 63 are checked."""
+    w = inp.workload("llama31_70b_128k")
+    bt, num_pages = inp.page_table(w)
+    n0 = w.context
+    log("workload llama31_70b_128k: prefill")
+    k, v = inp.sequence_kv(w, 0, 0, n0 + w.new_tokens, device=dev)
+    cache = torch.zeros((num_pages, w.num_kv_heads, 1664), dtype=torch.uint8, device=dev)
+    slots_all = torch.from_numpy(inp.slot_mapping(bt, 0, 0, n0 + w.new_tokens)).to(dev)
+    gpu_append(k[:n0], v[:n0], slots_all[:n0], cache)
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    btd = torch.from_numpy(bt).to(dev)
+    ws = kvq.alloc_workspace(1, w.num_q_heads, w.num_kv_heads, n0 + w.new_tokens)
+    for step in range(w.new_tokens):
+        gpu_append(k[n0 + step:n0 + step + 1], v[n0 + step:n0 + step + 1],
+                   slots_all[n0 + step:n0 + step + 1], cache)
+        n = n0 + step + 1
+        q = inp.queries(w, step)
+        lens = torch.tensor([n], dtype=torch.int32, device=dev)
+        out = kvq.decode_attention(q.to(dev), cache, btd, lens, n0 + w.new_tokens, workspace=ws)
+        if step in (0, 1, w.new_tokens - 1):
+            e = _check_group(cache, bt, 0, 5, n, kh, vh, q.numpy()[0], w.gqa, out.cpu().numpy()[0])
+            log(f"  step {step} (n={n}) kv 5: err {e:.2e}")

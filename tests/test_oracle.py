@@ -118,8 +118,11 @@ def test_matvec_f64():
 # Encoder
 # --------------------------------------------------------------------------
 
-def _dequant(codes, s, z):
-    return oracle.half_to_double(s) * codes.astype(np.float64) + oracle.half_to_double(z)
+def _dequant(codes, s, z, bits=4):
+    """Rotated-domain dequantisation: s*c + zero, where the stored offset is
+    the zero itself for 4-bit keys and the group mean for 2-bit values."""
+    zero = oracle.group_zero(codes, s, z, is_value=(bits == 2))
+    return oracle.half_to_double(s) * codes.astype(np.float64) + zero
 
 
 def test_zero_and_constant_groups():
@@ -140,7 +143,8 @@ def test_hand_derived_example():
         codes, s, z = oracle.quantize_group(x, bits)
         assert np.all(codes[0::2] == int(f[pre + "_codes_even"]))
         assert np.all(codes[1::2] == int(f[pre + "_codes_odd"]))
-        assert s == int(f[pre + "_s"], 16) and z == int(f[pre + "_z"], 16)
+        off = "_z" if pre == "key" else "_mean"
+        assert s == int(f[pre + "_s"], 16) and z == int(f[pre + off], 16)
 
 
 def _on_grid(rng, L, delta=2.0 ** -4, zero=-0.5):
@@ -164,8 +168,12 @@ def test_on_grid_round_trip_exact(bits):
         x16, c, delta, zero = _on_grid(rng, L)
         codes, s, z = oracle.quantize_group(x16, bits)
         assert np.array_equal(codes, c)
-        assert oracle.half_to_double(s) == delta and oracle.half_to_double(z) == zero
-        assert np.array_equal(_dequant(codes, s, z), zero + delta * c)
+        assert oracle.half_to_double(s) == delta
+        if bits == 4:
+            assert oracle.half_to_double(z) == zero
+        else:   # values store the group mean, zero + delta * sum(c) / 128
+            assert oracle.half_to_double(z) == zero + delta * c.sum() / 128
+        assert np.array_equal(_dequant(codes, s, z, bits), zero + delta * c)
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -181,7 +189,8 @@ def test_error_bound_and_brute_force_nearest_level(bits):
         x16 = x.astype(np.float16)
         y = H @ x16.astype(np.float64)                       # exact rotation
         codes, s16, z16 = oracle.quantize_group(x16, bits)
-        s, z = oracle.half_to_double(s16), oracle.half_to_double(z16)
+        s = oracle.half_to_double(s16)
+        z = oracle.group_zero(codes, s16, z16, is_value=(bits == 2))
         assert codes.max() <= L
         rec = s * codes + z
         slack = 2.0 ** -10 * (L * s + abs(z)) + 1e-6 * np.abs(y).max()
@@ -223,13 +232,31 @@ def test_rotation_spreads_key_outliers():
     for t in range(k.shape[0]):
         x = k[t].astype(np.float64)
         codes, s, z = oracle.quantize_group(k[t], 4)
-        xr = (H @ _dequant(codes, s, z)) / 128.0
+        xr = (H @ _dequant(codes, s, z, 4)) / 128.0
         err_rot += np.sum((xr - x) ** 2)
         lo, hi = x.min(), x.max()
         step = (hi - lo) / 15
         xq = lo + step * np.clip(np.rint((x - lo) / step), 0, 15)
         err_raw += np.sum((xq - x) ** 2)
     assert err_rot < 0.5 * err_raw
+
+
+def test_value_mean_is_dequantised_channel_zero():
+    """The stored value offset is the group mean in the rotated domain, which
+    equals channel 0 of the dequantised, un-rotated vector (H 1 = 128 e_0),
+    and it lies within the fp16 rounding of the exact mean of y / 128."""
+    rng = np.random.default_rng(50)
+    region = np.zeros(1664, np.uint8)
+    for trial in range(100):
+        x16 = (rng.standard_normal(D) * [0.01, 1, 40][trial % 3]).astype(np.float16)
+        kc, ks, kz = oracle.quantize_group(x16, 4)
+        vc, vs, vmu = oracle.quantize_group(x16, 2)
+        oracle.store_token(region, 3, kc, ks, kz, vc, vs, vmu)
+        _, v = oracle.dequant_slot(region, 3)
+        assert abs(v[0] - oracle.half_to_double(vmu)) <= 1e-12 * max(1.0, abs(v[0]))
+        # the mean of the rotated values is x_0; quantisation moves it by at most s/2
+        s = oracle.half_to_double(vs)
+        assert abs(oracle.half_to_double(vmu) - float(x16[0])) <= s / 2 + 2.0 ** -10 * (3 * s + abs(float(x16[0]))) + 1e-7
 
 
 # --------------------------------------------------------------------------
