@@ -27,9 +27,13 @@
  *     h = 1, 2, ..., 64;
  *   - variance normalisation: divide by the group RMS sigma = sqrt(sum y^2 /
  *     128) (pairwise sum, fixed tree), folded back into the stored metadata;
- *   - asymmetric round-to-nearest-even on the group's [min, max]: keys to
- *     4 bits (0..15), values to 2 bits (0..3); fp16 scale s and zero z, so
- *     that a rotated value is s * code + z and the original is H (s c + z) / 128;
+ *   - asymmetric round-to-nearest-even on the group's [min m, max M]: keys
+ *     to 4 bits (0..15), values to 2 bits (0..3), step delta = (M - m) / L;
+ *     fp16 scale s = delta * sigma and one fp16 offset per group: keys store
+ *     the zero z = m * sigma, values the group mean mu = sigma * (m + delta *
+ *     C / 128) with C the sum of the group's codes (z = mu - s * C / 128).
+ *     A rotated value is s * code + z and the original is H (s c + z) / 128;
+ *     mu is the dequantised original channel 0 (H 1 = 128 e_0);
  *   - pages of 16 tokens; the pool is u8 [num_pages][num_kv_heads][1664],
  *     one 1664-byte region per (page, KV head):
  *       [0, 1024)     key codes, token o at 64*o, byte b = c[2b] | c[2b+1] << 4
@@ -37,7 +41,7 @@
  *                     m = 0..15 the little-endian u16 at 1024 + 128g + 8m + 2i
  *                     holds the code of channel 16j + m in bits 2j..2j+1
  *       [1536, 1600)  key (s, z) fp16 pairs, token o at 1536 + 4*o
- *       [1600, 1664)  value (s, z) fp16 pairs, token o at 1600 + 4*o
+ *       [1600, 1664)  value (s, mu) fp16 pairs, token o at 1600 + 4*o
  *     104 bytes per token per KV head (fp16: 512 bytes).
  *
  * Conventions for every call:
@@ -51,9 +55,10 @@
  *   - Host-visible arguments are validated before anything is launched; a
  *     failed check returns a status and launches nothing.  Device-resident
  *     data (slot mappings, block tables, sequence lengths) are preconditions
- *     the host cannot read: slots and page ids outside the pool are skipped by
- *     the kernels (never written or read), other violations give undefined
- *     results.
+ *     the host cannot read.  The kernels never access memory outside the
+ *     buffers for any such value: append skips slots outside the pool, decode
+ *     reads a page id outside the pool as page 0 and clamps sequence lengths
+ *     to [0, max_seq_len]; the results under such violations are unspecified.
  *   - A launch failure returns KVQ_ERR_HIP; kvq_last_hip_error() gives the
  *     hipError_t code.
  */
@@ -142,15 +147,16 @@ size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs,
  *   cache           (device) pool as above.
  *   block_tables    (device) int32 [num_seqs][max_pages_per_seq]; entry i of
  *                   row b is the page holding tokens 16i..16i+15 of sequence b.
- *                   Only entries i < ceil(seq_lens[b]/16) are read; a page id
- *                   outside [0, num_pages) is treated as an empty page.
+ *                   Only entries i < ceil(seq_lens[b]/16) are read.
  *   seq_lens        (device) int32 [num_seqs], each in [1, max_seq_len]
  *                   (a zero length yields a zero output row).
  *   max_seq_len     host-side bound on seq_lens, <= max_pages_per_seq*16.
  *   workspace       (device) >= kvq_decode_workspace_bytes(...) bytes,
- *                   16-byte aligned, ZERO-FILLED before its first use; every
- *                   call returns its counters to zero.  Calls that share a
- *                   workspace must not overlap in time.
+ *                   16-byte aligned, any contents (split partials are written
+ *                   before they are read).  Calls that share a workspace must
+ *                   not overlap in time.
+ * Launches two kernels on `stream` (the split kernel, then the split combine
+ * with the Hadamard epilogue) unless every sequence fits one split.
  * Returns KVQ_ERR_SHAPE when num_q_heads % num_kv_heads != 0 or a size is
  * non-positive, KVQ_ERR_WORKSPACE when workspace_bytes is too small.
  */

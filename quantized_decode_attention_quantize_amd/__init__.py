@@ -181,10 +181,9 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, m
 
 def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
                     pages_per_split: int = 0, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the decode kernel requires zeroed counters on
-    first use and leaves them zero)."""
+    """Workspace for split partials (contents need no initialisation)."""
     n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pages_per_split)
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,

@@ -27,16 +27,21 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerGroup); }
 
-// Split heuristic: aim for about 1024 work-groups (4 per compute unit on a
-// 256-CU part) in total, at least 8 pages (one page pair per wave) per split.
+// Split heuristic: one round of resident work-groups.  A (sequence, KV head,
+// head group) unit is cut into S = max(1, resident / units) splits of equal
+// page count (rounded up to a page pair), so every work-group starts at once,
+// carries the same work, and pays its fixed cost (query rotation, wave merge,
+// partial write) once.
 int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
     const int64_t units = (int64_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads);
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
-    int64_t pps = ceil_div(units * max_pages, 1024);
-    pps = ceil_div(pps, 8) * 8;
-    if (pps < 8) pps = 8;
-    if (pps > max_pages) pps = ceil_div(max_pages, 2) * 2;
+    const int64_t resident = kvq::decode_resident_workgroups();
+    int64_t splits = resident / units;
+    if (splits < 1) splits = 1;
+    int64_t pps = ceil_div(max_pages, splits);
+    pps = ceil_div(pps, 2) * 2;
     if (pps < 2) pps = 2;
+    if (pps > 0x3fffffff) pps = 0x3fffffff;
     return (int32_t)pps;
 }
 
@@ -48,21 +53,16 @@ bool decode_sizes_ok(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads
 
 struct WorkspaceLayout {
     int32_t splits;
-    size_t partial_bytes;
-    size_t counter_offset;
     size_t total;
 };
 
-WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
-                       int32_t pps) {
+WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len, int32_t pps) {
     WorkspaceLayout w;
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
     w.splits = (int32_t)ceil_div(max_pages, pps);
-    w.partial_bytes = (size_t)num_seqs * num_q_heads * w.splits * kvq::kPartialFloats * sizeof(float);
-    w.counter_offset = (w.partial_bytes + 255) & ~(size_t)255;
-    const size_t counters =
-        (size_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads) * sizeof(int32_t);
-    w.total = w.counter_offset + ((counters + 255) & ~(size_t)255);
+    const size_t partial_bytes =
+        w.splits > 1 ? (size_t)num_seqs * num_q_heads * w.splits * kvq::kPartialFloats * sizeof(float) : 0;
+    w.total = ((partial_bytes + 255) & ~(size_t)255) + 256;
     return w;
 }
 
@@ -129,7 +129,7 @@ size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32
     if (pages_per_split < 0 || (pages_per_split % 2)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
                                         : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
-    return layout(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pps).total;
+    return layout(num_seqs, num_q_heads, max_seq_len, pps).total;
 }
 
 kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
@@ -153,7 +153,7 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
         return KVQ_ERR_ALIGN;
     const int32_t pps = pages_per_split ? pages_per_split
                                         : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
-    const WorkspaceLayout w = layout(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pps);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
     if (w.splits > 65535) return KVQ_ERR_SHAPE;
@@ -177,7 +177,6 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
     a.pages_per_split = pps;
     a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
     a.partials = static_cast<float *>(workspace);
-    a.counters = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + w.counter_offset);
     return hip_status(kvq::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -41,11 +41,14 @@
 //     fp16 subnormals exactly, so the value codes need one AND per pair of
 //     tokens and no conversion.  The power of two is removed per channel
 //     block in the epilogue.
-// Epilogue: merge the 4 waves in LDS; write one partial (m, l, zacc, acc) per
-// head (zacc = sum p mu); the last work-group of a (sequence, KV head) to
-// finish (device-scope atomic counter) merges the partials and writes
-// o_j = (H acc)_j / (128 l) for j >= 1 and o_0 = zacc / l, then resets the
-// counter to zero.
+// Epilogue: merge the 4 waves in LDS and write one partial (m, l, zacc, acc)
+// per head (zacc = sum p mu); a sequence that fits one split is finished in
+// place.  combine_kernel, launched next on the same stream, merges the
+// partials (LSE) and writes o_j = (H acc)_j / (128 l) for j >= 1 and
+// o_0 = zacc / l.  (A last-work-group-merges scheme inside one kernel needs a
+// device-scope release and acquire per work-group, i.e. a write-back and an
+// invalidate of the XCD's L2 each time; measured, that cost several times
+// the whole page stream.)
 #include <math.h>
 
 #include "kvq_device.h"
@@ -307,7 +310,51 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     __shared__ float s_c1[kHeadsPerGroup], s_c2[kHeadsPerGroup];
     __shared__ float s_m[kWaves][kHeadsPerGroup], s_l[kWaves][kHeadsPerGroup], s_z[kWaves][kHeadsPerGroup];
     __shared__ float s_acc[kWaves][kHeadsPerGroup][kHeadDim];
-    __shared__ int s_last;
+
+    // ---- page-pair loop ----
+    const int npairs = (p_end - p_begin + 1) >> 1;
+    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
+    const int64_t head_off = (int64_t)kvh * kRegion;
+    const int64_t page_stride = (int64_t)a.num_kv_heads * kRegion;
+
+    // A page id outside the pool is read as page 0: never an out-of-bounds
+    // access (the output is unspecified under that precondition violation).
+    const LaneOffsets lo(lane);
+    const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
+    auto page_ptr = [&](int p) -> const uint8_t * {
+        uint32_t id = (uint32_t)bt[p];
+        if (id >= num_pages32) id = 0;           // also catches negative ids
+        return a.cache + (int64_t)id * page_stride + head_off;
+    };
+
+    // Pairs of this split: all but possibly the last are full (both pages
+    // inside the split and every token < n_tokens).  Wave w takes pairs
+    // w, w + 4, ...; full pairs run through a triple-buffered loop whose loads
+    // are always issued (past the end they repeat the wave's last pair), so
+    // two pairs are in flight while one is computed.  The partial pair, if
+    // any, is loaded and processed afterwards with per-token masking.
+    const int last_pa = p_begin + 2 * (npairs - 1);
+    const bool last_partial = (last_pa + 1 >= p_end) || (last_pa + 2) * kPage > n_tokens;
+    const int nfull = npairs - (last_partial ? 1 : 0);
+    const int nk = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+
+    // The scheduling barrier keeps the compiler from sinking the prefetch
+    // loads into the next pair's arithmetic (which it otherwise does to save
+    // registers, leaving the current pair's loads as the newest in flight).
+    auto issue = [&](PageRegs &A, PageRegs &B, int i) {
+        const int kk = wave + kWaves * (i < nk ? i : nk - 1);
+        const int pa = p_begin + 2 * kk;
+        load_page(page_ptr(pa), lo, A);
+        load_page(page_ptr(pa + 1), lo, B);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The first two pairs are requested before the query prologue so that
+    // their HBM latency overlaps it.
+    PageRegs r0A, r0B, r1A, r1B, r2A, r2B;
+    if (nk > 0) {
+        issue(r0A, r0B, 0);
+        issue(r1A, r1B, 1);
+    }
 
     // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 ----
     // q' = H q in fp32, scaled by a power of two so that max |q'| lies in
@@ -387,47 +434,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; j++) st.acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- page-pair loop ----
-    const int npairs = (p_end - p_begin + 1) >> 1;
-    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
-    const int64_t head_off = (int64_t)kvh * kRegion;
-    const int64_t page_stride = (int64_t)a.num_kv_heads * kRegion;
-
-    // A page id outside the pool is read as page 0: never an out-of-bounds
-    // access (the output is unspecified under that precondition violation).
-    const LaneOffsets lo(lane);
-    const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
-    auto page_ptr = [&](int p) -> const uint8_t * {
-        uint32_t id = (uint32_t)bt[p];
-        if (id >= num_pages32) id = 0;           // also catches negative ids
-        return a.cache + (int64_t)id * page_stride + head_off;
-    };
-
-    // Pairs of this split: all but possibly the last are full (both pages
-    // inside the split and every token < n_tokens).  Wave w takes pairs
-    // w, w + 4, ...; full pairs run through a triple-buffered loop whose loads
-    // are always issued (past the end they repeat the wave's last pair), so
-    // two pairs are in flight while one is computed.  The partial pair, if
-    // any, is loaded and processed afterwards with per-token masking.
-    const int last_pa = p_begin + 2 * (npairs - 1);
-    const bool last_partial = (last_pa + 1 >= p_end) || (last_pa + 2) * kPage > n_tokens;
-    const int nfull = npairs - (last_partial ? 1 : 0);
-    const int nk = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
-
-    // The scheduling barrier keeps the compiler from sinking the prefetch
-    // loads into the next pair's arithmetic (which it otherwise does to save
-    // registers, leaving the current pair's loads as the newest in flight).
-    auto issue = [&](PageRegs &A, PageRegs &B, int i) {
-        const int kk = wave + kWaves * (i < nk ? i : nk - 1);
-        const int pa = p_begin + 2 * kk;
-        load_page(page_ptr(pa), lo, A);
-        load_page(page_ptr(pa + 1), lo, B);
-        __builtin_amdgcn_sched_barrier(0);
-    };
     if (nk > 0) {
-        PageRegs r0A, r0B, r1A, r1B, r2A, r2B;
-        issue(r0A, r0B, 0);
-        issue(r1A, r1B, 1);
         for (int i = 0;; i += 3) {
             issue(r2A, r2B, i + 2);
             process_pair<false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
@@ -506,41 +513,106 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         *reinterpret_cast<float4 *>(mine + 4 + c0) = make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
     }
-    __threadfence();
-    __syncthreads();
-    int32_t *counter = a.counters + ((int64_t)b * a.num_kv_heads + kvh) * a.head_groups + hg;
-    if (tid == 0) s_last = (atomicAdd(counter, 1) == nsplit - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
 
-    if (hh < nh) {
-        const float *base = a.partials + row * a.splits * kPartialFloats;
-        float Mt = -INFINITY;
-        for (int s = 0; s < nsplit; s++) Mt = fmaxf(Mt, base[s * kPartialFloats]);
-        float l2 = 0.0f, z2 = 0.0f, o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s = 0; s < nsplit; s++) {
-            const float *ps = base + s * kPartialFloats;
-            const float ms = ps[0];
-            const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - Mt);
-            l2 += f * ps[1];
-            z2 += f * ps[2];
-            const float4 v = *reinterpret_cast<const float4 *>(ps + 4 + c0);
-            o4[0] += f * v.x;
-            o4[1] += f * v.y;
-            o4[2] += f * v.z;
-            o4[3] += f * v.w;
-        }
-        finalize_head(o4, l2, z2, l32, a.out, a.out_f32, row);
+// Merge the split partials of each (sequence, query head) and apply the
+// Hadamard epilogue.  Runs after decode_kernel on the same stream (the kernel
+// boundary makes every partial visible).  Each wave handles two rows, 32 lanes
+// per row, 4 channels per lane.
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int l32 = lane & 31;
+    const int64_t row = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+    if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
+    const int b = (int)(row / a.num_q_heads);
+    int n_tokens = a.seq_lens[b];
+    n_tokens = n_tokens < 0 ? 0 : (n_tokens > a.max_seq_len ? a.max_seq_len : n_tokens);
+    const int npages = (n_tokens + kPage - 1) / kPage;
+    const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
+    if (nsplit <= 1) return;       // written by decode_kernel itself
+    const float *base = a.partials + row * a.splits * kPartialFloats;
+    // split maxima and weight sums: lane l32 takes splits l32, l32 + 32, ...
+    float M = -INFINITY;
+    for (int s = l32; s < nsplit; s += 32) M = fmaxf(M, base[s * kPartialFloats]);
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) M = fmaxf(M, xor_lane(M, x));
+    float l = 0.0f, z = 0.0f;
+    for (int s = l32; s < nsplit; s += 32) {
+        const float ms = base[s * kPartialFloats];
+        const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
+        l += f * base[s * kPartialFloats + 1];
+        z += f * base[s * kPartialFloats + 2];
     }
-    if (tid == 0) *counter = 0;
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) {
+        l += xor_lane(l, x);
+        z += xor_lane(z, x);
+    }
+    // value sums: every lane walks all splits for its 4 channels; unrolled so
+    // that eight splits' loads are in flight at once
+    const int c0 = 4 * l32;
+    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+        float ms[8];
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            ms[u] = base[(s + u) * kPartialFloats];
+            v[u] = *reinterpret_cast<const float4 *>(base + (s + u) * kPartialFloats + 4 + c0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float f = (ms[u] == -INFINITY) ? 0.0f : fast_exp2(ms[u] - M);
+            o4[0] += f * v[u].x;
+            o4[1] += f * v[u].y;
+            o4[2] += f * v[u].z;
+            o4[3] += f * v[u].w;
+        }
+    }
+    for (; s < nsplit; s++) {
+        const float ms = base[s * kPartialFloats];
+        const float4 v = *reinterpret_cast<const float4 *>(base + s * kPartialFloats + 4 + c0);
+        const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
+        o4[0] += f * v.x;
+        o4[1] += f * v.y;
+        o4[2] += f * v.z;
+        o4[3] += f * v.w;
+    }
+    finalize_head(o4, l, z, l32, a.out, a.out_f32, row);
 }
 
 }  // namespace
 
+int decode_resident_workgroups() {
+    // Work-groups of decode_kernel the current device holds at once (compute
+    // units x occupancy), queried once per device; 512 without a device.
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 512;
+    }
+    if (cached[dev] > 0) return cached[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel, 256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        return 512;
+    }
+    cached[dev] = cus * per_cu;
+    return cached[dev];
+}
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
     hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits <= 1) return e;
+    const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+    const int64_t blocks = (rows + 2 * kWaves - 1) / (2 * kWaves);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -92,9 +92,11 @@ struct DecodeArgs {
     int32_t pages_per_split;
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
-    int32_t *counters;        // [num_seqs][num_kv_heads][head_groups]
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// Work-groups of the decode kernel that the current device runs at once.
+int decode_resident_workgroups();
 
 }  // namespace kvq

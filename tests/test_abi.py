@@ -62,8 +62,10 @@ def test_workspace_sizing_and_heuristic():
     assert pps > 0 and pps % 2 == 0
     n = kvq.decode_workspace_bytes(8, 64, 8, 16385)
     splits = -(-1025 // pps)
-    assert n >= 8 * 64 * splits * 132 * 4 + 8 * 8 * 4
+    assert n >= 8 * 64 * splits * 132 * 4
     assert kvq.decode_workspace_bytes(8, 64, 8, 16385, 16) >= 8 * 64 * 65 * 132 * 4
+    # a single split needs no partials
+    assert kvq.decode_workspace_bytes(1, 8, 1, 32, 2) <= 256
     with pytest.raises(kvq.KvqError):
         kvq.decode_workspace_bytes(8, 60, 8, 16385)        # Hq % Hkv != 0
     with pytest.raises(kvq.KvqError):
