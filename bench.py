@@ -9,8 +9,17 @@ Synthetic seeded inputs (kvq_inputs); no model weights or datasets.
 Timing: inputs resident in HBM; W untimed warm-up steps, then K timed steps
 bracketed by torch.cuda.synchronize().  Each step runs on the next of R
 copies of the pool (R x 109 MB, more than the 256 MB Infinity Cache), so
-every decode reads its 109 MB from HBM.  The decode kernel is timed with HIP
-events on the stream it runs on, inside the timed region.
+every decode reads its 109 MB from HBM.  A step is three C-ABI calls on one
+stream: kvq_quantize_append, kvq_decode_partials (the split kernel, the
+dominant one) and kvq_decode_combine.  HIP events recorded on that stream
+around the split kernel time it inside the timed region (roofline.achieved).
+
+roofline.traffic: HBM bytes per launch of the split kernel from rocprofv3
+FETCH_SIZE and WRITE_SIZE counter runs, each scaled by the factor the same
+counter reads for a device-to-device copy of known size.  The figures are
+read from profiles/decode_kernel_qwen3_32b_16k_traffic.txt and reported only
+while the kernel sources still hash to the value recorded there (null
+otherwise).  --copy-probe-mb adds the calibration copy to a run.
 
 Prints one JSON line.  N > 1 GPUs is not supported: this build measures one
 GPU's share (see the design notes for how the path shards).
@@ -19,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -46,7 +56,42 @@ def parse():
     ap.add_argument("--cpu-groups", type=int, default=8, help="(sequence, KV head) groups in the CPU sample")
     ap.add_argument("--no-append-bench", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_32b_16k_traffic.txt")
+DECODE_SOURCES = [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "csrc", f)
+                  for f in ("kvq_decode.hip", "kvq_device.h")]
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None,
+    reason) when it is missing or the kernel changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    rec = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256") != decode_source_hash():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"]), \
+            f"fetch {rec['fetch_bytes_per_launch']} + write {rec['write_bytes_per_launch']} B (scaled)"
+    except (KeyError, ValueError):
+        return None, "malformed counter summary"
 
 
 class DecodeCall:
@@ -61,14 +106,20 @@ class DecodeCall:
                 ctypes.c_int64(v.stride(0)), P(slots.data_ptr()), ctypes.c_int64(k.shape[0]),
                 ctypes.c_int32(k.shape[1]), P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]), self.stream)
 
-    def decode_args(self, out, q, cache, bt, lens, max_len, ws, pps):
+    def partials_args(self, q, cache, bt, lens, max_len, ws, pps):
         P = ctypes.c_void_p
-        return (self.fmt, P(out.data_ptr()), 0 if out.dtype.itemsize == 2 else 1, P(q.data_ptr()),
-                P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]), P(bt.data_ptr()),
-                ctypes.c_int32(bt.shape[1]), P(lens.data_ptr()), ctypes.c_int32(q.shape[0]),
+        return (self.fmt, P(q.data_ptr()), P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]),
+                P(bt.data_ptr()), ctypes.c_int32(bt.shape[1]), P(lens.data_ptr()), ctypes.c_int32(q.shape[0]),
                 ctypes.c_int32(q.shape[1]), ctypes.c_int32(cache.shape[1]), ctypes.c_int32(max_len),
                 ctypes.c_float(1.0 / math.sqrt(128)), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                 ctypes.c_int32(pps), self.stream)
+
+    def combine_args(self, out, lens, num_q_heads, num_kv_heads, max_len, ws, pps):
+        P = ctypes.c_void_p
+        return (self.fmt, P(out.data_ptr()), 0 if out.dtype.itemsize == 2 else 1, P(lens.data_ptr()),
+                ctypes.c_int32(lens.numel()), ctypes.c_int32(num_q_heads), ctypes.c_int32(num_kv_heads),
+                ctypes.c_int32(max_len), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()), ctypes.c_int32(pps),
+                self.stream)
 
 
 def cpu_baseline(w, groups: int):
@@ -120,6 +171,15 @@ def main():
 
     dev = torch.device("cuda:0")
     lib = kvq.load()
+    if args.copy_probe_mb > 0:
+        # calibration for the byte counters: one plain copy of known size
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     fmt = kvq.format_from_string("kvarn_k4v2_g128")
     stream = torch.cuda.current_stream()
     call = DecodeCall(kvq, lib, fmt, stream.cuda_stream)
@@ -154,25 +214,28 @@ def main():
     torch.cuda.synchronize()
 
     app_args = [call.append_args(new_k, new_v, slots, p) for p in pools]
-    dec_args = [call.decode_args(out, q, p, bt, lens, n, ws, pps) for p in pools]
-    append_fn, decode_fn = lib.kvq_quantize_append, lib.kvq_decode_attention_ex
+    part_args = [call.partials_args(q, p, bt, lens, n, ws, pps) for p in pools]
+    comb_args = call.combine_args(out, lens, Hq, Hkv, n, ws, pps)
+    append_fn, part_fn, comb_fn = lib.kvq_quantize_append, lib.kvq_decode_partials, lib.kvq_decode_combine
 
     def step(i, ev=None):
         r = i % len(pools)
         st = append_fn(*app_args[r])
         if ev is not None:
             ev[0].record(stream)
-        st |= decode_fn(*dec_args[r])
+        st |= part_fn(*part_args[r])
         if ev is not None:
             ev[1].record(stream)
+        st |= comb_fn(*comb_args)
+        if ev is not None:
+            ev[2].record(stream)
         return st
 
     for i in range(args.warmup):
         if step(i):
             raise RuntimeError("kvq call failed during warm-up")
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     bad = 0
@@ -183,8 +246,10 @@ def main():
     if bad:
         raise RuntimeError("kvq call failed in the timed region")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
     dec_avg_ms = float(np.mean(dec_ms))
+    traffic, traffic_note = recorded_traffic()
 
     kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -202,9 +267,10 @@ def main():
         "decode_kernel_ms": round(dec_avg_ms, 5),
         "decode_kernel_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 5),
                                      round(float(np.percentile(dec_ms, 90)), 5)],
+        "combine_kernel_ms": round(float(np.mean(comb_ms)), 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "bytes_per_launch": kv_bytes},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel", "bytes_per_launch": kv_bytes, "traffic_note": traffic_note},
     }
 
     if not args.no_append_bench:

@@ -126,9 +126,11 @@ kvq_status kvq_quantize_append(const kvq_format *fmt,
                                int32_t num_kv_heads, uint8_t *cache, int64_t num_pages,
                                void *stream);
 
-/* Workspace bytes kvq_decode_attention needs for these sizes (0 on invalid
+/* Workspace bytes the decode calls need for these sizes (0 on invalid
  * input).  pages_per_split = 0 selects the library's split heuristic; a
- * positive value forces that many pages per split (see _ex below). */
+ * positive value forces that many pages per split (see _ex below).  The
+ * workspace holds the split partials, fp32 [num_seqs][num_q_heads][splits][132]
+ * with splits = ceil(ceil(max_seq_len / 16) / pages_per_split). */
 size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_seq_len, int32_t pages_per_split);
@@ -177,6 +179,47 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
                                    int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
                                    void *workspace, size_t workspace_bytes,
                                    int32_t pages_per_split, void *stream);
+
+/*
+ * The two phases of kvq_decode_attention_ex as separate calls, for callers
+ * that time or place them separately, or that merge partials computed over
+ * disjoint page sets of one sequence (each set's partials are combined by the
+ * same log-sum-exp rule; the combine needs them in one workspace).
+ *
+ * kvq_decode_partials: the split phase [KVARN-P stage 4].  Same arguments
+ * and preconditions as kvq_decode_attention_ex without the output.  For every
+ * (sequence b, query head h) and split i < ceil(ceil(len_b / 16) /
+ * pages_per_split), writes the partial of tokens [16 i pps, 16 (i+1) pps) at
+ * float offset ((b * num_q_heads + h) * splits + i) * 132 of the workspace:
+ *   [0] m     reference level of the base-2 logits scale * log2(e) * q.k
+ *             (at most 8 below their maximum over the split's tokens),
+ *   [1] l     sum of exp2(logit - m - 8) over the split's tokens,
+ *   [2] zacc  the same weights times the value mean of each token,
+ *   [3]       unused,
+ *   [4..131]  acc, the weights times the rotated, scaled value codes
+ *             s * c (Hadamard domain, not yet transformed back).
+ * Splits past a sequence's end are not written.
+ *
+ * kvq_decode_combine: merges the partials of each (sequence, query head) and
+ * applies the inverse rotation: after rescaling every split by
+ * exp2(m_i - max_i m_i) and summing, out_j = (H acc)_j / (128 l) for j >= 1
+ * and out_0 = zacc / l.  A sequence of
+ * length 0 gets a zero row.  seq_lens, max_seq_len and pages_per_split must
+ * be those of the kvq_decode_partials call that filled the workspace (0
+ * selects the same heuristic again); the call must follow it on the same
+ * stream or after a synchronisation.
+ */
+kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
+                               int64_t num_pages, const int32_t *block_tables, int32_t max_pages_per_seq,
+                               const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                               void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                               void *stream);
+
+kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t max_seq_len, const void *workspace,
+                              size_t workspace_bytes, int32_t pages_per_split, void *stream);
 
 /* Pages per split the heuristic picks for these sizes (0 on invalid input). */
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,

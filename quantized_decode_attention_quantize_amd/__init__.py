@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "KvqError", "Format", "load", "library_path", "format_from_string", "page_bytes",
     "cache_bytes", "alloc_cache", "quantize_append", "decode_workspace_bytes",
-    "decode_pages_per_split", "alloc_workspace", "decode_attention", "version",
+    "decode_pages_per_split", "alloc_workspace", "decode_attention", "decode_partials",
+    "decode_combine", "version",
     "HEAD_DIM", "PAGE", "REGION_BYTES",
 ]
 
@@ -79,6 +80,9 @@ def load():
                                                 i32, i32, ctypes.c_float, P, sz, P]),
         "kvq_decode_attention_ex": (ctypes.c_int, [FP, P, ctypes.c_int, P, P, i64, P, i32, P, i32,
                                                    i32, i32, i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_decode_partials": (ctypes.c_int, [FP, P, P, i64, P, i32, P, i32, i32, i32, i32,
+                                               ctypes.c_float, P, sz, i32, P]),
+        "kvq_decode_combine": (ctypes.c_int, [FP, P, ctypes.c_int, P, i32, i32, i32, i32, P, sz, i32, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvq_last_hip_error": (ctypes.c_int, []),
         "kvq_version": (ctypes.c_char_p, []),
@@ -186,6 +190,20 @@ def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _decode_checks(query, cache, block_tables, seq_lens):
+    if query.dtype != torch.float16 or query.dim() != 3 or query.shape[2] != HEAD_DIM:
+        raise ValueError("query must be float16 [B][Hq][128]")
+    if not query.is_contiguous():
+        raise ValueError("query must be contiguous")
+    B = query.shape[0]
+    if cache.dim() != 3 or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [B][max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+
+
 def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
                      seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float | None = None,
                      out: torch.Tensor | None = None, out_dtype=torch.float32,
@@ -193,18 +211,9 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
                      stream=None, fmt: Format | None = None) -> torch.Tensor:
     """One decode step: query fp16 [B][Hq][128] against the pool; returns
     out [B][Hq][128] (fp32 or fp16)."""
-    if query.dtype != torch.float16 or query.dim() != 3 or query.shape[2] != HEAD_DIM:
-        raise ValueError("query must be float16 [B][Hq][128]")
-    if not query.is_contiguous():
-        raise ValueError("query must be contiguous")
+    _decode_checks(query, cache, block_tables, seq_lens)
     B, Hq, _ = query.shape
-    if cache.dim() != 3 or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
-        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
     Hkv = cache.shape[1]
-    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
-        raise ValueError("block_tables must be contiguous int32 [B][max_pages]")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
-        raise ValueError("seq_lens must be contiguous int32 [B]")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
@@ -219,4 +228,44 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
         _ptr(seq_lens), B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
         workspace.numel(), int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def decode_partials(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
+                    softmax_scale: float | None = None, pages_per_split: int = 0,
+                    stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """Split phase of a decode step: fills `workspace` with the fp32 split
+    partials [B][Hq][splits][132] (see include/kvq.h) and returns it."""
+    _decode_checks(query, cache, block_tables, seq_lens)
+    B, Hq, _ = query.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load().kvq_decode_partials(
+        ctypes.byref(_fmt(fmt)), _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), B, Hq, cache.shape[1], int(max_seq_len),
+        float(softmax_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_decode_partials")
+    return workspace
+
+
+def decode_combine(workspace: torch.Tensor, seq_lens: torch.Tensor, num_q_heads: int, num_kv_heads: int,
+                   max_seq_len: int, out: torch.Tensor | None = None, out_dtype=torch.float32,
+                   pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """Combine phase: merges the partials written by ``decode_partials`` and
+    returns out [B][Hq][128] (fp32 or fp16)."""
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [B]")
+    B = seq_lens.numel()
+    if out is None:
+        out = torch.empty((B, num_q_heads, HEAD_DIM), dtype=out_dtype, device=seq_lens.device)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or \
+            out.shape != (B, num_q_heads, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
+    st = load().kvq_decode_combine(
+        ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
+        _ptr(seq_lens), B, num_q_heads, num_kv_heads, int(max_seq_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_decode_combine")
     return out

@@ -60,10 +60,71 @@ WorkspaceLayout layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_le
     WorkspaceLayout w;
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
     w.splits = (int32_t)ceil_div(max_pages, pps);
-    const size_t partial_bytes =
-        w.splits > 1 ? (size_t)num_seqs * num_q_heads * w.splits * kvq::kPartialFloats * sizeof(float) : 0;
+    const size_t partial_bytes = (size_t)num_seqs * num_q_heads * w.splits * kvq::kPartialFloats * sizeof(float);
     w.total = ((partial_bytes + 255) & ~(size_t)255) + 256;
     return w;
+}
+
+// Checks shared by the decode entry points; fills the sizes, the split
+// decomposition and the workspace of `a`.  max_pages_per_seq < 0: no block
+// table (the combine).
+kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                         int32_t max_pages_per_seq, void *workspace, size_t workspace_bytes,
+                         int32_t pages_per_split, kvq::DecodeArgs &a) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (!seq_lens) return KVQ_ERR_NULL;
+    if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len) || pages_per_split < 0 ||
+        (pages_per_split % 2))
+        return KVQ_ERR_SHAPE;
+    if (max_pages_per_seq >= 0 &&
+        (max_pages_per_seq == 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage))
+        return KVQ_ERR_SHAPE;
+    if ((uintptr_t)seq_lens & 3u) return KVQ_ERR_ALIGN;
+    const int32_t pps = pages_per_split ? pages_per_split
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
+    if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+    if (w.splits > 65535) return KVQ_ERR_SHAPE;
+    memset(&a, 0, sizeof(a));
+    a.max_seq_len = max_seq_len;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.gqa = num_q_heads / num_kv_heads;
+    a.head_groups = head_groups(a.gqa);
+    a.splits = w.splits;
+    a.pages_per_split = pps;
+    a.partials = static_cast<float *>(workspace);
+    return KVQ_OK;
+}
+
+kvq_status decode_inputs(const uint16_t *query, const uint8_t *cache, int64_t num_pages,
+                         const int32_t *block_tables, int32_t max_pages_per_seq, float softmax_scale,
+                         kvq::DecodeArgs &a) {
+    if (!query || !cache || !block_tables) return KVQ_ERR_NULL;
+    if (num_pages <= 0) return KVQ_ERR_SHAPE;
+    if (!(softmax_scale == softmax_scale)) return KVQ_ERR_SHAPE;
+    if (!aligned16(query) || !aligned16(cache) || ((uintptr_t)block_tables & 3u)) return KVQ_ERR_ALIGN;
+    a.query = query;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.block_tables = block_tables;
+    a.bt_stride = max_pages_per_seq;
+    a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
+    return KVQ_OK;
+}
+
+kvq_status decode_output(void *out, kvq_out_dtype out_dtype, kvq::DecodeArgs &a) {
+    if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32) return KVQ_ERR_UNSUPPORTED;
+    if (!out) return KVQ_ERR_NULL;
+    if (!aligned16(out)) return KVQ_ERR_ALIGN;
+    a.out = out;
+    a.out_f32 = out_dtype == KVQ_OUT_F32;
+    return KVQ_OK;
 }
 
 }  // namespace
@@ -139,45 +200,41 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
                                    int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
                                    void *workspace, size_t workspace_bytes, int32_t pages_per_split,
                                    void *stream) {
-    if (!fmt) return KVQ_ERR_NULL;
-    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
-    if (out_dtype != KVQ_OUT_F16 && out_dtype != KVQ_OUT_F32) return KVQ_ERR_UNSUPPORTED;
-    if (!out || !query || !cache || !block_tables || !seq_lens) return KVQ_ERR_NULL;
-    if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len) || num_pages <= 0 ||
-        max_pages_per_seq <= 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage ||
-        pages_per_split < 0 || (pages_per_split % 2))
-        return KVQ_ERR_SHAPE;
-    if (!(softmax_scale == softmax_scale)) return KVQ_ERR_SHAPE;
-    if (!aligned16(out) || !aligned16(query) || !aligned16(cache) || ((uintptr_t)block_tables & 3u) ||
-        ((uintptr_t)seq_lens & 3u))
-        return KVQ_ERR_ALIGN;
-    const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
-    const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
-    if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
-    if (w.splits > 65535) return KVQ_ERR_SHAPE;
-
     kvq::DecodeArgs a;
-    a.out = out;
-    a.out_f32 = out_dtype == KVQ_OUT_F32;
-    a.query = query;
-    a.cache = cache;
-    a.num_pages = num_pages;
-    a.block_tables = block_tables;
-    a.bt_stride = max_pages_per_seq;
-    a.max_seq_len = max_seq_len;
-    a.seq_lens = seq_lens;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.gqa = num_q_heads / num_kv_heads;
-    a.head_groups = head_groups(a.gqa);
-    a.splits = w.splits;
-    a.pages_per_split = pps;
-    a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
-    a.partials = static_cast<float *>(workspace);
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st != KVQ_OK) return st;
     return hip_status(kvq::launch_decode(a, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
+                               int64_t num_pages, const int32_t *block_tables, int32_t max_pages_per_seq,
+                               const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                               void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                               void *stream) {
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st != KVQ_OK) return st;
+    a.partials_only = 1;
+    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t max_seq_len, const void *workspace,
+                              size_t workspace_bytes, int32_t pages_per_split, void *stream) {
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len, -1,
+                                  const_cast<void *>(workspace), workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
+    if (st != KVQ_OK) return st;
+    a.partials_only = 1;
+    return hip_status(kvq::launch_decode_combine(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
 
     if (n_tokens == 0) {             // empty sequence: zero output rows
-        if (split == 0 && (tid >> 5) < nh) {
+        if (!a.partials_only && split == 0 && (tid >> 5) < nh) {
             const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
             if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
             else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 
     const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
-    if (nsplit == 1) {
+    if (nsplit == 1 && !a.partials_only) {
         if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row);
         return;
     }
@@ -529,7 +529,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     n_tokens = n_tokens < 0 ? 0 : (n_tokens > a.max_seq_len ? a.max_seq_len : n_tokens);
     const int npages = (n_tokens + kPage - 1) / kPage;
     const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    if (nsplit <= 1) return;       // written by decode_kernel itself
+    if (nsplit <= 1 && !a.partials_only) return;   // written by decode_kernel itself
+    // (with partials only: no split for an empty sequence gives l = 0 and a
+    // zero row; a single split is finished from its one partial)
     const float *base = a.partials + row * a.splits * kPartialFloats;
     // split maxima and weight sums: lane l32 takes splits l32, l32 + 32, ...
     float M = -INFINITY;
@@ -605,15 +607,23 @@ int decode_resident_workgroups() {
     return cached[dev];
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
     hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.splits <= 1) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
     const int64_t blocks = (rows + 2 * kWaves - 1) / (2 * kWaves);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    const hipError_t e = launch_decode_split(a, stream);
+    if (e != hipSuccess || (a.splits <= 1 && !a.partials_only)) return e;
+    return launch_decode_combine(a, stream);
 }
 
 }  // namespace kvq

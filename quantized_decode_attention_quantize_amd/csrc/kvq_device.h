@@ -92,9 +92,16 @@ struct DecodeArgs {
     int32_t pages_per_split;
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
+    int32_t partials_only;    // 1: the split kernel writes a partial for every
+                              // split it runs (also the only one) and leaves
+                              // every output row to the combine kernel
 };
 
+// Split kernel then, if any sequence spans more than one split, the combine.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// The two phases on their own (a.partials_only = 1 for both).
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
 
 // Work-groups of the decode kernel that the current device runs at once.
 int decode_resident_workgroups();

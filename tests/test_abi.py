@@ -64,8 +64,8 @@ def test_workspace_sizing_and_heuristic():
     splits = -(-1025 // pps)
     assert n >= 8 * 64 * splits * 132 * 4
     assert kvq.decode_workspace_bytes(8, 64, 8, 16385, 16) >= 8 * 64 * 65 * 132 * 4
-    # a single split needs no partials
-    assert kvq.decode_workspace_bytes(1, 8, 1, 32, 2) <= 256
+    # one split still holds one partial per (sequence, query head)
+    assert kvq.decode_workspace_bytes(1, 8, 1, 32, 2) >= 8 * 132 * 4
     with pytest.raises(kvq.KvqError):
         kvq.decode_workspace_bytes(8, 60, 8, 16385)        # Hq % Hkv != 0
     with pytest.raises(kvq.KvqError):
@@ -118,6 +118,40 @@ def test_decode_validation_launches_nothing():
     assert call(wsb=ws - 1) == 5
     assert call(ws=None) == 5
     assert lib.kvq_decode_attention(None, g, 1, g, g, 10, g, 7, g, 2, 8, 2, 100, 0.1, g, ws, None) == 1
+
+
+def test_two_phase_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    ws = kvq.decode_workspace_bytes(2, 8, 2, 100)
+
+    def part(**kw):
+        a = dict(q=g, cache=g, np=10, bt=g, mp=7, sl=g, B=2, Hq=8, Hkv=2, L=100, scale=0.088,
+                 ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        return lib.kvq_decode_partials(_fmt(), a["q"], a["cache"], a["np"], a["bt"], a["mp"], a["sl"],
+                                       a["B"], a["Hq"], a["Hkv"], a["L"], a["scale"], a["ws"], a["wsb"],
+                                       a["pps"], None)
+
+    def comb(**kw):
+        a = dict(out=g, dt=0, sl=g, B=2, Hq=8, Hkv=2, L=100, ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        return lib.kvq_decode_combine(_fmt(), a["out"], a["dt"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["L"],
+                                      a["ws"], a["wsb"], a["pps"], None)
+
+    assert part(q=None) == 1 and part(bt=None) == 1 and part(sl=None) == 1
+    assert part(Hq=6, Hkv=4) == 2 and part(L=200) == 2 and part(mp=0) == 2 and part(np=0) == 2
+    assert part(pps=5) == 2 and part(scale=float("nan")) == 2
+    assert part(cache=P(0x10004)) == 4 and part(sl=P(0x10002)) == 4
+    assert part(wsb=ws - 1) == 5 and part(ws=None) == 5
+    assert comb(out=None) == 1 and comb(sl=None) == 1
+    assert comb(dt=7) == 3 and comb(B=0) == 2 and comb(pps=1) == 2
+    assert comb(out=P(0x10008)) == 4
+    assert comb(wsb=16) == 5
+    assert lib.kvq_decode_partials(None, g, g, 10, g, 7, g, 2, 8, 2, 100, 0.1, g, ws, 0, None) == 1
+    bad = kvq.Format(128, 64, 4, 2, 16)
+    assert lib.kvq_decode_combine(ctypes.byref(bad), g, 0, g, 2, 8, 2, 100, g, ws, 0, None) == 3
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the error path of a GPU-less host")

@@ -242,6 +242,35 @@ def test_decode_deterministic_split_invariant_and_page_placement(dev):
     assert torch.equal(a, d)
 
 
+@pytest.mark.parametrize("lens,pps", [([400, 1, 777], 0), ([400, 1, 777], 2), ([20, 0, 50], 0),
+                                      ([20, 0, 50], 4)])
+def test_decode_two_phase_matches_fused(dev, lens, pps):
+    """kvq_decode_partials + kvq_decode_combine give the bits of
+    kvq_decode_attention_ex, also for single-split and empty sequences."""
+    B, Hq, Hkv = len(lens), 16, 2
+    log(f"decode two-phase lens={lens} pps={pps}")
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, [max(n, 1) for n in lens], seed=31)
+    lens_np = np.asarray(lens, np.int64)
+    qd = torch.from_numpy(q).to(dev)
+    btd = torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for dt in (torch.float32, torch.float16):
+        fused = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=dt, pages_per_split=pps).cpu()
+        ws = kvq.alloc_workspace(B, Hq, Hkv, L, pps)
+        ws.fill_(0xA5)                                # any contents
+        kvq.decode_partials(qd, cache, btd, ld, L, ws, pages_per_split=pps)
+        two = kvq.decode_combine(ws, ld, Hq, Hkv, L, out_dtype=dt, pages_per_split=pps).cpu()
+        assert torch.equal(fused, two), f"dtype={dt}"
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert torch.count_nonzero(two[b]).item() == 0
+    ref = oracle.decode_attention(pool, bt, np.maximum(lens_np, 1), q, SCALE)
+    for b, n in enumerate(lens):
+        if n:
+            assert np.max(np.abs(two[b].float().numpy() - ref[b])) <= TOL
+
+
 def test_decode_zero_query_gives_mean_value(dev):
     B, Hq, Hkv, lens = 1, 4, 1, [123]
     cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=9)
