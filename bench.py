@@ -9,10 +9,16 @@ Synthetic seeded inputs (kvq_inputs); no model weights or datasets.
 Timing: inputs resident in HBM; W untimed warm-up steps, then K timed steps
 bracketed by torch.cuda.synchronize().  Each step runs on the next of R
 copies of the pool (R x 109 MB, more than the 256 MB Infinity Cache), so
-every decode reads its 109 MB from HBM.  A step is three C-ABI calls on one
-stream: kvq_quantize_append, kvq_decode_partials (the split kernel, the
-dominant one) and kvq_decode_combine.  HIP events recorded on that stream
-around the split kernel time it inside the timed region (roofline.achieved).
+every decode reads its 109 MB from HBM.  A step is two C-ABI calls on one
+stream: kvq_append_decode_partials (the split kernel, which also encodes each
+sequence's new token into its page before reading it; the dominant kernel)
+and kvq_decode_combine.  On every --event-every'th timed step the split
+kernel records a pair of HIP events at its own start and end
+(kvq_set_split_kernel_events, i.e. hipExtLaunchKernel's kernel events on the
+launch stream); their average elapsed time is the kernel duration behind
+roofline.achieved.  Plain event records (hipEventRecord) would add a marker
+packet to the stream and time its gap too; kernel events time the kernel
+alone but still delay the next launch by a few microseconds, hence sampling.
 
 roofline.traffic: HBM bytes per launch of the split kernel from rocprofv3
 FETCH_SIZE and WRITE_SIZE counter runs, each scaled by the factor the same
@@ -56,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-groups", type=int, default=8, help="(sequence, KV head) groups in the CPU sample")
     ap.add_argument("--no-append-bench", action="store_true")
     ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="time the split kernel with kernel events on every N-th timed step")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -94,6 +102,34 @@ def recorded_traffic():
         return None, "malformed counter summary"
 
 
+class HipEvents:
+    """Timing events from the HIP runtime the process already uses (the one
+    libkvq is linked against), through ctypes."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def elapsed_ms(self, a, b):
+        t = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(t), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
 class DecodeCall:
     """Pre-marshalled C-ABI calls (one ctypes call per kernel launch)."""
 
@@ -105,6 +141,15 @@ class DecodeCall:
         return (self.fmt, P(k.data_ptr()), P(v.data_ptr()), ctypes.c_int64(k.stride(0)),
                 ctypes.c_int64(v.stride(0)), P(slots.data_ptr()), ctypes.c_int64(k.shape[0]),
                 ctypes.c_int32(k.shape[1]), P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]), self.stream)
+
+    def fused_args(self, k, v, q, cache, bt, lens, max_len, ws, pps):
+        P = ctypes.c_void_p
+        return (self.fmt, P(k.data_ptr()), P(v.data_ptr()), ctypes.c_int64(k.stride(0)),
+                ctypes.c_int64(v.stride(0)), P(q.data_ptr()), P(cache.data_ptr()), ctypes.c_int64(cache.shape[0]),
+                P(bt.data_ptr()), ctypes.c_int32(bt.shape[1]), P(lens.data_ptr()), ctypes.c_int32(q.shape[0]),
+                ctypes.c_int32(q.shape[1]), ctypes.c_int32(cache.shape[1]), ctypes.c_int32(max_len),
+                ctypes.c_float(1.0 / math.sqrt(128)), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                ctypes.c_int32(pps), self.stream)
 
     def partials_args(self, q, cache, bt, lens, max_len, ws, pps):
         P = ctypes.c_void_p
@@ -198,56 +243,54 @@ def main():
         k, v = inp.sequence_kv(w, b, 0, ctx, device=dev)
         kvq.quantize_append(k, v, torch.from_numpy(inp.slot_mapping(bt_np, b, 0, ctx)).to(dev), base)
     pools = [base] + [base.clone() for _ in range(args.replicas - 1)]
-    new_k, new_v, slots = [], [], []
+    new_k, new_v = [], []
     for b in range(B):
         k, v = inp.sequence_kv(w, b, ctx, 1, device=dev)
         new_k.append(k)
         new_v.append(v)
-        slots.append(inp.slot_mapping(bt_np, b, ctx, 1))
-    new_k = torch.cat(new_k).contiguous()
+    new_k = torch.cat(new_k).contiguous()       # [B][Hkv][128]: token ctx of every sequence
     new_v = torch.cat(new_v).contiguous()
-    slots = torch.from_numpy(np.concatenate(slots)).to(dev)
     q = inp.queries(w, 0, device=dev).contiguous()
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
     pps = args.pages_per_split
     ws = kvq.alloc_workspace(B, Hq, Hkv, n, pps)
     torch.cuda.synchronize()
 
-    app_args = [call.append_args(new_k, new_v, slots, p) for p in pools]
-    part_args = [call.partials_args(q, p, bt, lens, n, ws, pps) for p in pools]
+    part_args = [call.fused_args(new_k, new_v, q, p, bt, lens, n, ws, pps) for p in pools]
     comb_args = call.combine_args(out, lens, Hq, Hkv, n, ws, pps)
-    append_fn, part_fn, comb_fn = lib.kvq_quantize_append, lib.kvq_decode_partials, lib.kvq_decode_combine
+    part_fn, comb_fn = lib.kvq_append_decode_partials, lib.kvq_decode_combine
+
+    set_events = lib.kvq_set_split_kernel_events
 
     def step(i, ev=None):
         r = i % len(pools)
-        st = append_fn(*app_args[r])
         if ev is not None:
-            ev[0].record(stream)
-        st |= part_fn(*part_args[r])
+            set_events(hev.ev[2 * ev], hev.ev[2 * ev + 1])
+        st = part_fn(*part_args[r])
         if ev is not None:
-            ev[1].record(stream)
+            set_events(None, None)
         st |= comb_fn(*comb_args)
-        if ev is not None:
-            ev[2].record(stream)
         return st
 
     for i in range(args.warmup):
         if step(i):
             raise RuntimeError("kvq call failed during warm-up")
     torch.cuda.synchronize()
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    sampled = {i: k for k, i in enumerate(range(0, args.steps, every))}
+    hev = HipEvents(2 * len(sampled))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     bad = 0
     for i in range(args.steps):
-        bad |= step(args.warmup + i, events[i])
+        bad |= step(args.warmup + i, sampled.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if bad:
         raise RuntimeError("kvq call failed in the timed region")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in events]
+    dec_ms = [hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]
+    hev.close()
     dec_avg_ms = float(np.mean(dec_ms))
     traffic, traffic_note = recorded_traffic()
 
@@ -261,13 +304,14 @@ def main():
         "data": "synthetic (seeded kvq_inputs; no model weights)",
         "config": {"workload": "qwen3_32b_16k", "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": 128, "context": n, "page": 16, "format": "kvq-k4v2-g128 v1",
-                   "step": "append 1 token/seq + decode", "pool_replicas": len(pools),
+                   "step": "append 1 token/seq fused into the decode split kernel + combine",
+                   "pool_replicas": len(pools),
                    "pages_per_split": pps or kvq.decode_pages_per_split(B, Hq, Hkv, n)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_kernel_ms": round(dec_avg_ms, 5),
         "decode_kernel_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 5),
                                      round(float(np.percentile(dec_ms, 90)), 5)],
-        "combine_kernel_ms": round(float(np.mean(comb_ms)), 5),
+        "event_samples": len(dec_ms),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "decode_kernel", "bytes_per_launch": kv_bytes, "traffic_note": traffic_note},

@@ -170,8 +170,9 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype 
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* As kvq_decode_attention, with the split-K granularity forced to
- * pages_per_split pages (> 0, a multiple of 2) per work-group instead of the
- * heuristic.  The workspace must be sized with the same pages_per_split. */
+ * pages_per_split pages (a multiple of 2 in [2, 512]; else KVQ_ERR_SHAPE) per
+ * work-group instead of the heuristic (which also stays within 512).  The
+ * workspace must be sized with the same pages_per_split. */
 kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
                                    const uint16_t *query, const uint8_t *cache, int64_t num_pages,
                                    const int32_t *block_tables, int32_t max_pages_per_seq,
@@ -221,9 +222,57 @@ kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype ou
                               int32_t num_kv_heads, int32_t max_seq_len, const void *workspace,
                               size_t workspace_bytes, int32_t pages_per_split, void *stream);
 
+/*
+ * A decode step that first appends the step's new token: for every sequence
+ * b with seq_lens[b] >= 1, the key and value rows new_key[b], new_value[b]
+ * (fp16 [num_seqs][num_kv_heads][128], token strides in elements, >=
+ * num_kv_heads * 128 and multiples of 8, 16-byte aligned) are quantised into
+ * token seq_lens[b] - 1 (page block_tables[b][(seq_lens[b] - 1) / 16], slot
+ * (seq_lens[b] - 1) % 16) exactly as kvq_quantize_append would store them
+ * [KVARN-HN; KVARN-P stages 1-3], and the attention then covers seq_lens[b]
+ * tokens including it [KVARN-P stage 4].  The encoding runs inside the decode
+ * kernel, in the work-group that reads that page, so the step is one launch
+ * fewer than kvq_quantize_append followed by kvq_decode_attention_ex, with
+ * identical cache bytes and output.  A page id outside the pool is not
+ * written (and is read as page 0, as in every decode call).  The cache is
+ * written, so it is not const here, and must be 128-byte aligned (else
+ * KVQ_ERR_ALIGN); sequences must not share the page that receives their new
+ * token.
+ *
+ * kvq_append_decode_attention: both phases (as kvq_decode_attention_ex).
+ * kvq_append_decode_partials: the split phase only (as kvq_decode_partials);
+ * kvq_decode_combine finishes it.
+ */
+kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                       const uint16_t *new_key, const uint16_t *new_value,
+                                       int64_t key_token_stride, int64_t value_token_stride,
+                                       const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                       const int32_t *block_tables, int32_t max_pages_per_seq,
+                                       const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                       void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                       void *stream);
+
+kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new_key, const uint16_t *new_value,
+                                      int64_t key_token_stride, int64_t value_token_stride,
+                                      const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                      const int32_t *block_tables, int32_t max_pages_per_seq,
+                                      const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                      void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                      void *stream);
+
 /* Pages per split the heuristic picks for these sizes (0 on invalid input). */
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t max_seq_len);
+
+/* Timing hook.  While start_event / stop_event (hipEvent_t handles created
+ * by the caller; either may be NULL) are set, every decode split kernel that
+ * a kvq call on this thread launches records them at its own start and end
+ * (hipExtLaunchKernel's kernel events: no extra packets on the stream, so the
+ * elapsed time is the kernel's execution time).  kvq_set_split_kernel_events
+ * (NULL, NULL) clears the hook.  Always returns KVQ_OK. */
+kvq_status kvq_set_split_kernel_events(void *start_event, void *stop_event);
 
 /* Static description of a status code (never NULL). */
 const char *kvq_status_string(kvq_status status);

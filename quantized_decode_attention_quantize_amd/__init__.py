@@ -20,7 +20,7 @@ __all__ = [
     "KvqError", "Format", "load", "library_path", "format_from_string", "page_bytes",
     "cache_bytes", "alloc_cache", "quantize_append", "decode_workspace_bytes",
     "decode_pages_per_split", "alloc_workspace", "decode_attention", "decode_partials",
-    "decode_combine", "version",
+    "decode_combine", "append_decode_attention", "append_decode_partials", "version",
     "HEAD_DIM", "PAGE", "REGION_BYTES",
 ]
 
@@ -83,6 +83,11 @@ def load():
         "kvq_decode_partials": (ctypes.c_int, [FP, P, P, i64, P, i32, P, i32, i32, i32, i32,
                                                ctypes.c_float, P, sz, i32, P]),
         "kvq_decode_combine": (ctypes.c_int, [FP, P, ctypes.c_int, P, i32, i32, i32, i32, P, sz, i32, P]),
+        "kvq_append_decode_attention": (ctypes.c_int, [FP, P, ctypes.c_int, P, P, i64, i64, P, P, i64, P, i32,
+                                                       P, i32, i32, i32, i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_append_decode_partials": (ctypes.c_int, [FP, P, P, i64, i64, P, P, i64, P, i32, P, i32, i32, i32,
+                                                      i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_set_split_kernel_events": (ctypes.c_int, [P, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvq_last_hip_error": (ctypes.c_int, []),
         "kvq_version": (ctypes.c_char_p, []),
@@ -269,3 +274,61 @@ def decode_combine(workspace: torch.Tensor, seq_lens: torch.Tensor, num_q_heads:
         workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_decode_combine")
     return out
+
+
+def _new_token_checks(new_key, new_value, B, Hkv):
+    for t in (new_key, new_value):
+        if t.dtype != torch.float16 or t.dim() != 3 or tuple(t.shape) != (B, Hkv, HEAD_DIM):
+            raise ValueError("new_key/new_value must be float16 [B][num_kv_heads][128]")
+        if t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+            raise ValueError("new_key/new_value heads must be contiguous 128-element rows")
+
+
+def append_decode_attention(new_key: torch.Tensor, new_value: torch.Tensor, query: torch.Tensor,
+                            cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                            max_seq_len: int, softmax_scale: float | None = None, out: torch.Tensor | None = None,
+                            out_dtype=torch.float32, workspace: torch.Tensor | None = None,
+                            pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """One decode step that first appends the new token of every sequence:
+    new_key/new_value fp16 [B][num_kv_heads][128] go into token seq_lens[b]-1,
+    then attention over seq_lens[b] tokens.  Returns out [B][Hq][128]."""
+    _decode_checks(query, cache, block_tables, seq_lens)
+    B, Hq, _ = query.shape
+    Hkv = cache.shape[1]
+    _new_token_checks(new_key, new_value, B, Hkv)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=out_dtype, device=query.device)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device)
+    st = load().kvq_append_decode_attention(
+        ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
+        _ptr(new_key), _ptr(new_value), new_key.stride(0), new_value.stride(0), _ptr(query), _ptr(cache),
+        cache.shape[0], _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, Hq, Hkv,
+        int(max_seq_len), float(softmax_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_append_decode_attention")
+    return out
+
+
+def append_decode_partials(new_key: torch.Tensor, new_value: torch.Tensor, query: torch.Tensor,
+                           cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, workspace: torch.Tensor, softmax_scale: float | None = None,
+                           pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """Split phase of ``append_decode_attention``; ``decode_combine`` finishes it."""
+    _decode_checks(query, cache, block_tables, seq_lens)
+    B, Hq, _ = query.shape
+    Hkv = cache.shape[1]
+    _new_token_checks(new_key, new_value, B, Hkv)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load().kvq_append_decode_partials(
+        ctypes.byref(_fmt(fmt)), _ptr(new_key), _ptr(new_value), new_key.stride(0), new_value.stride(0),
+        _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_append_decode_partials")
+    return workspace

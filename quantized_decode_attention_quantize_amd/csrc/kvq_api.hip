@@ -9,6 +9,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local kvq::LaunchEvents g_split_events;
 
 bool is_v1(const kvq_format *f) {
     return f && f->head_dim == 128 && f->group_size == 128 && f->k_bits == 4 && f->v_bits == 2 &&
@@ -41,7 +42,7 @@ int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
     int64_t pps = ceil_div(max_pages, splits);
     pps = ceil_div(pps, 2) * 2;
     if (pps < 2) pps = 2;
-    if (pps > 0x3fffffff) pps = 0x3fffffff;
+    if (pps > kvq::kMaxPagesPerSplit) pps = kvq::kMaxPagesPerSplit;
     return (int32_t)pps;
 }
 
@@ -76,7 +77,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
     if (!seq_lens) return KVQ_ERR_NULL;
     if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len) || pages_per_split < 0 ||
-        (pages_per_split % 2))
+        (pages_per_split % 2) || pages_per_split > kvq::kMaxPagesPerSplit)
         return KVQ_ERR_SHAPE;
     if (max_pages_per_seq >= 0 &&
         (max_pages_per_seq == 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage))
@@ -115,6 +116,22 @@ kvq_status decode_inputs(const uint16_t *query, const uint8_t *cache, int64_t nu
     a.block_tables = block_tables;
     a.bt_stride = max_pages_per_seq;
     a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
+    return KVQ_OK;
+}
+
+kvq_status append_inputs(const uint16_t *new_key, const uint16_t *new_value, int64_t key_token_stride,
+                         int64_t value_token_stride, kvq::DecodeArgs &a) {
+    if (!new_key || !new_value) return KVQ_ERR_NULL;
+    const int64_t row = (int64_t)a.num_kv_heads * kvq::kHeadDim;
+    if (key_token_stride < row || value_token_stride < row) return KVQ_ERR_SHAPE;
+    if (!aligned16(new_key) || !aligned16(new_value) || (key_token_stride % 8) || (value_token_stride % 8) ||
+        ((uintptr_t)a.cache & 127u))
+        return KVQ_ERR_ALIGN;
+    a.append = 1;
+    a.new_key = new_key;
+    a.new_value = new_value;
+    a.new_key_stride = key_token_stride;
+    a.new_value_stride = value_token_stride;
     return KVQ_OK;
 }
 
@@ -187,7 +204,7 @@ int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads, int32_
 size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split) {
     if (!is_v1(fmt) || !decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
-    if (pages_per_split < 0 || (pages_per_split % 2)) return 0;
+    if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > kvq::kMaxPagesPerSplit) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
                                         : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
     return layout(num_seqs, num_q_heads, max_seq_len, pps).total;
@@ -206,7 +223,7 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
     if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
     if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
     if (st != KVQ_OK) return st;
-    return hip_status(kvq::launch_decode(a, (hipStream_t)stream));
+    return hip_status(kvq::launch_decode(a, (hipStream_t)stream, g_split_events));
 }
 
 kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
@@ -221,7 +238,44 @@ kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, con
     if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
     if (st != KVQ_OK) return st;
     a.partials_only = 1;
-    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream));
+    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream, g_split_events));
+}
+
+kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new_key, const uint16_t *new_value,
+                                      int64_t key_token_stride, int64_t value_token_stride,
+                                      const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                      const int32_t *block_tables, int32_t max_pages_per_seq,
+                                      const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                      void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                      void *stream) {
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
+    if (st != KVQ_OK) return st;
+    a.partials_only = 1;
+    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream, g_split_events));
+}
+
+kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                       const uint16_t *new_key, const uint16_t *new_value,
+                                       int64_t key_token_stride, int64_t value_token_stride,
+                                       const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                       const int32_t *block_tables, int32_t max_pages_per_seq,
+                                       const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                       void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                       void *stream) {
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
+    if (st != KVQ_OK) return st;
+    return hip_status(kvq::launch_decode(a, (hipStream_t)stream, g_split_events));
 }
 
 kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
@@ -246,6 +300,12 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype 
     return kvq_decode_attention_ex(fmt, out, out_dtype, query, cache, num_pages, block_tables,
                                    max_pages_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                                    max_seq_len, softmax_scale, workspace, workspace_bytes, 0, stream);
+}
+
+kvq_status kvq_set_split_kernel_events(void *start_event, void *stop_event) {
+    g_split_events.start = static_cast<hipEvent_t>(start_event);
+    g_split_events.stop = static_cast<hipEvent_t>(stop_event);
+    return KVQ_OK;
 }
 
 const char *kvq_status_string(kvq_status status) {

@@ -1,42 +1,14 @@
-// Quantise-on-write of new key/value tokens into the K4V2 g128 paged cache.
-//
-// Method: the KVarN write path -- Hadamard rotation, variance normalisation,
-// asymmetric round-to-nearest to 4-bit keys / 2-bit values (dothoosh.com,
-// "KVarN vs TurboQuant: 5x more context with higher accuracy", pipeline list
-// stages 1-3; beyondheadline.xyz, "Huawei's KV-cache trick", section "The
-// claim that breaks the usual trade-off").
-//
-// Mapping: one 16-lane row of a wave encodes one group = (token, KV head,
-// key|value); lane r of the row holds channels 8r..8r+7 in registers.  The
-// FWHT runs stages h = 1, 2, 4 inside a lane and h = 8, 16, 32, 64 across
-// lanes r^1, r^2, r^4, r^8, so every butterfly is the same fp32 a+b / a-b, in
-// the same stage order, as the format's definition.  The sum of squares uses
-// the format's fixed pairwise tree (lanes ^8, ^4, ^2, ^1, then in-lane 4, 2,
-// 1); IEEE addition is commutative, so both lanes of a pair hold identical
-// bits.  Codes are therefore bit-identical to any correct implementation of
-// the format.  No fused multiply-add may be formed in this file.
-//
-// Metadata per group: fp16 scale s = delta * sigma and one fp16 offset: the
-// zero m * sigma for keys, the group mean sigma * (m + delta * C / 128) for
-// values (C = sum of the codes), which is the dequantised original channel 0.
+// Quantise-on-write of new key/value tokens into the K4V2 g128 paged cache:
+// one 16-lane row per group = (token, KV head, key|value), encoded by
+// encode_group (kvq_quant.h).
 #pragma clang fp contract(off)
 
-#include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kRowsPerBlock = 16;   // 256 threads, 16 groups
-
-// The metadata is defined as an fp32 product rounded to fp16.  Left alone, the
-// compiler fuses "fp32 multiply, convert to fp16" into one mixed-precision FMA
-// that rounds only once, which differs from the definition at fp16 ties (and
-// rotated values of subnormal inputs land on such ties often).  An empty asm
-// statement pins the fp32 product in a register before the conversion.
-__device__ __forceinline__ float materialize(float x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
 
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
@@ -57,148 +29,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     const uint16_t *src = is_v ? a.value + tok * a.value_stride + (int64_t)head * kHeadDim
                                : a.key + tok * a.key_stride + (int64_t)head * kHeadDim;
-    const uint4 raw = *reinterpret_cast<const uint4 *>(src + 8 * r);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        y[2 * e] = half_bits_to_float(w[e] & 0xffffu);
-        y[2 * e + 1] = half_bits_to_float(w[e] >> 16);
-    }
-
-    // 1. Hadamard rotation: in-lane stages h = 1, 2, 4 ...
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            if ((e & h) == 0) {
-                const float p = y[e], q = y[e + h];
-                y[e] = p + q;
-                y[e + h] = p - q;
-            }
-        }
-    }
-    // ... cross-lane stages h = 8, 16, 32, 64 (lane r ^ (h / 8))
-#pragma unroll
-    for (int x = 1; x < 16; x <<= 1) {
-        const bool upper = (r & x) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const float other = xor_lane(y[e], x);
-            y[e] = upper ? (other - y[e]) : (y[e] + other);
-        }
-    }
-
-    // 2. Variance normalisation: RMS over the group, fixed pairwise tree.
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) p[e] = y[e] * y[e];
-#pragma unroll
-    for (int x = 8; x >= 1; x >>= 1) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) p[e] = p[e] + xor_lane(p[e], x);
-    }
-    p[0] = p[0] + p[4]; p[1] = p[1] + p[5]; p[2] = p[2] + p[6]; p[3] = p[3] + p[7];
-    p[0] = p[0] + p[2]; p[1] = p[1] + p[3];
-    const float ss = p[0] + p[1];
-
-    const int L = is_v ? 3 : 15;
-    uint32_t code[8];
-    float sm = 0.0f, zm = 0.0f;   // metadata before fp16 rounding
-    if (ss == 0.0f) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) code[e] = 0;
-    } else {
-        const float sigma = sqrtf(ss * 0x1p-7f);
-        const float rcp = 1.0f / sigma;
-        float lo, hi;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-            y[e] = y[e] * rcp;
-            lo = e ? fminf(lo, y[e]) : y[e];
-            hi = e ? fmaxf(hi, y[e]) : y[e];
-        }
-#pragma unroll
-        for (int x = 1; x < 16; x <<= 1) {
-            lo = fminf(lo, xor_lane(lo, x));
-            hi = fmaxf(hi, xor_lane(hi, x));
-        }
-        // 3. Asymmetric round-to-nearest (ties to even), clamp to [0, L].
-        float delta = 0.0f;
-        if (hi == lo) {
-#pragma unroll
-            for (int e = 0; e < 8; e++) code[e] = 0;
-        } else {
-            const float range = hi - lo;
-            delta = range / (float)L;
-            const float inv = (float)L / range;
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float c = rintf((y[e] - lo) * inv);
-                code[e] = c > (float)L ? (uint32_t)L : (uint32_t)c;
-            }
-        }
-        sm = delta * sigma;
-        if (!is_v) {
-            zm = lo * sigma;                       // keys: the zero
-        } else {
-            // values: the group mean sigma * (m + delta * C / 128), C = sum of codes
-            uint32_t csum = 0;
-#pragma unroll
-            for (int e = 0; e < 8; e++) csum += code[e];
-#pragma unroll
-            for (int x = 1; x < 16; x <<= 1) csum += xor_lane_u(csum, x);
-            float t = delta * (float)csum;
-            t = t * 0x1p-7f;
-            t = lo + t;
-            zm = t * sigma;
-        }
-    }
-    const uint32_t s16 = float_to_half_bits(materialize(sm));
-    uint32_t z16 = float_to_half_bits(materialize(zm));
-    if (z16 == 0x8000u) z16 = 0;   // a zero offset is stored as +0
-
     uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)kRegion;
-    if (!is_v) {
-        // keys: byte b of the token's 64 = code[2b] | code[2b+1] << 4
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < 8; e++) packed |= code[e] << (4 * e);
-        *reinterpret_cast<uint32_t *>(region + kKCodes + 64 * off + 4 * r) = packed;
-        if (r == 0)
-            *reinterpret_cast<uint32_t *>(region + kKMeta + 4 * off) = s16 | (z16 << 16);
-    } else {
-        // values: u16 word for m holds code(16j + m) << 2j, j = 0..7.  Lane r
-        // has channels 8r..8r+7, i.e. j = r/2 and m = 8(r&1) + e.  Reduce the
-        // 8 lanes that share r&1 with a transpose-OR over lanes ^2, ^4, ^8:
-        // each step keeps half of the words and ORs in the partner's half.
-        uint32_t v8[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) v8[e] = code[e] << (2 * (r >> 1));
-        const bool b1 = (r & 2) != 0, b2 = (r & 4) != 0, b3 = (r & 8) != 0;
-        uint32_t v4[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const uint32_t send = b1 ? v8[k] : v8[4 + k];
-            const uint32_t keep = b1 ? v8[4 + k] : v8[k];
-            v4[k] = keep | xor_lane_u(send, 2);
-        }
-        uint32_t v2[2];
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const uint32_t send = b2 ? v4[k] : v4[2 + k];
-            const uint32_t keep = b2 ? v4[2 + k] : v4[k];
-            v2[k] = keep | xor_lane_u(send, 4);
-        }
-        const uint32_t send = b3 ? v2[0] : v2[1];
-        const uint32_t keep = b3 ? v2[1] : v2[0];
-        const uint32_t word = keep | xor_lane_u(send, 8);
-        const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + (int)b3;
-        const int g = off >> 2, i = off & 3;
-        *reinterpret_cast<uint16_t *>(region + kVCodes + 128 * g + 8 * m + 2 * i) = (uint16_t)word;
-        if (r == 0)
-            *reinterpret_cast<uint32_t *>(region + kVMeta + 4 * off) = s16 | (z16 << 16);
-    }
+    encode_group(src, is_v, r, region, off);
 }
 
 }  // namespace

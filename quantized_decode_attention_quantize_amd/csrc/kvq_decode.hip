@@ -49,9 +49,11 @@
 // device-scope release and acquire per work-group, i.e. a write-back and an
 // invalidate of the XCD's L2 each time; measured, that cost several times
 // the whole page stream.)
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -285,6 +287,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    // Page ids of this wave's page pairs, one pair per lane: lane j holds the
+    // block-table entries of pages 2k and 2k + 1 of the split, k = wave + 4j
+    // (a split has at most 512 pages, so j < 64; indices are clamped into the
+    // row, and entries past the split or the sequence are never used).  One
+    // vector load at the start replaces a scalar load and wait per pair; the
+    // pair loop reads the ids with v_readlane.
+    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
+    int32_t bt_a, bt_b;
+    {
+        const int last = a.bt_stride - 1;
+        const int pa = split * a.pages_per_split + 2 * (wave + kWaves * lane);
+        bt_a = bt[pa < last ? pa : last];
+        bt_b = bt[pa + 1 < last ? pa + 1 : last];
+    }
+
     const int max_len = a.max_seq_len;
     int n_tokens = a.seq_lens[b];
     n_tokens = n_tokens < 0 ? 0 : (n_tokens > max_len ? max_len : n_tokens);
@@ -313,7 +330,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
-    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
     const int64_t head_off = (int64_t)kvh * kRegion;
     const int64_t page_stride = (int64_t)a.num_kv_heads * kRegion;
 
@@ -321,8 +337,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // access (the output is unspecified under that precondition violation).
     const LaneOffsets lo(lane);
     const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
-    auto page_ptr = [&](int p) -> const uint8_t * {
-        uint32_t id = (uint32_t)bt[p];
+    auto region_of = [&](int32_t page_id) -> const uint8_t * {
+        uint32_t id = (uint32_t)page_id;
         if (id >= num_pages32) id = 0;           // also catches negative ids
         return a.cache + (int64_t)id * page_stride + head_off;
     };
@@ -342,14 +358,46 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // loads into the next pair's arithmetic (which it otherwise does to save
     // registers, leaving the current pair's loads as the newest in flight).
     auto issue = [&](PageRegs &A, PageRegs &B, int i) {
-        const int kk = wave + kWaves * (i < nk ? i : nk - 1);
-        const int pa = p_begin + 2 * kk;
-        load_page(page_ptr(pa), lo, A);
-        load_page(page_ptr(pa + 1), lo, B);
+        const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
+        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j)), lo, A);
+        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j)), lo, B);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // Fused append: a work-group whose split holds the sequence's last token
+    // encodes that token (the key and the value group of its KV head) into
+    // the cache before any of its waves reads the page.  With more than one
+    // head group per KV head, every such work-group stores the same bytes; each
+    // reads the page only after its own stores have completed.
+    if (a.append) {
+        const int pos = n_tokens - 1;
+        const int pnew = pos / kPage;
+        if (pnew >= p_begin && pnew < p_end) {
+            if (wave == 0 && lane < 32) {
+                const uint32_t id = (uint32_t)bt[pnew];
+                if (id < num_pages32) {
+                    const int is_v = lane >> 4;
+                    const uint16_t *src = is_v
+                        ? a.new_value + (int64_t)b * a.new_value_stride + (int64_t)kvh * kHeadDim
+                        : a.new_key + (int64_t)b * a.new_key_stride + (int64_t)kvh * kHeadDim;
+                    uint8_t *region = const_cast<uint8_t *>(a.cache) + (int64_t)id * page_stride + head_off;
+                    encode_group(src, is_v, lane & 15, region, pos % kPage);
+                }
+            }
+            // the stores have reached L2 before any wave of the group loads
+            // the page (regions are 128-byte aligned, so no other work-group
+            // holds one of their cache lines)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __syncthreads();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
+    }
+
     // The first two pairs are requested before the query prologue so that
-    // their HBM latency overlaps it.
+    // their HBM latency overlaps it.  The empty asm consumes the page ids on
+    // every path, so the wait for their load is placed here and not repeated
+    // (as a wait for all loads in flight) inside the pair loop.
+    asm volatile("" ::"v"(bt_a), "v"(bt_b));
     PageRegs r0A, r0B, r1A, r1B, r2A, r2B;
     if (nk > 0) {
         issue(r0A, r0B, 0);
@@ -450,8 +498,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (last_partial && wave == (npairs - 1) % kWaves) {
         PageRegs tA, tB;
         const bool has_b = last_pa + 1 < p_end;
-        load_page(page_ptr(last_pa), lo, tA);
-        load_page(page_ptr(has_b ? last_pa + 1 : last_pa), lo, tB);
+        const int j = (npairs - 1) / kWaves;    // this wave's last pair
+        const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
+        load_page(region_of(id_a), lo, tA);
+        load_page(region_of(has_b ? __builtin_amdgcn_readlane(bt_b, j) : id_a), lo, tB);
         process_pair<true>(tA, tB, last_pa * kPage, has_b ? (last_pa + 1) * kPage : n_tokens,
                            n_tokens, bq, lc, g, st);
     }
@@ -607,9 +657,12 @@ int decode_resident_workgroups() {
     return cached[dev];
 }
 
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
-    hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
+    if (ev.start || ev.stop)
+        hipExtLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -620,8 +673,8 @@ hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-    const hipError_t e = launch_decode_split(a, stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+    const hipError_t e = launch_decode_split(a, stream, ev);
     if (e != hipSuccess || (a.splits <= 1 && !a.partials_only)) return e;
     return launch_decode_combine(a, stream);
 }

@@ -21,6 +21,7 @@ constexpr int kVMeta = 1600;    // token o: (s, z) fp16 at 1600 + 4o
 constexpr int kWaves = 4;           // waves per work-group
 constexpr int kHeadsPerGroup = 8;   // query heads per MFMA column block (hi + lo = 16 columns)
 constexpr int kPartialFloats = 132; // m, l, zacc, pad, acc[128]
+constexpr int kMaxPagesPerSplit = 512;  // 64 page pairs per wave (one per lane)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -95,12 +96,27 @@ struct DecodeArgs {
     int32_t partials_only;    // 1: the split kernel writes a partial for every
                               // split it runs (also the only one) and leaves
                               // every output row to the combine kernel
+    // Fused append (append != 0): token seq_lens[b] - 1 of every sequence is
+    // encoded from new_key / new_value [num_seqs][num_kv_heads][128] (token
+    // strides in elements) before it is attended to.
+    int32_t append;
+    const uint16_t *new_key;
+    const uint16_t *new_value;
+    int64_t new_key_stride;
+    int64_t new_value_stride;
+};
+
+// Start/stop events the split kernel records at its own start and end
+// (hipExtLaunchKernel's kernel events); NULL for none.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
 };
 
 // Split kernel then, if any sequence spans more than one split, the combine.
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev);
 // The two phases on their own (a.partials_only = 1 for both).
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev);
 hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
 
 // Work-groups of the decode kernel that the current device runs at once.

@@ -70,6 +70,11 @@ def test_workspace_sizing_and_heuristic():
         kvq.decode_workspace_bytes(8, 60, 8, 16385)        # Hq % Hkv != 0
     with pytest.raises(kvq.KvqError):
         kvq.decode_workspace_bytes(8, 64, 8, 16385, 3)     # odd split
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_workspace_bytes(8, 64, 8, 16385, 514)   # above 512 pages per split
+    assert kvq.decode_workspace_bytes(1, 8, 1, 1 << 20, 512) > 0
+    # the heuristic stays within 512 pages per split even for one long sequence
+    assert kvq.decode_pages_per_split(1, 8, 8, 1 << 24) <= 512
 
 
 def _fmt():
@@ -113,6 +118,7 @@ def test_decode_validation_launches_nothing():
     assert call(B=0) == 2
     assert call(L=200) == 2                     # max_seq_len > max_pages * 16
     assert call(pps=3) == 2
+    assert call(pps=514) == 2
     assert call(dt=5) == 3
     assert call(q=P(0x10008)) == 4
     assert call(wsb=ws - 1) == 5
@@ -173,3 +179,37 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError):
         mod.load()
     importlib.reload(kvq)
+
+
+def test_fused_append_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    ws = kvq.decode_workspace_bytes(2, 8, 2, 100)
+
+    def full(**kw):
+        a = dict(out=g, dt=1, k=g, v=g, ks=256, vs=256, q=g, cache=g, np=10, bt=g, mp=7, sl=g, B=2, Hq=8,
+                 Hkv=2, L=100, scale=0.088, ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        return lib.kvq_append_decode_attention(_fmt(), a["out"], a["dt"], a["k"], a["v"], a["ks"], a["vs"],
+                                               a["q"], a["cache"], a["np"], a["bt"], a["mp"], a["sl"], a["B"],
+                                               a["Hq"], a["Hkv"], a["L"], a["scale"], a["ws"], a["wsb"],
+                                               a["pps"], None)
+
+    def part(**kw):
+        a = dict(k=g, v=g, ks=256, vs=256, q=g, cache=g, np=10, bt=g, mp=7, sl=g, B=2, Hq=8, Hkv=2, L=100,
+                 scale=0.088, ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        return lib.kvq_append_decode_partials(_fmt(), a["k"], a["v"], a["ks"], a["vs"], a["q"], a["cache"],
+                                              a["np"], a["bt"], a["mp"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                                              a["L"], a["scale"], a["ws"], a["wsb"], a["pps"], None)
+
+    for f in (full, part):
+        assert f(k=None) == 1 and f(v=None) == 1 and f(q=None) == 1
+        assert f(ks=255) == 2 and f(vs=128) == 2           # below num_kv_heads * 128
+        assert f(ks=260) == 4                              # not a multiple of 8
+        assert f(k=P(0x10008)) == 4
+        assert f(cache=P(0x10010)) == 4                    # 16- but not 128-byte aligned
+        assert f(Hq=6, Hkv=4) == 2 and f(L=200) == 2
+        assert f(wsb=ws - 1) == 5
+    assert full(out=None) == 1 and full(dt=9) == 3

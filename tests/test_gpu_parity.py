@@ -6,6 +6,7 @@ output).  Small cases are checked in full; the five workloads at full size in
 the launch configuration the benchmark uses, on sampled (sequence, KV head)
 groups that the oracle recomputes from the same seeded inputs.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -269,6 +270,126 @@ def test_decode_two_phase_matches_fused(dev, lens, pps):
     for b, n in enumerate(lens):
         if n:
             assert np.max(np.abs(two[b].float().numpy() - ref[b])) <= TOL
+
+
+FUSED = [
+    # B, Hq, Hkv, lens including the new token, pages_per_split
+    (1, 8, 1, [1], 0),
+    (2, 8, 1, [16, 17], 0),
+    (3, 16, 2, [400, 33, 777], 0),
+    (3, 16, 2, [400, 32, 776], 2),      # new token fills a page inside the pair loop
+    (2, 32, 2, [300, 129], 0),          # G = 16: two head groups store the same bytes
+    (2, 64, 8, [513, 64], 4),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,pps", FUSED)
+def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps):
+    """kvq_append_decode_attention (and its partials + combine form) leaves the
+    cache bytes and the output of kvq_quantize_append followed by
+    kvq_decode_attention_ex, bit for bit, and both match the oracle."""
+    log(f"fused append+decode B={B} Hq={Hq} Hkv={Hkv} lens={lens} pps={pps}")
+    rng = np.random.default_rng(B * 7919 + Hq + sum(lens) + pps)
+    pages = [int(math.ceil(n / 16)) for n in lens]
+    num_pages = sum(pages) + 2
+    perm = rng.permutation(num_pages)
+    bt = np.full((B, max(pages) + 1), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    cache = torch.full((num_pages, Hkv, 1664), 0xFF, dtype=torch.uint8, device=dev)
+    pool = np.full((num_pages, Hkv, 1664), 0xFF, np.uint8)
+    new_k = np.zeros((B, Hkv, D), np.float16)
+    new_v = np.zeros((B, Hkv, D), np.float16)
+    for b, n in enumerate(lens):
+        k = (rng.standard_normal((n, Hkv, D)) * rng.choice([0.5, 2])).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        k[:, :, rng.integers(0, D, 3)] *= 10
+        new_k[b], new_v[b] = k[n - 1], v[n - 1]
+        if n > 1:
+            slots = inp.slot_mapping(bt, b, 0, n - 1)
+            gpu_append(torch.from_numpy(k[:n - 1]).to(dev), torch.from_numpy(v[:n - 1]).to(dev),
+                       torch.from_numpy(slots).to(dev), cache)
+            oracle.quantize_append(k[:n - 1], v[:n - 1], slots, pool)
+    q = (rng.standard_normal((B, Hq, D)) * 2).astype(np.float16)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.tensor(lens, dtype=torch.int32, device=dev)
+    nkd, nvd = torch.from_numpy(new_k).to(dev), torch.from_numpy(new_v).to(dev)
+    L = max(lens)
+    last_slots = np.array([bt[b, (n - 1) // 16] * 16 + (n - 1) % 16 for b, n in enumerate(lens)], np.int64)
+    cache_b, cache_c = cache.clone(), cache.clone()
+    # two calls
+    gpu_append(nkd, nvd, torch.from_numpy(last_slots).to(dev), cache)
+    out_a = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps).cpu()
+    # fused, one call
+    out_b = kvq.append_decode_attention(nkd, nvd, qd, cache_b, btd, ld, L, pages_per_split=pps).cpu()
+    assert torch.equal(cache.cpu(), cache_b.cpu()), "fused append changed other bytes or encoded differently"
+    assert torch.equal(out_a, out_b)
+    # fused split phase + combine, fp16 output
+    ws = kvq.alloc_workspace(B, Hq, Hkv, L, pps)
+    kvq.append_decode_partials(nkd, nvd, qd, cache_c, btd, ld, L, ws, pages_per_split=pps)
+    out_c = kvq.decode_combine(ws, ld, Hq, Hkv, L, out_dtype=torch.float16, pages_per_split=pps).cpu()
+    out_a16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, pages_per_split=pps).cpu()
+    assert torch.equal(cache.cpu(), cache_c.cpu())
+    assert torch.equal(out_a16, out_c)
+    # the oracle
+    oracle.quantize_append(new_k, new_v, last_slots, pool)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention(pool, bt, np.asarray(lens), q, SCALE)
+    assert np.max(np.abs(out_b.numpy() - ref)) <= TOL
+
+
+def test_fused_append_page_outside_pool_is_skipped(dev):
+    """A new token whose page id lies outside the pool is not stored by either
+    path; both read page 0 in its place and agree bit for bit."""
+    B, Hq, Hkv, lens = 2, 8, 1, [40, 20]
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=4242)
+    bt = bt.copy()
+    bt[1, 1] = cache.shape[0] + 3                     # sequence 1's last page: outside the pool
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    rng = np.random.default_rng(3)
+    nk = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float16)).to(dev)
+    nv = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float16)).to(dev)
+    cache_b = cache.clone()
+    slots = torch.tensor([bt[b, (n - 1) // 16] * 16 + (n - 1) % 16 for b, n in enumerate(lens)],
+                         dtype=torch.int64, device=dev)
+    gpu_append(nk, nv, slots, cache)
+    out_a = kvq.decode_attention(qd, cache, btd, ld, 40).cpu()
+    out_b = kvq.append_decode_attention(nk, nv, qd, cache_b, btd, ld, 40).cpu()
+    assert torch.equal(cache.cpu(), cache_b.cpu())
+    assert torch.equal(out_a, out_b)
+
+
+def test_split_kernel_events_hook(dev):
+    """kvq_set_split_kernel_events: the split kernel records the caller's
+    events at its start and end; results are unchanged, and clearing the hook
+    stops the recording."""
+    B, Hq, Hkv, lens = 2, 16, 2, [300, 77]
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=99)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(e0)) == 0 and hip.hipEventCreate(ctypes.byref(e1)) == 0
+    lib = kvq.load()
+    plain = kvq.decode_attention(qd, cache, btd, ld, 300).cpu()
+    assert lib.kvq_set_split_kernel_events(e0, e1) == 0
+    try:
+        timed = kvq.decode_attention(qd, cache, btd, ld, 300).cpu()
+    finally:
+        assert lib.kvq_set_split_kernel_events(None, None) == 0
+    torch.cuda.synchronize()
+    t = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(t), e0, e1) == 0
+    assert 0.0 < t.value < 100.0
+    assert torch.equal(plain, timed)
+    hip.hipEventDestroy(e0)
+    hip.hipEventDestroy(e1)
 
 
 def test_decode_zero_query_gives_mean_value(dev):
