@@ -567,9 +567,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 // Merge the split partials of each (sequence, query head) and apply the
 // Hadamard epilogue.  Runs after decode_kernel on the same stream (the kernel
-// boundary makes every partial visible).  Each wave handles two rows, 32 lanes
-// per row, 4 channels per lane.
+// boundary makes every partial visible).  Each wave handles two rows, 32
+// lanes per row, 4 channels per lane.  The kernel is latency-bound, so every
+// lane requests the (m, l, zacc) words and its 4 channels of up to 8 splits
+// at once (one memory round trip) and merges them in-lane; longer rows take
+// further groups of 8 with a running maximum.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    constexpr int kChunk = 8;
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31;
     const int64_t row = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * 2 + (lane >> 5);
@@ -583,53 +587,39 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     // (with partials only: no split for an empty sequence gives l = 0 and a
     // zero row; a single split is finished from its one partial)
     const float *base = a.partials + row * a.splits * kPartialFloats;
-    // split maxima and weight sums: lane l32 takes splits l32, l32 + 32, ...
-    float M = -INFINITY;
-    for (int s = l32; s < nsplit; s += 32) M = fmaxf(M, base[s * kPartialFloats]);
-#pragma unroll
-    for (int x = 1; x < 32; x <<= 1) M = fmaxf(M, xor_lane(M, x));
-    float l = 0.0f, z = 0.0f;
-    for (int s = l32; s < nsplit; s += 32) {
-        const float ms = base[s * kPartialFloats];
-        const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
-        l += f * base[s * kPartialFloats + 1];
-        z += f * base[s * kPartialFloats + 2];
-    }
-#pragma unroll
-    for (int x = 1; x < 32; x <<= 1) {
-        l += xor_lane(l, x);
-        z += xor_lane(z, x);
-    }
-    // value sums: every lane walks all splits for its 4 channels; unrolled so
-    // that eight splits' loads are in flight at once
     const int c0 = 4 * l32;
+    float M = -INFINITY, l = 0.0f, z = 0.0f;
     float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int s = 0;
-    for (; s + 8 <= nsplit; s += 8) {
-        float ms[8];
-        float4 v[8];
+    for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
+        float4 meta[kChunk], v[kChunk];
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            ms[u] = base[(s + u) * kPartialFloats];
-            v[u] = *reinterpret_cast<const float4 *>(base + (s + u) * kPartialFloats + 4 + c0);
+        for (int u = 0; u < kChunk; u++) {
+            const int sp = s0 + u < nsplit ? s0 + u : nsplit - 1;   // in range; duplicates get weight 0
+            meta[u] = *reinterpret_cast<const float4 *>(base + sp * kPartialFloats);
+            v[u] = *reinterpret_cast<const float4 *>(base + sp * kPartialFloats + 4 + c0);
+        }
+        float mc = M;
+#pragma unroll
+        for (int u = 0; u < kChunk; u++) mc = s0 + u < nsplit ? fmaxf(mc, meta[u].x) : mc;
+        if (mc != M) {                   // rescale what earlier groups accumulated
+            const float f = M == -INFINITY ? 0.0f : fast_exp2(M - mc);
+            l *= f;
+            z *= f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o4[e] *= f;
+            M = mc;
         }
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const float f = (ms[u] == -INFINITY) ? 0.0f : fast_exp2(ms[u] - M);
+        for (int u = 0; u < kChunk; u++) {
+            const bool live = s0 + u < nsplit && meta[u].x != -INFINITY;
+            const float f = live ? fast_exp2(meta[u].x - M) : 0.0f;
+            l += f * meta[u].y;
+            z += f * meta[u].z;
             o4[0] += f * v[u].x;
             o4[1] += f * v[u].y;
             o4[2] += f * v[u].z;
             o4[3] += f * v[u].w;
         }
-    }
-    for (; s < nsplit; s++) {
-        const float ms = base[s * kPartialFloats];
-        const float4 v = *reinterpret_cast<const float4 *>(base + s * kPartialFloats + 4 + c0);
-        const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
-        o4[0] += f * v.x;
-        o4[1] += f * v.y;
-        o4[2] += f * v.z;
-        o4[3] += f * v.w;
     }
     finalize_head(o4, l, z, l32, a.out, a.out_f32, row);
 }
