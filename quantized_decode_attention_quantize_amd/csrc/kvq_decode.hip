@@ -116,7 +116,7 @@ __device__ __forceinline__ v8h key_codes(uint32_t w) {
 // q_lo = q' - q_hi; adding the partner column (lane n ^ 8, one DPP move)
 // gives both lanes of a pair the same score for head n & 7.
 __device__ __forceinline__ void page_scores(const PageRegs &r, const v8h (&bq)[4],
-                                            float c1, float c2, float *lg) {
+                                            float c1, float c2, float mref, float *lg) {
     v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.x), bq[0], d, 0, 0, 0);
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.y), bq[1], d, 0, 0, 0);
@@ -128,7 +128,9 @@ __device__ __forceinline__ void page_scores(const PageRegs &r, const v8h (&bq)[4
         const float dot = d[i] + row_swap8(d[i]);     // q_hi . c + q_lo . c
         const float ks = half_bits_to_float(km[i] & 0xffffu);
         const float kz = half_bits_to_float(km[i] >> 16);
-        lg[i] = c1 * (ks * dot) + c2 * kz;
+        // base-2 logit minus the reference mref; the fp16 operands feed
+        // mixed-precision FMAs directly
+        lg[i] = __builtin_fmaf(dot * c1, ks, __builtin_fmaf(c2, kz, -mref));
     }
 }
 
@@ -175,14 +177,22 @@ struct LaneConsts {
 
 // One page pair.  kMasked: tokens at or beyond n_tokens (page A starts at
 // token tokA, page B at tokB; tokB = n_tokens marks an absent page B) take no
-// weight, whatever their (possibly never written) slots hold.
-template <bool kMasked>
+// weight, whatever their (possibly never written) slots hold.  kFirst: the
+// wave's first pair, which always sets the running maximum.
+//
+// Scores are formed relative to the reference mref = m + 8 (m the running
+// maximum; 0 before the first pair), so the weights are exp2 of them
+// directly.  When a score exceeds the reference (some logit beats m by more
+// than 8), the state is rescaled and the scores shifted to the new reference.
+template <bool kMasked, bool kFirst>
 __device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &B, int tokA, int tokB,
                                              int n_tokens, const v8h (&bq)[4], const LaneConsts &lc,
                                              int g, State &st) {
+    constexpr bool first = kFirst;
+    const float mref = first ? 0.0f : st.m + kLazyThreshold;
     float lg[8];
-    page_scores(A, bq, lc.c1, lc.c2, lg);
-    page_scores(B, bq, lc.c1, lc.c2, lg + 4);
+    page_scores(A, bq, lc.c1, lc.c2, mref, lg);
+    page_scores(B, bq, lc.c1, lc.c2, mref, lg + 4);
     bool valid[8];
     if (kMasked) {
 #pragma unroll
@@ -196,37 +206,39 @@ __device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &
     float lmax = lg[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) lmax = fmaxf(lmax, lg[i]);
-    if (__any(lmax > st.m + kLazyThreshold)) {
+    if (first || __any(lmax > 0.0f)) {
         float cm = fmaxf(lmax, xor_lane(lmax, 16));
         cm = fmaxf(cm, xor_lane(cm, 32));
-        const float m_new = fmaxf(st.m, cm);
-        const float f = (st.m == -INFINITY) ? 0.0f : fast_exp2(st.m - m_new);
+        const float m_new = first ? cm : fmaxf(st.m, cm + mref);
+        const float f = first ? 0.0f : fast_exp2(st.m - m_new);
         st.l *= f;
         st.z *= f;
 #pragma unroll
         for (int j = 0; j < 8; j++) st.acc[j] *= f;
         st.m = m_new;
+        const float shift = (m_new + kLazyThreshold) - mref;
+#pragma unroll
+        for (int i = 0; i < 8; i++) lg[i] -= shift;
     }
     // Weights are exp2(l - m - 8) <= 1 (the lazy threshold is folded into the
     // exponent), so w = p * s_v <= s_v stays inside fp16 for any value scale
     // the format can store; l and zacc carry the same factor, which cancels.
-    const float mref = ((st.m == -INFINITY) ? 0.0f : st.m) + kLazyThreshold;
     const uint32_t vm[8] = {A.vm.x, A.vm.y, A.vm.z, A.vm.w, B.vm.x, B.vm.y, B.vm.z, B.vm.w};
     v8h bw;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const float p = fast_exp2(lg[i] - mref);
+        const float p = fast_exp2(lg[i]);
         const float vs = half_bits_to_float(vm[i] & 0xffffu);
         const float vz = half_bits_to_float(vm[i] >> 16);
         float w;
         if (kMasked) {
             st.l += p;
             st.z += valid[i] ? p * vz : 0.0f;
-            w = valid[i] ? p * vs : 0.0f;
+            w = valid[i] ? __builtin_fmaf(p, vs, 0.0f) : 0.0f;
         } else {
             st.l += p;
-            st.z += p * vz;
-            w = p * vs;
+            st.z = __builtin_fmaf(p, vz, st.z);
+            w = __builtin_fmaf(p, vs, 0.0f);
         }
         // columns n < 8 take fp16(w), columns n >= 8 the exact residual
         // w - fp16(w), so that the value sum is carried to ~2^-22
@@ -483,16 +495,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; j++) st.acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (nk > 0) {
-        for (int i = 0;; i += 3) {
-            issue(r2A, r2B, i + 2);
-            process_pair<false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
-            if (i + 1 >= nk) break;
-            issue(r0A, r0B, i + 3);
-            process_pair<false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
-            if (i + 2 >= nk) break;
-            issue(r1A, r1B, i + 4);
-            process_pair<false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
-            if (i + 3 >= nk) break;
+        // the wave's first pair sets the running maximum; the loop then
+        // rotates the three buffers (pair i in r1, i + 1 in r2, i + 2 in r0)
+        issue(r2A, r2B, 2);
+        process_pair<false, true>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+        if (nk > 1) {
+            for (int i = 1;; i += 3) {
+                issue(r0A, r0B, i + 2);
+                process_pair<false, false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
+                if (i + 1 >= nk) break;
+                issue(r1A, r1B, i + 3);
+                process_pair<false, false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
+                if (i + 2 >= nk) break;
+                issue(r2A, r2B, i + 4);
+                process_pair<false, false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+                if (i + 3 >= nk) break;
+            }
         }
     }
     if (last_partial && wave == (npairs - 1) % kWaves) {
@@ -502,8 +520,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
         load_page(region_of(id_a), lo, tA);
         load_page(region_of(has_b ? __builtin_amdgcn_readlane(bt_b, j) : id_a), lo, tB);
-        process_pair<true>(tA, tB, last_pa * kPage, has_b ? (last_pa + 1) * kPage : n_tokens,
-                           n_tokens, bq, lc, g, st);
+        const int tok_b = has_b ? (last_pa + 1) * kPage : n_tokens;
+        if (nk == 0)
+            process_pair<true, true>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
+        else
+            process_pair<true, false>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
     }
 
     // ---- merge the 4 waves ----
