@@ -39,8 +39,8 @@
 //     zero-point sum in output channel 0.  A 2-bit code at bits 2j'..2j'+1 of a 16-bit
 //     word is, bit for bit, the fp16 subnormal c * 2^(2j' - 24); MFMA takes
 //     fp16 subnormals exactly, so the value codes need one AND per pair of
-//     tokens and no conversion.  The power of two is removed per channel
-//     block in the epilogue.
+//     tokens (and a shared shift) and no conversion.  The power of two is
+//     removed per channel block in the epilogue.
 // Epilogue: merge the 4 waves in LDS and write one partial (m, l, zacc, acc)
 // per head (zacc = sum p mu); a sequence that fits one split is finished in
 // place.  combine_kernel, launched next on the same stream, merges the
@@ -137,22 +137,24 @@ __device__ __forceinline__ void page_scores(const PageRegs &r, const v8h (&bq)[4
 // Value-code A operands of one page for one lane: u = two 16-bit words
 // (token slots 4g+i, 4g+i+1 for i = 0 or 2), crumb j of a word at bits
 // 2j..2j+1.  Each output dword is a pair of fp16 subnormals holding crumb j
-// of both words at mantissa bits 6-7 (value c * 2^-18, j = 0, 2, 6) or 8-9
-// (c * 2^-16, j = 1, 3, 4, 5, 7).  The codes are moved that high because the
-// MFMA accumulates very small products with less than fp32 precision (codes
-// at bits 0-1 lost up to ~3e-5 relative, biased towards zero; at bits 6-9 the
-// sums stay at fp32 rounding).  Left shifts only spill low-word bits into
-// bits 16-21 and right shifts high-word bits into bits 10-15; both lie
-// outside the masks.
+// of both words at mantissa bits 4-5 (value c * 2^-20: j = 2, 5), 6-7
+// (c * 2^-18: j = 0, 3, 6) or 8-9 (c * 2^-16: j = 1, 4, 7); crumbs 3 and 4
+// are in place, and one shift each way (<< 6, >> 6) serves the other six.
+// The codes sit that high because the MFMA accumulates very small products
+// with less than fp32 precision (codes at bits 0-1 lost up to ~3e-5
+// relative, biased towards zero; at bits 4-9 the output error stays below
+// 3e-5 absolute at 16K tokens).  The left shift only spills low-word bits
+// into bits 16-21 and the right shift high-word bits into bits 10-15; both
+// lie outside the masks.
 __device__ __forceinline__ uint32_t value_code(uint32_t u, int j) {
-    constexpr uint32_t kBits67 = 0x00C000C0u, kBits89 = 0x03000300u;
+    constexpr uint32_t kBits45 = 0x00300030u, kBits67 = 0x00C000C0u, kBits89 = 0x03000300u;
     switch (j) {
     case 0: return (u << 6) & kBits67;
     case 1: return (u << 6) & kBits89;
-    case 2: return (u << 2) & kBits67;
-    case 3: return (u << 2) & kBits89;
+    case 2: return u & kBits45;
+    case 3: return u & kBits67;
     case 4: return u & kBits89;
-    case 5: return (u >> 2) & kBits89;
+    case 5: return (u >> 6) & kBits45;
     case 6: return (u >> 6) & kBits67;
     default: return (u >> 6) & kBits89;
     }
@@ -160,7 +162,7 @@ __device__ __forceinline__ uint32_t value_code(uint32_t u, int j) {
 
 // log2 of the factor that removes the code scaling of channel block j
 __device__ __forceinline__ constexpr int value_unscale_log2(int j) {
-    return (j == 0 || j == 2 || j == 6) ? 18 : 16;
+    return (j == 2 || j == 5) ? 20 : (j == 0 || j == 3 || j == 6) ? 18 : 16;
 }
 
 struct State {
