@@ -110,7 +110,10 @@ def _mixed_tokens(rng, T, H):
     return x.astype(np.float16)
 
 
-@pytest.mark.parametrize("H,T,num_pages,seed", [(1, 37, 8, 1), (3, 200, 20, 2), (8, 515, 40, 3)])
+# The last case has 65600 (token, KV head) rows, which selects the bulk
+# one-lane-per-group kernel; the others run the 16-lane kernel.
+@pytest.mark.parametrize("H,T,num_pages,seed", [(1, 37, 8, 1), (3, 200, 20, 2), (8, 515, 40, 3),
+                                                (8, 8200, 600, 4)])
 def test_append_mixed_regimes_strided_and_skips(dev, H, T, num_pages, seed):
     rng = np.random.default_rng(100 + seed)
     log(f"append mixed H={H} T={T} pages={num_pages}")
