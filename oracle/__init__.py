@@ -76,6 +76,8 @@ def _load():
     lib.kvqo_decode_attention_folded.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
                                                  ctypes.c_double, P]
     lib.kvqo_decode_attention_folded.restype = ctypes.c_int
+    lib.kvqo_attention_f16.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
+    lib.kvqo_attention_f16.restype = None
     _lib = lib
     return lib
 
@@ -217,3 +219,17 @@ def decode_attention_folded(pool, block_tables, seq_lens, query_f16, scale):
     if rc != 0:
         raise ValueError("oracle folded decode: invalid shape or page id")
     return out
+
+
+def attention_f16(k_f16, v_f16, q_f16, scale):
+    """Plain fp64 attention of G query heads over fp16 tokens of one KV head:
+    k, v float16 [n][128], q float16 [G][128] -> float64 [G][128]."""
+    k = _c(k_f16, np.float16)
+    v = _c(v_f16, np.float16)
+    q = _c(q_f16, np.float16)
+    n = k.shape[0]
+    assert v.shape == k.shape and k.shape[1:] == (D,) and q.shape[1:] == (D,)
+    out = np.empty((q.shape[0], D), np.float64)
+    _load().kvqo_attention_f16(_ptr(k), _ptr(v), n, _ptr(q), q.shape[0], float(scale), _ptr(out))
+    return out
+

@@ -512,3 +512,41 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Uncompressed reference: attention over fp16 keys and values.              */
+/* ------------------------------------------------------------------------ */
+
+/* Plain decode attention of G query heads over n fp16 tokens of one KV head,
+ * in fp64: out[g] = sum_t softmax_t(scale * q_g . k_t) v_t.  This is the
+ * uncompressed cache the K4V2 format is measured against [KVARN-HN: fp16 as
+ * the accuracy and capacity reference].  k, v: [n][128]; q: [G][128];
+ * out: [G][128].  n == 0 gives zero rows. */
+void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const uint16_t *q,
+                        int32_t G, double scale, double *out)
+{
+    double *lg = n > 0 ? malloc(sizeof(double) * n) : NULL;
+    for (int g = 0; g < G; g++) {
+        double *dst = out + (int64_t)g * KVQO_D;
+        for (int i = 0; i < KVQO_D; i++) dst[i] = 0.0;
+        if (n <= 0 || !lg) continue;
+        double qd[KVQO_D];
+        for (int i = 0; i < KVQO_D; i++) qd[i] = kvqo_half_to_double(q[(int64_t)g * KVQO_D + i]);
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < n; t++) {
+            double d = 0.0;
+            for (int i = 0; i < KVQO_D; i++) d += qd[i] * kvqo_half_to_double(k[t * KVQO_D + i]);
+            lg[t] = scale * d;
+            if (lg[t] > mx) mx = lg[t];
+        }
+        double den = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            double e = exp(lg[t] - mx);
+            den += e;
+            for (int i = 0; i < KVQO_D; i++) dst[i] += e * kvqo_half_to_double(v[t * KVQO_D + i]);
+        }
+        for (int i = 0; i < KVQO_D; i++) dst[i] /= den;
+    }
+    free(lg);
+}
+

@@ -5,6 +5,7 @@ invariant, a special case that reduces to a library routine (numpy's binary16
 conversion, torch's scaled-dot-product attention), brute force, or a
 hand-derived fixture under tests/golden/.
 """
+import math
 import os
 
 import numpy as np
@@ -438,3 +439,41 @@ def test_attention_invariant_to_physical_page_placement():
     oa = oracle.decode_attention(a[0], a[1], a[2], a[3], scale)
     ob = oracle.decode_attention(b[0], b[1], b[2], b[3], scale)
     assert np.array_equal(oa, ob)
+
+
+# --------------------------------------------------------------------------
+# Uncompressed fp16 reference attention
+# --------------------------------------------------------------------------
+
+def test_attention_f16_matches_torch_sdpa_fp64():
+    """The plain fp64 attention over fp16 tokens equals torch's scaled
+    dot-product attention run in fp64 on the same values (an independent
+    implementation), for several lengths and GQA group sizes."""
+    rng = np.random.default_rng(7)
+    for n, G, qs in ((1, 1, 1.0), (17, 4, 2.0), (300, 8, 0.5), (1000, 2, 3.0)):
+        k = (rng.standard_normal((n, D)) * rng.choice([0.5, 2.0])).astype(np.float16)
+        v = rng.standard_normal((n, D)).astype(np.float16)
+        q = (rng.standard_normal((G, D)) * qs).astype(np.float16)
+        scale = 1 / math.sqrt(D)
+        got = oracle.attention_f16(k, v, q, scale)
+        kt = torch.from_numpy(k.astype(np.float64))[None, None].expand(1, G, n, D)
+        vt = torch.from_numpy(v.astype(np.float64))[None, None].expand(1, G, n, D)
+        qt = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0].numpy()
+        assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_f16_special_cases():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((50, D)).astype(np.float16)
+    v = rng.standard_normal((50, D)).astype(np.float16)
+    # one token: the output is that token's value
+    out = oracle.attention_f16(k[:1], v[:1], rng.standard_normal((3, D)).astype(np.float16), 0.1)
+    assert np.array_equal(out, np.repeat(v[:1].astype(np.float64), 3, 0))
+    # q = 0: uniform weights, the mean of the values
+    out = oracle.attention_f16(k, v, np.zeros((1, D), np.float16), 0.1)
+    assert np.max(np.abs(out[0] - v.astype(np.float64).mean(0))) < 1e-14
+    # no tokens: zero rows
+    out = oracle.attention_f16(k[:0], v[:0], np.ones((2, D), np.float16), 0.1)
+    assert np.array_equal(out, np.zeros((2, D)))
+
