@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="host threads for the oracle sample (default: min(16, cpu count)); one group each")
     ap.add_argument("--no-append-bench", action="store_true")
+    ap.add_argument("--no-fp16-baseline", action="store_true",
+                    help="skip the uncompressed fp16 cache decode on the same workload")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=10,
                     help="time the split kernel with kernel events on every N-th timed step")
@@ -334,6 +336,9 @@ def main():
                      "kernel": "decode_kernel", "bytes_per_launch": kv_bytes, "traffic_note": traffic_note},
     }
 
+    if not args.no_fp16_baseline:
+        result["fp16_baseline"] = fp16_baseline(torch, inp, kvq, lib, dev, stream, args, ms_per_step)
+
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
 
@@ -342,6 +347,61 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, threads, threads)
 
     print(json.dumps(result), flush=True)
+
+
+def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
+    """The same decode (8 x 16385 tokens, 64 / 8 heads) over the uncompressed
+    fp16 cache: 512 bytes per token per KV head instead of 104.  Each step is
+    the split kernel + the combine; the split kernel is timed with kernel
+    events on every --event-every'th step, as for K4V2."""
+    import numpy as np
+    w = inp.workload("qwen3_32b_16k")
+    B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    n = w.context + 1
+    f16 = kvq.format_from_string("fp16")
+    bt_np, num_pages = inp.page_table(w)
+    bt = torch.from_numpy(bt_np).to(dev)
+    lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    base = torch.zeros((num_pages, Hkv, kvq.page_bytes(f16)), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, 0, n, device=dev)
+        kvq.quantize_append(k, v, torch.from_numpy(inp.slot_mapping(bt_np, b, 0, n)).to(dev), base, fmt=f16)
+    pools = [base, base.clone()]          # 2 x 537 MB: no step finds its pool in the 256 MB cache
+    q = inp.queries(w, 0, device=dev).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    ws = kvq.alloc_workspace(B, Hq, Hkv, n, fmt=f16)
+    call = DecodeCall(kvq, lib, f16, stream.cuda_stream)
+    part = [call.partials_args(q, p, bt, lens, n, ws, 0) for p in pools]
+    comb = call.combine_args(out, lens, Hq, Hkv, n, ws, 0)
+    pf, cfn, set_events = lib.kvq_decode_partials, lib.kvq_decode_combine, lib.kvq_set_split_kernel_events
+    steps = max(20, args.steps // 2)
+    every = max(1, args.event_every)
+    sampled = {i: k for k, i in enumerate(range(0, steps, every))}
+    hev = HipEvents(2 * len(sampled))
+    for i in range(5):
+        pf(*part[i % 2]); cfn(*comb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        k = sampled.get(i)
+        if k is not None:
+            set_events(hev.ev[2 * k], hev.ev[2 * k + 1])
+        st = pf(*part[i % 2])
+        if k is not None:
+            set_events(None, None)
+        st |= cfn(*comb)
+        if st:
+            raise RuntimeError("fp16 decode call failed")
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = float(np.mean([hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]))
+    hev.close()
+    fp16_bytes = B * n * Hkv * 512
+    return {"workload": "qwen3_32b_16k, fp16 cache (512 B per token-head)", "ms_per_step": round(ms, 5),
+            "split_kernel_ms": round(kern, 5),
+            "kernel_GBps": round(fp16_bytes / (kern * 1e-3) / 1e9, 2),
+            "kernel_pct_hbm_peak": round(100 * fp16_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "k4v2_step_speedup": round(ms / k4v2_ms_per_step, 3)}
 
 
 def append_bench(torch, inp, kvq, call, dev):

@@ -44,6 +44,19 @@
  *       [1600, 1664)  value (s, mu) fp16 pairs, token o at 1600 + 4*o
  *     104 bytes per token per KV head (fp16: 512 bytes).
  *
+ * Baseline format "fp16" (k_bits = v_bits = 16): the uncompressed cache the
+ * K4V2 format is measured against (the pages compare KVarN with fp16 on
+ * accuracy, capacity and throughput [KVARN-HN lede; KVARN-P results]).  The
+ * same calls accept it, except the fused append-and-decode (KVQ_ERR_
+ * UNSUPPORTED).  One 8192-byte region per (page, KV head), fp16 elements:
+ *       [0, 4096)     keys: token n, channel c = 32d + 8g + e at element
+ *                     n*128 + 32g + 8d + e
+ *       [4096, 8192)  values: token t (q = t/4, i = t%4), channel c = 16j + m
+ *                     at element 2048 + ((16q + m)*8 + j)*4 + i
+ *     512 bytes per token per KV head.  kvq_quantize_append copies the rows
+ *     (no quantisation); decode computes softmax(scale * q.k) v in fp32 with
+ *     the same split-K structure, at most 256 pages per split.
+ *
  * Conventions for every call:
  *   - All buffers are owned by the caller.  The library never allocates,
  *     frees or synchronises device memory and keeps no global mutable state
@@ -76,13 +89,14 @@ typedef enum kvq_status {
     KVQ_OK = 0,
     KVQ_ERR_NULL = 1,         /* a required pointer is NULL                    */
     KVQ_ERR_SHAPE = 2,        /* a size is out of range or inconsistent        */
-    KVQ_ERR_UNSUPPORTED = 3,  /* format/preset other than k4v2_g128 v1         */
+    KVQ_ERR_UNSUPPORTED = 3,  /* unknown format, or a call the format lacks     */
     KVQ_ERR_ALIGN = 4,        /* a device pointer is not suitably aligned      */
     KVQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required    */
     KVQ_ERR_HIP = 6           /* the HIP runtime reported an error             */
 } kvq_status;
 
-/* Format descriptor.  v1 supports exactly {128, 128, 4, 2, 16}. */
+/* Format descriptor: {128, 128, 4, 2, 16} (K4V2 v1) or {128, 128, 16, 16, 16}
+ * (the fp16 baseline). */
 typedef struct kvq_format {
     int32_t head_dim;    /* channels per head                    */
     int32_t group_size;  /* channels per quantisation group      */
@@ -94,12 +108,13 @@ typedef struct kvq_format {
 typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
 
 /* Parse a preset name ([KVARN-HN] flag value; [KVARN-P] kv_cache_dtype string).
- * Accepts "k4v2_g128" and "kvarn_k4v2_g128".  preset, out: (host).
+ * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16}) and the
+ * baseline "fp16" ({128, 128, 16, 16, 16}).  preset, out: (host).
  * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
 
-/* Bytes of one (page, KV head) region: 1664 for v1; 0 for an unsupported
- * format or NULL. */
+/* Bytes of one (page, KV head) region: 1664 for K4V2 v1, 8192 for fp16; 0 for
+ * an unsupported format or NULL. */
 size_t kvq_page_bytes(const kvq_format *fmt);
 
 /* Bytes of a pool of num_pages pages and num_kv_heads heads; 0 on invalid input. */

@@ -136,9 +136,17 @@ def cache_bytes(num_pages: int, num_kv_heads: int, fmt: Format | None = None) ->
     return int(load().kvq_cache_bytes(ctypes.byref(_fmt(fmt)), num_pages, num_kv_heads))
 
 
-def alloc_cache(num_pages: int, num_kv_heads: int, device="cuda") -> torch.Tensor:
-    """Uninitialised pool u8 [num_pages][num_kv_heads][1664]."""
-    return torch.empty((num_pages, num_kv_heads, REGION_BYTES), dtype=torch.uint8, device=device)
+def alloc_cache(num_pages: int, num_kv_heads: int, device="cuda", fmt: Format | None = None) -> torch.Tensor:
+    """Uninitialised pool u8 [num_pages][num_kv_heads][page_bytes(fmt)] (1664 for
+    K4V2, 8192 for the fp16 baseline)."""
+    return torch.empty((num_pages, num_kv_heads, page_bytes(fmt)), dtype=torch.uint8, device=device)
+
+
+def _region(fmt: Format | None) -> int:
+    n = page_bytes(fmt)
+    if n == 0:
+        raise KvqError(3, "unsupported format")
+    return n
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:
@@ -165,8 +173,8 @@ def quantize_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.
     for t in (key, value):
         if t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
             raise ValueError("key/value heads must be contiguous 128-element rows")
-    if cache.dim() != 3 or cache.shape[1] != H or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
-        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
+    if cache.dim() != 3 or cache.shape[1] != H or cache.shape[2] != _region(fmt) or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][page_bytes]")
     if not slot_mapping.is_contiguous() or slot_mapping.numel() != T:
         raise ValueError("slot_mapping must be a contiguous int64 vector of length T")
     st = load().kvq_quantize_append(ctypes.byref(_fmt(fmt)), _ptr(key), _ptr(value), key.stride(0),
@@ -189,20 +197,20 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, m
 
 
 def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
-                    pages_per_split: int = 0, device="cuda") -> torch.Tensor:
+                    pages_per_split: int = 0, device="cuda", fmt: Format | None = None) -> torch.Tensor:
     """Workspace for split partials (contents need no initialisation)."""
-    n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pages_per_split)
+    n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, max_seq_len, pages_per_split, fmt)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _decode_checks(query, cache, block_tables, seq_lens):
+def _decode_checks(query, cache, block_tables, seq_lens, fmt=None):
     if query.dtype != torch.float16 or query.dim() != 3 or query.shape[2] != HEAD_DIM:
         raise ValueError("query must be float16 [B][Hq][128]")
     if not query.is_contiguous():
         raise ValueError("query must be contiguous")
     B = query.shape[0]
-    if cache.dim() != 3 or cache.shape[2] != REGION_BYTES or not cache.is_contiguous():
-        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][1664]")
+    if cache.dim() != 3 or cache.shape[2] != _region(fmt) or not cache.is_contiguous():
+        raise ValueError("cache must be contiguous [num_pages][num_kv_heads][page_bytes]")
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or not block_tables.is_contiguous():
         raise ValueError("block_tables must be contiguous int32 [B][max_pages]")
     if seq_lens.dtype != torch.int32 or seq_lens.numel() != B or not seq_lens.is_contiguous():
@@ -216,7 +224,7 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
                      stream=None, fmt: Format | None = None) -> torch.Tensor:
     """One decode step: query fp16 [B][Hq][128] against the pool; returns
     out [B][Hq][128] (fp32 or fp16)."""
-    _decode_checks(query, cache, block_tables, seq_lens)
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
     B, Hq, _ = query.shape
     Hkv = cache.shape[1]
     if softmax_scale is None:
@@ -226,7 +234,7 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
     if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
         raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
     if workspace is None:
-        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device)
+        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device, fmt=fmt)
     st = load().kvq_decode_attention_ex(
         ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
         _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables), block_tables.shape[1],
@@ -242,7 +250,7 @@ def decode_partials(query: torch.Tensor, cache: torch.Tensor, block_tables: torc
                     stream=None, fmt: Format | None = None) -> torch.Tensor:
     """Split phase of a decode step: fills `workspace` with the fp32 split
     partials [B][Hq][splits][132] (see include/kvq.h) and returns it."""
-    _decode_checks(query, cache, block_tables, seq_lens)
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
     B, Hq, _ = query.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
@@ -292,7 +300,7 @@ def append_decode_attention(new_key: torch.Tensor, new_value: torch.Tensor, quer
     """One decode step that first appends the new token of every sequence:
     new_key/new_value fp16 [B][num_kv_heads][128] go into token seq_lens[b]-1,
     then attention over seq_lens[b] tokens.  Returns out [B][Hq][128]."""
-    _decode_checks(query, cache, block_tables, seq_lens)
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
     B, Hq, _ = query.shape
     Hkv = cache.shape[1]
     _new_token_checks(new_key, new_value, B, Hkv)
@@ -303,7 +311,7 @@ def append_decode_attention(new_key: torch.Tensor, new_value: torch.Tensor, quer
     if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
         raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
     if workspace is None:
-        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device)
+        workspace = alloc_workspace(B, Hq, Hkv, max_seq_len, pages_per_split, device=query.device, fmt=fmt)
     st = load().kvq_append_decode_attention(
         ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
         _ptr(new_key), _ptr(new_value), new_key.stride(0), new_value.stride(0), _ptr(query), _ptr(cache),
@@ -319,7 +327,7 @@ def append_decode_partials(new_key: torch.Tensor, new_value: torch.Tensor, query
                            max_seq_len: int, workspace: torch.Tensor, softmax_scale: float | None = None,
                            pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
     """Split phase of ``append_decode_attention``; ``decode_combine`` finishes it."""
-    _decode_checks(query, cache, block_tables, seq_lens)
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
     B, Hq, _ = query.shape
     Hkv = cache.shape[1]
     _new_token_checks(new_key, new_value, B, Hkv)

@@ -31,6 +31,7 @@ COMMON = [
 SOURCES = {
     "kvq_append.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
+    "kvq_fp16.hip": [],
     "kvq_api.hip": [],
 }
 

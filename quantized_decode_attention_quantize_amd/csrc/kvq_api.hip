@@ -16,6 +16,20 @@ bool is_v1(const kvq_format *f) {
            f->block_size == 16;
 }
 
+// The uncompressed fp16 baseline cache.
+bool is_fp16(const kvq_format *f) {
+    return f && f->head_dim == 128 && f->group_size == 128 && f->k_bits == 16 && f->v_bits == 16 &&
+           f->block_size == 16;
+}
+
+bool is_known(const kvq_format *f) { return is_v1(f) || is_fp16(f); }
+
+size_t region_bytes(const kvq_format *f) {
+    return is_v1(f) ? (size_t)kvq::kRegion : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
+}
+
+int32_t max_pps(bool fp16) { return fp16 ? kvq::kMaxPagesPerSplitF16 : kvq::kMaxPagesPerSplit; }
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 kvq_status hip_status(hipError_t e) {
@@ -33,16 +47,17 @@ int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerG
 // page count (rounded up to a page pair), so every work-group starts at once,
 // carries the same work, and pays its fixed cost (query rotation, wave merge,
 // partial write) once.
-int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len) {
+int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                      bool fp16 = false) {
     const int64_t units = (int64_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads);
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
-    const int64_t resident = kvq::decode_resident_workgroups();
+    const int64_t resident = fp16 ? kvq::decode_fp16_resident_workgroups() : kvq::decode_resident_workgroups();
     int64_t splits = resident / units;
     if (splits < 1) splits = 1;
     int64_t pps = ceil_div(max_pages, splits);
     pps = ceil_div(pps, 2) * 2;
     if (pps < 2) pps = 2;
-    if (pps > kvq::kMaxPagesPerSplit) pps = kvq::kMaxPagesPerSplit;
+    if (pps > max_pps(fp16)) pps = max_pps(fp16);
     return (int32_t)pps;
 }
 
@@ -74,22 +89,24 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
                          int32_t max_pages_per_seq, void *workspace, size_t workspace_bytes,
                          int32_t pages_per_split, kvq::DecodeArgs &a) {
     if (!fmt) return KVQ_ERR_NULL;
-    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (!is_known(fmt)) return KVQ_ERR_UNSUPPORTED;
     if (!seq_lens) return KVQ_ERR_NULL;
+    const bool fp16 = is_fp16(fmt);
     if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len) || pages_per_split < 0 ||
-        (pages_per_split % 2) || pages_per_split > kvq::kMaxPagesPerSplit)
+        (pages_per_split % 2) || pages_per_split > max_pps(fp16))
         return KVQ_ERR_SHAPE;
     if (max_pages_per_seq >= 0 &&
         (max_pages_per_seq == 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage))
         return KVQ_ERR_SHAPE;
     if ((uintptr_t)seq_lens & 3u) return KVQ_ERR_ALIGN;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
     if (w.splits > 65535) return KVQ_ERR_SHAPE;
     memset(&a, 0, sizeof(a));
+    a.rotated = fp16 ? 0 : 1;
     a.max_seq_len = max_seq_len;
     a.seq_lens = seq_lens;
     a.num_seqs = num_seqs;
@@ -115,12 +132,14 @@ kvq_status decode_inputs(const uint16_t *query, const uint8_t *cache, int64_t nu
     a.num_pages = num_pages;
     a.block_tables = block_tables;
     a.bt_stride = max_pages_per_seq;
-    a.alpha = softmax_scale * 1.4426950408889634f / 128.0f;
+    // K4V2 scores carry the 128 of H H = 128 I; fp16 scores do not
+    a.alpha = a.rotated ? softmax_scale * 1.4426950408889634f / 128.0f : softmax_scale * 1.4426950408889634f;
     return KVQ_OK;
 }
 
 kvq_status append_inputs(const uint16_t *new_key, const uint16_t *new_value, int64_t key_token_stride,
                          int64_t value_token_stride, kvq::DecodeArgs &a) {
+    if (!a.rotated) return KVQ_ERR_UNSUPPORTED;   // the fused append exists for K4V2 only
     if (!new_key || !new_value) return KVQ_ERR_NULL;
     const int64_t row = (int64_t)a.num_kv_heads * kvq::kHeadDim;
     if (key_token_stride < row || value_token_stride < row) return KVQ_ERR_SHAPE;
@@ -144,27 +163,40 @@ kvq_status decode_output(void *out, kvq_out_dtype out_dtype, kvq::DecodeArgs &a)
     return KVQ_OK;
 }
 
+hipError_t launch_split(const kvq::DecodeArgs &a, hipStream_t stream) {
+    return a.rotated ? kvq::launch_decode_split(a, stream, g_split_events)
+                     : kvq::launch_fp16_decode_split(a, stream, g_split_events);
+}
+
+// Split kernel, then the combine unless every sequence fits one split.
+hipError_t launch_both(const kvq::DecodeArgs &a, hipStream_t stream) {
+    const hipError_t e = launch_split(a, stream);
+    if (e != hipSuccess || (a.splits <= 1 && !a.partials_only)) return e;
+    return kvq::launch_decode_combine(a, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
     if (!preset || !out) return KVQ_ERR_NULL;
-    if (strcmp(preset, "k4v2_g128") != 0 && strcmp(preset, "kvarn_k4v2_g128") != 0)
-        return KVQ_ERR_UNSUPPORTED;
+    const bool k4v2 = strcmp(preset, "k4v2_g128") == 0 || strcmp(preset, "kvarn_k4v2_g128") == 0;
+    const bool f16 = strcmp(preset, "fp16") == 0;
+    if (!k4v2 && !f16) return KVQ_ERR_UNSUPPORTED;
     out->head_dim = 128;
     out->group_size = 128;
-    out->k_bits = 4;
-    out->v_bits = 2;
+    out->k_bits = k4v2 ? 4 : 16;
+    out->v_bits = k4v2 ? 2 : 16;
     out->block_size = 16;
     return KVQ_OK;
 }
 
-size_t kvq_page_bytes(const kvq_format *fmt) { return is_v1(fmt) ? (size_t)kvq::kRegion : 0; }
+size_t kvq_page_bytes(const kvq_format *fmt) { return region_bytes(fmt); }
 
 size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_heads) {
-    if (!is_v1(fmt) || num_pages < 0 || num_kv_heads <= 0) return 0;
-    return (size_t)num_pages * (size_t)num_kv_heads * (size_t)kvq::kRegion;
+    if (!is_known(fmt) || num_pages < 0 || num_kv_heads <= 0) return 0;
+    return (size_t)num_pages * (size_t)num_kv_heads * region_bytes(fmt);
 }
 
 kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const uint16_t *value,
@@ -172,7 +204,7 @@ kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const
                                const int64_t *slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                                uint8_t *cache, int64_t num_pages, void *stream) {
     if (!fmt) return KVQ_ERR_NULL;
-    if (!is_v1(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (!is_known(fmt)) return KVQ_ERR_UNSUPPORTED;
     if (num_tokens < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
     if (num_tokens == 0) return KVQ_OK;
     if (!key || !value || !slot_mapping || !cache) return KVQ_ERR_NULL;
@@ -192,7 +224,8 @@ kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const
     a.num_kv_heads = num_kv_heads;
     a.cache = cache;
     a.num_pages = num_pages;
-    return hip_status(kvq::launch_append(a, (hipStream_t)stream));
+    return hip_status(is_fp16(fmt) ? kvq::launch_fp16_append(a, (hipStream_t)stream)
+                                   : kvq::launch_append(a, (hipStream_t)stream));
 }
 
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -203,10 +236,11 @@ int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads, int32_
 
 size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split) {
-    if (!is_v1(fmt) || !decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
-    if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > kvq::kMaxPagesPerSplit) return 0;
+    if (!is_known(fmt) || !decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
+    const bool fp16 = is_fp16(fmt);
+    if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
     return layout(num_seqs, num_q_heads, max_seq_len, pps).total;
 }
 
@@ -223,7 +257,7 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
     if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
     if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
     if (st != KVQ_OK) return st;
-    return hip_status(kvq::launch_decode(a, (hipStream_t)stream, g_split_events));
+    return hip_status(launch_both(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
@@ -238,7 +272,7 @@ kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, con
     if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
     if (st != KVQ_OK) return st;
     a.partials_only = 1;
-    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream, g_split_events));
+    return hip_status(launch_split(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new_key, const uint16_t *new_value,
@@ -256,7 +290,7 @@ kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new
     if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
     if (st != KVQ_OK) return st;
     a.partials_only = 1;
-    return hip_status(kvq::launch_decode_split(a, (hipStream_t)stream, g_split_events));
+    return hip_status(launch_split(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
@@ -275,7 +309,7 @@ kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out
     if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
     if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
     if (st != KVQ_OK) return st;
-    return hip_status(kvq::launch_decode(a, (hipStream_t)stream, g_split_events));
+    return hip_status(launch_both(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,

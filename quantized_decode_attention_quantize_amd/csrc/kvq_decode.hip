@@ -52,13 +52,13 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include "kvq_decode_common.h"
 #include "kvq_device.h"
 #include "kvq_quant.h"
 
 namespace kvq {
 namespace {
 
-constexpr float kLazyThreshold = 8.0f;   // log2 of the largest unnormalised weight
 
 struct PageRegs {
     uint4 k;    // key codes: token (lane & 15), bytes 16*(lane >> 4) .. +15
@@ -165,13 +165,6 @@ __device__ __forceinline__ constexpr int value_unscale_log2(int j) {
     return (j == 2 || j == 5) ? 20 : (j == 0 || j == 3 || j == 6) ? 18 : 16;
 }
 
-struct State {
-    float m;        // running max (base 2) of this lane's column
-    float l;        // partial sum of weights over this lane's tokens
-    float z;        // partial sum of weight * value zero-point
-    v4f acc[8];     // value accumulators, channel 16j + 4g + i, column n
-};
-
 struct LaneConsts {
     float c1, c2;          // folded score constants of head n & 7
     float res_k;           // 0 (lanes n < 8: weight) or -1 (lanes n >= 8: residual)
@@ -256,42 +249,6 @@ __device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &
     }
 }
 
-// o_j = (H acc)_j / (128 l), j >= 1, and o_0 = zacc / l for one head: 32 lanes (lane & 31) hold
-// channels 4*(lane & 31) .. +3; the FWHT runs 2 stages in-lane and 5 across.
-__device__ __forceinline__ void finalize_head(float (&acc)[4], float l, float z, int lane32,
-                                              void *out, int out_f32, int64_t row) {
-    float y[4] = {acc[0], acc[1], acc[2], acc[3]};
-    {
-        float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
-        p = y[2]; q = y[3]; y[2] = p + q; y[3] = p - q;
-        p = y[0]; q = y[2]; y[0] = p + q; y[2] = p - q;
-        p = y[1]; q = y[3]; y[1] = p + q; y[3] = p - q;
-    }
-#pragma unroll
-    for (int x = 1; x < 32; x <<= 1) {
-        const bool upper = (lane32 & x) != 0;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const float other = xor_lane(y[e], x);
-            y[e] = upper ? (other - y[e]) : (y[e] + other);
-        }
-    }
-    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-    const float sc = inv_l * (1.0f / 128.0f);
-    float o[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) o[e] = y[e] * sc;
-    if (lane32 == 0) o[0] = z * inv_l;   // channel 0 is the weighted mean of the stored value means
-    const int64_t base = row * kHeadDim + 4 * lane32;
-    if (out_f32) {
-        *reinterpret_cast<float4 *>(static_cast<float *>(out) + base) = make_float4(o[0], o[1], o[2], o[3]);
-    } else {
-        const uint32_t lo = (uint32_t)float_to_half_bits(o[0]) | ((uint32_t)float_to_half_bits(o[1]) << 16);
-        const uint32_t hi = (uint32_t)float_to_half_bits(o[2]) | ((uint32_t)float_to_half_bits(o[3]) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + base) = make_uint2(lo, hi);
-    }
-}
-
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int split = blockIdx.x;
     const int kvh = blockIdx.y / a.head_groups;
@@ -326,11 +283,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
 
     if (n_tokens == 0) {             // empty sequence: zero output rows
-        if (!a.partials_only && split == 0 && (tid >> 5) < nh) {
-            const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
-            if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
-            else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
-        }
+        zero_rows(a, tid, b, hq0, nh, split);
         return;
     }
     if (p_begin >= npages) return;   // this split lies past the sequence end
@@ -339,8 +292,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     __shared__ _Float16 s_qb[16][kHeadDim];   // [column][slot], slot = 32g + 8d + e
     __shared__ float s_c1[kHeadsPerGroup], s_c2[kHeadsPerGroup];
-    __shared__ float s_m[kWaves][kHeadsPerGroup], s_l[kWaves][kHeadsPerGroup], s_z[kWaves][kHeadsPerGroup];
-    __shared__ float s_acc[kWaves][kHeadsPerGroup][kHeadDim];
+    __shared__ MergeLds s_merge;
 
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
@@ -529,63 +481,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             process_pair<true, false>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
     }
 
-    // ---- merge the 4 waves ----
-    float lsum = st.l + xor_lane(st.l, 16);
-    lsum += xor_lane(lsum, 32);
-    float zsum = st.z + xor_lane(st.z, 16);
-    zsum += xor_lane(zsum, 32);
-    // value sums: column n holds the fp16 part, column n + 8 the residual
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) st.acc[j][i] += row_swap8(st.acc[j][i]);
-    if (n16 < kHeadsPerGroup) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float unscale = __builtin_ldexpf(1.0f, value_unscale_log2(j));
-#pragma unroll
-            for (int i = 0; i < 4; i++) s_acc[wave][n16][16 * j + 4 * g + i] = st.acc[j][i] * unscale;
-        }
-        if (g == 0) {
-            s_m[wave][n16] = st.m;
-            s_l[wave][n16] = lsum;
-            s_z[wave][n16] = zsum;
-        }
-    }
-    __syncthreads();
-
-    const int hh = tid >> 5;          // head of this thread in the merge
-    const int l32 = tid & 31;
-    const int c0 = 4 * l32;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, s_m[w][hh]);
-    float lt = 0.0f, zt = 0.0f, acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) {
-        const float mw = s_m[w][hh];
-        const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
-        lt += f * s_l[w][hh];
-        zt += f * s_z[w][hh];
-#pragma unroll
-        for (int e = 0; e < 4; e++) acc4[e] += f * s_acc[w][hh][c0 + e];
-    }
-
-    const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
-    if (nsplit == 1 && !a.partials_only) {
-        if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row);
-        return;
-    }
-
-    float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
-    if (hh < nh) {
-        if (l32 == 0) {
-            mine[0] = M;
-            mine[1] = lt;
-            mine[2] = zt;
-        }
-        *reinterpret_cast<float4 *>(mine + 4 + c0) = make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
-    }
+    // ---- merge the 4 waves; write the partial (or the output) ----
+    merge_and_store(st, s_merge, a, 1, [](int j) { return __builtin_ldexpf(1.0f, value_unscale_log2(j)); },
+                    wave, tid, b, hq0, nh, split, nsplit);
 }
 
 // Merge the split partials of each (sequence, query head) and apply the
@@ -644,7 +542,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
             o4[3] += f * v[u].w;
         }
     }
-    finalize_head(o4, l, z, l32, a.out, a.out_f32, row);
+    finalize_head(o4, l, z, l32, a.out, a.out_f32, row, a.rotated);
 }
 
 }  // namespace

@@ -1,0 +1,150 @@
+// Device pieces shared by the decode split kernels (K4V2 and the fp16
+// baseline) and the split combine: the per-lane softmax state, the merge of
+// the 4 waves of a work-group, the partial write, and the output epilogue.
+#pragma once
+
+#include <math.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+constexpr float kLazyThreshold = 8.0f;   // log2 of the largest unnormalised weight
+
+struct State {
+    float m;        // running max (base 2) of this lane's column
+    float l;        // partial sum of weights over this lane's tokens
+    float z;        // partial sum of weight * value mean (K4V2 only)
+    v4f acc[8];     // value accumulators, channel 16j + 4g + i, column n
+};
+
+// Output of one head from merged sums: 32 lanes (lane32 = lane & 31) hold
+// channels 4*lane32 .. +3.  rotated (the K4V2 path): o_j = (H acc)_j / (128 l)
+// for j >= 1 and o_0 = z / l (the FWHT runs 2 stages in-lane and 5 across);
+// otherwise o = acc / l.  l = 0 gives a zero row.
+__device__ __forceinline__ void finalize_head(const float (&acc)[4], float l, float z, int lane32,
+                                              void *out, int out_f32, int64_t row, int rotated) {
+    float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+    float o[4];
+    if (rotated) {
+        {
+            float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
+            p = y[2]; q = y[3]; y[2] = p + q; y[3] = p - q;
+            p = y[0]; q = y[2]; y[0] = p + q; y[2] = p - q;
+            p = y[1]; q = y[3]; y[1] = p + q; y[3] = p - q;
+        }
+#pragma unroll
+        for (int x = 1; x < 32; x <<= 1) {
+            const bool upper = (lane32 & x) != 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float other = xor_lane(y[e], x);
+                y[e] = upper ? (other - y[e]) : (y[e] + other);
+            }
+        }
+        const float sc = inv_l * (1.0f / 128.0f);
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = y[e] * sc;
+        if (lane32 == 0) o[0] = z * inv_l;   // channel 0 is the weighted mean of the stored value means
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = y[e] * inv_l;
+    }
+    const int64_t base = row * kHeadDim + 4 * lane32;
+    if (out_f32) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(out) + base) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+        const uint32_t lo = (uint32_t)float_to_half_bits(o[0]) | ((uint32_t)float_to_half_bits(o[1]) << 16);
+        const uint32_t hi = (uint32_t)float_to_half_bits(o[2]) | ((uint32_t)float_to_half_bits(o[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + base) = make_uint2(lo, hi);
+    }
+}
+
+// LDS of the wave merge.
+struct MergeLds {
+    float m[kWaves][kHeadsPerGroup];
+    float l[kWaves][kHeadsPerGroup];
+    float z[kWaves][kHeadsPerGroup];
+    float acc[kWaves][kHeadsPerGroup][kHeadDim];
+};
+
+// Merge the 4 waves' states of a work-group (heads hq0 .. hq0 + nh - 1 of
+// sequence b) and write the split's partial, or the output when the sequence
+// has a single split.  unscale(j) is the factor of channel block j.  Every
+// thread of the work-group must call it.
+template <typename Unscale>
+__device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const DecodeArgs &a, int rotated,
+                                                Unscale unscale, int wave, int tid, int b, int hq0, int nh,
+                                                int split, int nsplit) {
+    const int lane = tid & 63;
+    const int n16 = lane & 15;
+    const int g = lane >> 4;
+    float lsum = st.l + xor_lane(st.l, 16);
+    lsum += xor_lane(lsum, 32);
+    float zsum = st.z + xor_lane(st.z, 16);
+    zsum += xor_lane(zsum, 32);
+    // value sums: column n holds the fp16 part, column n + 8 the residual
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) st.acc[j][i] += row_swap8(st.acc[j][i]);
+    if (n16 < kHeadsPerGroup) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float u = unscale(j);
+#pragma unroll
+            for (int i = 0; i < 4; i++) s.acc[wave][n16][16 * j + 4 * g + i] = st.acc[j][i] * u;
+        }
+        if (g == 0) {
+            s.m[wave][n16] = st.m;
+            s.l[wave][n16] = lsum;
+            s.z[wave][n16] = zsum;
+        }
+    }
+    __syncthreads();
+
+    const int hh = tid >> 5;          // head of this thread in the merge
+    const int l32 = tid & 31;
+    const int c0 = 4 * l32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) M = fmaxf(M, s.m[w][hh]);
+    float lt = 0.0f, zt = 0.0f, acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const float mw = s.m[w][hh];
+        const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+        lt += f * s.l[w][hh];
+        zt += f * s.z[w][hh];
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc4[e] += f * s.acc[w][hh][c0 + e];
+    }
+
+    const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
+    if (nsplit == 1 && !a.partials_only) {
+        if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row, rotated);
+        return;
+    }
+    float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
+    if (hh < nh) {
+        if (l32 == 0) {
+            mine[0] = M;
+            mine[1] = lt;
+            mine[2] = zt;
+        }
+        *reinterpret_cast<float4 *>(mine + 4 + c0) = make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
+    }
+}
+
+// Zero output rows of an empty sequence (split 0 writes them; nothing when
+// only partials are produced).
+__device__ __forceinline__ void zero_rows(const DecodeArgs &a, int tid, int b, int hq0, int nh, int split) {
+    if (!a.partials_only && split == 0 && (tid >> 5) < nh) {
+        const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+        if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
+        else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
+    }
+}
+
+}  // namespace kvq

@@ -23,6 +23,11 @@ constexpr int kHeadsPerGroup = 8;   // query heads per MFMA column block (hi + l
 constexpr int kPartialFloats = 132; // m, l, zacc, pad, acc[128]
 constexpr int kMaxPagesPerSplit = 512;  // 64 page pairs per wave (one per lane)
 
+// Uncompressed fp16 baseline cache: one 8192-byte region per (page, KV head).
+constexpr int kRegionF16 = 8192;
+constexpr int kVCodesF16 = 4096;           // values after the 4096 bytes of keys
+constexpr int kMaxPagesPerSplitF16 = 256;  // 64 pages per wave (one per lane)
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -93,6 +98,7 @@ struct DecodeArgs {
     int32_t pages_per_split;
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
+    int32_t rotated;          // 1: K4V2 (Hadamard epilogue); 0: fp16 baseline
     int32_t partials_only;    // 1: the split kernel writes a partial for every
                               // split it runs (also the only one) and leaves
                               // every output row to the combine kernel
@@ -121,5 +127,11 @@ hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
 
 // Work-groups of the decode kernel that the current device runs at once.
 int decode_resident_workgroups();
+
+// fp16 baseline cache: append, decode split kernel (the combine is shared,
+// with a.rotated = 0), resident work-groups of its split kernel.
+hipError_t launch_fp16_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_fp16_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev);
+int decode_fp16_resident_workgroups();
 
 }  // namespace kvq

@@ -213,3 +213,25 @@ def test_fused_append_validation_launches_nothing():
         assert f(Hq=6, Hkv=4) == 2 and f(L=200) == 2
         assert f(wsb=ws - 1) == 5
     assert full(out=None) == 1 and full(dt=9) == 3
+
+
+def test_fp16_baseline_format():
+    lib = kvq.load()
+    f = kvq.Format()
+    assert lib.kvq_format_from_string(b"fp16", ctypes.byref(f)) == 0
+    assert (f.head_dim, f.group_size, f.k_bits, f.v_bits, f.block_size) == (128, 128, 16, 16, 16)
+    assert kvq.page_bytes(f) == 8192 == 16 * 128 * 2 * 2
+    assert kvq.cache_bytes(10, 8, f) == 10 * 8 * 8192
+    # 512 bytes per token per KV head against K4V2's 104
+    assert kvq.page_bytes(f) / 16 == 512 and kvq.page_bytes() / 16 == 104
+    # splits hold at most 256 fp16 pages
+    assert kvq.decode_workspace_bytes(1, 8, 1, 1 << 20, 256, f) > 0
+    with pytest.raises(kvq.KvqError):
+        kvq.decode_workspace_bytes(1, 8, 1, 1 << 20, 258, f)
+    # the fused append-and-decode exists for K4V2 only
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    ws = kvq.decode_workspace_bytes(2, 8, 2, 100, 0, f)
+    assert lib.kvq_append_decode_partials(ctypes.byref(f), g, g, 256, 256, g, g, 10, g, 7, g, 2, 8, 2, 100,
+                                          0.088, g, ws, 0, None) == 3
+

@@ -543,3 +543,145 @@ def test_workload_llama31_70b_prefill_then_decode(dev):
         if step in (0, 1, w.new_tokens - 1):
             e = _check_group(cache, bt, 0, 5, n, kh, vh, q.numpy()[0], w.gqa, out.cpu().numpy()[0])
             log(f"  step {step} (n={n}) kv 5: err {e:.2e}")
+
+
+# --------------------------------------------------------------------------
+# Uncompressed fp16 baseline cache (the reference the K4V2 format saves on)
+# --------------------------------------------------------------------------
+
+F16 = None
+
+
+def _f16():
+    global F16
+    if F16 is None:
+        F16 = kvq.format_from_string("fp16")
+    return F16
+
+
+def _f16_read_token(region, off):
+    """Key and value rows of token slot `off` from one 8192-byte fp16 region,
+    per the layout in include/kvq.h."""
+    e = region.view(np.uint16)
+    n = np.arange(D)
+    k_idx = off * 128 + 32 * ((n >> 3) & 3) + 8 * (n >> 5) + (n & 7)
+    q, i = off // 4, off % 4
+    v_idx = 2048 + ((16 * q + (n & 15)) * 8 + (n >> 4)) * 4 + i
+    return e[k_idx].view(np.float16), e[v_idx].view(np.float16)
+
+
+def test_fp16_append_layout_round_trip(dev):
+    """fp16 append stores every row bit for bit at the documented positions
+    and touches nothing else (skipped and out-of-pool slots included)."""
+    rng = np.random.default_rng(61)
+    T, H, num_pages = 300, 3, 30
+    k = rng.standard_normal((T, H, D)).astype(np.float16)
+    v = rng.standard_normal((T, H, D)).astype(np.float16)
+    slots = rng.permutation(num_pages * 16)[:T].astype(np.int64)
+    slots[rng.integers(0, T, 4)] = -1
+    slots[1] = num_pages * 16 + 7
+    cache = torch.full((num_pages, H, 8192), 0xA5, dtype=torch.uint8, device=dev)
+    kvq.quantize_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(slots).to(dev),
+                        cache, fmt=_f16())
+    got = cache.cpu().numpy()
+    touched = np.zeros(got.shape, bool)
+    for t in range(T):
+        s_ = int(slots[t])
+        if s_ < 0 or s_ >= num_pages * 16:
+            continue
+        for h in range(H):
+            kk, vv = _f16_read_token(got[s_ // 16, h], s_ % 16)
+            assert np.array_equal(kk.view(np.uint16), k[t, h].view(np.uint16))
+            assert np.array_equal(vv.view(np.uint16), v[t, h].view(np.uint16))
+    # every written byte belongs to an appended slot: count them
+    written = int(np.count_nonzero(got != 0xA5))
+    expected_max = int(((slots >= 0) & (slots < num_pages * 16)).sum()) * H * 512
+    assert written <= expected_max
+
+
+def _build_case_f16(dev, B, Hq, Hkv, lens, seed):
+    rng = np.random.default_rng(seed)
+    pages = [int(math.ceil(n / 16)) for n in lens]
+    num_pages = sum(pages) + 2
+    perm = rng.permutation(num_pages)
+    bt = np.full((B, max(pages) + 1), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    # unwritten slots hold NaN bit patterns: a partial page must not read them
+    cache = torch.full((num_pages, Hkv, 8192), 0xFF, dtype=torch.uint8, device=dev)
+    kv = []
+    for b, n in enumerate(lens):
+        k = (rng.standard_normal((n, Hkv, D)) * rng.choice([0.5, 2])).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        k[:, :, rng.integers(0, D, 3)] *= 10
+        slots = inp.slot_mapping(bt, b, 0, n)
+        kvq.quantize_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                            torch.from_numpy(slots).to(dev), cache, fmt=_f16())
+        kv.append((k, v))
+    q = (rng.standard_normal((B, Hq, D)) * rng.choice([0.5, 1, 3])).astype(np.float16)
+    return cache, bt, np.asarray(lens), q, kv
+
+
+def _f16_ref(kv, lens, q, Hq, Hkv):
+    G = Hq // Hkv
+    out = np.zeros((len(lens), Hq, D))
+    for b, n in enumerate(lens):
+        k, v = kv[b]
+        for h in range(Hkv):
+            out[b, h * G:(h + 1) * G] = oracle.attention_f16(k[:, h], v[:, h], q[b, h * G:(h + 1) * G], SCALE)
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens", SMALL)
+def test_fp16_decode_small_matches_oracle(dev, B, Hq, Hkv, lens):
+    log(f"fp16 decode small B={B} Hq={Hq} Hkv={Hkv} lens={lens}")
+    cache, bt, lens_np, q, kv = _build_case_f16(dev, B, Hq, Hkv, lens, seed=B * 31 + Hq + sum(lens))
+    ref = _f16_ref(kv, lens, q, Hq, Hkv)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (0, 2, 6):
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=_f16())
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+    out16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, fmt=_f16())
+    assert np.max(np.abs(out16.float().cpu().numpy() - ref)) <= TOL
+    # the two-phase form gives the same bits
+    ws = kvq.alloc_workspace(B, Hq, Hkv, L, 2, fmt=_f16())
+    kvq.decode_partials(qd, cache, btd, ld, L, ws, pages_per_split=2, fmt=_f16())
+    two = kvq.decode_combine(ws, ld, Hq, Hkv, L, pages_per_split=2, fmt=_f16())
+    one = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=2, fmt=_f16())
+    assert torch.equal(one, two)
+
+
+def test_fp16_decode_qwen3_32b_shape_sampled(dev):
+    """The Qwen3-32B decode shape (8 x 16385 tokens, 64 / 8 heads) on the fp16
+    cache: every sequence decoded; the oracle recomputes sequences 0 and 5."""
+    B, Hq, Hkv, n = 8, 64, 8, 16385
+    log("fp16 decode qwen3_32b shape")
+    rng = np.random.default_rng(2024)
+    pages = -(-n // 16)
+    num_pages = B * pages
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(B, pages)
+    cache = torch.empty((num_pages, Hkv, 8192), dtype=torch.uint8, device=dev)
+    kv = {}
+    for b in range(B):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + b)
+        k = torch.randn((n, Hkv, D), generator=g, device=dev).half()
+        v = torch.randn((n, Hkv, D), generator=g, device=dev).half()
+        kvq.quantize_append(k, v, torch.from_numpy(inp.slot_mapping(bt, b, 0, n)).to(dev), cache, fmt=_f16())
+        if b in (0, 5):
+            kv[b] = (k.cpu().numpy(), v.cpu().numpy())
+    q = (rng.standard_normal((B, Hq, D))).astype(np.float16)
+    out = kvq.decode_attention(torch.from_numpy(q).to(dev), cache, torch.from_numpy(bt).to(dev),
+                               torch.full((B,), n, dtype=torch.int32, device=dev), n, fmt=_f16()).cpu().numpy()
+    G = Hq // Hkv
+    for b in (0, 5):
+        k, v = kv[b]
+        for h in (0, 7):
+            ref = oracle.attention_f16(k[:, h], v[:, h], q[b, h * G:(h + 1) * G], SCALE)
+            assert np.max(np.abs(out[b, h * G:(h + 1) * G] - ref)) <= TOL
+
