@@ -214,16 +214,18 @@ kvq_status kvq_decode_attention_ex(const kvq_format *fmt, void *out, kvq_out_dty
  *   [3]       unused,
  *   [4..131]  acc, the weights times the rotated, scaled value codes
  *             s * c (Hadamard domain, not yet transformed back).
- * Splits past a sequence's end are not written.
+ * Split slots past a sequence's end (and every slot of an empty sequence)
+ * receive an empty partial: m = -inf, l = zacc = 0, acc = 0.
  *
  * kvq_decode_combine: merges the partials of each (sequence, query head) and
  * applies the inverse rotation: after rescaling every split by
  * exp2(m_i - max_i m_i) and summing, out_j = (H acc)_j / (128 l) for j >= 1
  * and out_0 = zacc / l.  A sequence of
- * length 0 gets a zero row.  seq_lens, max_seq_len and pages_per_split must
- * be those of the kvq_decode_partials call that filled the workspace (0
- * selects the same heuristic again); the call must follow it on the same
- * stream or after a synchronisation.
+ * length 0 gets a zero row.  max_seq_len and pages_per_split must be those of
+ * the kvq_decode_partials call that filled the workspace (0 selects the same
+ * heuristic again), since they fix the number of split slots; seq_lens is
+ * validated but not read (every slot holds a partial).  The call must follow
+ * the partials call on the same stream or after a synchronisation.
  */
 kvq_status kvq_decode_partials(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
                                int64_t num_pages, const int32_t *block_tables, int32_t max_pages_per_seq,

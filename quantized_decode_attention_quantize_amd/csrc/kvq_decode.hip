@@ -282,13 +282,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int hq0 = kvh * a.gqa + hg * kHeadsPerGroup;
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
 
-    if (n_tokens == 0) {             // empty sequence: zero output rows
-        zero_rows(a, tid, b, hq0, nh, split);
+    if (p_begin >= npages) {         // an empty sequence, or a split past its end
+        write_empty(a, tid, b, hq0, nh, split);
         return;
     }
-    if (p_begin >= npages) return;   // this split lies past the sequence end
     const int p_end = min(p_begin + pps, npages);
-    const int nsplit = (npages + pps - 1) / pps;
 
     __shared__ _Float16 s_qb[16][kHeadDim];   // [column][slot], slot = 32g + 8d + e
     __shared__ float s_c1[kHeadsPerGroup], s_c2[kHeadsPerGroup];
@@ -483,7 +481,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // ---- merge the 4 waves; write the partial (or the output) ----
     merge_and_store(st, s_merge, a, 1, [](int j) { return __builtin_ldexpf(1.0f, value_unscale_log2(j)); },
-                    wave, tid, b, hq0, nh, split, nsplit);
+                    wave, tid, b, hq0, nh, split);
 }
 
 // Merge the split partials of each (sequence, query head) and apply the
@@ -499,14 +497,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const int l32 = lane & 31;
     const int64_t row = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * 2 + (lane >> 5);
     if (row >= (int64_t)a.num_seqs * a.num_q_heads) return;
-    const int b = (int)(row / a.num_q_heads);
-    int n_tokens = a.seq_lens[b];
-    n_tokens = n_tokens < 0 ? 0 : (n_tokens > a.max_seq_len ? a.max_seq_len : n_tokens);
-    const int npages = (n_tokens + kPage - 1) / kPage;
-    const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-    if (nsplit <= 1 && !a.partials_only) return;   // written by decode_kernel itself
-    // (with partials only: no split for an empty sequence gives l = 0 and a
-    // zero row; a single split is finished from its one partial)
+    // Every split slot of every row holds a partial (empty ones: m = -inf,
+    // l = 0), so the merge needs no sequence lengths; a row with no tokens
+    // ends with l = 0 and a zero output.
+    const int nsplit = a.splits;
     const float *base = a.partials + row * a.splits * kPartialFloats;
     const int c0 = 4 * l32;
     float M = -INFINITY, l = 0.0f, z = 0.0f;

@@ -70,13 +70,13 @@ struct MergeLds {
 };
 
 // Merge the 4 waves' states of a work-group (heads hq0 .. hq0 + nh - 1 of
-// sequence b) and write the split's partial, or the output when the sequence
-// has a single split.  unscale(j) is the factor of channel block j.  Every
-// thread of the work-group must call it.
+// sequence b) and write the split's partial, or the output when the launch
+// has a single split (then no combine runs).  unscale(j) is the factor of
+// channel block j.  Every thread of the work-group must call it.
 template <typename Unscale>
 __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const DecodeArgs &a, int rotated,
                                                 Unscale unscale, int wave, int tid, int b, int hq0, int nh,
-                                                int split, int nsplit) {
+                                                int split) {
     const int lane = tid & 63;
     const int n16 = lane & 15;
     const int g = lane >> 4;
@@ -122,7 +122,7 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
     }
 
     const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
-    if (nsplit == 1 && !a.partials_only) {
+    if (a.splits == 1 && !a.partials_only) {
         if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row, rotated);
         return;
     }
@@ -137,13 +137,26 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
     }
 }
 
-// Zero output rows of an empty sequence (split 0 writes them; nothing when
-// only partials are produced).
-__device__ __forceinline__ void zero_rows(const DecodeArgs &a, int tid, int b, int hq0, int nh, int split) {
-    if (!a.partials_only && split == 0 && (tid >> 5) < nh) {
-        const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
-        if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
-        else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
+// A work-group with no tokens (an empty sequence, or a split past the
+// sequence's end).  With a single split and no combine to follow it writes
+// zero output rows; otherwise it writes empty partials (m = -inf, l = zacc =
+// acc = 0), so that the combine can merge every split slot of every row
+// without knowing the sequence lengths.
+__device__ __forceinline__ void write_empty(const DecodeArgs &a, int tid, int b, int hq0, int nh, int split) {
+    if (a.splits == 1 && !a.partials_only) {
+        if ((tid >> 5) < nh) {
+            const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+            if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
+            else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
+        }
+        return;
+    }
+    constexpr int kQuads = kPartialFloats / 4;   // 33 float4 per partial
+    for (int i = tid; i < nh * kQuads; i += 256) {
+        const int hh = i / kQuads, qd = i % kQuads;
+        const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
+        float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
+        *reinterpret_cast<float4 *>(mine + 4 * qd) = qd == 0 ? make_float4(-INFINITY, 0, 0, 0) : make_float4(0, 0, 0, 0);
     }
 }
 

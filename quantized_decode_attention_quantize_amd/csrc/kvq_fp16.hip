@@ -176,13 +176,11 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
     const int p_begin = split * pps;
     const int hq0 = kvh * a.gqa + hg * kHeadsPerGroup;
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
-    if (n_tokens == 0) {
-        zero_rows(a, tid, b, hq0, nh, split);
+    if (p_begin >= npages) {         // an empty sequence, or a split past its end
+        write_empty(a, tid, b, hq0, nh, split);
         return;
     }
-    if (p_begin >= npages) return;
     const int p_end = min(p_begin + pps, npages);
-    const int nsplit = (npages + pps - 1) / pps;
 
     __shared__ _Float16 s_q[kHeadsPerGroup][kHeadDim];
     __shared__ MergeLds s_merge;
@@ -271,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
             process_page16<true, false>(t, tok0, n_tokens, bq, c1, res_k, g, st);
     }
 
-    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, hq0, nh, split, nsplit);
+    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, hq0, nh, split);
 }
 
 }  // namespace
