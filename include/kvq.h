@@ -18,6 +18,9 @@
  *              accuracy" -- the four-stage pipeline list (Hadamard rotation;
  *              variance normalisation; asymmetric round-to-nearest; scale
  *              folding on read-back) and the preset kv_cache_dtype string.
+ *   [KV-INFRA] encorp.ai, "KV cache compression is an infrastructure decision,
+ *              not a model debate" -- decode bound by HBM traffic; the section
+ *              on OSCAR (sink and recent tokens kept in BF16).
  *
  * Cache format "kvq-k4v2-g128 v1" (the pages fix no numbers; this library
  * fixes them):
@@ -278,6 +281,48 @@ kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new
                                       int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
                                       void *workspace, size_t workspace_bytes, int32_t pages_per_split,
                                       void *stream);
+
+/*
+ * Mixed caches: the partials of several caches merged by one combine.  A
+ * decode step may read its tokens from more than one cache -- e.g. the first
+ * (sink) and the most recent tokens kept uncompressed in an fp16 cache beside
+ * the K4V2 history, as deployed low-bit caches do ([KV-INFRA] section on
+ * OSCAR: sink and recent tokens in BF16, the history compressed) -- and the
+ * attention over the union of their tokens is the log-sum-exp merge of each
+ * cache's split partials.  Both formats produce partials in the same base-2
+ * logit units.
+ *
+ * kvq_decode_split_slots: number of partial slots (splits) a partials call
+ * over one cache with these sizes uses; 0 on invalid input.
+ *
+ * kvq_decode_partials_slots: as kvq_decode_partials, but the partial of split
+ * i goes to slot slot_offset + i of rows holding total_slots slots each: the
+ * workspace holds fp32 [num_seqs][num_q_heads][total_slots][132], at least
+ * num_seqs * num_q_heads * total_slots * 528 bytes, 16-byte aligned.
+ * rotated = 1 stores the partial in the K4V2 Hadamard domain (acc' = H acc,
+ * zacc = acc_0), as K4V2 partials always are (0 is rejected for K4V2); set it
+ * for an fp16 cache whose partials are merged with K4V2 ones.  slot_offset +
+ * the call's split count must not exceed total_slots (else KVQ_ERR_SHAPE).
+ *
+ * kvq_decode_combine_slots: merges all total_slots slots of every (sequence,
+ * query head) row and writes out (fp16 or fp32 [num_seqs][num_q_heads][128]).
+ * rotated = 1 applies the K4V2 epilogue (any mix holding K4V2 partials or
+ * rotated fp16 ones), 0 the plain one (unrotated fp16 partials only).  Every
+ * slot must have been written by a partials call for this step.
+ */
+int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split);
+
+kvq_status kvq_decode_partials_slots(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
+                                     int64_t num_pages, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                     const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                     void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                     int32_t slot_offset, int32_t total_slots, int32_t rotated, void *stream);
+
+kvq_status kvq_decode_combine_slots(void *out, kvq_out_dtype out_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                    const void *workspace, size_t workspace_bytes, int32_t total_slots,
+                                    int32_t rotated, void *stream);
 
 /* Pages per split the heuristic picks for these sizes (0 on invalid input). */
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,

@@ -78,6 +78,8 @@ def _load():
     lib.kvqo_decode_attention_folded.restype = ctypes.c_int
     lib.kvqo_attention_f16.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
     lib.kvqo_attention_f16.restype = None
+    lib.kvqo_attention_f64.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
+    lib.kvqo_attention_f64.restype = None
     _lib = lib
     return lib
 
@@ -231,5 +233,17 @@ def attention_f16(k_f16, v_f16, q_f16, scale):
     assert v.shape == k.shape and k.shape[1:] == (D,) and q.shape[1:] == (D,)
     out = np.empty((q.shape[0], D), np.float64)
     _load().kvqo_attention_f16(_ptr(k), _ptr(v), n, _ptr(q), q.shape[0], float(scale), _ptr(out))
+    return out
+
+
+def attention_f64(k, v, q_f16, scale):
+    """Plain fp64 attention of G query heads over tokens given in fp64:
+    k, v [n][128], q float16 [G][128] -> float64 [G][128]."""
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    q = _c(q_f16, np.float16)
+    assert v.shape == k.shape and k.shape[1:] == (D,) and q.shape[1:] == (D,)
+    out = np.empty((q.shape[0], D), np.float64)
+    _load().kvqo_attention_f64(_ptr(k), _ptr(v), k.shape[0], _ptr(q), q.shape[0], float(scale), _ptr(out))
     return out
 

@@ -517,13 +517,11 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
 /* Uncompressed reference: attention over fp16 keys and values.              */
 /* ------------------------------------------------------------------------ */
 
-/* Plain decode attention of G query heads over n fp16 tokens of one KV head,
- * in fp64: out[g] = sum_t softmax_t(scale * q_g . k_t) v_t.  This is the
- * uncompressed cache the K4V2 format is measured against [KVARN-HN: fp16 as
- * the accuracy and capacity reference].  k, v: [n][128]; q: [G][128];
- * out: [G][128].  n == 0 gives zero rows. */
-void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const uint16_t *q,
-                        int32_t G, double scale, double *out)
+/* Plain decode attention of G query heads over n tokens of one KV head, in
+ * fp64: out[g] = sum_t softmax_t(scale * q_g . k_t) v_t.  k, v: [n][128]
+ * (fp64); q: fp16 [G][128]; out: [G][128].  n == 0 gives zero rows. */
+void kvqo_attention_f64(const double *k, const double *v, int64_t n, const uint16_t *q, int32_t G,
+                        double scale, double *out)
 {
     double *lg = n > 0 ? malloc(sizeof(double) * n) : NULL;
     for (int g = 0; g < G; g++) {
@@ -535,7 +533,7 @@ void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const u
         double mx = -INFINITY;
         for (int64_t t = 0; t < n; t++) {
             double d = 0.0;
-            for (int i = 0; i < KVQO_D; i++) d += qd[i] * kvqo_half_to_double(k[t * KVQO_D + i]);
+            for (int i = 0; i < KVQO_D; i++) d += qd[i] * k[t * KVQO_D + i];
             lg[t] = scale * d;
             if (lg[t] > mx) mx = lg[t];
         }
@@ -543,10 +541,31 @@ void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const u
         for (int64_t t = 0; t < n; t++) {
             double e = exp(lg[t] - mx);
             den += e;
-            for (int i = 0; i < KVQO_D; i++) dst[i] += e * kvqo_half_to_double(v[t * KVQO_D + i]);
+            for (int i = 0; i < KVQO_D; i++) dst[i] += e * v[t * KVQO_D + i];
         }
         for (int i = 0; i < KVQO_D; i++) dst[i] /= den;
     }
     free(lg);
 }
 
+/* The same over fp16 tokens: the uncompressed cache the K4V2 format is
+ * measured against [KVARN-HN: fp16 as the accuracy and capacity reference].
+ * k, v: fp16 [n][128]. */
+void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const uint16_t *q,
+                        int32_t G, double scale, double *out)
+{
+    double *kd = n > 0 ? malloc(sizeof(double) * KVQO_D * n) : NULL;
+    double *vd = n > 0 ? malloc(sizeof(double) * KVQO_D * n) : NULL;
+    if (n > 0 && (!kd || !vd)) {
+        free(kd); free(vd);
+        for (int64_t i = 0; i < (int64_t)G * KVQO_D; i++) out[i] = NAN;
+        return;
+    }
+    for (int64_t i = 0; i < n * KVQO_D; i++) {
+        kd[i] = kvqo_half_to_double(k[i]);
+        vd[i] = kvqo_half_to_double(v[i]);
+    }
+    kvqo_attention_f64(kd, vd, n, q, G, scale, out);
+    free(kd);
+    free(vd);
+}

@@ -20,7 +20,8 @@ __all__ = [
     "KvqError", "Format", "load", "library_path", "format_from_string", "page_bytes",
     "cache_bytes", "alloc_cache", "quantize_append", "decode_workspace_bytes",
     "decode_pages_per_split", "alloc_workspace", "decode_attention", "decode_partials",
-    "decode_combine", "append_decode_attention", "append_decode_partials", "version",
+    "decode_combine", "append_decode_attention", "append_decode_partials", "decode_split_slots",
+    "decode_partials_slots", "decode_combine_slots", "version",
     "HEAD_DIM", "PAGE", "REGION_BYTES",
 ]
 
@@ -88,6 +89,10 @@ def load():
         "kvq_append_decode_partials": (ctypes.c_int, [FP, P, P, i64, i64, P, P, i64, P, i32, P, i32, i32, i32,
                                                       i32, ctypes.c_float, P, sz, i32, P]),
         "kvq_set_split_kernel_events": (ctypes.c_int, [P, P]),
+        "kvq_decode_split_slots": (i32, [FP, i32, i32, i32, i32, i32]),
+        "kvq_decode_partials_slots": (ctypes.c_int, [FP, P, P, i64, P, i32, P, i32, i32, i32, i32,
+                                                     ctypes.c_float, P, sz, i32, i32, i32, i32, P]),
+        "kvq_decode_combine_slots": (ctypes.c_int, [P, ctypes.c_int, i32, i32, P, sz, i32, i32, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvq_last_hip_error": (ctypes.c_int, []),
         "kvq_version": (ctypes.c_char_p, []),
@@ -340,3 +345,54 @@ def append_decode_partials(new_key: torch.Tensor, new_value: torch.Tensor, query
         workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_append_decode_partials")
     return workspace
+
+
+def decode_split_slots(num_seqs: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                       pages_per_split: int = 0, fmt: Format | None = None) -> int:
+    """Partial slots a partials call over one cache with these sizes uses."""
+    n = load().kvq_decode_split_slots(ctypes.byref(_fmt(fmt)), num_seqs, num_q_heads, num_kv_heads,
+                                      max_seq_len, pages_per_split)
+    if n <= 0:
+        raise KvqError(2, "kvq_decode_split_slots")
+    return int(n)
+
+
+def decode_partials_slots(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
+                          seq_lens: torch.Tensor, max_seq_len: int, workspace: torch.Tensor, slot_offset: int,
+                          total_slots: int, rotated: bool = True, softmax_scale: float | None = None,
+                          pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """Partials of one cache into slots [slot_offset, slot_offset + splits) of a
+    workspace of fp32 [B][Hq][total_slots][132] (see include/kvq.h)."""
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
+    B, Hq, _ = query.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load().kvq_decode_partials_slots(
+        ctypes.byref(_fmt(fmt)), _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), B, Hq, cache.shape[1], int(max_seq_len), float(softmax_scale),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), int(pages_per_split), int(slot_offset),
+        int(total_slots), int(bool(rotated)), _stream_ptr(stream))
+    _check(st, "kvq_decode_partials_slots")
+    return workspace
+
+
+def decode_combine_slots(workspace: torch.Tensor, num_seqs: int, num_q_heads: int, total_slots: int,
+                         rotated: bool = True, out: torch.Tensor | None = None, out_dtype=torch.float32,
+                         stream=None) -> torch.Tensor:
+    """Merge all slots of every row of a slotted workspace into out [B][Hq][128]."""
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, HEAD_DIM), dtype=out_dtype, device=workspace.device)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or \
+            out.shape != (num_seqs, num_q_heads, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
+    st = load().kvq_decode_combine_slots(
+        _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16, num_seqs, num_q_heads, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(total_slots), int(bool(rotated)), _stream_ptr(stream))
+    _check(st, "kvq_decode_combine_slots")
+    return out
+
+
+def slots_workspace_bytes(num_seqs: int, num_q_heads: int, total_slots: int) -> int:
+    """Bytes of a slotted workspace: fp32 [B][Hq][total_slots][132]."""
+    return num_seqs * num_q_heads * total_slots * 132 * 4
+

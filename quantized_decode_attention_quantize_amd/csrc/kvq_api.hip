@@ -115,6 +115,8 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     a.gqa = num_q_heads / num_kv_heads;
     a.head_groups = head_groups(a.gqa);
     a.splits = w.splits;
+    a.slot_offset = 0;
+    a.slot_stride = w.splits;
     a.pages_per_split = pps;
     a.partials = static_cast<float *>(workspace);
     return KVQ_OK;
@@ -310,6 +312,68 @@ kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out
     if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
     if (st != KVQ_OK) return st;
     return hip_status(launch_both(a, (hipStream_t)stream));
+}
+
+int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split) {
+    if (!is_known(fmt) || !decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return 0;
+    const bool fp16 = is_fp16(fmt);
+    if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
+    const int32_t pps = pages_per_split ? pages_per_split
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
+    return w.splits > 65535 ? 0 : w.splits;
+}
+
+kvq_status kvq_decode_partials_slots(const kvq_format *fmt, const uint16_t *query, const uint8_t *cache,
+                                     int64_t num_pages, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                     const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                     void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                     int32_t slot_offset, int32_t total_slots, int32_t rotated, void *stream) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_known(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (rotated != 0 && rotated != 1) return KVQ_ERR_SHAPE;
+    if (is_v1(fmt) && !rotated) return KVQ_ERR_UNSUPPORTED;   // K4V2 partials are always rotated
+    if (total_slots <= 0 || total_slots > 65535 || slot_offset < 0) return KVQ_ERR_SHAPE;
+    if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return KVQ_ERR_SHAPE;
+    // the slotted workspace: [num_seqs][num_q_heads][total_slots] partials
+    const size_t need = (size_t)num_seqs * num_q_heads * total_slots * kvq::kPartialFloats * sizeof(float);
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, (size_t)-1, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st != KVQ_OK) return st;
+    if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if ((int64_t)slot_offset + a.splits > total_slots) return KVQ_ERR_SHAPE;
+    a.slot_offset = slot_offset;
+    a.slot_stride = total_slots;
+    a.partials_only = 1;
+    a.rotate_partials = is_fp16(fmt) ? rotated : 0;
+    return hip_status(launch_split(a, (hipStream_t)stream));
+}
+
+kvq_status kvq_decode_combine_slots(void *out, kvq_out_dtype out_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                    const void *workspace, size_t workspace_bytes, int32_t total_slots,
+                                    int32_t rotated, void *stream) {
+    if (rotated != 0 && rotated != 1) return KVQ_ERR_SHAPE;
+    if (num_seqs <= 0 || num_q_heads <= 0 || total_slots <= 0 || total_slots > 65535) return KVQ_ERR_SHAPE;
+    if (!workspace) return KVQ_ERR_WORKSPACE;
+    const size_t need = (size_t)num_seqs * num_q_heads * total_slots * kvq::kPartialFloats * sizeof(float);
+    if (workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+    kvq::DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    kvq_status st = decode_output(out, out_dtype, a);
+    if (st != KVQ_OK) return st;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.splits = total_slots;
+    a.slot_stride = total_slots;
+    a.rotated = rotated;
+    a.partials_only = 1;
+    a.partials = static_cast<float *>(const_cast<void *>(workspace));
+    return hip_status(kvq::launch_decode_combine(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,

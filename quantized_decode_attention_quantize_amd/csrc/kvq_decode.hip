@@ -500,8 +500,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     // Every split slot of every row holds a partial (empty ones: m = -inf,
     // l = 0), so the merge needs no sequence lengths; a row with no tokens
     // ends with l = 0 and a zero output.
-    const int nsplit = a.splits;
-    const float *base = a.partials + row * a.splits * kPartialFloats;
+    const int nsplit = a.slot_stride;
+    const float *base = a.partials + row * a.slot_stride * kPartialFloats;
     const int c0 = 4 * l32;
     float M = -INFINITY, l = 0.0f, z = 0.0f;
     float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};

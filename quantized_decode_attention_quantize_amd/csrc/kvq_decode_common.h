@@ -22,27 +22,33 @@ struct State {
 // channels 4*lane32 .. +3.  rotated (the K4V2 path): o_j = (H acc)_j / (128 l)
 // for j >= 1 and o_0 = z / l (the FWHT runs 2 stages in-lane and 5 across);
 // otherwise o = acc / l.  l = 0 gives a zero row.
+// In-place unnormalised Hadamard transform of one head's 128 values held by
+// 32 lanes (lane32 = lane & 31), 4 channels each: 2 stages in-lane, 5 across.
+__device__ __forceinline__ void hadamard_128(float (&y)[4], int lane32) {
+    {
+        float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
+        p = y[2]; q = y[3]; y[2] = p + q; y[3] = p - q;
+        p = y[0]; q = y[2]; y[0] = p + q; y[2] = p - q;
+        p = y[1]; q = y[3]; y[1] = p + q; y[3] = p - q;
+    }
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) {
+        const bool upper = (lane32 & x) != 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const float other = xor_lane(y[e], x);
+            y[e] = upper ? (other - y[e]) : (y[e] + other);
+        }
+    }
+}
+
 __device__ __forceinline__ void finalize_head(const float (&acc)[4], float l, float z, int lane32,
                                               void *out, int out_f32, int64_t row, int rotated) {
     float y[4] = {acc[0], acc[1], acc[2], acc[3]};
     const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     float o[4];
     if (rotated) {
-        {
-            float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
-            p = y[2]; q = y[3]; y[2] = p + q; y[3] = p - q;
-            p = y[0]; q = y[2]; y[0] = p + q; y[2] = p - q;
-            p = y[1]; q = y[3]; y[1] = p + q; y[3] = p - q;
-        }
-#pragma unroll
-        for (int x = 1; x < 32; x <<= 1) {
-            const bool upper = (lane32 & x) != 0;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const float other = xor_lane(y[e], x);
-                y[e] = upper ? (other - y[e]) : (y[e] + other);
-            }
-        }
+        hadamard_128(y, lane32);
         const float sc = inv_l * (1.0f / 128.0f);
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = y[e] * sc;
@@ -73,10 +79,13 @@ struct MergeLds {
 // sequence b) and write the split's partial, or the output when the launch
 // has a single split (then no combine runs).  unscale(j) is the factor of
 // channel block j.  Every thread of the work-group must call it.
+// (rotate_out: the partial is stored in the K4V2 Hadamard domain, acc' = H acc
+// and zacc = acc_0, so that it merges with K4V2 partials in one combine:
+// (H acc')_j / 128 = acc_j for j >= 1 and channel 0 comes from zacc.)
 template <typename Unscale>
 __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const DecodeArgs &a, int rotated,
                                                 Unscale unscale, int wave, int tid, int b, int hq0, int nh,
-                                                int split) {
+                                                int split, int rotate_out = 0) {
     const int lane = tid & 63;
     const int n16 = lane & 15;
     const int g = lane >> 4;
@@ -126,7 +135,11 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
         if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row, rotated);
         return;
     }
-    float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
+    if (rotate_out) {
+        zt = __shfl(acc4[0], tid & 32, 64);   // channel 0 of this head, from its lane 0
+        hadamard_128(acc4, l32);
+    }
+    float *mine = a.partials + (row * a.slot_stride + a.slot_offset + split) * kPartialFloats;
     if (hh < nh) {
         if (l32 == 0) {
             mine[0] = M;
@@ -155,7 +168,7 @@ __device__ __forceinline__ void write_empty(const DecodeArgs &a, int tid, int b,
     for (int i = tid; i < nh * kQuads; i += 256) {
         const int hh = i / kQuads, qd = i % kQuads;
         const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
-        float *mine = a.partials + (row * a.splits + split) * kPartialFloats;
+        float *mine = a.partials + (row * a.slot_stride + a.slot_offset + split) * kPartialFloats;
         *reinterpret_cast<float4 *>(mine + 4 * qd) = qd == 0 ? make_float4(-INFINITY, 0, 0, 0) : make_float4(0, 0, 0, 0);
     }
 }

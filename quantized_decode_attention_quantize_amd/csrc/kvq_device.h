@@ -99,6 +99,9 @@ struct DecodeArgs {
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
     int32_t rotated;          // 1: K4V2 (Hadamard epilogue); 0: fp16 baseline
+    int32_t slot_offset;      // partial of split s goes to slot slot_offset + s ...
+    int32_t slot_stride;      // ... of rows holding slot_stride slots each
+    int32_t rotate_partials;  // fp16: store partials in the Hadamard domain
     int32_t partials_only;    // 1: the split kernel writes a partial for every
                               // split it runs (also the only one) and leaves
                               // every output row to the combine kernel

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
             process_page16<true, false>(t, tok0, n_tokens, bq, c1, res_k, g, st);
     }
 
-    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, hq0, nh, split);
+    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, hq0, nh, split, a.rotate_partials);
 }
 
 }  // namespace

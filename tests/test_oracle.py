@@ -477,3 +477,31 @@ def test_attention_f16_special_cases():
     out = oracle.attention_f16(k[:0], v[:0], np.ones((2, D), np.float16), 0.1)
     assert np.array_equal(out, np.zeros((2, D)))
 
+
+def test_attention_f64_matches_torch_sdpa_and_concatenation():
+    """fp64 attention over arbitrary rows equals torch SDPA (fp64), and
+    attention over a union of two token sets equals the softmax-weighted merge
+    of the two sets' own attentions (the log-sum-exp identity the split and
+    mixed-cache decode rely on)."""
+    rng = np.random.default_rng(9)
+    n1, n2, G = 40, 70, 3
+    k = rng.standard_normal((n1 + n2, D)) * 0.7
+    v = rng.standard_normal((n1 + n2, D))
+    q = rng.standard_normal((G, D)).astype(np.float16)
+    scale = 1 / math.sqrt(D)
+    got = oracle.attention_f64(k, v, q, scale)
+    kt = torch.from_numpy(k)[None, None].expand(1, G, n1 + n2, D)
+    vt = torch.from_numpy(v)[None, None].expand(1, G, n1 + n2, D)
+    qt = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0].numpy()
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # merge of the two halves by their log-sum-exp weights
+    qd = q.astype(np.float64)
+    parts = []
+    for lo, hi in ((0, n1), (n1, n1 + n2)):
+        lg = scale * qd @ k[lo:hi].T                     # [G][n]
+        parts.append((np.log(np.exp(lg).sum(1)), oracle.attention_f64(k[lo:hi], v[lo:hi], q, scale)))
+    w = np.exp(np.stack([p[0] for p in parts]))          # [2][G]
+    merged = (w[0][:, None] * parts[0][1] + w[1][:, None] * parts[1][1]) / (w[0] + w[1])[:, None]
+    assert np.max(np.abs(merged - got)) < 1e-12
+
