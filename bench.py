@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--no-append-bench", action="store_true")
     ap.add_argument("--no-fp16-baseline", action="store_true",
                     help="skip the uncompressed fp16 cache decode on the same workload")
+    ap.add_argument("--no-mixed-window", action="store_true",
+                    help="skip the fp16 sink + recent window beside the K4V2 history")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=10,
                     help="time the split kernel with kernel events on every N-th timed step")
@@ -74,7 +76,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_32b_16k_traffic.txt")
 DECODE_SOURCES = [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h")]
+                  for f in ("kvq_decode.hip", "kvq_decode_common.h", "kvq_device.h", "kvq_quant.h")]
 
 
 def decode_source_hash() -> str:
@@ -339,6 +341,9 @@ def main():
     if not args.no_fp16_baseline:
         result["fp16_baseline"] = fp16_baseline(torch, inp, kvq, lib, dev, stream, args, ms_per_step)
 
+    if not args.no_mixed_window:
+        result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
+
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
 
@@ -402,6 +407,71 @@ def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
             "kernel_GBps": round(fp16_bytes / (kern * 1e-3) / 1e9, 2),
             "kernel_pct_hbm_peak": round(100 * fp16_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "k4v2_step_speedup": round(ms / k4v2_ms_per_step, 3)}
+
+
+def mixed_window(torch, inp, kvq, lib, dev, stream, args, sink=4, recent=124):
+    """The same decode with each sequence's first `sink` and last `recent`
+    tokens uncompressed in an fp16 cache and the other 16257 in K4V2: K4V2
+    partials, rotated fp16 partials, one combine (three launches per step)."""
+    import numpy as np
+    w = inp.workload("qwen3_32b_16k")
+    B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    n = w.context + 1
+    nf = sink + recent
+    nh = n - nf
+    f16 = kvq.format_from_string("fp16")
+    k4 = kvq.format_from_string("k4v2_g128")
+    bt_np, num_pages = inp.page_table(w)
+    hp = -(-nh // 16)
+    bt_h = torch.from_numpy(np.ascontiguousarray(bt_np[:, :hp])).to(dev)
+    cache_h = torch.zeros((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    pf = -(-nf // 16)
+    bt_f = torch.arange(B * pf, dtype=torch.int32, device=dev).view(B, pf)
+    cache_f = torch.zeros((B * pf, Hkv, 8192), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, 0, n, device=dev)
+        kw = torch.cat([k[:sink], k[n - recent:]]).contiguous()
+        vw = torch.cat([v[:sink], v[n - recent:]]).contiguous()
+        kvq.quantize_append(kw, vw, torch.from_numpy(inp.slot_mapping(bt_f.cpu().numpy(), b, 0, nf)).to(dev),
+                            cache_f, fmt=f16)
+        kh, vh = k[sink:n - recent].contiguous(), v[sink:n - recent].contiguous()
+        kvq.quantize_append(kh, vh, torch.from_numpy(inp.slot_mapping(bt_np, b, 0, nh)).to(dev), cache_h)
+    pools = [cache_h] + [cache_h.clone() for _ in range(5)]
+    q = inp.queries(w, 0, device=dev).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    lens_h = torch.full((B,), nh, dtype=torch.int32, device=dev)
+    lens_f = torch.full((B,), nf, dtype=torch.int32, device=dev)
+    s_h = kvq.decode_split_slots(B, Hq, Hkv, nh, fmt=k4)
+    s_f = kvq.decode_split_slots(B, Hq, Hkv, nf, fmt=f16)
+    total = s_h + s_f
+    ws = torch.empty((kvq.slots_workspace_bytes(B, Hq, total),), dtype=torch.uint8, device=dev)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sc = ctypes.c_float(1.0 / math.sqrt(128))
+
+    def part_args(fmt, cache, bt, lens, L, off):
+        return (ctypes.byref(fmt), P(q.data_ptr()), P(cache.data_ptr()), i64(cache.shape[0]), P(bt.data_ptr()),
+                i32(bt.shape[1]), P(lens.data_ptr()), i32(B), i32(Hq), i32(Hkv), i32(L), sc, P(ws.data_ptr()),
+                ctypes.c_size_t(ws.numel()), i32(0), i32(off), i32(total), i32(1), P(stream.cuda_stream))
+    ah = [part_args(k4, p, bt_h, lens_h, nh, 0) for p in pools]
+    af = part_args(f16, cache_f, bt_f, lens_f, nf, s_h)
+    ac = (P(out.data_ptr()), 0, i32(B), i32(Hq), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()), i32(total), i32(1),
+          P(stream.cuda_stream))
+    fp, fc = lib.kvq_decode_partials_slots, lib.kvq_decode_combine_slots
+    steps = max(20, args.steps)
+    for i in range(10):
+        fp(*ah[i % 6]); fp(*af); fc(*ac)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st = fp(*ah[i % 6]) | fp(*af) | fc(*ac)
+        if st:
+            raise RuntimeError("mixed-window decode failed")
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kv_bytes = B * Hkv * (nh * KV_BYTES_PER_TOKEN_HEAD + nf * 512)
+    return {"workload": f"qwen3_32b_16k, {sink} sink + {recent} recent tokens fp16, {nh} K4V2",
+            "ms_per_step": round(ms, 5), "GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+            "kv_bytes": kv_bytes, "launches_per_step": 3}
 
 
 def append_bench(torch, inp, kvq, call, dev):

@@ -685,3 +685,74 @@ def test_fp16_decode_qwen3_32b_shape_sampled(dev):
             ref = oracle.attention_f16(k[:, h], v[:, h], q[b, h * G:(h + 1) * G], SCALE)
             assert np.max(np.abs(out[b, h * G:(h + 1) * G] - ref)) <= TOL
 
+
+# --------------------------------------------------------------------------
+# Mixed caches: fp16 sink + recent window beside the K4V2 history
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sink,window,hist", [(4, 48, [300, 1000, 0]), (0, 16, [513, 77, 1]), (2, 1, [64, 31, 200])])
+def test_mixed_fp16_window_with_k4v2_history(dev, sink, window, hist):
+    """Attention over a sequence whose first `sink` and last `window` tokens
+    sit uncompressed in an fp16 cache and whose other tokens sit in a K4V2
+    cache: K4V2 partials and rotated fp16 partials merged by one combine equal
+    the oracle's attention over the union (history dequantised, window raw)."""
+    B, Hq, Hkv = len(hist), 16, 2
+    G = Hq // Hkv
+    log(f"mixed cache sink={sink} window={window} hist={hist}")
+    rng = np.random.default_rng(sink * 131 + window + sum(hist))
+    # K4V2 history cache
+    cache_h, pool_h, bt_h, lens_h, q = _build_case(dev, B, Hq, Hkv, [max(n, 1) for n in hist], seed=sum(hist) + 5)
+    lens_h = np.asarray(hist, np.int64)
+    # fp16 window cache: sink + recent tokens of every sequence
+    nf = sink + window
+    pages_f = -(-max(nf, 1) // 16)
+    bt_f = (np.arange(B * pages_f, dtype=np.int32).reshape(B, pages_f))
+    cache_f = torch.full((B * pages_f, Hkv, 8192), 0xFF, dtype=torch.uint8, device=dev)
+    kf = (rng.standard_normal((B, nf, Hkv, D)) * 0.8).astype(np.float16)
+    vf = rng.standard_normal((B, nf, Hkv, D)).astype(np.float16)
+    for b in range(B):
+        if nf:
+            kvq.quantize_append(torch.from_numpy(kf[b]).to(dev), torch.from_numpy(vf[b]).to(dev),
+                                torch.from_numpy(inp.slot_mapping(bt_f, b, 0, nf)).to(dev), cache_f, fmt=_f16())
+    qd = torch.from_numpy(q).to(dev)
+    Lh, Lf = max(int(lens_h.max()), 1), max(nf, 1)
+    s_h = kvq.decode_split_slots(B, Hq, Hkv, Lh)
+    s_f = kvq.decode_split_slots(B, Hq, Hkv, Lf, fmt=_f16())
+    total = s_h + s_f
+    ws = torch.full((kvq.slots_workspace_bytes(B, Hq, total),), 0xFF, dtype=torch.uint8, device=dev)
+    kvq.decode_partials_slots(qd, cache_h, torch.from_numpy(bt_h).to(dev),
+                              torch.from_numpy(lens_h.astype(np.int32)).to(dev), Lh, ws, 0, total)
+    kvq.decode_partials_slots(qd, cache_f, torch.from_numpy(bt_f).to(dev),
+                              torch.full((B,), nf, dtype=torch.int32, device=dev), Lf, ws, s_h, total,
+                              rotated=True, fmt=_f16())
+    out = kvq.decode_combine_slots(ws, B, Hq, total).cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            kh = np.zeros((hist[b], D)); vh = np.zeros((hist[b], D))
+            for t in range(hist[b]):
+                kh[t], vh[t] = oracle.dequant_slot(pool_h[bt_h[b, t // 16], h], t % 16)
+            k_all = np.concatenate([kf[b, :, h].astype(np.float64), kh])
+            v_all = np.concatenate([vf[b, :, h].astype(np.float64), vh])
+            ref = oracle.attention_f64(k_all, v_all, q[b, h * G:(h + 1) * G], SCALE)
+            err = np.max(np.abs(out[b, h * G:(h + 1) * G] - ref))
+            assert err <= TOL, f"b={b} h={h} err={err}"
+
+
+def test_rotated_fp16_partials_alone(dev):
+    """fp16 partials stored in the Hadamard domain and combined with the K4V2
+    epilogue give the plain fp16 decode (to rounding)."""
+    B, Hq, Hkv, lens = 2, 8, 1, [400, 33]
+    cache, bt, lens_np, q, kv = _build_case_f16(dev, B, Hq, Hkv, lens, seed=77)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    plain = kvq.decode_attention(qd, cache, btd, ld, 400, fmt=_f16()).cpu().numpy()
+    total = kvq.decode_split_slots(B, Hq, Hkv, 400, fmt=_f16()) + 1        # one spare slot, written below
+    ws = torch.empty((kvq.slots_workspace_bytes(B, Hq, total),), dtype=torch.uint8, device=dev)
+    kvq.decode_partials_slots(qd, cache, btd, ld, 400, ws, 1, total, rotated=True, fmt=_f16())
+    # slot 0: an empty cache's partials (all sequences of length 0)
+    kvq.decode_partials_slots(qd, cache, btd, torch.zeros(B, dtype=torch.int32, device=dev), 16, ws, 0, total,
+                              rotated=True, pages_per_split=2, fmt=_f16())
+    out = kvq.decode_combine_slots(ws, B, Hq, total).cpu().numpy()
+    assert np.max(np.abs(out - plain)) <= 1e-5
+    assert np.max(np.abs(out - _f16_ref(kv, lens, q, Hq, Hkv))) <= TOL
+
