@@ -12,13 +12,15 @@ copies of the pool (R x 109 MB, more than the 256 MB Infinity Cache), so
 every decode reads its 109 MB from HBM.  A step is two C-ABI calls on one
 stream: kvq_append_decode_partials (the split kernel, which also encodes each
 sequence's new token into its page before reading it; the dominant kernel)
-and kvq_decode_combine.  On every --event-every'th timed step the split
-kernel records a pair of HIP events at its own start and end
-(kvq_set_split_kernel_events, i.e. hipExtLaunchKernel's kernel events on the
-launch stream); their average elapsed time is the kernel duration behind
-roofline.achieved.  Plain event records (hipEventRecord) would add a marker
-packet to the stream and time its gap too; kernel events time the kernel
-alone but still delay the next launch by a few microseconds, hence sampling.
+and kvq_decode_combine.  The timed steps carry no events.
+
+roofline.achieved: after the timed steps, --kernel-launches back-to-back
+launches of the split kernel alone (same arguments, same pool rotation) run
+between two HIP events recorded on the launch stream; their elapsed time over
+the launch count is the kernel's average launch duration.  Per-launch kernel
+events (kvq_set_split_kernel_events, hipExtLaunchKernel's start/stop events)
+are available with --event-every N, but each timed launch then runs a few
+microseconds longer than an untimed one, so they are not the default.
 
 roofline.traffic: HBM bytes per launch of the split kernel from rocprofv3
 FETCH_SIZE and WRITE_SIZE counter runs, each scaled by the factor the same
@@ -67,8 +69,10 @@ def parse():
     ap.add_argument("--no-mixed-window", action="store_true",
                     help="skip the fp16 sink + recent window beside the K4V2 history")
     ap.add_argument("--pages-per-split", type=int, default=0)
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="time the split kernel with kernel events on every N-th timed step")
+    ap.add_argument("--kernel-launches", type=int, default=200,
+                    help="back-to-back split-kernel launches timed for roofline.achieved")
+    ap.add_argument("--event-every", type=int, default=0,
+                    help="also time the split kernel with kernel events on every N-th timed step (0: off)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -122,6 +126,10 @@ class HipEvents:
             if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.ev.append(e)
+
+    def record(self, i, stream_ptr):
+        if self.hip.hipEventRecord(self.ev[i], ctypes.c_void_p(stream_ptr)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         t = ctypes.c_float()
@@ -297,9 +305,10 @@ def main():
         if step(i):
             raise RuntimeError("kvq call failed during warm-up")
     torch.cuda.synchronize()
-    every = max(1, args.event_every)
-    sampled = {i: k for k, i in enumerate(range(0, args.steps, every))}
-    hev = HipEvents(2 * len(sampled))
+    sampled = {}
+    if args.event_every > 0:
+        sampled = {i: k for k, i in enumerate(range(0, args.steps, args.event_every))}
+    hev = HipEvents(2 * len(sampled) + 2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     bad = 0
@@ -310,9 +319,20 @@ def main():
     if bad:
         raise RuntimeError("kvq call failed in the timed region")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]
+
+    # the split kernel alone, back to back, between two events on its stream
+    nl = max(1, args.kernel_launches)
+    kl0 = 2 * len(sampled)
+    hev.record(kl0, stream.cuda_stream)
+    for i in range(nl):
+        bad |= part_fn(*part_args[(args.warmup + args.steps + i) % len(pools)])
+    hev.record(kl0 + 1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError("kvq call failed in the kernel-only launches")
+    dec_avg_ms = hev.elapsed_ms(kl0, kl0 + 1) / nl
+    ev_ms = [hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]
     hev.close()
-    dec_avg_ms = float(np.mean(dec_ms))
     traffic, traffic_note = recorded_traffic()
 
     kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
@@ -330,13 +350,16 @@ def main():
                    "pages_per_split": pps or kvq.decode_pages_per_split(B, Hq, Hkv, n)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_kernel_ms": round(dec_avg_ms, 5),
-        "decode_kernel_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 5),
-                                     round(float(np.percentile(dec_ms, 90)), 5)],
-        "event_samples": len(dec_ms),
+        "decode_kernel_launches_timed": nl,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "decode_kernel", "bytes_per_launch": kv_bytes, "traffic_note": traffic_note},
     }
+
+    if ev_ms:
+        result["kernel_events_in_steps"] = {
+            "samples": len(ev_ms), "mean_ms": round(float(np.mean(ev_ms)), 5),
+            "p10_p90_ms": [round(float(np.percentile(ev_ms, 10)), 5), round(float(np.percentile(ev_ms, 90)), 5)]}
 
     if not args.no_fp16_baseline:
         result["fp16_baseline"] = fp16_baseline(torch, inp, kvq, lib, dev, stream, args, ms_per_step)
@@ -357,8 +380,8 @@ def main():
 def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
     """The same decode (8 x 16385 tokens, 64 / 8 heads) over the uncompressed
     fp16 cache: 512 bytes per token per KV head instead of 104.  Each step is
-    the split kernel + the combine; the split kernel is timed with kernel
-    events on every --event-every'th step, as for K4V2."""
+    the split kernel + the combine; the split kernel alone is then timed back
+    to back between two events, as for K4V2."""
     import numpy as np
     w = inp.workload("qwen3_32b_16k")
     B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
@@ -378,28 +401,28 @@ def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
     call = DecodeCall(kvq, lib, f16, stream.cuda_stream)
     part = [call.partials_args(q, p, bt, lens, n, ws, 0) for p in pools]
     comb = call.combine_args(out, lens, Hq, Hkv, n, ws, 0)
-    pf, cfn, set_events = lib.kvq_decode_partials, lib.kvq_decode_combine, lib.kvq_set_split_kernel_events
+    pf, cfn = lib.kvq_decode_partials, lib.kvq_decode_combine
     steps = max(20, args.steps // 2)
-    every = max(1, args.event_every)
-    sampled = {i: k for k, i in enumerate(range(0, steps, every))}
-    hev = HipEvents(2 * len(sampled))
     for i in range(5):
         pf(*part[i % 2]); cfn(*comb)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        k = sampled.get(i)
-        if k is not None:
-            set_events(hev.ev[2 * k], hev.ev[2 * k + 1])
-        st = pf(*part[i % 2])
-        if k is not None:
-            set_events(None, None)
-        st |= cfn(*comb)
-        if st:
+        if pf(*part[i % 2]) | cfn(*comb):
             raise RuntimeError("fp16 decode call failed")
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = float(np.mean([hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]))
+    hev = HipEvents(2)
+    nl = max(1, args.kernel_launches // 2)
+    hev.record(0, stream.cuda_stream)
+    bad = 0
+    for i in range(nl):
+        bad |= pf(*part[i % 2])
+    hev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError("fp16 decode call failed")
+    kern = hev.elapsed_ms(0, 1) / nl
     hev.close()
     fp16_bytes = B * n * Hkv * 512
     return {"workload": "qwen3_32b_16k, fp16 cache (512 B per token-head)", "ms_per_step": round(ms, 5),
