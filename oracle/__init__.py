@@ -17,6 +17,10 @@ Functions and the passages they follow (pages cited by title and section):
   its plain definition (softmax(scale q.k) v), fp64.
 * ``decode_attention_folded`` -- the same result reached by scale folding on
   read-back (same pipeline list, stage 4), fp64; pins the algebra.
+* ``fmt=(kbits, vbits)`` -- the same pipeline at the other bit widths the pages
+  report (8-bit keys with 4-bit values, 4-bit both: dzen.ru summary of the
+  vLLM TurboQuant post, sections on accuracy and memory); keys 4 or 8 bits,
+  values 2 or 4 bits.  The default (4, 2) is the KVarN preset.
 """
 from __future__ import annotations
 
@@ -80,6 +84,26 @@ def _load():
     lib.kvqo_attention_f16.restype = None
     lib.kvqo_attention_f64.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
     lib.kvqo_attention_f64.restype = None
+    ci = ctypes.c_int
+    lib.kvqo_region_bytes.argtypes = [ci, ci]
+    lib.kvqo_region_bytes.restype = i64
+    lib.kvqo_store_token_fmt.argtypes = [ci, ci, P, ci, P, ctypes.c_uint16, ctypes.c_uint16,
+                                         P, ctypes.c_uint16, ctypes.c_uint16]
+    lib.kvqo_store_token_fmt.restype = None
+    lib.kvqo_load_token_fmt.argtypes = [ci, ci, P, ci, P, P, P, P, P, P]
+    lib.kvqo_load_token_fmt.restype = None
+    lib.kvqo_quantize_append_fmt.argtypes = [ci, ci, P, P, i64, i64, P, i64, i32, P, i64]
+    lib.kvqo_quantize_append_fmt.restype = ctypes.c_int
+    lib.kvqo_dequant_slot_fmt.argtypes = [ci, ci, P, ci, P, P]
+    lib.kvqo_dequant_slot_fmt.restype = None
+    lib.kvqo_dequant_slot_rotated_fmt.argtypes = [ci, ci, P, ci, P, P]
+    lib.kvqo_dequant_slot_rotated_fmt.restype = None
+    lib.kvqo_decode_attention_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
+                                              ctypes.c_double, P, P]
+    lib.kvqo_decode_attention_fmt.restype = ctypes.c_int
+    lib.kvqo_decode_attention_folded_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
+                                                     ctypes.c_double, P]
+    lib.kvqo_decode_attention_folded_fmt.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -141,58 +165,71 @@ def group_zero(codes: np.ndarray, s_bits: int, off_bits: int, is_value: bool) ->
     return off - half_to_double(s_bits) * int(np.sum(codes, dtype=np.int64)) / 128.0
 
 
-def store_token(region: np.ndarray, off: int, kc, ks, kz, vc, vs, vz):
-    assert region.dtype == np.uint8 and region.size == REGION and region.flags.c_contiguous
-    _load().kvqo_store_token(_ptr(region), int(off), _ptr(_c(kc, np.uint8)), int(ks), int(kz),
-                             _ptr(_c(vc, np.uint8)), int(vs), int(vz))
+K4V2 = (4, 2)
 
 
-def load_token(region: np.ndarray, off: int):
+def region_bytes(fmt=K4V2) -> int:
+    """Bytes of one (page, KV head) region for (kbits, vbits)."""
+    n = int(_load().kvqo_region_bytes(int(fmt[0]), int(fmt[1])))
+    if n <= 0:
+        raise ValueError(f"unsupported bit widths {fmt}")
+    return n
+
+
+def store_token(region: np.ndarray, off: int, kc, ks, kz, vc, vs, vz, fmt=K4V2):
+    assert region.dtype == np.uint8 and region.size == region_bytes(fmt) and region.flags.c_contiguous
+    _load().kvqo_store_token_fmt(int(fmt[0]), int(fmt[1]), _ptr(region), int(off), _ptr(_c(kc, np.uint8)),
+                                 int(ks), int(kz), _ptr(_c(vc, np.uint8)), int(vs), int(vz))
+
+
+def load_token(region: np.ndarray, off: int, fmt=K4V2):
     r = _c(region, np.uint8)
+    assert r.size == region_bytes(fmt)
     kc = np.empty(D, np.uint8)
     vc = np.empty(D, np.uint8)
     m = np.zeros(4, np.uint16)
-    _load().kvqo_load_token(_ptr(r), int(off), _ptr(kc), _ptr(m[0:1]), _ptr(m[1:2]),
-                            _ptr(vc), _ptr(m[2:3]), _ptr(m[3:4]))
+    _load().kvqo_load_token_fmt(int(fmt[0]), int(fmt[1]), _ptr(r), int(off), _ptr(kc), _ptr(m[0:1]),
+                                _ptr(m[1:2]), _ptr(vc), _ptr(m[2:3]), _ptr(m[3:4]))
     return kc, int(m[0]), int(m[1]), vc, int(m[2]), int(m[3])
 
 
 def quantize_append(key_f16: np.ndarray, value_f16: np.ndarray, slot_mapping: np.ndarray,
-                    pool: np.ndarray) -> None:
+                    pool: np.ndarray, fmt=K4V2) -> None:
     """key/value: float16 [T][Hkv][128]; slot_mapping int64[T]; pool uint8
-    [num_pages][Hkv][1664], written in place."""
+    [num_pages][Hkv][region_bytes(fmt)], written in place."""
     k = _c(key_f16, np.float16)
     v = _c(value_f16, np.float16)
     T, H, d = k.shape
     assert d == D and v.shape == k.shape
-    assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.shape[1:] == (H, REGION)
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.shape[1:] == (H, region_bytes(fmt))
     sm = _c(slot_mapping, np.int64)
-    rc = _load().kvqo_quantize_append(_ptr(k), _ptr(v), H * D, H * D, _ptr(sm), T, H,
-                                      _ptr(pool), pool.shape[0])
+    rc = _load().kvqo_quantize_append_fmt(int(fmt[0]), int(fmt[1]), _ptr(k), _ptr(v), H * D, H * D, _ptr(sm),
+                                          T, H, _ptr(pool), pool.shape[0])
     if rc != 0:
         raise ValueError("oracle append: slot outside the pool")
 
 
-def dequant_slot(region: np.ndarray, off: int):
+def dequant_slot(region: np.ndarray, off: int, fmt=K4V2):
     r = _c(region, np.uint8)
     k = np.empty(D, np.float64)
     v = np.empty(D, np.float64)
-    _load().kvqo_dequant_slot(_ptr(r), int(off), _ptr(k), _ptr(v))
+    _load().kvqo_dequant_slot_fmt(int(fmt[0]), int(fmt[1]), _ptr(r), int(off), _ptr(k), _ptr(v))
     return k, v
 
 
-def dequant_slot_rotated(region: np.ndarray, off: int):
+def dequant_slot_rotated(region: np.ndarray, off: int, fmt=K4V2):
     r = _c(region, np.uint8)
     k = np.empty(D, np.float64)
     v = np.empty(D, np.float64)
-    _load().kvqo_dequant_slot_rotated(_ptr(r), int(off), _ptr(k), _ptr(v))
+    _load().kvqo_dequant_slot_rotated_fmt(int(fmt[0]), int(fmt[1]), _ptr(r), int(off), _ptr(k), _ptr(v))
     return k, v
 
 
-def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=None):
+def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=None, fmt=K4V2):
     """Plain-definition decode attention in fp64.  query: float16 [B][Hq][128].
     Returns float64 [B][Hq][128] (NaN where head_mask excludes a head)."""
     pool = _c(pool, np.uint8)
+    assert pool.shape[2] == region_bytes(fmt)
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     q = _c(query_f16, np.float16)
@@ -200,24 +237,25 @@ def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=N
     Hkv = pool.shape[1]
     out = np.full((B, Hq, D), np.nan, np.float64)
     hm = None if head_mask is None else _c(head_mask, np.uint8)
-    rc = _load().kvqo_decode_attention(_ptr(pool), pool.shape[0], Hkv, _ptr(bt), bt.shape[1],
-                                       _ptr(sl), B, Hq, _ptr(q), float(scale),
-                                       None if hm is None else _ptr(hm), _ptr(out))
+    rc = _load().kvqo_decode_attention_fmt(int(fmt[0]), int(fmt[1]), _ptr(pool), pool.shape[0], Hkv, _ptr(bt),
+                                           bt.shape[1], _ptr(sl), B, Hq, _ptr(q), float(scale),
+                                           None if hm is None else _ptr(hm), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode: invalid shape or page id")
     return out
 
 
-def decode_attention_folded(pool, block_tables, seq_lens, query_f16, scale):
+def decode_attention_folded(pool, block_tables, seq_lens, query_f16, scale, fmt=K4V2):
     pool = _c(pool, np.uint8)
+    assert pool.shape[2] == region_bytes(fmt)
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     q = _c(query_f16, np.float16)
     B, Hq, d = q.shape
     out = np.empty((B, Hq, D), np.float64)
-    rc = _load().kvqo_decode_attention_folded(_ptr(pool), pool.shape[0], pool.shape[1], _ptr(bt),
-                                              bt.shape[1], _ptr(sl), B, Hq, _ptr(q),
-                                              float(scale), _ptr(out))
+    rc = _load().kvqo_decode_attention_folded_fmt(int(fmt[0]), int(fmt[1]), _ptr(pool), pool.shape[0],
+                                                  pool.shape[1], _ptr(bt), bt.shape[1], _ptr(sl), B, Hq,
+                                                  _ptr(q), float(scale), _ptr(out))
     if rc != 0:
         raise ValueError("oracle folded decode: invalid shape or page id")
     return out

@@ -40,11 +40,28 @@
 
 #define KVQO_D 128          /* head_dim == group size                     */
 #define KVQO_PAGE 16        /* tokens per page                            */
-#define KVQO_REGION 1664    /* bytes per (page, kv head)                  */
-#define KVQO_K_CODES 0      /* token o: 64 bytes at 64*o                  */
-#define KVQO_V_CODES 1024   /* quad g=o/4, slot i=o%4: u16 at 128g+8m+2i  */
-#define KVQO_K_META 1536    /* token o: fp16 s, fp16 z at 1536+4o         */
-#define KVQO_V_META 1600    /* token o: fp16 s, fp16 z at 1600+4o         */
+#define KVQO_REGION 1664    /* bytes per (page, kv head), 4-bit K / 2-bit V */
+
+/* Bit widths.  The pages name the KVarN preset with 4-bit keys and 2-bit
+ * values, and report presets of other widths (8-bit keys with 4-bit values,
+ * 4-bit both) as nearly lossless next to fp16 (dzen.ru summary of the vLLM
+ * TurboQuant post, the sections on accuracy and on memory).  The same KVarN
+ * pipeline is applied at those widths: keys take kbits in {4, 8}, values
+ * vbits in {2, 4}.  A (page, KV head) region then holds, in this order:
+ *   key codes    16 tokens x 16*kbits bytes   at 0
+ *   value codes  16 tokens x 16*vbits bytes   at 256*kbits
+ *   key (s, z)   16 tokens x 4 bytes          at 256*(kbits+vbits)
+ *   value (s, mu) 16 tokens x 4 bytes         at 256*(kbits+vbits) + 64
+ * i.e. 256*(kbits+vbits) + 128 bytes (1664 at 4/2, a multiple of 128). */
+static int fmt_ok(int kbits, int vbits)
+{
+    return (kbits == 4 || kbits == 8) && (vbits == 2 || vbits == 4);
+}
+
+int64_t kvqo_region_bytes(int kbits, int vbits)
+{
+    return fmt_ok(kbits, vbits) ? 256 * (kbits + vbits) + 128 : -1;
+}
 
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32/64, written from the format definition.        */
@@ -237,63 +254,116 @@ void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
 /* Byte layout of one (page, KV head) region.                                */
 /* ------------------------------------------------------------------------ */
 
-/* Write token slot `off` (0..15) of a region: 128 key codes (0..15), 128
- * value codes (0..3) and the two (s, z) pairs.
- *   key codes:   byte 64*off + b = code[2b] | code[2b+1] << 4
- *   value codes: for quad g = off/4, slot i = off%4 and m = 0..15, the 16-bit
- *                little-endian word at 1024 + 128g + 8m + 2i holds the code of
- *                channel 16j + m in bits 2j..2j+1 (j = 0..7)
- *   metadata:    fp16 s then fp16 z, little-endian, at 1536 + 4*off (keys)
- *                and 1600 + 4*off (values). */
-void kvqo_store_token(uint8_t *region, int off,
-                      const uint8_t *kc, uint16_t ks, uint16_t kz,
-                      const uint8_t *vc, uint16_t vs, uint16_t vz)
+/* Write token slot `off` (0..15) of a region: 128 key codes (0..2^kbits-1),
+ * 128 value codes (0..2^vbits-1) and the two (s, offset) pairs.
+ *   key codes:   the token's row of 16*kbits bytes at 16*kbits*off holds the
+ *                code of channel c at bits kbits*c .. kbits*c+kbits-1 of the
+ *                row, least significant bit first (4 bits: byte b = code[2b]
+ *                | code[2b+1] << 4; 8 bits: byte c = code[c]).
+ *   value codes, for quad g = off/4, slot i = off%4 and channel c = 16j + m:
+ *     2 bits: the 16-bit little-endian word at vbase + 128g + 8m + 2i holds
+ *             the code of channel 16j + m in bits 2j..2j+1 (j = 0..7);
+ *     4 bits: with j = 4h + k (h = 0, 1; k = 0..3), the 16-bit word at
+ *             vbase + 256g + 16m + 8(i/2) + 4h + 2(i%2) holds the code of
+ *             channel 16j + m in bits 4k..4k+3.
+ *   metadata:    fp16 s then fp16 offset, little-endian, 4 bytes per token at
+ *                kmeta + 4*off (keys) and kmeta + 64 + 4*off (values).
+ * (vbase = 256*kbits, kmeta = 256*(kbits+vbits).) */
+void kvqo_store_token_fmt(int kbits, int vbits, uint8_t *region, int off,
+                          const uint8_t *kc, uint16_t ks, uint16_t kz,
+                          const uint8_t *vc, uint16_t vs, uint16_t vz)
 {
-    uint8_t *kb = region + KVQO_K_CODES + 64 * off;
-    for (int b = 0; b < 64; b++)
-        kb[b] = (uint8_t)((kc[2 * b] & 15) | ((kc[2 * b + 1] & 15) << 4));
+    const int vbase = 256 * kbits, kmeta = 256 * (kbits + vbits);
+    const unsigned kmask = (1u << kbits) - 1, vmask = (1u << vbits) - 1;
 
-    int g = off / 4, i = off % 4;
-    for (int m = 0; m < 16; m++) {
-        unsigned w = 0;
-        for (int j = 0; j < 8; j++)
-            w |= (unsigned)(vc[16 * j + m] & 3) << (2 * j);
-        uint8_t *vb = region + KVQO_V_CODES + 128 * g + 8 * m + 2 * i;
-        vb[0] = (uint8_t)(w & 0xff);
-        vb[1] = (uint8_t)(w >> 8);
+    uint8_t *kb = region + 16 * kbits * off;
+    memset(kb, 0, (size_t)(16 * kbits));
+    for (int c = 0; c < KVQO_D; c++) {
+        int bit = kbits * c;
+        kb[bit / 8] |= (uint8_t)((kc[c] & kmask) << (bit % 8));
     }
 
-    uint8_t *km = region + KVQO_K_META + 4 * off;
+    int g = off / 4, i = off % 4;
+    if (vbits == 2) {
+        for (int m = 0; m < 16; m++) {
+            unsigned w = 0;
+            for (int j = 0; j < 8; j++)
+                w |= (unsigned)(vc[16 * j + m] & vmask) << (2 * j);
+            uint8_t *vb = region + vbase + 128 * g + 8 * m + 2 * i;
+            vb[0] = (uint8_t)(w & 0xff);
+            vb[1] = (uint8_t)(w >> 8);
+        }
+    } else {
+        for (int m = 0; m < 16; m++)
+            for (int h = 0; h < 2; h++) {
+                unsigned w = 0;
+                for (int k = 0; k < 4; k++)
+                    w |= (unsigned)(vc[16 * (4 * h + k) + m] & vmask) << (4 * k);
+                uint8_t *vb = region + vbase + 256 * g + 16 * m + 8 * (i / 2) + 4 * h + 2 * (i % 2);
+                vb[0] = (uint8_t)(w & 0xff);
+                vb[1] = (uint8_t)(w >> 8);
+            }
+    }
+
+    uint8_t *km = region + kmeta + 4 * off;
     km[0] = (uint8_t)(ks & 0xff); km[1] = (uint8_t)(ks >> 8);
     km[2] = (uint8_t)(kz & 0xff); km[3] = (uint8_t)(kz >> 8);
-    uint8_t *vm = region + KVQO_V_META + 4 * off;
+    uint8_t *vm = region + kmeta + 64 + 4 * off;
     vm[0] = (uint8_t)(vs & 0xff); vm[1] = (uint8_t)(vs >> 8);
     vm[2] = (uint8_t)(vz & 0xff); vm[3] = (uint8_t)(vz >> 8);
 }
 
-/* Inverse of kvqo_store_token. */
+/* Inverse of kvqo_store_token_fmt. */
+void kvqo_load_token_fmt(int kbits, int vbits, const uint8_t *region, int off,
+                         uint8_t *kc, uint16_t *ks, uint16_t *kz,
+                         uint8_t *vc, uint16_t *vs, uint16_t *vz)
+{
+    const int vbase = 256 * kbits, kmeta = 256 * (kbits + vbits);
+    const unsigned kmask = (1u << kbits) - 1, vmask = (1u << vbits) - 1;
+
+    const uint8_t *kb = region + 16 * kbits * off;
+    for (int c = 0; c < KVQO_D; c++) {
+        int bit = kbits * c;
+        kc[c] = (uint8_t)((kb[bit / 8] >> (bit % 8)) & kmask);
+    }
+    int g = off / 4, i = off % 4;
+    if (vbits == 2) {
+        for (int m = 0; m < 16; m++) {
+            const uint8_t *vb = region + vbase + 128 * g + 8 * m + 2 * i;
+            unsigned w = (unsigned)vb[0] | ((unsigned)vb[1] << 8);
+            for (int j = 0; j < 8; j++)
+                vc[16 * j + m] = (uint8_t)((w >> (2 * j)) & vmask);
+        }
+    } else {
+        for (int m = 0; m < 16; m++)
+            for (int h = 0; h < 2; h++) {
+                const uint8_t *vb = region + vbase + 256 * g + 16 * m + 8 * (i / 2) + 4 * h + 2 * (i % 2);
+                unsigned w = (unsigned)vb[0] | ((unsigned)vb[1] << 8);
+                for (int k = 0; k < 4; k++)
+                    vc[16 * (4 * h + k) + m] = (uint8_t)((w >> (4 * k)) & vmask);
+            }
+    }
+    const uint8_t *km = region + kmeta + 4 * off;
+    *ks = (uint16_t)(km[0] | (km[1] << 8));
+    *kz = (uint16_t)(km[2] | (km[3] << 8));
+    const uint8_t *vm = region + kmeta + 64 + 4 * off;
+    *vs = (uint16_t)(vm[0] | (vm[1] << 8));
+    *vz = (uint16_t)(vm[2] | (vm[3] << 8));
+}
+
+/* The 4-bit key / 2-bit value layout (KVarN's preset). */
+void kvqo_store_token(uint8_t *region, int off,
+                      const uint8_t *kc, uint16_t ks, uint16_t kz,
+                      const uint8_t *vc, uint16_t vs, uint16_t vz)
+{
+    kvqo_store_token_fmt(4, 2, region, off, kc, ks, kz, vc, vs, vz);
+}
+
 void kvqo_load_token(const uint8_t *region, int off,
                      uint8_t *kc, uint16_t *ks, uint16_t *kz,
                      uint8_t *vc, uint16_t *vs, uint16_t *vz)
 {
-    const uint8_t *kb = region + KVQO_K_CODES + 64 * off;
-    for (int b = 0; b < 64; b++) {
-        kc[2 * b] = kb[b] & 15;
-        kc[2 * b + 1] = kb[b] >> 4;
-    }
-    int g = off / 4, i = off % 4;
-    for (int m = 0; m < 16; m++) {
-        const uint8_t *vb = region + KVQO_V_CODES + 128 * g + 8 * m + 2 * i;
-        unsigned w = (unsigned)vb[0] | ((unsigned)vb[1] << 8);
-        for (int j = 0; j < 8; j++)
-            vc[16 * j + m] = (uint8_t)((w >> (2 * j)) & 3);
-    }
-    const uint8_t *km = region + KVQO_K_META + 4 * off;
-    *ks = (uint16_t)(km[0] | (km[1] << 8));
-    *kz = (uint16_t)(km[2] | (km[3] << 8));
-    const uint8_t *vm = region + KVQO_V_META + 4 * off;
-    *vs = (uint16_t)(vm[0] | (vm[1] << 8));
-    *vz = (uint16_t)(vm[2] | (vm[3] << 8));
+    kvqo_load_token_fmt(4, 2, region, off, kc, ks, kz, vc, vs, vz);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -306,11 +376,13 @@ void kvqo_load_token(const uint8_t *region, int off,
  * offset, or < 0 to skip the token.  pool: u8 [num_pages][num_kv_heads][1664].
  * Returns 0, or -1 on a slot outside the pool (nothing is written for it).
  */
-int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
-                         int64_t key_token_stride, int64_t value_token_stride,
-                         const int64_t *slot_mapping, int64_t num_tokens,
-                         int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+int kvqo_quantize_append_fmt(int kbits, int vbits, const uint16_t *key, const uint16_t *value,
+                             int64_t key_token_stride, int64_t value_token_stride,
+                             const int64_t *slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
 {
+    if (!fmt_ok(kbits, vbits)) return -1;
+    const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     int rc = 0;
     uint8_t kc[KVQO_D], vc[KVQO_D];
     for (int64_t t = 0; t < num_tokens; t++) {
@@ -321,13 +393,22 @@ int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
         if (page >= num_pages) { rc = -1; continue; }
         for (int h = 0; h < num_kv_heads; h++) {
             uint16_t ks, kz, vs, vz;
-            kvqo_quantize_group(key + t * key_token_stride + (int64_t)h * KVQO_D, 4, kc, &ks, &kz);
-            kvqo_quantize_group(value + t * value_token_stride + (int64_t)h * KVQO_D, 2, vc, &vs, &vz);
-            uint8_t *region = pool + (page * num_kv_heads + h) * (int64_t)KVQO_REGION;
-            kvqo_store_token(region, off, kc, ks, kz, vc, vs, vz);
+            kvqo_quantize_group_mode(key + t * key_token_stride + (int64_t)h * KVQO_D, kbits, 0, kc, &ks, &kz);
+            kvqo_quantize_group_mode(value + t * value_token_stride + (int64_t)h * KVQO_D, vbits, 1, vc, &vs, &vz);
+            uint8_t *region = pool + (page * num_kv_heads + h) * region_bytes;
+            kvqo_store_token_fmt(kbits, vbits, region, off, kc, ks, kz, vc, vs, vz);
         }
     }
     return rc;
+}
+
+int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
+                         int64_t key_token_stride, int64_t value_token_stride,
+                         const int64_t *slot_mapping, int64_t num_tokens,
+                         int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+{
+    return kvqo_quantize_append_fmt(4, 2, key, value, key_token_stride, value_token_stride, slot_mapping,
+                                    num_tokens, num_kv_heads, pool, num_pages);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -335,7 +416,7 @@ int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
 /* ------------------------------------------------------------------------ */
 
 /* Zero-point of a group in the rotated domain: z itself for keys; for values
- * z = mu - s * C / 128 (exact in double: C <= 384). */
+ * z = mu - s * C / 128 (exact in double: C <= 128 * 15). */
 static double group_zero(const uint8_t *codes, uint16_t s16, uint16_t off16, int is_value)
 {
     double off = kvqo_half_to_double(off16);
@@ -359,26 +440,37 @@ static void dequant_unrotate(const uint8_t *codes, uint16_t s16, uint16_t z16, i
 }
 
 /* Public helper for tests: dequantised, un-rotated key and value of one slot. */
-void kvqo_dequant_slot(const uint8_t *region, int off, double *k_out, double *v_out)
+void kvqo_dequant_slot_fmt(int kbits, int vbits, const uint8_t *region, int off, double *k_out, double *v_out)
 {
     uint8_t kc[KVQO_D], vc[KVQO_D];
     uint16_t ks, kz, vs, vz;
-    kvqo_load_token(region, off, kc, &ks, &kz, vc, &vs, &vz);
+    kvqo_load_token_fmt(kbits, vbits, region, off, kc, &ks, &kz, vc, &vs, &vz);
     dequant_unrotate(kc, ks, kz, 0, k_out);
     dequant_unrotate(vc, vs, vz, 1, v_out);
 }
 
+void kvqo_dequant_slot(const uint8_t *region, int off, double *k_out, double *v_out)
+{
+    kvqo_dequant_slot_fmt(4, 2, region, off, k_out, v_out);
+}
+
 /* Rotated-domain dequantised values of one slot (s*c + z per channel). */
-void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, double *v_out)
+void kvqo_dequant_slot_rotated_fmt(int kbits, int vbits, const uint8_t *region, int off, double *k_out,
+                                   double *v_out)
 {
     uint8_t kc[KVQO_D], vc[KVQO_D];
     uint16_t ks, kz, vs, vz;
-    kvqo_load_token(region, off, kc, &ks, &kz, vc, &vs, &vz);
+    kvqo_load_token_fmt(kbits, vbits, region, off, kc, &ks, &kz, vc, &vs, &vz);
     double kzero = group_zero(kc, ks, kz, 0), vzero = group_zero(vc, vs, vz, 1);
     for (int i = 0; i < KVQO_D; i++) {
         k_out[i] = kvqo_half_to_double(ks) * kc[i] + kzero;
         v_out[i] = kvqo_half_to_double(vs) * vc[i] + vzero;
     }
+}
+
+void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, double *v_out)
+{
+    kvqo_dequant_slot_rotated_fmt(4, 2, region, off, k_out, v_out);
 }
 
 /*
@@ -393,12 +485,14 @@ void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, do
  * entry are computed; the rest of `out` is left untouched.
  * Returns 0, or -1 on an invalid shape or page id.
  */
-int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
-                          const int32_t *block_tables, int32_t max_pages_per_seq,
-                          const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                          const uint16_t *query, double scale,
-                          const uint8_t *head_mask, double *out)
+int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
+                              int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              const uint16_t *query, double scale,
+                              const uint8_t *head_mask, double *out)
 {
+    if (!fmt_ok(kbits, vbits)) return -1;
+    const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
     const int G = num_q_heads / num_kv_heads;
     for (int b = 0; b < num_seqs; b++) {
@@ -416,8 +510,8 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
             for (int64_t t = 0; t < n; t++) {
                 int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
                 if (page < 0 || page >= num_pages) { free(K); free(V); free(lg); return -1; }
-                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
-                kvqo_dequant_slot(region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
+                kvqo_dequant_slot_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
             }
             for (int g = 0; g < G; g++) {
                 int hq = kvh * G + g;
@@ -447,6 +541,16 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
     return 0;
 }
 
+int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                          const int32_t *block_tables, int32_t max_pages_per_seq,
+                          const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                          const uint16_t *query, double scale,
+                          const uint8_t *head_mask, double *out)
+{
+    return kvqo_decode_attention_fmt(4, 2, pool, num_pages, num_kv_heads, block_tables, max_pages_per_seq,
+                                     seq_lens, num_seqs, num_q_heads, query, scale, head_mask, out);
+}
+
 /*
  * The same step reached by scale folding on read-back [KVARN-P stage 4], in
  * fp64: never materialise k_t or v_t.  With q' = H q (H symmetric):
@@ -457,11 +561,13 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
  *     only; there (H acc)_0 + 128 zv = 128 sum_t p_t mu_t, the stored means.
  * Exists to pin this algebra against the plain definition above.
  */
-int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
-                                 const int32_t *block_tables, int32_t max_pages_per_seq,
-                                 const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                                 const uint16_t *query, double scale, double *out)
+int kvqo_decode_attention_folded_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
+                                     int32_t num_kv_heads, const int32_t *block_tables,
+                                     int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, const uint16_t *query, double scale, double *out)
 {
+    if (!fmt_ok(kbits, vbits)) return -1;
+    const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
     const int G = num_q_heads / num_kv_heads;
     uint8_t kc[KVQO_D], vc[KVQO_D];
@@ -481,9 +587,9 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
             for (int64_t t = 0; t < n; t++) {
                 int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
                 if (page < 0 || page >= num_pages) { free(lg); return -1; }
-                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
                 uint16_t ks, kz, vs, vz;
-                kvqo_load_token(region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
+                kvqo_load_token_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
                 double dot = 0.0;
                 for (int i = 0; i < KVQO_D; i++) dot += qr[i] * kc[i];
                 lg[t] = scale * (kvqo_half_to_double(ks) * dot + kvqo_half_to_double(kz) * qsum) / 128.0;
@@ -492,9 +598,9 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
             double l = 0.0, zacc = 0.0, acc[KVQO_D] = {0};
             for (int64_t t = 0; t < n; t++) {
                 int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
-                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_REGION;
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
                 uint16_t ks, kz, vs, vz;
-                kvqo_load_token(region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
+                kvqo_load_token_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), kc, &ks, &kz, vc, &vs, &vz);
                 double p = exp(lg[t] - mx);
                 double sv = kvqo_half_to_double(vs);
                 l += p;
@@ -511,6 +617,16 @@ int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t
         free(lg);
     }
     return 0;
+}
+
+int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                                 const int32_t *block_tables, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 const uint16_t *query, double scale, double *out)
+{
+    return kvqo_decode_attention_folded_fmt(4, 2, pool, num_pages, num_kv_heads, block_tables,
+                                            max_pages_per_seq, seq_lens, num_seqs, num_q_heads, query,
+                                            scale, out);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -505,3 +505,246 @@ def test_attention_f64_matches_torch_sdpa_and_concatenation():
     merged = (w[0][:, None] * parts[0][1] + w[1][:, None] * parts[1][1]) / (w[0] + w[1])[:, None]
     assert np.max(np.abs(merged - got)) < 1e-12
 
+
+
+# --------------------------------------------------------------------------
+# Other bit widths: 8-bit or 4-bit keys, 4-bit or 2-bit values
+# --------------------------------------------------------------------------
+
+PRESETS = [(4, 2), (4, 4), (8, 2), (8, 4)]
+
+
+def test_region_sizes():
+    # key codes 16 x 16*kbits, value codes 16 x 16*vbits, 2 x 16 x 4 metadata
+    for kb, vb in PRESETS:
+        assert oracle.region_bytes((kb, vb)) == 16 * (16 * kb + 16 * vb + 8)
+    assert oracle.region_bytes((4, 2)) == 1664
+    with pytest.raises(ValueError):
+        oracle.region_bytes((3, 2))
+
+
+def test_layout_golden_k8v4():
+    f = _read_fixture("layout_k8v4.txt")
+    off, size = int(f["off"]), int(f["region_bytes"])
+    region = np.zeros(size, np.uint8)
+    c = np.arange(D)
+    kc = 2 * c + 1
+    vc = (c // 16 + c % 16) % 16
+    oracle.store_token(region, off, kc, 0x1234, 0x5678, vc, 0x9ABC, 0xDEF0, fmt=(8, 4))
+    expect = np.zeros(size, np.uint8)
+    ko = int(f["key_row_offset"])
+    expect[ko:ko + D] = np.arange(1, 256, 2)
+    base = int(f["value_word_base"])
+    for h in (0, 1):
+        for m, w in enumerate(f[f"value_words_h{h}"].split()):
+            v = int(w, 16)
+            expect[base + 16 * m + 4 * h] = v & 0xFF
+            expect[base + 16 * m + 4 * h + 1] = v >> 8
+    expect[3096:3100] = np.frombuffer(bytes.fromhex(f["key_meta_at_3096"]), np.uint8)
+    expect[3160:3164] = np.frombuffer(bytes.fromhex(f["value_meta_at_3160"]), np.uint8)
+    assert np.array_equal(region, expect)
+
+
+def test_layout_k4_keys_are_the_k4v2_keys():
+    """Key rows do not depend on the value width: 4-bit keys in the 4/4 layout
+    are byte-identical to the 4/2 layout's (pinned by layout_pattern.txt)."""
+    rng = np.random.default_rng(41)
+    kc = rng.integers(0, 16, D)
+    a = np.zeros(1664, np.uint8)
+    b = np.zeros(oracle.region_bytes((4, 4)), np.uint8)
+    oracle.store_token(a, 9, kc, 1, 2, np.zeros(D, np.uint8), 3, 4)
+    oracle.store_token(b, 9, kc, 1, 2, np.zeros(D, np.uint8), 3, 4, fmt=(4, 4))
+    assert np.array_equal(a[:1024], b[:1024])
+
+
+@pytest.mark.parametrize("fmt", PRESETS)
+def test_layout_round_trip_and_isolation_presets(fmt):
+    kb, vb = fmt
+    size = oracle.region_bytes(fmt)
+    rng = np.random.default_rng(42 + kb + vb)
+    region = np.full(size, 0xA5, np.uint8)
+    tokens = {}
+    owned = np.zeros(size, np.int64)
+    for off in rng.permutation(16):
+        kc = rng.integers(0, 1 << kb, D)
+        vc = rng.integers(0, 1 << vb, D)
+        meta = [int(v) for v in rng.integers(0, 65536, 4)]
+        before = region.copy()
+        oracle.store_token(region, int(off), kc, meta[0], meta[1], vc, meta[2], meta[3], fmt=fmt)
+        # a token owns exactly 16*(kbits + vbits) + 8 bytes, disjoint from every other token's
+        tokens[int(off)] = (kc, meta, vc)
+        assert np.count_nonzero(before != region) <= 16 * (kb + vb) + 8
+    for off, (kc, meta, vc) in tokens.items():
+        kc2, ks, kz, vc2, vs, vz = oracle.load_token(region, off, fmt=fmt)
+        assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
+        assert [ks, kz, vs, vz] == meta
+    # ownership: flipping one token's codes changes only its own bytes
+    for off in range(16):
+        kc, meta, vc = tokens[off]
+        before = region.copy()
+        oracle.store_token(region, off, (1 << kb) - 1 - kc, meta[0] ^ 0xFFFF, meta[1] ^ 0xFFFF,
+                           (1 << vb) - 1 - vc, meta[2] ^ 0xFFFF, meta[3] ^ 0xFFFF, fmt=fmt)
+        diff = np.nonzero(before != region)[0]
+        assert diff.size == 16 * (kb + vb) + 8          # every owned bit flipped
+        owned[diff] += 1
+        for o2, (kc2, meta2, vc2) in tokens.items():
+            if o2 != off:
+                assert np.array_equal(oracle.load_token(region, o2, fmt=fmt)[0], kc2)
+        oracle.store_token(region, off, kc, *meta[:2], vc, *meta[2:], fmt=fmt)
+    assert np.all(owned == 1)                         # the 16 tokens tile the region
+
+
+def _sparse_on_grid_8bit(rng, delta=2.0 ** -4, zero=-0.5):
+    """Rotated-domain group y = zero + delta * c with codes c spanning 0..255
+    whose inverse rotation x = H y / 128 is sparse and fp16-exact: c_j =
+    sum_r 2^r (1 - H[j, k_r]) / 2 over 8 distinct columns k_r, each of which
+    has H[j*, k_r] = -1 at one row j* (so c_0 = 0 and c_j* = 255)."""
+    jstar = int(rng.integers(1, D))
+    cols = [k for k in range(1, D) if H[jstar, k] == -1]
+    ks = rng.choice(cols, 8, replace=False)
+    c = np.zeros(D, np.int64)
+    for r, k in enumerate(ks):
+        c += (1 << r) * (1 - H[:, k]) // 2
+    assert c.min() == 0 and c.max() == 255 and c[0] == 0 and c[jstar] == 255
+    y = zero + delta * c
+    x = (H @ y) / 128.0
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x)
+    return x16, c, delta, zero
+
+
+@pytest.mark.parametrize("bits,mode", [(8, 0), (4, 1), (8, 1)])
+def test_on_grid_round_trip_exact_other_widths(bits, mode):
+    """8-bit keys and 4-bit (or 8-bit) groups with the value offset (the group
+    mean): codes, scale and offset come back exactly."""
+    rng = np.random.default_rng(60 + bits + mode)
+    L = (1 << bits) - 1
+    for _ in range(40):
+        x16, c, delta, zero = _sparse_on_grid_8bit(rng) if bits == 8 else _on_grid(rng, L)
+        codes, s, z = oracle.quantize_group(x16, bits, offset_mode=mode)
+        assert np.array_equal(codes, c)
+        assert oracle.half_to_double(s) == delta
+        expect_off = zero if mode == 0 else zero + delta * c.sum() / 128
+        assert oracle.half_to_double(z) == expect_off
+        rec = oracle.half_to_double(s) * codes + oracle.group_zero(codes, s, z, is_value=(mode == 1))
+        assert np.array_equal(rec, zero + delta * c)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_error_bound_and_brute_force_nearest_level_other_widths(bits):
+    rng = np.random.default_rng(70 + bits)
+    L = (1 << bits) - 1
+    levels = np.arange(L + 1, dtype=np.float64)
+    for trial in range(200):
+        mode = trial % 2
+        x = rng.standard_normal(D) * [1.0, 0.01, 50.0][trial % 3]
+        if trial % 5 == 0:
+            x[rng.integers(0, D, 3)] *= 20
+        x16 = x.astype(np.float16)
+        y = H @ x16.astype(np.float64)
+        codes, s16, z16 = oracle.quantize_group(x16, bits, offset_mode=mode)
+        s = oracle.half_to_double(s16)
+        z = oracle.group_zero(codes, s16, z16, is_value=(mode == 1))
+        assert codes.max() <= L
+        rec = s * codes + z
+        # the fp16 offset of a value group is the mean, so its rounding is
+        # spread over L*s/2 at most; keys round z itself
+        slack = 2.0 ** -10 * (L * s + abs(z)) + 1e-6 * np.abs(y).max()
+        err = np.abs(y - rec)
+        assert np.all(err <= s / 2 + slack)
+        best = np.min(np.abs(y[:, None] - (s * levels[None, :] + z)), axis=1)
+        assert np.all(err <= best + slack)
+        assert codes[np.argmin(y)] == 0 and codes[np.argmax(y)] == L
+
+
+def test_wider_codes_lower_the_error():
+    """Same groups at 2, 4 and 8 bits: the mean squared reconstruction error
+    falls by about 4x per extra bit (uniform quantiser, step ~ range / L)."""
+    rng = np.random.default_rng(80)
+    err = {2: 0.0, 4: 0.0, 8: 0.0}
+    for _ in range(200):
+        x16 = rng.standard_normal(D).astype(np.float16)
+        y = H @ x16.astype(np.float64)
+        for bits in err:
+            codes, s, z = oracle.quantize_group(x16, bits, offset_mode=1)
+            rec = oracle.half_to_double(s) * codes + oracle.group_zero(codes, s, z, is_value=True)
+            err[bits] += np.mean((y - rec) ** 2)
+    assert err[4] < err[2] / 16 * 2.5 and err[4] > err[2] / 16 / 2.5
+    assert err[8] < err[4] / 256 * 2.5
+
+
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+def test_append_per_token_and_idempotent_presets(fmt):
+    w = inp.workload("tiny", context=48)
+    k, v = inp.sequence_kv(w, 0)
+    k, v = k.numpy(), v.numpy()
+    bt, npages = inp.page_table(w)
+    slots = inp.slot_mapping(bt, 0, 0, 48)
+    size = oracle.region_bytes(fmt)
+    pool_a = np.full((npages, 1, size), 0x5A, np.uint8)
+    oracle.quantize_append(k, v, slots, pool_a, fmt=fmt)
+    pool_b = np.zeros_like(pool_a)
+    for t in reversed(range(48)):
+        oracle.quantize_append(k[t:t + 1], v[t:t + 1], slots[t:t + 1], pool_b, fmt=fmt)
+    assert np.array_equal(pool_a, pool_b)
+    # the codes and metadata stored are the group encoder's at the preset's widths
+    for t in (0, 17, 47):
+        page, off = slots[t] // 16, slots[t] % 16
+        kc, ks, kz, vc, vs, vz = oracle.load_token(pool_a[page, 0], off, fmt=fmt)
+        assert (kc.tolist(), ks, kz) == _tolist(oracle.quantize_group(k[t, 0], fmt[0], offset_mode=0))
+        assert (vc.tolist(), vs, vz) == _tolist(oracle.quantize_group(v[t, 0], fmt[1], offset_mode=1))
+
+
+def _tolist(g):
+    return g[0].tolist(), g[1], g[2]
+
+
+def _small_case_fmt(fmt, num_seqs=2, hq=4, hkv=2, lens=(37, 70), seed=5, on_grid=False):
+    rng = np.random.default_rng(seed)
+    kb, vb = fmt
+    pages = [int(np.ceil(n / 16)) for n in lens]
+    perm = rng.permutation(sum(pages))
+    bt = np.full((num_seqs, max(pages)), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    pool = np.zeros((sum(pages), hkv, oracle.region_bytes(fmt)), np.uint8)
+    ks, vs = [], []
+    for b in range(num_seqs):
+        n = int(lens[b])
+        if on_grid:
+            gk = (lambda: _sparse_on_grid_8bit(rng)[0]) if kb == 8 else (lambda: _on_grid(rng, 15)[0])
+            k = np.stack([[gk() for _ in range(hkv)] for _ in range(n)])
+            v = np.stack([[_on_grid(rng, (1 << vb) - 1)[0] for _ in range(hkv)] for _ in range(n)])
+        else:
+            k = rng.standard_normal((n, hkv, D)).astype(np.float16)
+            v = rng.standard_normal((n, hkv, D)).astype(np.float16)
+        oracle.quantize_append(k, v, inp.slot_mapping(bt, b, 0, n), pool, fmt=fmt)
+        ks.append(k)
+        vs.append(v)
+    q = rng.standard_normal((num_seqs, hq, D)).astype(np.float16)
+    return pool, bt, np.asarray(lens, np.int64), q, ks, vs
+
+
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+def test_attention_on_grid_equals_sdpa_presets(fmt):
+    pool, bt, lens, q, ks, vs = _small_case_fmt(fmt, on_grid=True, seed=9)
+    scale = 1 / np.sqrt(D)
+    out = oracle.decode_attention(pool, bt, lens, q, scale, fmt=fmt)
+    G = q.shape[1] // pool.shape[1]
+    for b in range(len(lens)):
+        K = torch.from_numpy(ks[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+        V = torch.from_numpy(vs[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+        Q = torch.from_numpy(q[b].astype(np.float64))[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)[:, 0, :]
+        assert np.max(np.abs(out[b] - ref.numpy())) < 1e-12
+
+
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+def test_attention_folded_equals_plain_presets(fmt):
+    pool, bt, lens, q, _, _ = _small_case_fmt(fmt, seed=11, lens=(1, 129))
+    scale = 1 / np.sqrt(D)
+    a = oracle.decode_attention(pool, bt, lens, q, scale, fmt=fmt)
+    b = oracle.decode_attention_folded(pool, bt, lens, q, scale, fmt=fmt)
+    assert np.max(np.abs(a - b)) < 1e-9
