@@ -142,8 +142,9 @@ def cache_bytes(num_pages: int, num_kv_heads: int, fmt: Format | None = None) ->
 
 
 def alloc_cache(num_pages: int, num_kv_heads: int, device="cuda", fmt: Format | None = None) -> torch.Tensor:
-    """Uninitialised pool u8 [num_pages][num_kv_heads][page_bytes(fmt)] (1664 for
-    K4V2, 8192 for the fp16 baseline)."""
+    """Uninitialised pool u8 [num_pages][num_kv_heads][page_bytes(fmt)]
+    (256 (k_bits + v_bits) + 128 bytes for a quantised preset: 1664 for K4V2;
+    8192 for the fp16 baseline)."""
     return torch.empty((num_pages, num_kv_heads, page_bytes(fmt)), dtype=torch.uint8, device=device)
 
 

@@ -11,21 +11,23 @@ namespace {
 thread_local int g_last_hip_error = 0;
 thread_local kvq::LaunchEvents g_split_events;
 
-bool is_v1(const kvq_format *f) {
-    return f && f->head_dim == 128 && f->group_size == 128 && f->k_bits == 4 && f->v_bits == 2 &&
-           f->block_size == 16;
+bool is_g128(const kvq_format *f) {
+    return f && f->head_dim == 128 && f->group_size == 128 && f->block_size == 16;
+}
+
+// A quantised cache: 4- or 8-bit keys, 2- or 4-bit values (4/2 is KVarN's).
+bool is_quant(const kvq_format *f) {
+    return is_g128(f) && (f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4);
 }
 
 // The uncompressed fp16 baseline cache.
-bool is_fp16(const kvq_format *f) {
-    return f && f->head_dim == 128 && f->group_size == 128 && f->k_bits == 16 && f->v_bits == 16 &&
-           f->block_size == 16;
-}
+bool is_fp16(const kvq_format *f) { return is_g128(f) && f->k_bits == 16 && f->v_bits == 16; }
 
-bool is_known(const kvq_format *f) { return is_v1(f) || is_fp16(f); }
+bool is_known(const kvq_format *f) { return is_quant(f) || is_fp16(f); }
 
 size_t region_bytes(const kvq_format *f) {
-    return is_v1(f) ? (size_t)kvq::kRegion : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
+    return is_quant(f) ? (size_t)(256 * (f->k_bits + f->v_bits) + 128)
+                       : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
 }
 
 int32_t max_pps(bool fp16) { return fp16 ? kvq::kMaxPagesPerSplitF16 : kvq::kMaxPagesPerSplit; }
@@ -48,10 +50,12 @@ int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerG
 // carries the same work, and pays its fixed cost (query rotation, wave merge,
 // partial write) once.
 int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
-                      bool fp16 = false) {
+                      int32_t k_bits = 4, int32_t v_bits = 2) {
+    const bool fp16 = k_bits == 16;
     const int64_t units = (int64_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads);
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
-    const int64_t resident = fp16 ? kvq::decode_fp16_resident_workgroups() : kvq::decode_resident_workgroups();
+    const int64_t resident = fp16 ? kvq::decode_fp16_resident_workgroups()
+                                  : kvq::decode_resident_workgroups(k_bits, v_bits);
     int64_t splits = resident / units;
     if (splits < 1) splits = 1;
     int64_t pps = ceil_div(max_pages, splits);
@@ -100,13 +104,16 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
         return KVQ_ERR_SHAPE;
     if ((uintptr_t)seq_lens & 3u) return KVQ_ERR_ALIGN;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                                        fmt->k_bits, fmt->v_bits);
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
     if (w.splits > 65535) return KVQ_ERR_SHAPE;
     memset(&a, 0, sizeof(a));
     a.rotated = fp16 ? 0 : 1;
+    a.k_bits = fmt->k_bits;
+    a.v_bits = fmt->v_bits;
     a.max_seq_len = max_seq_len;
     a.seq_lens = seq_lens;
     a.num_seqs = num_seqs;
@@ -134,14 +141,14 @@ kvq_status decode_inputs(const uint16_t *query, const uint8_t *cache, int64_t nu
     a.num_pages = num_pages;
     a.block_tables = block_tables;
     a.bt_stride = max_pages_per_seq;
-    // K4V2 scores carry the 128 of H H = 128 I; fp16 scores do not
+    // quantised-cache scores carry the 128 of H H = 128 I; fp16 scores do not
     a.alpha = a.rotated ? softmax_scale * 1.4426950408889634f / 128.0f : softmax_scale * 1.4426950408889634f;
     return KVQ_OK;
 }
 
 kvq_status append_inputs(const uint16_t *new_key, const uint16_t *new_value, int64_t key_token_stride,
                          int64_t value_token_stride, kvq::DecodeArgs &a) {
-    if (!a.rotated) return KVQ_ERR_UNSUPPORTED;   // the fused append exists for K4V2 only
+    if (!a.rotated) return KVQ_ERR_UNSUPPORTED;   // the fused append exists for quantised caches only
     if (!new_key || !new_value) return KVQ_ERR_NULL;
     const int64_t row = (int64_t)a.num_kv_heads * kvq::kHeadDim;
     if (key_token_stride < row || value_token_stride < row) return KVQ_ERR_SHAPE;
@@ -183,15 +190,25 @@ extern "C" {
 
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
     if (!preset || !out) return KVQ_ERR_NULL;
-    const bool k4v2 = strcmp(preset, "k4v2_g128") == 0 || strcmp(preset, "kvarn_k4v2_g128") == 0;
-    const bool f16 = strcmp(preset, "fp16") == 0;
-    if (!k4v2 && !f16) return KVQ_ERR_UNSUPPORTED;
-    out->head_dim = 128;
-    out->group_size = 128;
-    out->k_bits = k4v2 ? 4 : 16;
-    out->v_bits = k4v2 ? 2 : 16;
-    out->block_size = 16;
-    return KVQ_OK;
+    static const struct {
+        const char *name;
+        int32_t k_bits, v_bits;
+    } presets[] = {
+        {"k4v2_g128", 4, 2}, {"kvarn_k4v2_g128", 4, 2}, {"k4v4_g128", 4, 4}, {"kvarn_k4v4_g128", 4, 4},
+        {"k8v2_g128", 8, 2}, {"kvarn_k8v2_g128", 8, 2}, {"k8v4_g128", 8, 4}, {"kvarn_k8v4_g128", 8, 4},
+        {"fp16", 16, 16},
+    };
+    for (const auto &p : presets) {
+        if (strcmp(preset, p.name) == 0) {
+            out->head_dim = 128;
+            out->group_size = 128;
+            out->k_bits = p.k_bits;
+            out->v_bits = p.v_bits;
+            out->block_size = 16;
+            return KVQ_OK;
+        }
+    }
+    return KVQ_ERR_UNSUPPORTED;
 }
 
 size_t kvq_page_bytes(const kvq_format *fmt) { return region_bytes(fmt); }
@@ -226,6 +243,8 @@ kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const
     a.num_kv_heads = num_kv_heads;
     a.cache = cache;
     a.num_pages = num_pages;
+    a.k_bits = fmt->k_bits;
+    a.v_bits = fmt->v_bits;
     return hip_status(is_fp16(fmt) ? kvq::launch_fp16_append(a, (hipStream_t)stream)
                                    : kvq::launch_append(a, (hipStream_t)stream));
 }
@@ -242,7 +261,7 @@ size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32
     const bool fp16 = is_fp16(fmt);
     if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits);
     return layout(num_seqs, num_q_heads, max_seq_len, pps).total;
 }
 
@@ -320,7 +339,7 @@ int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t 
     const bool fp16 = is_fp16(fmt);
     if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fp16);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits);
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     return w.splits > 65535 ? 0 : w.splits;
 }
@@ -334,7 +353,7 @@ kvq_status kvq_decode_partials_slots(const kvq_format *fmt, const uint16_t *quer
     if (!fmt) return KVQ_ERR_NULL;
     if (!is_known(fmt)) return KVQ_ERR_UNSUPPORTED;
     if (rotated != 0 && rotated != 1) return KVQ_ERR_SHAPE;
-    if (is_v1(fmt) && !rotated) return KVQ_ERR_UNSUPPORTED;   // K4V2 partials are always rotated
+    if (is_quant(fmt) && !rotated) return KVQ_ERR_UNSUPPORTED;   // quantised-cache partials are always rotated
     if (total_slots <= 0 || total_slots > 65535 || slot_offset < 0) return KVQ_ERR_SHAPE;
     if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, max_seq_len)) return KVQ_ERR_SHAPE;
     // the slotted workspace: [num_seqs][num_q_heads][total_slots] partials

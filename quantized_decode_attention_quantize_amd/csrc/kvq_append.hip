@@ -1,4 +1,5 @@
-// Quantise-on-write of new key/value tokens into the K4V2 g128 paged cache.
+// Quantise-on-write of new key/value tokens into the g128 paged cache (4/8-bit
+// keys, 2/4-bit values; the KVarN preset is 4-bit keys and 2-bit values).
 //
 // Two kernels encode the same bytes:
 //   quantize_append_kernel   one 16-lane row per group = (token, KV head,
@@ -23,6 +24,7 @@ constexpr int kRowsPerBlock = 16;   // 256 threads, 16 groups
 // wave per SIMD (1024 SIMDs x 64 lanes) and more
 constexpr int64_t kLaneKernelMinRows = 65536;
 
+template <int KB, int VB>
 __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;                                  // lane within the row
@@ -42,8 +44,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     const uint16_t *src = is_v ? a.value + tok * a.value_stride + (int64_t)head * kHeadDim
                                : a.key + tok * a.key_stride + (int64_t)head * kHeadDim;
-    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)kRegion;
-    encode_group(src, is_v, r, region, off);
+    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)Layout<KB, VB>::kBytes;
+    encode_group_fmt<KB, VB>(src, is_v, r, region, off);
 }
 
 // Groups per lane-kernel work-group: waves 0 and 1 encode the keys of 128
@@ -51,9 +53,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 constexpr int kLaneRows = 128;
 
 // One group per lane: encode the 128 fp16 values at `src` and store token
-// slot `off` of `region`.  kValue selects the 2-bit value encoding.
-template <bool kValue>
+// slot `off` of `region` (KB-bit key / VB-bit value layout).  kValue selects
+// the value encoding.
+template <int KB, int VB, bool kValue>
 __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region, int off) {
+    using Lay = Layout<KB, VB>;
     float y[kHeadDim];
 #pragma unroll
     for (int c = 0; c < kHeadDim / 8; c++) {
@@ -94,10 +98,13 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
         }
         ss = p[0];
     }
-    constexpr int L = kValue ? 3 : 15;
-    uint32_t packed[16];     // keys: 16 dwords of nibbles; values: 16 words of crumbs
+    constexpr int L = kValue ? Lay::kVL : Lay::kKL;
+    // keys: the token's code row as dwords (16 of nibbles or 32 of bytes);
+    // values: the 16-bit words of the layout (16 of crumbs or 32 of nibbles)
+    constexpr int kWords = kValue ? (VB == 2 ? 16 : 32) : (KB == 4 ? 16 : 32);
+    uint32_t packed[kWords];
 #pragma unroll
-    for (int d = 0; d < 16; d++) packed[d] = 0;
+    for (int d = 0; d < kWords; d++) packed[d] = 0;
     float sm = 0.0f, zm = 0.0f;
     if (ss != 0.0f) {
         const float sigma = sqrtf(ss * 0x1p-7f);
@@ -121,9 +128,14 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
                 const uint32_t code = (uint32_t)fminf(rintf((y[i] - lo) * inv), (float)L);
                 if (kValue) {
                     csum += code;
-                    packed[i & 15] |= code << (2 * (i >> 4));     // word m: channel 16j + m at bits 2j
-                } else {
+                    if (VB == 2)
+                        packed[i & 15] |= code << (2 * (i >> 4));     // word m: channel 16j + m at bits 2j
+                    else   // word 2m + h: channel 16(4h + k) + m at bits 4k
+                        packed[2 * (i & 15) + (i >> 6)] |= code << (4 * ((i >> 4) & 3));
+                } else if (KB == 4) {
                     packed[i >> 3] |= code << (4 * (i & 7));      // byte b = c[2b] | c[2b+1] << 4
+                } else {
+                    packed[i >> 2] |= code << (8 * (i & 3));      // byte c = c[c]
                 }
             }
         }
@@ -141,19 +153,29 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
     uint32_t z16 = float_to_half_bits(materialize(zm));
     if (z16 == 0x8000u) z16 = 0;         // a zero offset is stored as +0
     if (!kValue) {
-        uint4 *dst = reinterpret_cast<uint4 *>(region + kKCodes + 64 * off);
+        uint4 *dst = reinterpret_cast<uint4 *>(region + Lay::kKCodes + 16 * KB * off);
 #pragma unroll
-        for (int q = 0; q < 4; q++)
+        for (int q = 0; q < kWords / 4; q++)
             dst[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
-        *reinterpret_cast<uint32_t *>(region + kKMeta + 4 * off) = s16 | (z16 << 16);
-    } else {
-        uint8_t *vb = region + kVCodes + 128 * (off >> 2) + 2 * (off & 3);
+        *reinterpret_cast<uint32_t *>(region + Lay::kKMeta + 4 * off) = s16 | (z16 << 16);
+    } else if (VB == 2) {
+        uint8_t *vb = region + Lay::kVCodes + 128 * (off >> 2) + 2 * (off & 3);
 #pragma unroll
         for (int m = 0; m < 16; m++) *reinterpret_cast<uint16_t *>(vb + 8 * m) = (uint16_t)packed[m];
-        *reinterpret_cast<uint32_t *>(region + kVMeta + 4 * off) = s16 | (z16 << 16);
+        *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
+    } else {
+        const int i = off & 3;
+        uint8_t *vb = region + Lay::kVCodes + 256 * (off >> 2) + 8 * (i >> 1) + 2 * (i & 1);
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            *reinterpret_cast<uint16_t *>(vb + 16 * m) = (uint16_t)packed[2 * m];
+            *reinterpret_cast<uint16_t *>(vb + 16 * m + 4) = (uint16_t)packed[2 * m + 1];
+        }
+        *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     }
 }
 
+template <int KB, int VB>
 __global__ __launch_bounds__(256) void quantize_append_lanes(AppendArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -166,29 +188,40 @@ __global__ __launch_bounds__(256) void quantize_append_lanes(AppendArgs a) {
     const int64_t page = slot / kPage;
     const int off = (int)(slot % kPage);
     if (page >= a.num_pages) return;
-    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)kRegion;
+    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)Layout<KB, VB>::kBytes;
     if (wave >> 1)
-        encode_lane<true>(a.value + tok * a.value_stride + (int64_t)head * kHeadDim, region, off);
+        encode_lane<KB, VB, true>(a.value + tok * a.value_stride + (int64_t)head * kHeadDim, region, off);
     else
-        encode_lane<false>(a.key + tok * a.key_stride + (int64_t)head * kHeadDim, region, off);
+        encode_lane<KB, VB, false>(a.key + tok * a.key_stride + (int64_t)head * kHeadDim, region, off);
 }
 
-}  // namespace
-
-hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
+template <int KB, int VB>
+hipError_t launch_append_fmt(const AppendArgs &a, hipStream_t stream) {
     const int64_t rows = a.num_tokens * a.num_kv_heads;
     if (rows >= kLaneKernelMinRows) {
         const int64_t blocks = (rows + kLaneRows - 1) / kLaneRows;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(quantize_append_lanes, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(quantize_append_lanes<KB, VB>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, a);
         return hipGetLastError();
     }
     const int64_t groups = a.num_tokens * a.num_kv_heads * 2;
     const int64_t blocks = (groups + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quantize_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(quantize_append_kernel<KB, VB>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
+    if (a.k_bits == 4 && a.v_bits == 2) return launch_append_fmt<4, 2>(a, stream);
+    if (a.k_bits == 4 && a.v_bits == 4) return launch_append_fmt<4, 4>(a, stream);
+    if (a.k_bits == 8 && a.v_bits == 2) return launch_append_fmt<8, 2>(a, stream);
+    if (a.k_bits == 8 && a.v_bits == 4) return launch_append_fmt<8, 4>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

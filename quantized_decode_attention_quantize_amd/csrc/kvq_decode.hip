@@ -60,39 +60,53 @@ namespace kvq {
 namespace {
 
 
+// One page of one lane, for KB-bit keys and VB-bit values.
+template <int KB, int VB>
 struct PageRegs {
-    uint4 k;    // key codes: token (lane & 15), bytes 16*(lane >> 4) .. +15
-    uint2 v;    // value codes: 8 bytes at 8*lane (quad lane>>4, channel lane&15)
-    uint4 km;   // key (s, z) of tokens 4g..4g+3
-    uint4 vm;   // value (s, z) of tokens 4g..4g+3
+    uint32_t k[KB];   // key codes: token (lane & 15), channels 32g..32g+31 (g = lane >> 4),
+                      // the 4*KB bytes at 4*KB*g of the token's code row
+    uint32_t v[VB];   // value codes: the 4*VB bytes at 4*VB*lane (quad g, channel lane & 15)
+    uint4 km;         // key (s, z) of tokens 4g..4g+3
+    uint4 vm;         // value (s, mu) of tokens 4g..4g+3
 };
 
 // Byte offsets of a lane's loads inside a page region (loop invariant).
+template <int KB, int VB>
 struct LaneOffsets {
     uint32_t k, v, km, vm;
     __device__ explicit LaneOffsets(int lane)
-        : k(kKCodes + (uint32_t)(lane & 15) * 64u + (uint32_t)(lane >> 4) * 16u),
-          v(kVCodes + (uint32_t)lane * 8u),
-          km(kKMeta + (uint32_t)(lane >> 4) * 16u),
-          vm(kVMeta + (uint32_t)(lane >> 4) * 16u) {}
+        : k(Layout<KB, VB>::kKCodes + (uint32_t)(lane & 15) * (16u * KB) + (uint32_t)(lane >> 4) * (4u * KB)),
+          v(Layout<KB, VB>::kVCodes + (uint32_t)lane * (4u * VB)),
+          km(Layout<KB, VB>::kKMeta + (uint32_t)(lane >> 4) * 16u),
+          vm(Layout<KB, VB>::kVMeta + (uint32_t)(lane >> 4) * 16u) {}
 };
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // `region` is wave-uniform: it becomes a buffer resource in scalar registers
-// (1664-byte range, so the hardware bounds-checks every access) and the
-// per-lane 32-bit offsets are loop invariant, so a page costs four buffer
-// loads and no vector address arithmetic.
-__device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffsets &o, PageRegs &r) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(region), (short)0, kRegion, 0x00020000);
-    const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k, 0, 0);
-    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.v, 0, 0);
+// (the region's byte range, so the hardware bounds-checks every access) and
+// the per-lane 32-bit offsets are loop invariant, so a page costs four to six
+// buffer loads and no vector address arithmetic.
+template <int KB, int VB>
+__device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffsets<KB, VB> &o,
+                                          PageRegs<KB, VB> &r) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(region), (short)0, Layout<KB, VB>::kBytes, 0x00020000);
+#pragma unroll
+    for (int h = 0; h < KB / 4; h++) {
+        const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 16 * h, 0, 0);
+        r.k[4 * h] = k.x; r.k[4 * h + 1] = k.y; r.k[4 * h + 2] = k.z; r.k[4 * h + 3] = k.w;
+    }
+    if (VB == 2) {
+        const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.v, 0, 0);
+        r.v[0] = v.x; r.v[1] = v.y;
+    } else {
+        const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v, 0, 0);
+        r.v[0] = v.x; r.v[1] = v.y; r.v[VB > 2 ? 2 : 0] = v.z; r.v[VB > 2 ? 3 : 1] = v.w;
+    }
     const v4u km = __builtin_amdgcn_raw_buffer_load_b128(rs, o.km, 0, 0);
     const v4u vm = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vm, 0, 0);
-    r.k = make_uint4(k.x, k.y, k.z, k.w);
-    r.v = make_uint2(v.x, v.y);
     r.km = make_uint4(km.x, km.y, km.z, km.w);
     r.vm = make_uint4(vm.x, vm.y, vm.z, vm.w);
 }
@@ -110,18 +124,29 @@ __device__ __forceinline__ v8h key_codes(uint32_t w) {
     return __builtin_bit_cast(v8h, u);
 }
 
+// 8-bit keys: the A operand of the 8 channels in dwords w0, w1 (bytes =
+// channels 8d..8d+7 of the lane-group's 32).  A byte at bits 0-7 of a 16-bit
+// half is the fp16 subnormal c * 2^-24, so one AND (and one shift) per pair of
+// channels; slot e holds channel {0,2,1,3,4,6,5,7}[e], all scaled by 2^-24.
+__device__ __forceinline__ v8h key_codes8(uint32_t w0, uint32_t w1) {
+    const uint4 u = {w0 & 0x00FF00FFu, (w0 >> 8) & 0x00FF00FFu, w1 & 0x00FF00FFu, (w1 >> 8) & 0x00FF00FFu};
+    return __builtin_bit_cast(v8h, u);
+}
+
 // Folded base-2 scores of the lane's 4 tokens of one page:
 // v_mfma_f32_16x16x32_f16 x 4 (32 channels per instruction and lane-group),
 // columns n < 8 the fp16 query q_hi of head n, columns n >= 8 its residual
 // q_lo = q' - q_hi; adding the partner column (lane n ^ 8, one DPP move)
 // gives both lanes of a pair the same score for head n & 7.
-__device__ __forceinline__ void page_scores(const PageRegs &r, const v8h (&bq)[4],
+template <int KB, int VB>
+__device__ __forceinline__ void page_scores(const PageRegs<KB, VB> &r, const v8h (&bq)[4],
                                             float c1, float c2, float mref, float *lg) {
     v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
-    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.x), bq[0], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.y), bq[1], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.z), bq[2], d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes(r.k.w), bq[3], d, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const v8h a = KB == 4 ? key_codes(r.k[q]) : key_codes8(r.k[(2 * q) % KB], r.k[(2 * q + 1) % KB]);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[q], d, 0, 0, 0);
+    }
     const uint32_t km[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -165,6 +190,21 @@ __device__ __forceinline__ constexpr int value_unscale_log2(int j) {
     return (j == 2 || j == 5) ? 20 : (j == 0 || j == 3 || j == 6) ? 18 : 16;
 }
 
+// 4-bit values: u = one 32-bit word of the layout, the 16-bit word of the
+// lane's channel m for token slots (i, i + 1) of a quad (low, high half), each
+// holding the codes of channel blocks 4h..4h+3 in nibbles k = 0..3.  Returns
+// nibble k of both halves at mantissa bits 4-7: the fp16 subnormals
+// c * 2^-20.  Shifted-in bits of the other half fall outside the mask.
+__device__ __forceinline__ uint32_t value_code4(uint32_t u, int k) {
+    constexpr uint32_t kBits47 = 0x00F000F0u;
+    switch (k) {
+    case 0: return (u << 4) & kBits47;
+    case 1: return u & kBits47;
+    case 2: return (u >> 4) & kBits47;
+    default: return (u >> 8) & kBits47;
+    }
+}
+
 struct LaneConsts {
     float c1, c2;          // folded score constants of head n & 7
     float res_k;           // 0 (lanes n < 8: weight) or -1 (lanes n >= 8: residual)
@@ -179,15 +219,16 @@ struct LaneConsts {
 // maximum; 0 before the first pair), so the weights are exp2 of them
 // directly.  When a score exceeds the reference (some logit beats m by more
 // than 8), the state is rescaled and the scores shifted to the new reference.
-template <bool kMasked, bool kFirst>
-__device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &B, int tokA, int tokB,
+template <int KB, int VB, bool kMasked, bool kFirst>
+__device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
+                                             int tokB,
                                              int n_tokens, const v8h (&bq)[4], const LaneConsts &lc,
                                              int g, State &st) {
     constexpr bool first = kFirst;
     const float mref = first ? 0.0f : st.m + kLazyThreshold;
     float lg[8];
-    page_scores(A, bq, lc.c1, lc.c2, mref, lg);
-    page_scores(B, bq, lc.c1, lc.c2, mref, lg + 4);
+    page_scores<KB, VB>(A, bq, lc.c1, lc.c2, mref, lg);
+    page_scores<KB, VB>(B, bq, lc.c1, lc.c2, mref, lg + 4);
     bool valid[8];
     if (kMasked) {
 #pragma unroll
@@ -242,14 +283,23 @@ __device__ __forceinline__ void process_pair(const PageRegs &A, const PageRegs &
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const uint4 packed = {value_code(A.v.x, j), value_code(A.v.y, j),
-                              value_code(B.v.x, j), value_code(B.v.y, j)};
+        // tokens 4g, 4g+1 | 4g+2, 4g+3 of page A, then of page B
+        uint4 packed;
+        if (VB == 2) {
+            packed = {value_code(A.v[0], j), value_code(A.v[1], j), value_code(B.v[0], j), value_code(B.v[1], j)};
+        } else {
+            const int h = j >> 2, k = j & 3;
+            packed = {value_code4(A.v[h], k), value_code4(A.v[(2 + h) % VB], k), value_code4(B.v[h], k),
+                      value_code4(B.v[(2 + h) % VB], k)};
+        }
         const v8h av = __builtin_bit_cast(v8h, packed);
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, st.acc[j], 0, 0, 0);
     }
 }
 
+template <int KB, int VB>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    using Lay = Layout<KB, VB>;
     const int split = blockIdx.x;
     const int kvh = blockIdx.y / a.head_groups;
     const int hg = blockIdx.y % a.head_groups;
@@ -294,12 +344,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
-    const int64_t head_off = (int64_t)kvh * kRegion;
-    const int64_t page_stride = (int64_t)a.num_kv_heads * kRegion;
+    const int64_t head_off = (int64_t)kvh * Lay::kBytes;
+    const int64_t page_stride = (int64_t)a.num_kv_heads * Lay::kBytes;
 
     // A page id outside the pool is read as page 0: never an out-of-bounds
     // access (the output is unspecified under that precondition violation).
-    const LaneOffsets lo(lane);
+    const LaneOffsets<KB, VB> lo(lane);
     const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
     auto region_of = [&](int32_t page_id) -> const uint8_t * {
         uint32_t id = (uint32_t)page_id;
@@ -321,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // The scheduling barrier keeps the compiler from sinking the prefetch
     // loads into the next pair's arithmetic (which it otherwise does to save
     // registers, leaving the current pair's loads as the newest in flight).
-    auto issue = [&](PageRegs &A, PageRegs &B, int i) {
+    auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, int i) {
         const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
         load_page(region_of(__builtin_amdgcn_readlane(bt_a, j)), lo, A);
         load_page(region_of(__builtin_amdgcn_readlane(bt_b, j)), lo, B);
@@ -344,7 +394,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                         ? a.new_value + (int64_t)b * a.new_value_stride + (int64_t)kvh * kHeadDim
                         : a.new_key + (int64_t)b * a.new_key_stride + (int64_t)kvh * kHeadDim;
                     uint8_t *region = const_cast<uint8_t *>(a.cache) + (int64_t)id * page_stride + head_off;
-                    encode_group(src, is_v, lane & 15, region, pos % kPage);
+                    encode_group_fmt<KB, VB>(src, is_v, lane & 15, region, pos % kPage);
                 }
             }
             // the stores have reached L2 before any wave of the group loads
@@ -362,7 +412,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // every path, so the wait for their load is placed here and not repeated
     // (as a wait for all loads in flight) inside the pair loop.
     asm volatile("" ::"v"(bt_a), "v"(bt_b));
-    PageRegs r0A, r0B, r1A, r1B, r2A, r2B;
+    PageRegs<KB, VB> r0A, r0B, r1A, r1B, r2A, r2B;
     if (nk > 0) {
         issue(r0A, r0B, 0);
         issue(r1A, r1B, 1);
@@ -414,8 +464,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; e++) {
             const int ch = c0 + e;
             const int r8 = ch & 7;
-            const int slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
-            const int hi_nibble = (slot >> 1) & 1;       // slots scaled by 2^-20 in the key operand
+            // slot of channel ch in the key operand's order (see key_codes,
+            // key_codes8); 4-bit keys in slots 2, 3, 6, 7 carry 2^-20
+            int slot, hi_nibble = 0;
+            if (KB == 4) {
+                slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
+                hi_nibble = (slot >> 1) & 1;
+            } else {
+                slot = (ch & ~7) + ((r8 & 4) | ((r8 & 1) << 1) | ((r8 >> 1) & 1));
+            }
             const float v = __builtin_ldexpf(q[e], shift - 4 * hi_nibble);
             const _Float16 vh = (_Float16)v;
             s_qb[hh][slot] = vh;
@@ -450,23 +507,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // the wave's first pair sets the running maximum; the loop then
         // rotates the three buffers (pair i in r1, i + 1 in r2, i + 2 in r0)
         issue(r2A, r2B, 2);
-        process_pair<false, true>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+        process_pair<KB, VB, false, true>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
         if (nk > 1) {
             for (int i = 1;; i += 3) {
                 issue(r0A, r0B, i + 2);
-                process_pair<false, false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, false, false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
                 if (i + 1 >= nk) break;
                 issue(r1A, r1B, i + 3);
-                process_pair<false, false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, false, false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
                 if (i + 2 >= nk) break;
                 issue(r2A, r2B, i + 4);
-                process_pair<false, false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, false, false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
                 if (i + 3 >= nk) break;
             }
         }
     }
     if (last_partial && wave == (npairs - 1) % kWaves) {
-        PageRegs tA, tB;
+        PageRegs<KB, VB> tA, tB;
         const bool has_b = last_pa + 1 < p_end;
         const int j = (npairs - 1) / kWaves;    // this wave's last pair
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
@@ -474,13 +531,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         load_page(region_of(has_b ? __builtin_amdgcn_readlane(bt_b, j) : id_a), lo, tB);
         const int tok_b = has_b ? (last_pa + 1) * kPage : n_tokens;
         if (nk == 0)
-            process_pair<true, true>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
+            process_pair<KB, VB, true, true>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
         else
-            process_pair<true, false>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
+            process_pair<KB, VB, true, false>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
     }
 
     // ---- merge the 4 waves; write the partial (or the output) ----
-    merge_and_store(st, s_merge, a, 1, [](int j) { return __builtin_ldexpf(1.0f, value_unscale_log2(j)); },
+    merge_and_store(st, s_merge, a, 1,
+                    [](int j) { return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : 20); },
                     wave, tid, b, hq0, nh, split);
 }
 
@@ -539,11 +597,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     finalize_head(o4, l, z, l32, a.out, a.out_f32, row, a.rotated);
 }
 
-}  // namespace
-
-int decode_resident_workgroups() {
-    // Work-groups of decode_kernel the current device holds at once (compute
-    // units x occupancy), queried once per device; 512 without a device.
+// Work-groups of decode_kernel<KB, VB> the current device holds at once
+// (compute units x occupancy), queried once per device; 512 without a device.
+template <int KB, int VB>
+int resident_workgroups() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -553,7 +610,7 @@ int decode_resident_workgroups() {
     if (cached[dev] > 0) return cached[dev];
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB>, 256, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -562,13 +619,33 @@ int decode_resident_workgroups() {
     return cached[dev];
 }
 
-hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+template <int KB, int VB>
+hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB>), grid, dim3(256), 0, stream, ev.start,
+                              ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(decode_kernel, grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_resident_workgroups(int k_bits, int v_bits) {
+    if (k_bits == 4 && v_bits == 2) return resident_workgroups<4, 2>();
+    if (k_bits == 4 && v_bits == 4) return resident_workgroups<4, 4>();
+    if (k_bits == 8 && v_bits == 2) return resident_workgroups<8, 2>();
+    if (k_bits == 8 && v_bits == 4) return resident_workgroups<8, 4>();
+    return 512;
+}
+
+hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+    if (a.k_bits == 4 && a.v_bits == 2) return launch_split_fmt<4, 2>(a, stream, ev);
+    if (a.k_bits == 4 && a.v_bits == 4) return launch_split_fmt<4, 4>(a, stream, ev);
+    if (a.k_bits == 8 && a.v_bits == 2) return launch_split_fmt<8, 2>(a, stream, ev);
+    if (a.k_bits == 8 && a.v_bits == 4) return launch_split_fmt<8, 4>(a, stream, ev);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream) {

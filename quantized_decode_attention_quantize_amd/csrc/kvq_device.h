@@ -2,6 +2,7 @@
 //
 // Cache format "kvq-k4v2-g128 v1": one 1664-byte region per (page, KV head);
 // 16 tokens per page; 128 channels per head; see include/kvq.h for the layout.
+// The same layout family holds 8-bit keys and 4-bit values (Layout below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,21 @@ constexpr int kKCodes = 0;      // token o: 64 bytes at 64*o
 constexpr int kVCodes = 1024;   // quad g, slot i, m: u16 at 1024 + 128g + 8m + 2i
 constexpr int kKMeta = 1536;    // token o: (s, z) fp16 at 1536 + 4o
 constexpr int kVMeta = 1600;    // token o: (s, z) fp16 at 1600 + 4o
+
+// Region of KB-bit keys (4 or 8) and VB-bit values (2 or 4): key codes (16
+// tokens x 16 KB bytes, token-major), value codes (16 x 16 VB bytes), key and
+// value metadata (16 x 4 bytes each).  Layout<4, 2> is the 1664-byte region.
+template <int KB, int VB>
+struct Layout {
+    static_assert((KB == 4 || KB == 8) && (VB == 2 || VB == 4), "unsupported bit widths");
+    static constexpr int kKCodes = 0;
+    static constexpr int kVCodes = 256 * KB;
+    static constexpr int kKMeta = 256 * (KB + VB);
+    static constexpr int kVMeta = kKMeta + 64;
+    static constexpr int kBytes = kKMeta + 128;
+    static constexpr int kKL = (1 << KB) - 1;   // largest key code
+    static constexpr int kVL = (1 << VB) - 1;   // largest value code
+};
 
 // Decode work decomposition.
 constexpr int kWaves = 4;           // waves per work-group
@@ -75,6 +91,8 @@ struct AppendArgs {
     int32_t num_kv_heads;
     uint8_t *cache;
     int64_t num_pages;
+    int32_t k_bits;    // 4 or 8
+    int32_t v_bits;    // 2 or 4
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
@@ -98,7 +116,8 @@ struct DecodeArgs {
     int32_t pages_per_split;
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
-    int32_t rotated;          // 1: K4V2 (Hadamard epilogue); 0: fp16 baseline
+    int32_t k_bits, v_bits;   // quantised cache: 4|8, 2|4 (16, 16: fp16 baseline)
+    int32_t rotated;          // 1: quantised (Hadamard epilogue); 0: fp16 baseline
     int32_t slot_offset;      // partial of split s goes to slot slot_offset + s ...
     int32_t slot_stride;      // ... of rows holding slot_stride slots each
     int32_t rotate_partials;  // fp16: store partials in the Hadamard domain
@@ -128,8 +147,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const LaunchEv
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev);
 hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
 
-// Work-groups of the decode kernel that the current device runs at once.
-int decode_resident_workgroups();
+// Work-groups of the decode kernel for these bit widths that the current
+// device runs at once.
+int decode_resident_workgroups(int k_bits, int v_bits);
 
 // fp16 baseline cache: append, decode split kernel (the combine is shared,
 // with a.rotated = 0), resident work-groups of its split kernel.

@@ -1,5 +1,6 @@
-// Encoder of one K4V2 g128 group (one token of one KV head, keys or values),
-// shared by the quantise-append kernel and the fused append-and-decode path.
+// Encoder of one g128 group (one token of one KV head, keys or values) at
+// 4/8-bit keys and 2/4-bit values, shared by the quantise-append kernel and
+// the fused append-and-decode path.
 //
 // Method: the KVarN write path -- Hadamard rotation, variance normalisation,
 // asymmetric round-to-nearest to 4-bit keys / 2-bit values (dothoosh.com,
@@ -40,9 +41,12 @@ __device__ __forceinline__ float materialize(float x) {
 // Encode the 128 fp16 values at `src` (16-byte aligned) with the 16 lanes of
 // one row (r = lane within the row; all 16 lanes must be active and share the
 // arguments) and store codes and metadata of token slot `off` (0..15) in the
-// (page, KV head) region `region`.
-__device__ __forceinline__ void encode_group(const uint16_t *src, int is_v, int r, uint8_t *region, int off) {
+// (page, KV head) region `region` of the KB-bit key / VB-bit value layout.
+template <int KB, int VB>
+__device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, int r, uint8_t *region,
+                                                 int off) {
 #pragma clang fp contract(off)
+    using Lay = Layout<KB, VB>;
     const uint4 raw = *reinterpret_cast<const uint4 *>(src + 8 * r);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     float y[8];
@@ -88,7 +92,7 @@ __device__ __forceinline__ void encode_group(const uint16_t *src, int is_v, int 
     p[0] = p[0] + p[2]; p[1] = p[1] + p[3];
     const float ss = p[0] + p[1];
 
-    const int L = is_v ? 3 : 15;
+    const int L = is_v ? Lay::kVL : Lay::kKL;
     uint32_t code[8];
     float sm = 0.0f, zm = 0.0f;   // metadata before fp16 rounding
     if (ss == 0.0f) {
@@ -145,13 +149,49 @@ __device__ __forceinline__ void encode_group(const uint16_t *src, int is_v, int 
     if (z16 == 0x8000u) z16 = 0;   // a zero offset is stored as +0
 
     if (!is_v) {
-        // keys: byte b of the token's 64 = code[2b] | code[2b+1] << 4
-        uint32_t packed = 0;
+        if (KB == 4) {
+            // keys: byte b of the token's 64 = code[2b] | code[2b+1] << 4
+            uint32_t packed = 0;
 #pragma unroll
-        for (int e = 0; e < 8; e++) packed |= code[e] << (4 * e);
-        *reinterpret_cast<uint32_t *>(region + kKCodes + 64 * off + 4 * r) = packed;
+            for (int e = 0; e < 8; e++) packed |= code[e] << (4 * e);
+            *reinterpret_cast<uint32_t *>(region + Lay::kKCodes + 64 * off + 4 * r) = packed;
+        } else {
+            // keys: byte c of the token's 128 = code[c]
+            const uint32_t lo = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            const uint32_t hi = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+            *reinterpret_cast<uint2 *>(region + Lay::kKCodes + 128 * off + 8 * r) = make_uint2(lo, hi);
+        }
         if (r == 0)
-            *reinterpret_cast<uint32_t *>(region + kKMeta + 4 * off) = s16 | (z16 << 16);
+            *reinterpret_cast<uint32_t *>(region + Lay::kKMeta + 4 * off) = s16 | (z16 << 16);
+    } else if (VB == 4) {
+        // values: with channel 16j + m and j = 4h + k, the u16 word for
+        // (m, h) holds code(16j + m) << 4k, k = 0..3.  Lane r has channels
+        // 8r..8r+7: j = r/2 (h = r/8, k = (r/2) & 3) and m = 8(r&1) + e.  The
+        // 4 lanes that differ in bits 1 and 2 of r fill the same 8 words;
+        // a transpose-OR over lanes ^2, ^4 leaves each lane 2 whole words.
+        uint32_t v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) v8[e] = code[e] << (4 * ((r >> 1) & 3));
+        const bool b1 = (r & 2) != 0, b2 = (r & 4) != 0;
+        uint32_t v4[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t send = b1 ? v8[k] : v8[4 + k];
+            const uint32_t keep = b1 ? v8[4 + k] : v8[k];
+            v4[k] = keep | xor_lane_u(send, 2);
+        }
+        const int g = off >> 2, i = off & 3, h = r >> 3;
+        uint8_t *base = region + Lay::kVCodes + 256 * g + 8 * (i >> 1) + 4 * h + 2 * (i & 1);
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const uint32_t send = b2 ? v4[u] : v4[2 + u];
+            const uint32_t keep = b2 ? v4[2 + u] : v4[u];
+            const uint32_t word = keep | xor_lane_u(send, 4);
+            const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + u;
+            *reinterpret_cast<uint16_t *>(base + 16 * m) = (uint16_t)word;
+        }
+        if (r == 0)
+            *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     } else {
         // values: u16 word for m holds code(16j + m) << 2j, j = 0..7.  Lane r
         // has channels 8r..8r+7, i.e. j = r/2 and m = 8(r&1) + e.  Reduce the
@@ -180,10 +220,15 @@ __device__ __forceinline__ void encode_group(const uint16_t *src, int is_v, int 
         const uint32_t word = keep | xor_lane_u(send, 8);
         const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + (int)b3;
         const int g = off >> 2, i = off & 3;
-        *reinterpret_cast<uint16_t *>(region + kVCodes + 128 * g + 8 * m + 2 * i) = (uint16_t)word;
+        *reinterpret_cast<uint16_t *>(region + Lay::kVCodes + 128 * g + 8 * m + 2 * i) = (uint16_t)word;
         if (r == 0)
-            *reinterpret_cast<uint32_t *>(region + kVMeta + 4 * off) = s16 | (z16 << 16);
+            *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     }
+}
+
+// The K4V2 layout.
+__device__ __forceinline__ void encode_group(const uint16_t *src, int is_v, int r, uint8_t *region, int off) {
+    encode_group_fmt<4, 2>(src, is_v, r, region, off);
 }
 
 }  // namespace kvq

@@ -33,7 +33,8 @@ def test_format_and_sizes():
     assert lib.kvq_format_from_string(b"kvarn_k4v2_g128", ctypes.byref(f)) == 0
     assert (f.head_dim, f.group_size, f.k_bits, f.v_bits, f.block_size) == (128, 128, 4, 2, 16)
     assert lib.kvq_format_from_string(b"k4v2_g128", ctypes.byref(f)) == 0
-    assert lib.kvq_format_from_string(b"k8v4_g128", ctypes.byref(f)) == 3
+    assert lib.kvq_format_from_string(b"k3v2_g128", ctypes.byref(f)) == 3
+    assert lib.kvq_format_from_string(b"k4v2_g64", ctypes.byref(f)) == 3
     assert lib.kvq_format_from_string(None, ctypes.byref(f)) == 1
     assert kvq.page_bytes() == 1664 == 64 * 16 + 32 * 16 + 4 * 16 + 4 * 16
     # 104 bytes per token per KV head against 512 for fp16: 4.92x, inside the
@@ -41,9 +42,22 @@ def test_format_and_sizes():
     ratio = 512 / (1664 / 16)
     assert 3.0 <= ratio <= 5.0 and abs(ratio - 4.923) < 1e-3
     assert kvq.cache_bytes(10, 8) == 10 * 8 * 1664
-    bad = kvq.Format(128, 128, 8, 4, 16)
-    assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
-    assert lib.kvq_cache_bytes(ctypes.byref(bad), 10, 8) == 0
+    for bad in (kvq.Format(128, 128, 8, 8, 16), kvq.Format(128, 128, 2, 2, 16), kvq.Format(128, 64, 4, 2, 16),
+                kvq.Format(128, 128, 4, 2, 32)):
+        assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
+        assert lib.kvq_cache_bytes(ctypes.byref(bad), 10, 8) == 0
+
+
+@pytest.mark.parametrize("preset,kb,vb", [("k4v4_g128", 4, 4), ("kvarn_k4v4_g128", 4, 4), ("k8v2_g128", 8, 2),
+                                          ("k8v4_g128", 8, 4), ("kvarn_k8v4_g128", 8, 4)])
+def test_other_bit_width_presets(preset, kb, vb):
+    """Presets of the same pipeline at other widths: region = key codes (16 x
+    16 kb bytes) + value codes (16 x 16 vb) + two 16 x 4 metadata arrays."""
+    f = kvq.format_from_string(preset)
+    assert (f.head_dim, f.group_size, f.k_bits, f.v_bits, f.block_size) == (128, 128, kb, vb, 16)
+    assert kvq.page_bytes(f) == 16 * (16 * kb + 16 * vb + 8)
+    assert kvq.page_bytes(f) % 128 == 0
+    assert kvq.cache_bytes(3, 8, f) == 3 * 8 * kvq.page_bytes(f)
 
 
 def test_kv_memory_closed_form():
@@ -87,7 +101,7 @@ def test_append_validation_launches_nothing():
     good = P(0x10000)
     # null format / unsupported format
     assert lib.kvq_quantize_append(None, good, good, 1024, 1024, good, 4, 8, good, 10, None) == 1
-    bad = kvq.Format(128, 128, 8, 4, 16)
+    bad = kvq.Format(128, 128, 8, 8, 16)
     assert lib.kvq_quantize_append(ctypes.byref(bad), good, good, 1024, 1024, good, 4, 8, good, 10, None) == 3
     # zero tokens: no-op success
     assert lib.kvq_quantize_append(_fmt(), None, None, 1024, 1024, None, 0, 8, None, 10, None) == 0

@@ -50,8 +50,17 @@ def valid_byte_mask(n_tokens_in_page: int) -> np.ndarray:
     return m
 
 
-def gpu_append(k, v, slots, cache):
-    kvq.quantize_append(k, v, slots, cache)
+def gpu_append(k, v, slots, cache, fmt=None):
+    kvq.quantize_append(k, v, slots, cache, fmt=fmt)
+
+
+# bit widths (keys, values) of the quantised presets; (4, 2) is KVarN's
+PRESET_FMTS = [(4, 4), (8, 2), (8, 4)]
+
+
+def _kfmt(fmt):
+    """The library's format of (kbits, vbits), None for the default (4, 2)."""
+    return None if tuple(fmt) == (4, 2) else kvq.format_from_string(f"k{fmt[0]}v{fmt[1]}_g128")
 
 
 # --------------------------------------------------------------------------
@@ -160,8 +169,9 @@ def test_append_one_token_at_a_time_matches_bulk(dev):
 # Decode attention, small cases in full
 # --------------------------------------------------------------------------
 
-def _build_case(dev, B, Hq, Hkv, lens, seed, spare_pages=3):
+def _build_case(dev, B, Hq, Hkv, lens, seed, spare_pages=3, fmt=(4, 2)):
     rng = np.random.default_rng(seed)
+    region = oracle.region_bytes(fmt)
     lens = np.asarray(lens, np.int64)
     pages = [int(math.ceil(n / 16)) for n in lens]
     num_pages = sum(pages) + spare_pages
@@ -172,8 +182,8 @@ def _build_case(dev, B, Hq, Hkv, lens, seed, spare_pages=3):
     for b, p in enumerate(pages):
         bt[b, :p] = perm[o:o + p]
         o += p
-    cache = torch.full((num_pages, Hkv, 1664), 0xFF, dtype=torch.uint8, device=dev)  # NaN metadata in unused slots
-    pool = np.full((num_pages, Hkv, 1664), 0xFF, np.uint8)
+    cache = torch.full((num_pages, Hkv, region), 0xFF, dtype=torch.uint8, device=dev)  # NaN metadata in unused slots
+    pool = np.full((num_pages, Hkv, region), 0xFF, np.uint8)
     for b in range(B):
         n = int(lens[b])
         k = (rng.standard_normal((n, Hkv, D)) * rng.choice([0.5, 1, 2])).astype(np.float16)
@@ -181,8 +191,8 @@ def _build_case(dev, B, Hq, Hkv, lens, seed, spare_pages=3):
         k[:, :, rng.integers(0, D, 3)] *= 10
         slots = inp.slot_mapping(bt, b, 0, n)
         gpu_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
-                   torch.from_numpy(slots).to(dev), cache)
-        oracle.quantize_append(k, v, slots, pool)
+                   torch.from_numpy(slots).to(dev), cache, fmt=_kfmt(fmt))
+        oracle.quantize_append(k, v, slots, pool, fmt=fmt)
     q = (rng.standard_normal((B, Hq, D)) * rng.choice([0.5, 1, 3])).astype(np.float16)
     return cache, pool, bt, lens, q
 
@@ -286,13 +296,15 @@ FUSED = [
 ]
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,lens,pps", FUSED)
-def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps):
+@pytest.mark.parametrize("B,Hq,Hkv,lens,pps,fmt", [c + ((4, 2),) for c in FUSED] +
+                         [FUSED[2] + (f,) for f in PRESET_FMTS] + [FUSED[5] + (f,) for f in PRESET_FMTS])
+def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps, fmt):
     """kvq_append_decode_attention (and its partials + combine form) leaves the
     cache bytes and the output of kvq_quantize_append followed by
     kvq_decode_attention_ex, bit for bit, and both match the oracle."""
-    log(f"fused append+decode B={B} Hq={Hq} Hkv={Hkv} lens={lens} pps={pps}")
+    log(f"fused append+decode B={B} Hq={Hq} Hkv={Hkv} lens={lens} pps={pps} fmt={fmt}")
     rng = np.random.default_rng(B * 7919 + Hq + sum(lens) + pps)
+    region, kf = oracle.region_bytes(fmt), _kfmt(fmt)
     pages = [int(math.ceil(n / 16)) for n in lens]
     num_pages = sum(pages) + 2
     perm = rng.permutation(num_pages)
@@ -301,8 +313,8 @@ def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps):
     for b, p in enumerate(pages):
         bt[b, :p] = perm[o:o + p]
         o += p
-    cache = torch.full((num_pages, Hkv, 1664), 0xFF, dtype=torch.uint8, device=dev)
-    pool = np.full((num_pages, Hkv, 1664), 0xFF, np.uint8)
+    cache = torch.full((num_pages, Hkv, region), 0xFF, dtype=torch.uint8, device=dev)
+    pool = np.full((num_pages, Hkv, region), 0xFF, np.uint8)
     new_k = np.zeros((B, Hkv, D), np.float16)
     new_v = np.zeros((B, Hkv, D), np.float16)
     for b, n in enumerate(lens):
@@ -313,8 +325,8 @@ def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps):
         if n > 1:
             slots = inp.slot_mapping(bt, b, 0, n - 1)
             gpu_append(torch.from_numpy(k[:n - 1]).to(dev), torch.from_numpy(v[:n - 1]).to(dev),
-                       torch.from_numpy(slots).to(dev), cache)
-            oracle.quantize_append(k[:n - 1], v[:n - 1], slots, pool)
+                       torch.from_numpy(slots).to(dev), cache, fmt=kf)
+            oracle.quantize_append(k[:n - 1], v[:n - 1], slots, pool, fmt=fmt)
     q = (rng.standard_normal((B, Hq, D)) * 2).astype(np.float16)
     qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
     ld = torch.tensor(lens, dtype=torch.int32, device=dev)
@@ -323,23 +335,24 @@ def test_fused_append_decode_matches_two_calls(dev, B, Hq, Hkv, lens, pps):
     last_slots = np.array([bt[b, (n - 1) // 16] * 16 + (n - 1) % 16 for b, n in enumerate(lens)], np.int64)
     cache_b, cache_c = cache.clone(), cache.clone()
     # two calls
-    gpu_append(nkd, nvd, torch.from_numpy(last_slots).to(dev), cache)
-    out_a = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps).cpu()
+    gpu_append(nkd, nvd, torch.from_numpy(last_slots).to(dev), cache, fmt=kf)
+    out_a = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=kf).cpu()
     # fused, one call
-    out_b = kvq.append_decode_attention(nkd, nvd, qd, cache_b, btd, ld, L, pages_per_split=pps).cpu()
+    out_b = kvq.append_decode_attention(nkd, nvd, qd, cache_b, btd, ld, L, pages_per_split=pps, fmt=kf).cpu()
     assert torch.equal(cache.cpu(), cache_b.cpu()), "fused append changed other bytes or encoded differently"
     assert torch.equal(out_a, out_b)
     # fused split phase + combine, fp16 output
-    ws = kvq.alloc_workspace(B, Hq, Hkv, L, pps)
-    kvq.append_decode_partials(nkd, nvd, qd, cache_c, btd, ld, L, ws, pages_per_split=pps)
-    out_c = kvq.decode_combine(ws, ld, Hq, Hkv, L, out_dtype=torch.float16, pages_per_split=pps).cpu()
-    out_a16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, pages_per_split=pps).cpu()
+    ws = kvq.alloc_workspace(B, Hq, Hkv, L, pps, fmt=kf)
+    kvq.append_decode_partials(nkd, nvd, qd, cache_c, btd, ld, L, ws, pages_per_split=pps, fmt=kf)
+    out_c = kvq.decode_combine(ws, ld, Hq, Hkv, L, out_dtype=torch.float16, pages_per_split=pps, fmt=kf).cpu()
+    out_a16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, pages_per_split=pps,
+                                   fmt=kf).cpu()
     assert torch.equal(cache.cpu(), cache_c.cpu())
     assert torch.equal(out_a16, out_c)
     # the oracle
-    oracle.quantize_append(new_k, new_v, last_slots, pool)
+    oracle.quantize_append(new_k, new_v, last_slots, pool, fmt=fmt)
     assert np.array_equal(cache.cpu().numpy(), pool)
-    ref = oracle.decode_attention(pool, bt, np.asarray(lens), q, SCALE)
+    ref = oracle.decode_attention(pool, bt, np.asarray(lens), q, SCALE, fmt=fmt)
     assert np.max(np.abs(out_b.numpy() - ref)) <= TOL
 
 
@@ -756,3 +769,107 @@ def test_rotated_fp16_partials_alone(dev):
     assert np.max(np.abs(out - plain)) <= 1e-5
     assert np.max(np.abs(out - _f16_ref(kv, lens, q, Hq, Hkv))) <= TOL
 
+
+
+# --------------------------------------------------------------------------
+# Other bit widths: 4/8-bit keys, 2/4-bit values
+# --------------------------------------------------------------------------
+
+# 65600 (token, KV head) rows select the one-lane-per-group append kernel
+@pytest.mark.parametrize("fmt", PRESET_FMTS)
+@pytest.mark.parametrize("H,T,num_pages,seed", [(3, 200, 20, 12), (8, 8200, 600, 14)])
+def test_preset_append_bit_exact(dev, fmt, H, T, num_pages, seed):
+    rng = np.random.default_rng(300 + seed + 10 * fmt[0] + fmt[1])
+    log(f"preset append fmt={fmt} H={H} T={T}")
+    region = oracle.region_bytes(fmt)
+    k = _mixed_tokens(rng, T, H)
+    v = _mixed_tokens(rng, T, H)
+    slots = rng.permutation(num_pages * 16)[:T].astype(np.int64)
+    slots[rng.integers(0, T, 5)] = -1
+    slots[0] = num_pages * 16 + 3
+    cache = torch.full((num_pages, H, region), 0x3C, dtype=torch.uint8, device=dev)
+    gpu_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(slots).to(dev), cache,
+               fmt=_kfmt(fmt))
+    pool = np.full((num_pages, H, region), 0x3C, np.uint8)
+    ok = (slots >= 0) & (slots < num_pages * 16)
+    oracle.quantize_append(k[ok], v[ok], slots[ok], pool, fmt=fmt)
+    diff = np.argwhere(cache.cpu().numpy() != pool)
+    assert diff.size == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
+
+
+PRESET_SMALL = [
+    (1, 1, 1, [1]),
+    (2, 4, 1, [17, 33]),
+    (3, 8, 1, [100, 1, 257]),
+    (1, 32, 2, [700]),
+    (4, 12, 4, [64, 65, 127, 300]),
+    (2, 64, 8, [513, 77]),
+]
+
+
+@pytest.mark.parametrize("fmt", PRESET_FMTS)
+@pytest.mark.parametrize("B,Hq,Hkv,lens", PRESET_SMALL)
+def test_preset_decode_small_matches_oracle(dev, fmt, B, Hq, Hkv, lens):
+    log(f"preset decode fmt={fmt} B={B} Hq={Hq} Hkv={Hkv} lens={lens}")
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=B * 1000 + Hq + sum(lens) + fmt[0],
+                                              fmt=fmt)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention(pool, bt, lens_np, q, SCALE, fmt=fmt)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (0, 2, 6):
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=_kfmt(fmt))
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+    out16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, fmt=_kfmt(fmt))
+    assert np.max(np.abs(out16.float().cpu().numpy() - ref)) <= TOL
+
+
+@pytest.mark.parametrize("fmt", PRESET_FMTS)
+def test_preset_workload_qwen3_32b_16k_sampled(dev, fmt):
+    """Qwen3-32B shape (8 x 16384 cached tokens + 1 appended, 64 q / 8 KV
+    heads) in the benchmark's launch configuration: bulk fill, then the fused
+    append + decode step; 2 sequences x 2 KV heads checked against the oracle
+    (codes of all 16385 tokens, attention of the 8 query heads)."""
+    w = inp.workload("qwen3_32b_16k")
+    kf = _kfmt(fmt)
+    region = oracle.region_bytes(fmt)
+    log(f"preset qwen3_32b_16k fmt={fmt}: fill")
+    bt, num_pages = inp.page_table(w)
+    ctx = w.context
+    cache = torch.zeros((num_pages, w.num_kv_heads, region), dtype=torch.uint8, device=dev)
+    keep = (2, 7)
+    kept = {}
+    new_k, new_v = [], []
+    for b in range(w.num_seqs):
+        k, v = inp.sequence_kv(w, b, 0, ctx + 1, device=dev)
+        gpu_append(k[:ctx], v[:ctx], torch.from_numpy(inp.slot_mapping(bt, b, 0, ctx)).to(dev), cache, fmt=kf)
+        new_k.append(k[ctx:])
+        new_v.append(v[ctx:])
+        if b in keep:
+            kept[b] = (k.cpu().numpy(), v.cpu().numpy())
+        del k, v
+    nk, nv = torch.cat(new_k).contiguous(), torch.cat(new_v).contiguous()
+    q = inp.queries(w)
+    lens = torch.full((w.num_seqs,), ctx + 1, dtype=torch.int32, device=dev)
+    log(f"preset qwen3_32b_16k fmt={fmt}: fused append + decode")
+    out = kvq.append_decode_attention(nk, nv, q.to(dev), cache, torch.from_numpy(bt).to(dev), lens, ctx + 1,
+                                      out_dtype=torch.float16, fmt=kf).float().cpu().numpy()
+    n = ctx + 1
+    pages = int(math.ceil(n / 16))
+    for b in keep:
+        k_seq, v_seq = kept[b]
+        for kvh in (1, 6):
+            pool = np.zeros((pages, 1, region), np.uint8)
+            oracle.quantize_append(k_seq[:, kvh:kvh + 1], v_seq[:, kvh:kvh + 1], np.arange(n, dtype=np.int64), pool,
+                                   fmt=fmt)
+            ids = torch.from_numpy(bt[b, :pages].astype(np.int64)).to(dev)
+            got = cache[ids, kvh].cpu().numpy()
+            assert np.array_equal(got, pool[:, 0]), f"codes differ: seq {b} head {kvh}"
+            qh = q.numpy()[b, kvh * w.gqa:(kvh + 1) * w.gqa][None]
+            ref = oracle.decode_attention(pool, np.arange(pages, dtype=np.int32)[None], np.array([n]), qh, SCALE,
+                                          fmt=fmt)[0]
+            err = np.max(np.abs(out[b, kvh * w.gqa:(kvh + 1) * w.gqa] - ref))
+            log(f"  seq {b} kv {kvh}: err {err:.2e}")
+            assert err <= TOL
