@@ -68,6 +68,8 @@ def parse():
                     help="skip the uncompressed fp16 cache decode on the same workload")
     ap.add_argument("--no-mixed-window", action="store_true",
                     help="skip the fp16 sink + recent window beside the K4V2 history")
+    ap.add_argument("--no-presets", action="store_true",
+                    help="skip the k4v4 / k8v2 / k8v4 presets on the same workload")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
@@ -367,6 +369,10 @@ def main():
     if not args.no_mixed_window:
         result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
 
+    if not args.no_presets:
+        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p)
+                             for p in ("k4v4_g128", "k8v2_g128", "k8v4_g128")]
+
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
 
@@ -430,6 +436,67 @@ def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
             "kernel_GBps": round(fp16_bytes / (kern * 1e-3) / 1e9, 2),
             "kernel_pct_hbm_peak": round(100 * fp16_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "k4v2_step_speedup": round(ms / k4v2_ms_per_step, 3)}
+
+
+def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset):
+    """The benchmark step (fused append + decode split kernel, then the
+    combine) on the same workload with another preset's bit widths; the split
+    kernel alone is then timed back to back between two events."""
+    w = inp.workload("qwen3_32b_16k")
+    B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    ctx, n = w.context, w.context + 1
+    fmt = kvq.format_from_string(preset)
+    region = kvq.page_bytes(fmt)
+    bt_np, num_pages = inp.page_table(w)
+    bt = torch.from_numpy(bt_np).to(dev)
+    lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    base = torch.zeros((num_pages, Hkv, region), dtype=torch.uint8, device=dev)
+    nk, nv = [], []
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, 0, n, device=dev)
+        kvq.quantize_append(k[:ctx], v[:ctx], torch.from_numpy(inp.slot_mapping(bt_np, b, 0, ctx)).to(dev), base,
+                            fmt=fmt)
+        nk.append(k[ctx:])
+        nv.append(v[ctx:])
+        del k, v
+    nk, nv = torch.cat(nk).contiguous(), torch.cat(nv).contiguous()
+    pools = [base] + [base.clone() for _ in range(2)]     # >= 3 x 139 MB: beyond the 256 MB cache
+    q = inp.queries(w, 0, device=dev).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    ws = kvq.alloc_workspace(B, Hq, Hkv, n, fmt=fmt)
+    call = DecodeCall(kvq, lib, fmt, stream.cuda_stream)
+    part = [call.fused_args(nk, nv, q, p, bt, lens, n, ws, 0) for p in pools]
+    comb = call.combine_args(out, lens, Hq, Hkv, n, ws, 0)
+    pf, cfn = lib.kvq_append_decode_partials, lib.kvq_decode_combine
+    steps = max(20, args.steps // 2)
+    for i in range(5):
+        pf(*part[i % 3]); cfn(*comb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if pf(*part[i % 3]) | cfn(*comb):
+            raise RuntimeError(f"{preset} decode call failed")
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    hev = HipEvents(2)
+    nl = max(1, args.kernel_launches // 2)
+    hev.record(0, stream.cuda_stream)
+    bad = 0
+    for i in range(nl):
+        bad |= pf(*part[i % 3])
+    hev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError(f"{preset} decode call failed")
+    kern = hev.elapsed_ms(0, 1) / nl
+    hev.close()
+    per_token_head = 16 * (fmt.k_bits + fmt.v_bits) + 8
+    kv_bytes = B * n * Hkv * per_token_head
+    del pools, base
+    return {"preset": preset, "bytes_per_token_head": per_token_head, "ms_per_step": round(ms, 5),
+            "step_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "split_kernel_ms": round(kern, 5),
+            "kernel_GBps": round(kv_bytes / (kern * 1e-3) / 1e9, 2),
+            "kernel_pct_hbm_peak": round(100 * kv_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
 
 
 def mixed_window(torch, inp, kvq, lib, dev, stream, args, sink=4, recent=124):

@@ -1,6 +1,7 @@
 /*
- * kvq.h -- C ABI of libkvq: K4V2 group-128 quantised paged KV cache for
- * AMD Instinct MI355X (gfx950).
+ * kvq.h -- C ABI of libkvq: K4V2 group-128 quantised paged KV cache (and the
+ * same pipeline at 8-bit keys / 4-bit values) for AMD Instinct MI355X
+ * (gfx950).
  *
  * Two operations on a paged KV cache:
  *   kvq_quantize_append   quantise-on-write of new key/value tokens
@@ -18,6 +19,9 @@
  *              accuracy" -- the four-stage pipeline list (Hadamard rotation;
  *              variance normalisation; asymmetric round-to-nearest; scale
  *              folding on read-back) and the preset kv_cache_dtype string.
+ *   [TQ]       dzen.ru summary of the vLLM TurboQuant post -- sections on
+ *              accuracy and on memory (8-bit keys with 4-bit values, and 4-bit
+ *              both, nearly lossless; 3-bit noticeably worse).
  *   [KV-INFRA] encorp.ai, "KV cache compression is an infrastructure decision,
  *              not a model debate" -- decode bound by HBM traffic; the section
  *              on OSCAR (sink and recent tokens kept in BF16).
@@ -46,6 +50,24 @@
  *       [1536, 1600)  key (s, z) fp16 pairs, token o at 1536 + 4*o
  *       [1600, 1664)  value (s, mu) fp16 pairs, token o at 1600 + 4*o
  *     104 bytes per token per KV head (fp16: 512 bytes).
+ *
+ * Other bit widths (k_bits in {4, 8}, v_bits in {2, 4}; presets "k4v4_g128",
+ * "k8v2_g128", "k8v4_g128", also with the "kvarn_" prefix): the same pipeline
+ * with L = 2^bits - 1, at the widths whose accuracy the pages compare (8-bit
+ * keys with 4-bit values and 4-bit both reported as nearly lossless:
+ * [TQ] dzen.ru summary of the vLLM TurboQuant post, sections on accuracy and
+ * memory).  Values still store the group mean.  Region of
+ * 256 * (k_bits + v_bits) + 128 bytes (2176, 2688, 3200), in this order:
+ *       key codes     16 tokens x 16*k_bits bytes, token-major; the code of
+ *                     channel c at bits k_bits*c.. of the token's row, least
+ *                     significant first (8 bits: byte c)
+ *       value codes   16 tokens x 16*v_bits bytes at 256*k_bits; 2 bits: as
+ *                     above (u16 at base + 128g + 8m + 2i); 4 bits: with
+ *                     j = 4h + k, the u16 at base + 256g + 16m + 8(i/2) + 4h +
+ *                     2(i%2) holds the code of channel 16j + m in bits
+ *                     4k..4k+3
+ *       key (s, z)    16 x 4 bytes at 256*(k_bits + v_bits)
+ *       value (s, mu) 16 x 4 bytes after them
  *
  * Baseline format "fp16" (k_bits = v_bits = 16): the uncompressed cache the
  * K4V2 format is measured against (the pages compare KVarN with fp16 on
@@ -98,7 +120,8 @@ typedef enum kvq_status {
     KVQ_ERR_HIP = 6           /* the HIP runtime reported an error             */
 } kvq_status;
 
-/* Format descriptor: {128, 128, 4, 2, 16} (K4V2 v1) or {128, 128, 16, 16, 16}
+/* Format descriptor: {128, 128, k_bits, v_bits, 16} with k_bits in {4, 8} and
+ * v_bits in {2, 4} ({128, 128, 4, 2, 16} is K4V2 v1), or {128, 128, 16, 16, 16}
  * (the fp16 baseline). */
 typedef struct kvq_format {
     int32_t head_dim;    /* channels per head                    */
@@ -111,13 +134,15 @@ typedef struct kvq_format {
 typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
 
 /* Parse a preset name ([KVARN-HN] flag value; [KVARN-P] kv_cache_dtype string).
- * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16}) and the
+ * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16}); "k4v4_g128",
+ * "k8v2_g128", "k8v4_g128" (with or without the "kvarn_" prefix); and the
  * baseline "fp16" ({128, 128, 16, 16, 16}).  preset, out: (host).
  * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
 
-/* Bytes of one (page, KV head) region: 1664 for K4V2 v1, 8192 for fp16; 0 for
- * an unsupported format or NULL. */
+/* Bytes of one (page, KV head) region: 256 * (k_bits + v_bits) + 128 for a
+ * quantised format (1664 for K4V2 v1), 8192 for fp16; 0 for an unsupported
+ * format or NULL. */
 size_t kvq_page_bytes(const kvq_format *fmt);
 
 /* Bytes of a pool of num_pages pages and num_kv_heads heads; 0 on invalid input. */
@@ -131,8 +156,9 @@ size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_
  *   slot_mapping      (device) int64 [num_tokens]; slot = page*16 + offset.
  *                     A negative slot skips the token; a slot whose page is
  *                     >= num_pages is skipped.  Slots must be distinct.
- *   cache             (device) u8 pool [num_pages][num_kv_heads][1664],
- *                     16-byte aligned.  Only the addressed token slots change.
+ *   cache             (device) u8 pool [num_pages][num_kv_heads][page bytes]
+ *                     (kvq_page_bytes(fmt): 1664 for K4V2), 16-byte aligned.
+ *                     Only the addressed token slots change.
  * The codes depend only on the token's own 128 values (no calibration), so
  * appends are order-independent and idempotent.
  * num_tokens == 0 is a no-op returning KVQ_OK.
@@ -299,16 +325,18 @@ kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new
  * i goes to slot slot_offset + i of rows holding total_slots slots each: the
  * workspace holds fp32 [num_seqs][num_q_heads][total_slots][132], at least
  * num_seqs * num_q_heads * total_slots * 528 bytes, 16-byte aligned.
- * rotated = 1 stores the partial in the K4V2 Hadamard domain (acc' = H acc,
- * zacc = acc_0), as K4V2 partials always are (0 is rejected for K4V2); set it
- * for an fp16 cache whose partials are merged with K4V2 ones.  slot_offset +
- * the call's split count must not exceed total_slots (else KVQ_ERR_SHAPE).
+ * rotated = 1 stores the partial in the Hadamard domain of the quantised
+ * caches (acc' = H acc, zacc = acc_0), as their partials always are (0 is
+ * rejected for them); set it for an fp16 cache whose partials are merged with
+ * quantised-cache ones.  slot_offset + the call's split count must not exceed
+ * total_slots (else KVQ_ERR_SHAPE).  Caches of different quantised widths
+ * may also share one workspace row.
  *
  * kvq_decode_combine_slots: merges all total_slots slots of every (sequence,
  * query head) row and writes out (fp16 or fp32 [num_seqs][num_q_heads][128]).
- * rotated = 1 applies the K4V2 epilogue (any mix holding K4V2 partials or
- * rotated fp16 ones), 0 the plain one (unrotated fp16 partials only).  Every
- * slot must have been written by a partials call for this step.
+ * rotated = 1 applies the quantised-cache epilogue (any mix holding their
+ * partials or rotated fp16 ones), 0 the plain one (unrotated fp16 partials
+ * only).  Every slot must have been written by a partials call for this step.
  */
 int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,
                                int32_t num_kv_heads, int32_t max_seq_len, int32_t pages_per_split);

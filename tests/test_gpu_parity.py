@@ -873,3 +873,37 @@ def test_preset_workload_qwen3_32b_16k_sampled(dev, fmt):
             err = np.max(np.abs(out[b, kvh * w.gqa:(kvh + 1) * w.gqa] - ref))
             log(f"  seq {b} kv {kvh}: err {err:.2e}")
             assert err <= TOL
+
+
+def test_mixed_widths_recent_k8v4_history_k4v2(dev):
+    """Two quantised caches of different widths in one step (older tokens in
+    K4V2, the recent ones in k8v4): their partials share one workspace row
+    and one combine, and equal the oracle's attention over the union."""
+    B, Hq, Hkv = 3, 16, 2
+    G = Hq // Hkv
+    hist, recent = [700, 1, 130], [64, 17, 1]
+    log(f"mixed widths hist={hist} recent={recent}")
+    cache_h, pool_h, bt_h, _, q = _build_case(dev, B, Hq, Hkv, hist, seed=77)
+    cache_r, pool_r, bt_r, _, _ = _build_case(dev, B, Hq, Hkv, recent, seed=78, fmt=(8, 4))
+    f84 = _kfmt((8, 4))
+    qd = torch.from_numpy(q).to(dev)
+    Lh, Lr = max(hist), max(recent)
+    s_h = kvq.decode_split_slots(B, Hq, Hkv, Lh, pages_per_split=4)
+    s_r = kvq.decode_split_slots(B, Hq, Hkv, Lr, fmt=f84)
+    total = s_h + s_r
+    ws = torch.full((kvq.slots_workspace_bytes(B, Hq, total),), 0xFF, dtype=torch.uint8, device=dev)
+    kvq.decode_partials_slots(qd, cache_r, torch.from_numpy(bt_r).to(dev),
+                              torch.tensor(recent, dtype=torch.int32, device=dev), Lr, ws, 0, total, fmt=f84)
+    kvq.decode_partials_slots(qd, cache_h, torch.from_numpy(bt_h).to(dev),
+                              torch.tensor(hist, dtype=torch.int32, device=dev), Lh, ws, s_r, total,
+                              pages_per_split=4)
+    out = kvq.decode_combine_slots(ws, B, Hq, total).cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            kv = [oracle.dequant_slot(pool_h[bt_h[b, t // 16], h], t % 16) for t in range(hist[b])]
+            kv += [oracle.dequant_slot(pool_r[bt_r[b, t // 16], h], t % 16, fmt=(8, 4)) for t in range(recent[b])]
+            k_all = np.stack([x[0] for x in kv])
+            v_all = np.stack([x[1] for x in kv])
+            ref = oracle.attention_f64(k_all, v_all, q[b, h * G:(h + 1) * G], SCALE)
+            err = np.max(np.abs(out[b, h * G:(h + 1) * G] - ref))
+            assert err <= TOL, f"b={b} h={h} err={err}"
