@@ -17,6 +17,8 @@ Functions and the passages they follow (pages cited by title and section):
   its plain definition (softmax(scale q.k) v), fp64.
 * ``decode_attention_folded`` -- the same result reached by scale folding on
   read-back (same pipeline list, stage 4), fp64; pins the algebra.
+* ``decode_attention_mq`` -- several causal query rows per sequence (the
+  multi-token decode of speculative drafts and prefill chunks), fp64.
 * ``fmt=(kbits, vbits)`` -- the same pipeline at the other bit widths the pages
   report (8-bit keys with 4-bit values, 4-bit both: dzen.ru summary of the
   vLLM TurboQuant post, sections on accuracy and memory); keys 4 or 8 bits,
@@ -104,6 +106,9 @@ def _load():
     lib.kvqo_decode_attention_folded_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
                                                      ctypes.c_double, P]
     lib.kvqo_decode_attention_folded_fmt.restype = ctypes.c_int
+    lib.kvqo_decode_attention_mq_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
+                                                 ctypes.c_double, P]
+    lib.kvqo_decode_attention_mq_fmt.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -242,6 +247,25 @@ def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=N
                                            None if hm is None else _ptr(hm), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode: invalid shape or page id")
+    return out
+
+
+def decode_attention_mq(pool, block_tables, seq_lens, query_f16, scale, fmt=K4V2):
+    """Several query rows per sequence, causal: query float16 [B][M][Hq][128];
+    row m of sequence b attends to tokens 0 .. seq_lens[b] - M + m.  Returns
+    float64 [B][M][Hq][128]."""
+    pool = _c(pool, np.uint8)
+    assert pool.shape[2] == region_bytes(fmt)
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    q = _c(query_f16, np.float16)
+    B, M, Hq, d = q.shape
+    out = np.empty((B, M, Hq, D), np.float64)
+    rc = _load().kvqo_decode_attention_mq_fmt(int(fmt[0]), int(fmt[1]), _ptr(pool), pool.shape[0], pool.shape[1],
+                                              _ptr(bt), bt.shape[1], _ptr(sl), B, M, Hq, _ptr(q), float(scale),
+                                              _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle multi-query decode: invalid shape or page id")
     return out
 
 

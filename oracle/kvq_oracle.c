@@ -63,6 +63,9 @@ int64_t kvqo_region_bytes(int kbits, int vbits)
     return fmt_ok(kbits, vbits) ? 256 * (kbits + vbits) + 128 : -1;
 }
 
+void kvqo_attention_f64(const double *k, const double *v, int64_t n, const uint16_t *q, int32_t G,
+                        double scale, double *out);
+
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32/64, written from the format definition.        */
 /* ------------------------------------------------------------------------ */
@@ -549,6 +552,54 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
 {
     return kvqo_decode_attention_fmt(4, 2, pool, num_pages, num_kv_heads, block_tables, max_pages_per_seq,
                                      seq_lens, num_seqs, num_q_heads, query, scale, head_mask, out);
+}
+
+/*
+ * Several query rows per sequence (the tokens of a speculative-decoding draft
+ * or a prefill chunk): q_len rows, the last q_len tokens of the sequence, all
+ * already in the cache.  Row m of sequence b sits at position n - q_len + m
+ * (n = seq_lens[b]) and attends causally, to tokens 0 .. n - q_len + m:
+ *     out[b][m][hq] = sum_{t <= n - q_len + m} softmax(scale * q.k_t) v_t
+ * with k_t, v_t as in kvqo_decode_attention_fmt, in fp64.  query, out:
+ * [num_seqs][q_len][num_q_heads][128] (fp16 in, fp64 out).  A row that sees
+ * no token (n - q_len + m < 0) is zero.  Returns 0, or -1 on an invalid shape
+ * or page id.
+ */
+int kvqo_decode_attention_mq_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
+                                 int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                                 const uint16_t *query, double scale, double *out)
+{
+    if (!fmt_ok(kbits, vbits) || q_len <= 0) return -1;
+    const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+    const int G = num_q_heads / num_kv_heads;
+    for (int b = 0; b < num_seqs; b++) {
+        const int64_t n = seq_lens[b];
+        if (n < 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        for (int kvh = 0; kvh < num_kv_heads; kvh++) {
+            double *K = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
+            double *V = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
+            if (!K || !V) { free(K); free(V); return -1; }
+            for (int64_t t = 0; t < n; t++) {
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                if (page < 0 || page >= num_pages) { free(K); free(V); return -1; }
+                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
+                kvqo_dequant_slot_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+            }
+            for (int m = 0; m < q_len; m++) {
+                const int64_t visible = n - q_len + m + 1;        /* tokens 0 .. n - q_len + m */
+                for (int g = 0; g < G; g++) {
+                    const int hq = kvh * G + g;
+                    const int64_t row = ((int64_t)b * q_len + m) * num_q_heads + hq;
+                    kvqo_attention_f64(K, V, visible > 0 ? visible : 0, query + row * KVQO_D, 1, scale,
+                                       out + row * KVQO_D);
+                }
+            }
+            free(K); free(V);
+        }
+    }
+    return 0;
 }
 
 /*

@@ -149,10 +149,16 @@ def test_hand_derived_example():
 
 
 def _on_grid(rng, L, delta=2.0 ** -4, zero=-0.5):
+    """fp16 group whose rotation lies exactly on an L-level grid.  Groups whose
+    exact mean zero + delta * sum(c) / 128 is 0 are redrawn: the value mean is
+    evaluated in fp32 from rounded normalised operands, and fp16 keeps the
+    ~2^-24 residual of that cancellation as a subnormal (see
+    test_value_mean_cancellation_stays_tiny), so such a group is not stored
+    exactly."""
     c = rng.integers(0, L + 1, D)
     c[rng.integers(D)] = 0
     c[rng.integers(D)] = L
-    while c.min() != 0 or c.max() != L:
+    while c.min() != 0 or c.max() != L or zero + delta * c.sum() / 128 == 0:
         c = rng.integers(0, L + 1, D)
     y = zero + delta * c                               # rotated-domain values, on the grid
     x = (H @ y) / 128.0                                # H^-1 = H / 128
@@ -748,3 +754,72 @@ def test_attention_folded_equals_plain_presets(fmt):
     a = oracle.decode_attention(pool, bt, lens, q, scale, fmt=fmt)
     b = oracle.decode_attention_folded(pool, bt, lens, q, scale, fmt=fmt)
     assert np.max(np.abs(a - b)) < 1e-9
+
+
+# --------------------------------------------------------------------------
+# Several query rows per sequence (causal)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [(4, 2), (8, 4)])
+def test_attention_mq_on_grid_equals_causal_sdpa(fmt):
+    """On-grid K/V survive quantisation exactly, so the multi-row decode must
+    equal torch SDPA (fp64) with a causal mask aligned to the sequence end,
+    over the original tensors."""
+    M = 5
+    pool, bt, lens, _, ks, vs = _small_case_fmt(fmt, on_grid=True, seed=21, lens=(37, 70))
+    rng = np.random.default_rng(22)
+    B, Hkv = len(lens), pool.shape[1]
+    Hq = 4
+    G = Hq // Hkv
+    q = rng.standard_normal((B, M, Hq, D)).astype(np.float16)
+    scale = 1 / np.sqrt(D)
+    out = oracle.decode_attention_mq(pool, bt, lens, q, scale, fmt=fmt)
+    for b in range(B):
+        n = int(lens[b])
+        K = torch.from_numpy(ks[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+        V = torch.from_numpy(vs[b].astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+        Q = torch.from_numpy(q[b].astype(np.float64)).permute(1, 0, 2).contiguous()      # [Hq][M][D]
+        mask = torch.arange(n)[None, :] <= (n - M + torch.arange(M))[:, None]            # [M][n]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+        assert np.max(np.abs(out[b] - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
+def test_attention_mq_rows_are_truncated_single_decodes():
+    pool, bt, lens, _, _, _ = _small_case(num_seqs=3, seed=23, lens=(20, 33, 1))
+    rng = np.random.default_rng(24)
+    M, Hq = 3, 4
+    q = rng.standard_normal((3, M, Hq, D)).astype(np.float16)
+    scale = 1 / np.sqrt(D)
+    out = oracle.decode_attention_mq(pool, bt, lens, q, scale)
+    for m in range(M):
+        trunc = np.maximum(lens - M + m + 1, 0)
+        ref = oracle.decode_attention(pool, bt, trunc, q[:, m], scale)
+        for b in range(3):
+            if trunc[b] == 0:
+                assert not out[b, m].any()            # a row that sees no token is zero
+            else:
+                assert np.max(np.abs(out[b, m] - ref[b])) < 1e-13
+    one = oracle.decode_attention_mq(pool, bt, lens, q[:, :1], scale)
+    assert np.max(np.abs(one[:, 0] - oracle.decode_attention(pool, bt, lens, q[:, 0], scale))) < 1e-13
+
+
+def test_value_mean_cancellation_stays_tiny():
+    """An on-grid value group whose exact mean is 0: the fp32 mean comes out
+    within a few units of 2^-24 (the cancellation residual, kept by fp16 as a
+    subnormal), far inside the quantiser's error bound s/2."""
+    rng = np.random.default_rng(90)
+    hits = 0
+    while hits < 20:
+        c = rng.integers(0, 16, D)
+        c[0], c[1] = 0, 15
+        c[2] += 1024 - c.sum()
+        if not (0 <= c[2] <= 15):
+            continue
+        y = -0.5 + 2.0 ** -4 * c
+        x16 = ((H @ y) / 128.0).astype(np.float16)
+        if not np.array_equal(x16.astype(np.float64), (H @ y) / 128.0):
+            continue
+        codes, s, mu = oracle.quantize_group(x16, 4, offset_mode=1)
+        assert np.array_equal(codes, c) and oracle.half_to_double(s) == 2.0 ** -4
+        assert abs(oracle.half_to_double(mu)) <= 4 * 2.0 ** -24
+        hits += 1
