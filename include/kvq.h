@@ -309,6 +309,36 @@ kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new
                                       void *stream);
 
 /*
+ * Several query rows per sequence: the q_len newest tokens of every sequence
+ * (a speculative-decoding draft being verified, or a chunk of a prefill),
+ * already appended to the cache, attend at once.  Row m of sequence b sits at
+ * position seq_lens[b] - q_len + m and attends causally to tokens
+ * 0 .. seq_lens[b] - q_len + m (a row that sees no token is zero).  The page
+ * stream is read once for all rows: each (row, head) pair takes a column of
+ * the decode kernel's MFMA tiles, so q_len * G columns per KV head fill the
+ * tiles that a small GQA group leaves empty.
+ *   query      (device) fp16 [num_seqs][q_len][num_q_heads][128], contiguous
+ *   out        (device) fp16|fp32 [num_seqs][q_len][num_q_heads][128]
+ *   q_len      1 .. 16; q_len * num_q_heads <= 65535
+ *   workspace  kvq_decode_workspace_bytes_mq(...) bytes (the workspace of a
+ *              decode with q_len * num_q_heads query heads)
+ * Quantised formats only for q_len > 1 (fp16: KVQ_ERR_UNSUPPORTED).  Other
+ * arguments, checks and ownership as kvq_decode_attention_ex; q_len = 1 is
+ * that call.  Precondition: seq_lens[b] >= q_len.
+ */
+size_t kvq_decode_workspace_bytes_mq(const kvq_format *fmt, int32_t num_seqs, int32_t q_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                                     int32_t pages_per_split);
+
+kvq_status kvq_decode_attention_mq(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                   const uint16_t *query, int32_t q_len, const uint8_t *cache, int64_t num_pages,
+                                   const int32_t *block_tables, int32_t max_pages_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                   void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                   void *stream);
+
+/*
  * Mixed caches: the partials of several caches merged by one combine.  A
  * decode step may read its tokens from more than one cache -- e.g. the first
  * (sink) and the most recent tokens kept uncompressed in an fp16 cache beside

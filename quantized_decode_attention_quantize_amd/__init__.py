@@ -88,6 +88,9 @@ def load():
                                                        P, i32, i32, i32, i32, ctypes.c_float, P, sz, i32, P]),
         "kvq_append_decode_partials": (ctypes.c_int, [FP, P, P, i64, i64, P, P, i64, P, i32, P, i32, i32, i32,
                                                       i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_decode_workspace_bytes_mq": (sz, [FP, i32, i32, i32, i32, i32, i32]),
+        "kvq_decode_attention_mq": (ctypes.c_int, [FP, P, ctypes.c_int, P, i32, P, i64, P, i32, P, i32, i32,
+                                                   i32, i32, ctypes.c_float, P, sz, i32, P]),
         "kvq_set_split_kernel_events": (ctypes.c_int, [P, P]),
         "kvq_decode_split_slots": (i32, [FP, i32, i32, i32, i32, i32]),
         "kvq_decode_partials_slots": (ctypes.c_int, [FP, P, P, i64, P, i32, P, i32, i32, i32, i32,
@@ -247,6 +250,46 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
         _ptr(seq_lens), B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
         workspace.numel(), int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def decode_workspace_bytes_mq(num_seqs: int, q_len: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                              pages_per_split: int = 0, fmt: Format | None = None) -> int:
+    n = load().kvq_decode_workspace_bytes_mq(ctypes.byref(_fmt(fmt)), num_seqs, q_len, num_q_heads,
+                                             num_kv_heads, max_seq_len, pages_per_split)
+    if n == 0:
+        raise KvqError(2, "kvq_decode_workspace_bytes_mq")
+    return int(n)
+
+
+def decode_attention_mq(query: torch.Tensor, cache: torch.Tensor, block_tables: torch.Tensor,
+                        seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float | None = None,
+                        out: torch.Tensor | None = None, out_dtype=torch.float32,
+                        workspace: torch.Tensor | None = None, pages_per_split: int = 0,
+                        stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """Several causal query rows per sequence: query fp16 [B][M][Hq][128]
+    (the sequence's last M positions); returns out [B][M][Hq][128]."""
+    if query.dtype != torch.float16 or query.dim() != 4 or query.shape[3] != HEAD_DIM or not query.is_contiguous():
+        raise ValueError("query must be contiguous float16 [B][M][Hq][128]")
+    B, M, Hq, _ = query.shape
+    _decode_checks(query.view(B, M * Hq, HEAD_DIM), cache, block_tables, seq_lens, fmt)
+    Hkv = cache.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, M, Hq, HEAD_DIM), dtype=out_dtype, device=query.device)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or \
+            tuple(out.shape) != (B, M, Hq, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][M][Hq][128]")
+    if workspace is None:
+        n = decode_workspace_bytes_mq(B, M, Hq, Hkv, max_seq_len, pages_per_split, fmt)
+        workspace = torch.empty(n, dtype=torch.uint8, device=query.device)
+    st = load().kvq_decode_attention_mq(
+        ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
+        _ptr(query), M, _ptr(cache), cache.shape[0], _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_decode_attention_mq")
     return out
 
 

@@ -111,6 +111,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
     if (w.splits > 65535) return KVQ_ERR_SHAPE;
     memset(&a, 0, sizeof(a));
+    a.q_len = 1;
     a.rotated = fp16 ? 0 : 1;
     a.k_bits = fmt->k_bits;
     a.v_bits = fmt->v_bits;
@@ -406,6 +407,40 @@ kvq_status kvq_decode_combine(const kvq_format *fmt, void *out, kvq_out_dtype ou
     if (st != KVQ_OK) return st;
     a.partials_only = 1;
     return hip_status(kvq::launch_decode_combine(a, (hipStream_t)stream));
+}
+
+size_t kvq_decode_workspace_bytes_mq(const kvq_format *fmt, int32_t num_seqs, int32_t q_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                                     int32_t pages_per_split) {
+    if (q_len < 1 || q_len > 16 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    if ((int64_t)num_q_heads * q_len > 65535) return 0;
+    return kvq_decode_workspace_bytes(fmt, num_seqs, num_q_heads * q_len, num_kv_heads, max_seq_len,
+                                      pages_per_split);
+}
+
+kvq_status kvq_decode_attention_mq(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                   const uint16_t *query, int32_t q_len, const uint8_t *cache, int64_t num_pages,
+                                   const int32_t *block_tables, int32_t max_pages_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                   void *workspace, size_t workspace_bytes, int32_t pages_per_split,
+                                   void *stream) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_known(fmt)) return KVQ_ERR_UNSUPPORTED;
+    if (q_len < 1 || q_len > 16 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        (int64_t)num_q_heads * q_len > 65535)
+        return KVQ_ERR_SHAPE;
+    if (q_len > 1 && !is_quant(fmt)) return KVQ_ERR_UNSUPPORTED;   // the fp16 baseline decodes one row
+    // (row, head) pairs take the place of query heads: q_len * num_q_heads of them
+    kvq::DecodeArgs a;
+    kvq_status st = decode_common(fmt, seq_lens, num_seqs, q_len * num_q_heads, num_kv_heads, max_seq_len,
+                                  max_pages_per_seq, workspace, workspace_bytes, pages_per_split, a);
+    if (st == KVQ_OK) st = decode_output(out, out_dtype, a);
+    if (st == KVQ_OK) st = decode_inputs(query, cache, num_pages, block_tables, max_pages_per_seq, softmax_scale, a);
+    if (st != KVQ_OK) return st;
+    a.q_len = q_len;
+    return hip_status(launch_both(a, (hipStream_t)stream));
 }
 
 kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,

@@ -210,10 +210,12 @@ struct LaneConsts {
     float res_k;           // 0 (lanes n < 8: weight) or -1 (lanes n >= 8: residual)
 };
 
-// One page pair.  kMasked: tokens at or beyond n_tokens (page A starts at
-// token tokA, page B at tokB; tokB = n_tokens marks an absent page B) take no
-// weight, whatever their (possibly never written) slots hold.  kFirst: the
-// wave's first pair, which always sets the running maximum.
+// One page pair.  kMasked: tokens at or beyond this lane's limit `lim` (the
+// tokens its query row sees; page A starts at token tokA, page B at tokB;
+// tokB >= every limit marks an absent page B) take no weight, whatever their
+// (possibly never written) slots hold.  kFirst: the wave's first pair, which
+// always sets the running maximum (-inf for a column that sees none of its
+// tokens, which is then also the wave's last pair).
 //
 // Scores are formed relative to the reference mref = m + 8 (m the running
 // maximum; 0 before the first pair), so the weights are exp2 of them
@@ -222,7 +224,7 @@ struct LaneConsts {
 template <int KB, int VB, bool kMasked, bool kFirst>
 __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
                                              int tokB,
-                                             int n_tokens, const v8h (&bq)[4], const LaneConsts &lc,
+                                             int lim, const v8h (&bq)[4], const LaneConsts &lc,
                                              int g, State &st) {
     constexpr bool first = kFirst;
     const float mref = first ? 0.0f : st.m + kLazyThreshold;
@@ -233,8 +235,8 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
     if (kMasked) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            valid[i] = tokA + 4 * g + i < n_tokens;
-            valid[4 + i] = tokB + 4 * g + i < n_tokens;
+            valid[i] = tokA + 4 * g + i < lim;
+            valid[4 + i] = tokB + 4 * g + i < lim;
         }
 #pragma unroll
         for (int i = 0; i < 8; i++) lg[i] = valid[i] ? lg[i] : -INFINITY;
@@ -252,7 +254,7 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
 #pragma unroll
         for (int j = 0; j < 8; j++) st.acc[j] *= f;
         st.m = m_new;
-        const float shift = (m_new + kLazyThreshold) - mref;
+        const float shift = (kMasked && first && m_new == -INFINITY) ? 0.0f : (m_new + kLazyThreshold) - mref;
 #pragma unroll
         for (int i = 0; i < 8; i++) lg[i] -= shift;
     }
@@ -297,7 +299,7 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
     }
 }
 
-template <int KB, int VB>
+template <int KB, int VB, bool kMQ>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using Lay = Layout<KB, VB>;
     const int split = blockIdx.x;
@@ -326,14 +328,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int max_len = a.max_seq_len;
     int n_tokens = a.seq_lens[b];
     n_tokens = n_tokens < 0 ? 0 : (n_tokens > max_len ? max_len : n_tokens);
+    // query rows per sequence (kMQ; at most 16); row m sees tokens below
+    // n_tokens - (M - 1 - m), so every row sees the first n_min (at least one
+    // token when there is one)
+    const int M = kMQ ? a.q_len : 1;
+    const int n_min = kMQ ? max(min(n_tokens, 1), n_tokens - (M - 1)) : n_tokens;
     const int npages = (n_tokens + kPage - 1) / kPage;
     const int pps = a.pages_per_split;
     const int p_begin = split * pps;
-    const int hq0 = kvh * a.gqa + hg * kHeadsPerGroup;
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
 
     if (p_begin >= npages) {         // an empty sequence, or a split past its end
-        write_empty(a, tid, b, hq0, nh, split);
+        write_empty<kMQ>(a, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
         return;
     }
     const int p_end = min(p_begin + pps, npages);
@@ -357,15 +363,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         return a.cache + (int64_t)id * page_stride + head_off;
     };
 
-    // Pairs of this split: all but possibly the last are full (both pages
-    // inside the split and every token < n_tokens).  Wave w takes pairs
-    // w, w + 4, ...; full pairs run through a triple-buffered loop whose loads
-    // are always issued (past the end they repeat the wave's last pair), so
-    // two pairs are in flight while one is computed.  The partial pair, if
-    // any, is loaded and processed afterwards with per-token masking.
-    const int last_pa = p_begin + 2 * (npairs - 1);
-    const bool last_partial = (last_pa + 1 >= p_end) || (last_pa + 2) * kPage > n_tokens;
-    const int nfull = npairs - (last_partial ? 1 : 0);
+    // Pairs of this split: the leading ones are full (both pages inside the
+    // split, every token seen by every query row), the rest -- the last one
+    // or two (query rows span at most 16 tokens) -- are masked.  Wave w takes
+    // pairs w, w + 4, ...; full pairs run through a triple-buffered loop whose
+    // loads are always issued (past the end they repeat the wave's last pair),
+    // so two pairs are in flight while one is computed.  A masked pair is
+    // loaded and processed afterwards with per-token masking.
+    const int full_end = min(p_end, n_min / kPage);       // pages below: full
+    const int nfull = full_end > p_begin ? (full_end - p_begin) >> 1 : 0;
     const int nk = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
 
     // The scheduling barrier keeps the compiler from sinking the prefetch
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (hh < nh) {
             const uint2 raw = *reinterpret_cast<const uint2 *>(
-                a.query + ((int64_t)b * a.num_q_heads + hq0 + hh) * kHeadDim + c0);
+                a.query + io_row<kMQ>(a, b, kvh, hg * kHeadsPerGroup + hh) * kHeadDim + c0);
             q[0] = half_bits_to_float(raw.x & 0xffffu);
             q[1] = half_bits_to_float(raw.x >> 16);
             q[2] = half_bits_to_float(raw.y & 0xffffu);
@@ -522,24 +528,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
         }
     }
-    if (last_partial && wave == (npairs - 1) % kWaves) {
+    // Masked pairs: the last pair, and with several query rows possibly the
+    // one before it (each the last pair of its wave).
+    auto masked_pair = [&](int i) {
+        int lim = n_tokens;                     // the tokens this lane's query row sees
+        if (kMQ) {
+            const int G = a.gqa / M;
+            const int mrow = min((hg * kHeadsPerGroup + (n16 & 7)) / G, M - 1);
+            lim = n_tokens - (M - 1 - mrow);
+        }
         PageRegs<KB, VB> tA, tB;
-        const bool has_b = last_pa + 1 < p_end;
-        const int j = (npairs - 1) / kWaves;    // this wave's last pair
+        const int pa = p_begin + 2 * i;
+        const bool has_b = pa + 1 < p_end;
+        const int j = i / kWaves;               // the pair's lane in bt_a / bt_b
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
         load_page(region_of(id_a), lo, tA);
         load_page(region_of(has_b ? __builtin_amdgcn_readlane(bt_b, j) : id_a), lo, tB);
-        const int tok_b = has_b ? (last_pa + 1) * kPage : n_tokens;
+        const int tok_b = has_b ? (pa + 1) * kPage : n_tokens;
         if (nk == 0)
-            process_pair<KB, VB, true, true>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
+            process_pair<KB, VB, true, true>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
         else
-            process_pair<KB, VB, true, false>(tA, tB, last_pa * kPage, tok_b, n_tokens, bq, lc, g, st);
-    }
+            process_pair<KB, VB, true, false>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
+    };
+    if (nfull < npairs && wave == (npairs - 1) % kWaves) masked_pair(npairs - 1);
+    if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kWaves) masked_pair(npairs - 2);
 
     // ---- merge the 4 waves; write the partial (or the output) ----
-    merge_and_store(st, s_merge, a, 1,
+    merge_and_store<kMQ>(st, s_merge, a, 1,
                     [](int j) { return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : 20); },
-                    wave, tid, b, hq0, nh, split);
+                    wave, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
 }
 
 // Merge the split partials of each (sequence, query head) and apply the
@@ -594,7 +611,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
             o4[3] += f * v[u].w;
         }
     }
-    finalize_head(o4, l, z, l32, a.out, a.out_f32, row, a.rotated);
+    // output row: with several query rows per sequence, the combine's rows
+    // are (sequence, KV head, row-head pair) and the output is [B][q_len][Hq]
+    int64_t orow = row;
+    if (a.q_len > 1) {
+        const int bb = (int)(row / a.num_q_heads), v = (int)(row % a.num_q_heads);
+        orow = io_row<true>(a, bb, v / a.gqa, v % a.gqa);
+    }
+    finalize_head(o4, l, z, l32, a.out, a.out_f32, orow, a.rotated);
 }
 
 // Work-groups of decode_kernel<KB, VB> the current device holds at once
@@ -610,7 +634,7 @@ int resident_workgroups() {
     if (cached[dev] > 0) return cached[dev];
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false>, 256, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -619,15 +643,22 @@ int resident_workgroups() {
     return cached[dev];
 }
 
-template <int KB, int VB>
-hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+template <int KB, int VB, bool kMQ>
+hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB>), grid, dim3(256), 0, stream, ev.start,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ>), grid, dim3(256), 0, stream, ev.start,
                               ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+// One query row per sequence, or several (causal among them).
+template <int KB, int VB>
+hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+    return a.q_len > 1 ? launch_split_kernel<KB, VB, true>(a, stream, ev)
+                       : launch_split_kernel<KB, VB, false>(a, stream, ev);
 }
 
 }  // namespace

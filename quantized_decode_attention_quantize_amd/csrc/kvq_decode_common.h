@@ -67,6 +67,18 @@ __device__ __forceinline__ void finalize_head(const float (&acc)[4], float l, fl
     }
 }
 
+// Query / output row of head index v (0 <= v < a.gqa) of KV head kvh of
+// sequence b.  One query row per sequence: row b * Hq + kvh * G + v.  With
+// q_len rows, v = m * G + g is head kvh * G + g of row m, and rows are laid
+// out [num_seqs][q_len][Hq].  kMQ = false: one query row (q_len is not read).
+template <bool kMQ>
+__device__ __forceinline__ int64_t io_row(const DecodeArgs &a, int b, int kvh, int v) {
+    if (!kMQ || a.q_len <= 1) return (int64_t)b * a.num_q_heads + kvh * a.gqa + v;
+    const int G = a.gqa / a.q_len;
+    const int m = v / G;
+    return ((int64_t)b * a.q_len + m) * (a.num_q_heads / a.q_len) + kvh * G + (v - m * G);
+}
+
 // LDS of the wave merge.
 struct MergeLds {
     float m[kWaves][kHeadsPerGroup];
@@ -75,17 +87,18 @@ struct MergeLds {
     float acc[kWaves][kHeadsPerGroup][kHeadDim];
 };
 
-// Merge the 4 waves' states of a work-group (heads hq0 .. hq0 + nh - 1 of
-// sequence b) and write the split's partial, or the output when the launch
-// has a single split (then no combine runs).  unscale(j) is the factor of
-// channel block j.  Every thread of the work-group must call it.
+// Merge the 4 waves' states of a work-group (head indices v0 .. v0 + nh - 1
+// of KV head kvh of sequence b) and write the split's partial, or the output
+// when the launch has a single split (then no combine runs).  unscale(j) is
+// the factor of channel block j.  Every thread of the work-group must call it.
 // (rotate_out: the partial is stored in the K4V2 Hadamard domain, acc' = H acc
 // and zacc = acc_0, so that it merges with K4V2 partials in one combine:
 // (H acc')_j / 128 = acc_j for j >= 1 and channel 0 comes from zacc.)
-template <typename Unscale>
+template <bool kMQ = false, typename Unscale>
 __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const DecodeArgs &a, int rotated,
-                                                Unscale unscale, int wave, int tid, int b, int hq0, int nh,
-                                                int split, int rotate_out = 0) {
+                                                Unscale unscale, int wave, int tid, int b, int kvh, int v0,
+                                                int nh, int split, int rotate_out = 0) {
+    const int hq0 = kvh * a.gqa + v0;
     const int lane = tid & 63;
     const int n16 = lane & 15;
     const int g = lane >> 4;
@@ -132,7 +145,8 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
 
     const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
     if (a.splits == 1 && !a.partials_only) {
-        if (hh < nh) finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, row, rotated);
+        if (hh < nh)
+            finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, io_row<kMQ>(a, b, kvh, v0 + hh), rotated);
         return;
     }
     if (rotate_out) {
@@ -155,10 +169,13 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
 // zero output rows; otherwise it writes empty partials (m = -inf, l = zacc =
 // acc = 0), so that the combine can merge every split slot of every row
 // without knowing the sequence lengths.
-__device__ __forceinline__ void write_empty(const DecodeArgs &a, int tid, int b, int hq0, int nh, int split) {
+template <bool kMQ = false>
+__device__ __forceinline__ void write_empty(const DecodeArgs &a, int tid, int b, int kvh, int v0, int nh,
+                                            int split) {
+    const int hq0 = kvh * a.gqa + v0;
     if (a.splits == 1 && !a.partials_only) {
         if ((tid >> 5) < nh) {
-            const int64_t base = ((int64_t)b * a.num_q_heads + hq0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
+            const int64_t base = io_row<kMQ>(a, b, kvh, v0 + (tid >> 5)) * kHeadDim + 4 * (tid & 31);
             if (a.out_f32) *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base) = make_float4(0, 0, 0, 0);
             else *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base) = make_uint2(0, 0);
         }

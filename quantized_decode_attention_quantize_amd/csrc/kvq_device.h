@@ -112,6 +112,11 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t gqa;              // num_q_heads / num_kv_heads
     int32_t head_groups;      // ceil(gqa / 8)
+    // Query rows per sequence (1: plain decode).  With q_len > 1, num_q_heads
+    // and gqa count (row, head) pairs: q_len * Hq and q_len * G, the pair
+    // (m, g) being index m * G + g of its KV head; query and output rows are
+    // [num_seqs][q_len][Hq], and row m attends to tokens 0 .. n - q_len + m.
+    int32_t q_len;
     int32_t splits;           // work-groups per (seq, kv head, head group)
     int32_t pages_per_split;
     float alpha;              // softmax_scale * log2(e) / 128

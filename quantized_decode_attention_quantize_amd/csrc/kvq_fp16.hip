@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
     const int hq0 = kvh * a.gqa + hg * kHeadsPerGroup;
     const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
     if (p_begin >= npages) {         // an empty sequence, or a split past its end
-        write_empty(a, tid, b, hq0, nh, split);
+        write_empty(a, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
         return;
     }
     const int p_end = min(p_begin + pps, npages);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
             process_page16<true, false>(t, tok0, n_tokens, bq, c1, res_k, g, st);
     }
 
-    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, hq0, nh, split, a.rotate_partials);
+    merge_and_store(st, s_merge, a, 0, [](int) { return 1.0f; }, wave, tid, b, kvh, hg * kHeadsPerGroup, nh, split, a.rotate_partials);
 }
 
 }  // namespace

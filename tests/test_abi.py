@@ -249,3 +249,30 @@ def test_fp16_baseline_format():
     assert lib.kvq_append_decode_partials(ctypes.byref(f), g, g, 256, 256, g, g, 10, g, 7, g, 2, 8, 2, 100,
                                           0.088, g, ws, 0, None) == 3
 
+
+
+def test_multi_query_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    assert kvq.decode_workspace_bytes_mq(2, 4, 8, 2, 100) == kvq.decode_workspace_bytes(2, 32, 2, 100)
+    for bad in ((2, 0, 8, 2, 100), (2, 17, 8, 2, 100), (2, 4, 7, 2, 100)):
+        with pytest.raises(kvq.KvqError):
+            kvq.decode_workspace_bytes_mq(*bad)
+    ws = kvq.decode_workspace_bytes_mq(2, 4, 8, 2, 100)
+
+    def call(fmt=None, **kw):
+        a = dict(out=g, dt=1, q=g, M=4, cache=g, np=10, bt=g, mp=7, sl=g, B=2, Hq=8, Hkv=2, L=100,
+                 scale=0.088, ws=g, wsb=ws, pps=0)
+        a.update(kw)
+        f = ctypes.byref(fmt or kvq.format_from_string())
+        return lib.kvq_decode_attention_mq(f, a["out"], a["dt"], a["q"], a["M"], a["cache"], a["np"], a["bt"],
+                                           a["mp"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["L"], a["scale"],
+                                           a["ws"], a["wsb"], a["pps"], None)
+
+    assert call(M=0) == 2 and call(M=17) == 2
+    assert call(Hq=7) == 2
+    assert call(fmt=kvq.format_from_string("fp16")) == 3      # one query row only for the fp16 baseline
+    assert call(out=None) == 1
+    assert call(wsb=ws - 1) == 5                              # the workspace of q_len * Hq heads
+    assert call(q=P(0x10008)) == 4

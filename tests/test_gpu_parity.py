@@ -907,3 +907,43 @@ def test_mixed_widths_recent_k8v4_history_k4v2(dev):
             ref = oracle.attention_f64(k_all, v_all, q[b, h * G:(h + 1) * G], SCALE)
             err = np.max(np.abs(out[b, h * G:(h + 1) * G] - ref))
             assert err <= TOL, f"b={b} h={h} err={err}"
+
+
+# --------------------------------------------------------------------------
+# Several query rows per sequence (causal)
+# --------------------------------------------------------------------------
+
+MQ_CASES = [
+    # B, Hq, Hkv, lens, q_len, pages_per_split, fmt
+    (2, 8, 1, [40, 16], 2, 0, (4, 2)),        # G = 8: 16 (row, head) pairs, two column groups
+    (3, 2, 2, [100, 8, 33], 8, 0, (4, 2)),     # G = 1: 8 rows fill one column group
+    (2, 8, 2, [300, 47], 4, 2, (4, 2)),        # masked tokens straddle two splits of one page pair
+    (1, 4, 4, [16], 16, 0, (4, 2)),            # q_len = whole sequence
+    (2, 48, 3, [129, 64], 3, 4, (4, 2)),       # G = 16: 48 pairs per KV head
+    (2, 8, 2, [513, 31], 5, 0, (8, 4)),
+    (2, 4, 1, [77, 200], 6, 2, (4, 4)),
+    (2, 4, 1, [34, 66], 5, 0, (4, 2)),         # two masked page pairs in one split
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,M,pps,fmt", MQ_CASES)
+def test_multi_query_decode_matches_oracle(dev, B, Hq, Hkv, lens, M, pps, fmt):
+    log(f"multi-query B={B} Hq={Hq} Hkv={Hkv} lens={lens} q_len={M} pps={pps} fmt={fmt}")
+    cache, pool, bt, lens_np, _ = _build_case(dev, B, Hq, Hkv, lens, seed=M * 100 + sum(lens), fmt=fmt)
+    rng = np.random.default_rng(M + sum(lens))
+    q = (rng.standard_normal((B, M, Hq, D)) * 1.5).astype(np.float16)
+    ref = oracle.decode_attention_mq(pool, bt, lens_np, q, SCALE, fmt=fmt)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    kf = _kfmt(fmt)
+    out = kvq.decode_attention_mq(qd, cache, btd, ld, L, pages_per_split=pps, fmt=kf).cpu().numpy()
+    err = np.max(np.abs(out - ref))
+    assert err <= TOL, f"err={err}"
+    out16 = kvq.decode_attention_mq(qd, cache, btd, ld, L, out_dtype=torch.float16, pages_per_split=pps,
+                                    fmt=kf).float().cpu().numpy()
+    assert np.max(np.abs(out16 - ref)) <= TOL
+    # q_len = 1 is the plain decode, bit for bit
+    one = kvq.decode_attention_mq(qd[:, -1:].contiguous(), cache, btd, ld, L, pages_per_split=pps, fmt=kf)
+    plain = kvq.decode_attention(qd[:, -1].contiguous(), cache, btd, ld, L, pages_per_split=pps, fmt=kf)
+    assert torch.equal(one[:, 0], plain)
