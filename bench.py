@@ -70,6 +70,8 @@ def parse():
                     help="skip the fp16 sink + recent window beside the K4V2 history")
     ap.add_argument("--no-presets", action="store_true",
                     help="skip the k4v4 / k8v2 / k8v4 presets on the same workload")
+    ap.add_argument("--no-multi-query", action="store_true",
+                    help="skip the multi-row (speculative draft) decode on the same cache")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
@@ -366,6 +368,9 @@ def main():
     if not args.no_fp16_baseline:
         result["fp16_baseline"] = fp16_baseline(torch, inp, kvq, lib, dev, stream, args, ms_per_step)
 
+    if not args.no_multi_query:
+        result["multi_query"] = multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, n)
+
     if not args.no_mixed_window:
         result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
 
@@ -436,6 +441,44 @@ def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
             "kernel_GBps": round(fp16_bytes / (kern * 1e-3) / 1e9, 2),
             "kernel_pct_hbm_peak": round(100 * fp16_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "k4v2_step_speedup": round(ms / k4v2_ms_per_step, 3)}
+
+
+def multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, n):
+    """kvq_decode_attention_mq (split kernel + combine) on the K4V2 cache of
+    the main workload: q_len causal query rows per sequence, with the
+    workload's 64 query heads (G = 8) and with 32 (G = 4, where two rows fill
+    the 8-column MFMA group one row leaves half empty)."""
+    import numpy as np
+    B, Hkv = lens.numel(), pools[0].shape[1]
+    fmt = kvq.format_from_string("k4v2_g128")
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    fn = lib.kvq_decode_attention_mq
+    res = []
+    rng = np.random.default_rng(20260605 + 77)
+    for hq, m in ((64, 1), (64, 2), (64, 4), (32, 1), (32, 2)):
+        q = torch.from_numpy(rng.standard_normal((B, m, hq, 128)).astype(np.float16)).to(dev)
+        out = torch.empty((B, m, hq, 128), dtype=torch.float16, device=dev)
+        wsb = kvq.decode_workspace_bytes_mq(B, m, hq, Hkv, n)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        argl = [(ctypes.byref(fmt), P(out.data_ptr()), 0, P(q.data_ptr()), i32(m), P(p.data_ptr()), i64(p.shape[0]),
+                 P(bt.data_ptr()), i32(bt.shape[1]), P(lens.data_ptr()), i32(B), i32(hq), i32(Hkv), i32(n),
+                 ctypes.c_float(1.0 / math.sqrt(128)), P(ws.data_ptr()), ctypes.c_size_t(wsb), i32(0),
+                 P(stream.cuda_stream)) for p in pools]
+        for i in range(5):
+            fn(*argl[i % len(pools)])
+        torch.cuda.synchronize()
+        steps = max(20, args.steps // 2)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if fn(*argl[i % len(pools)]):
+                raise RuntimeError("multi-row decode failed")
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
+        res.append({"num_q_heads": hq, "q_len": m, "ms_per_call": round(ms, 5),
+                    "query_rows_per_s": round(B * m / (ms * 1e-3), 1),
+                    "kv_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2)})
+    return res
 
 
 def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset):

@@ -302,10 +302,28 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
 template <int KB, int VB, bool kMQ>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using Lay = Layout<KB, VB>;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / a.head_groups;
-    const int hg = blockIdx.y % a.head_groups;
-    const int b = blockIdx.z;
+    int split, kvh, hg, b;
+    if (!kMQ) {
+        split = blockIdx.x;
+        kvh = blockIdx.y / a.head_groups;
+        hg = blockIdx.y % a.head_groups;
+        b = blockIdx.z;
+    } else {
+        // One-dimensional grid, XCD-aware: work-groups are dispatched to the 8
+        // XCDs in turn, so block L runs on XCD L % 8.  The head groups of one
+        // (split, sequence, KV head) take consecutive blocks of one XCD and
+        // read the same pages at about the same time: the later reads are
+        // served by that XCD's L2.  Blocks past the work (the grid is padded
+        // to whole rounds) exit at once.
+        const int L = blockIdx.x;
+        hg = (L >> 3) % a.head_groups;
+        const int64_t w = (int64_t)((L >> 3) / a.head_groups) * 8 + (L & 7);
+        const int64_t units = (int64_t)a.splits * a.num_kv_heads * a.num_seqs;
+        if (w >= units) return;
+        split = (int)(w % a.splits);
+        kvh = (int)((w / a.splits) % a.num_kv_heads);
+        b = (int)(w / ((int64_t)a.splits * a.num_kv_heads));
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -645,7 +663,14 @@ int resident_workgroups() {
 
 template <int KB, int VB, bool kMQ>
 hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
-    const dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
+    dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
+    if (kMQ) {
+        // one dimension: rounds of 8 (split, sequence, KV head) units x head groups
+        const int64_t units = (int64_t)a.splits * a.num_kv_heads * a.num_seqs;
+        const int64_t blocks = (units + 7) / 8 * 8 * a.head_groups;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        grid = dim3((unsigned)blocks, 1, 1);
+    }
     if (ev.start || ev.stop)
         hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ>), grid, dim3(256), 0, stream, ev.start,
                               ev.stop, 0, a);
