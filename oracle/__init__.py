@@ -19,6 +19,9 @@ Functions and the passages they follow (pages cited by title and section):
   read-back (same pipeline list, stage 4), fp64; pins the algebra.
 * ``decode_attention_mq`` -- several causal query rows per sequence (the
   multi-token decode of speculative drafts and prefill chunks), fp64.
+* ``page_tokens`` -- pages of 16, 32, 64 or 128 tokens, each (page, KV head)
+  made of page_tokens / 16 consecutive 16-token regions (the variable page
+  size the dothoosh.com page announces in its closing list).
 * ``fmt=(kbits, vbits)`` -- the same pipeline at the other bit widths the pages
   report (8-bit keys with 4-bit values, 4-bit both: dzen.ru summary of the
   vLLM TurboQuant post, sections on accuracy and memory); keys 4 or 8 bits,
@@ -109,6 +112,14 @@ def _load():
     lib.kvqo_decode_attention_mq_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
                                                  ctypes.c_double, P]
     lib.kvqo_decode_attention_mq_fmt.restype = ctypes.c_int
+    lib.kvqo_quantize_append_paged.argtypes = [ci, ci, ci, P, P, i64, i64, P, i64, i32, P, i64]
+    lib.kvqo_quantize_append_paged.restype = ctypes.c_int
+    lib.kvqo_decode_attention_paged.argtypes = [ci, ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
+                                                ctypes.c_double, P, P]
+    lib.kvqo_decode_attention_paged.restype = ctypes.c_int
+    lib.kvqo_decode_attention_mq_paged.argtypes = [ci, ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
+                                                   ctypes.c_double, P]
+    lib.kvqo_decode_attention_mq_paged.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -199,17 +210,19 @@ def load_token(region: np.ndarray, off: int, fmt=K4V2):
 
 
 def quantize_append(key_f16: np.ndarray, value_f16: np.ndarray, slot_mapping: np.ndarray,
-                    pool: np.ndarray, fmt=K4V2) -> None:
-    """key/value: float16 [T][Hkv][128]; slot_mapping int64[T]; pool uint8
-    [num_pages][Hkv][region_bytes(fmt)], written in place."""
+                    pool: np.ndarray, fmt=K4V2, page_tokens: int = PAGE) -> None:
+    """key/value: float16 [T][Hkv][128]; slot_mapping int64[T] (page *
+    page_tokens + offset); pool uint8 [num_pages][Hkv][page_tokens / 16 *
+    region_bytes(fmt)], written in place."""
     k = _c(key_f16, np.float16)
     v = _c(value_f16, np.float16)
     T, H, d = k.shape
     assert d == D and v.shape == k.shape
-    assert pool.dtype == np.uint8 and pool.flags.c_contiguous and pool.shape[1:] == (H, region_bytes(fmt))
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    assert pool.shape[1:] == (H, page_tokens // PAGE * region_bytes(fmt))
     sm = _c(slot_mapping, np.int64)
-    rc = _load().kvqo_quantize_append_fmt(int(fmt[0]), int(fmt[1]), _ptr(k), _ptr(v), H * D, H * D, _ptr(sm),
-                                          T, H, _ptr(pool), pool.shape[0])
+    rc = _load().kvqo_quantize_append_paged(int(fmt[0]), int(fmt[1]), int(page_tokens), _ptr(k), _ptr(v), H * D,
+                                            H * D, _ptr(sm), T, H, _ptr(pool), pool.shape[0])
     if rc != 0:
         raise ValueError("oracle append: slot outside the pool")
 
@@ -230,11 +243,12 @@ def dequant_slot_rotated(region: np.ndarray, off: int, fmt=K4V2):
     return k, v
 
 
-def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=None, fmt=K4V2):
+def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=None, fmt=K4V2,
+                     page_tokens: int = PAGE):
     """Plain-definition decode attention in fp64.  query: float16 [B][Hq][128].
     Returns float64 [B][Hq][128] (NaN where head_mask excludes a head)."""
     pool = _c(pool, np.uint8)
-    assert pool.shape[2] == region_bytes(fmt)
+    assert pool.shape[2] == page_tokens // PAGE * region_bytes(fmt)
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     q = _c(query_f16, np.float16)
@@ -242,28 +256,28 @@ def decode_attention(pool, block_tables, seq_lens, query_f16, scale, head_mask=N
     Hkv = pool.shape[1]
     out = np.full((B, Hq, D), np.nan, np.float64)
     hm = None if head_mask is None else _c(head_mask, np.uint8)
-    rc = _load().kvqo_decode_attention_fmt(int(fmt[0]), int(fmt[1]), _ptr(pool), pool.shape[0], Hkv, _ptr(bt),
-                                           bt.shape[1], _ptr(sl), B, Hq, _ptr(q), float(scale),
-                                           None if hm is None else _ptr(hm), _ptr(out))
+    rc = _load().kvqo_decode_attention_paged(int(fmt[0]), int(fmt[1]), int(page_tokens), _ptr(pool), pool.shape[0],
+                                             Hkv, _ptr(bt), bt.shape[1], _ptr(sl), B, Hq, _ptr(q), float(scale),
+                                             None if hm is None else _ptr(hm), _ptr(out))
     if rc != 0:
         raise ValueError("oracle decode: invalid shape or page id")
     return out
 
 
-def decode_attention_mq(pool, block_tables, seq_lens, query_f16, scale, fmt=K4V2):
+def decode_attention_mq(pool, block_tables, seq_lens, query_f16, scale, fmt=K4V2, page_tokens: int = PAGE):
     """Several query rows per sequence, causal: query float16 [B][M][Hq][128];
     row m of sequence b attends to tokens 0 .. seq_lens[b] - M + m.  Returns
     float64 [B][M][Hq][128]."""
     pool = _c(pool, np.uint8)
-    assert pool.shape[2] == region_bytes(fmt)
+    assert pool.shape[2] == page_tokens // PAGE * region_bytes(fmt)
     bt = _c(block_tables, np.int32)
     sl = _c(seq_lens, np.int32)
     q = _c(query_f16, np.float16)
     B, M, Hq, d = q.shape
     out = np.empty((B, M, Hq, D), np.float64)
-    rc = _load().kvqo_decode_attention_mq_fmt(int(fmt[0]), int(fmt[1]), _ptr(pool), pool.shape[0], pool.shape[1],
-                                              _ptr(bt), bt.shape[1], _ptr(sl), B, M, Hq, _ptr(q), float(scale),
-                                              _ptr(out))
+    rc = _load().kvqo_decode_attention_mq_paged(int(fmt[0]), int(fmt[1]), int(page_tokens), _ptr(pool),
+                                                pool.shape[0], pool.shape[1], _ptr(bt), bt.shape[1], _ptr(sl), B, M,
+                                                Hq, _ptr(q), float(scale), _ptr(out))
     if rc != 0:
         raise ValueError("oracle multi-query decode: invalid shape or page id")
     return out

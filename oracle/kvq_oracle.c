@@ -66,6 +66,24 @@ int64_t kvqo_region_bytes(int kbits, int vbits)
 void kvqo_attention_f64(const double *k, const double *v, int64_t n, const uint16_t *q, int32_t G,
                         double scale, double *out);
 
+/* Page size.  The pages promise a variable page size [KVARN-P, closing list];
+ * read here as pages of page_tokens = 16 * S tokens (S = 1, 2, 4, 8), each
+ * (page, KV head) holding S consecutive 16-token regions of the layout above:
+ * the pool is u8 [num_pages][num_kv_heads][S][region].  Token r (0 <=
+ * r < page_tokens) of a page sits in region r / 16, slot r % 16. */
+static int page_ok(int page_tokens)
+{
+    return page_tokens == 16 || page_tokens == 32 || page_tokens == 64 || page_tokens == 128;
+}
+
+/* The 16-token region holding token r of page `page`, KV head h. */
+static const uint8_t *token_region(const uint8_t *pool, int64_t page, int h, int num_kv_heads, int r,
+                                   int page_tokens, int64_t region_bytes)
+{
+    const int subs = page_tokens / KVQO_PAGE;
+    return pool + ((page * num_kv_heads + h) * subs + r / KVQO_PAGE) * region_bytes;
+}
+
 /* ------------------------------------------------------------------------ */
 /* IEEE binary16 <-> binary32/64, written from the format definition.        */
 /* ------------------------------------------------------------------------ */
@@ -379,30 +397,39 @@ void kvqo_load_token(const uint8_t *region, int off,
  * offset, or < 0 to skip the token.  pool: u8 [num_pages][num_kv_heads][1664].
  * Returns 0, or -1 on a slot outside the pool (nothing is written for it).
  */
-int kvqo_quantize_append_fmt(int kbits, int vbits, const uint16_t *key, const uint16_t *value,
-                             int64_t key_token_stride, int64_t value_token_stride,
-                             const int64_t *slot_mapping, int64_t num_tokens,
-                             int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+int kvqo_quantize_append_paged(int kbits, int vbits, int page_tokens, const uint16_t *key, const uint16_t *value,
+                               int64_t key_token_stride, int64_t value_token_stride,
+                               const int64_t *slot_mapping, int64_t num_tokens,
+                               int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
 {
-    if (!fmt_ok(kbits, vbits)) return -1;
+    if (!fmt_ok(kbits, vbits) || !page_ok(page_tokens)) return -1;
     const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     int rc = 0;
     uint8_t kc[KVQO_D], vc[KVQO_D];
     for (int64_t t = 0; t < num_tokens; t++) {
         int64_t slot = slot_mapping[t];
         if (slot < 0) continue;
-        int64_t page = slot / KVQO_PAGE;
-        int off = (int)(slot % KVQO_PAGE);
+        int64_t page = slot / page_tokens;
+        int r = (int)(slot % page_tokens);
         if (page >= num_pages) { rc = -1; continue; }
         for (int h = 0; h < num_kv_heads; h++) {
             uint16_t ks, kz, vs, vz;
             kvqo_quantize_group_mode(key + t * key_token_stride + (int64_t)h * KVQO_D, kbits, 0, kc, &ks, &kz);
             kvqo_quantize_group_mode(value + t * value_token_stride + (int64_t)h * KVQO_D, vbits, 1, vc, &vs, &vz);
-            uint8_t *region = pool + (page * num_kv_heads + h) * region_bytes;
-            kvqo_store_token_fmt(kbits, vbits, region, off, kc, ks, kz, vc, vs, vz);
+            uint8_t *region = (uint8_t *)token_region(pool, page, h, num_kv_heads, r, page_tokens, region_bytes);
+            kvqo_store_token_fmt(kbits, vbits, region, r % KVQO_PAGE, kc, ks, kz, vc, vs, vz);
         }
     }
     return rc;
+}
+
+int kvqo_quantize_append_fmt(int kbits, int vbits, const uint16_t *key, const uint16_t *value,
+                             int64_t key_token_stride, int64_t value_token_stride,
+                             const int64_t *slot_mapping, int64_t num_tokens,
+                             int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+{
+    return kvqo_quantize_append_paged(kbits, vbits, KVQO_PAGE, key, value, key_token_stride, value_token_stride,
+                                      slot_mapping, num_tokens, num_kv_heads, pool, num_pages);
 }
 
 int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
@@ -488,19 +515,19 @@ void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, do
  * entry are computed; the rest of `out` is left untouched.
  * Returns 0, or -1 on an invalid shape or page id.
  */
-int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
-                              int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
-                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                              const uint16_t *query, double scale,
-                              const uint8_t *head_mask, double *out)
+int kvqo_decode_attention_paged(int kbits, int vbits, int page_tokens, const uint8_t *pool, int64_t num_pages,
+                                int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                const uint16_t *query, double scale,
+                                const uint8_t *head_mask, double *out)
 {
-    if (!fmt_ok(kbits, vbits)) return -1;
+    if (!fmt_ok(kbits, vbits) || !page_ok(page_tokens)) return -1;
     const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
     const int G = num_q_heads / num_kv_heads;
     for (int b = 0; b < num_seqs; b++) {
         const int64_t n = seq_lens[b];
-        if (n < 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        if (n < 0 || n > (int64_t)max_pages_per_seq * page_tokens) return -1;
         for (int kvh = 0; kvh < num_kv_heads; kvh++) {
             int any = 0;
             for (int g = 0; g < G; g++)
@@ -511,10 +538,11 @@ int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t
             double *lg = malloc(sizeof(double) * n);
             if (!K || !V || !lg) { free(K); free(V); free(lg); return -1; }
             for (int64_t t = 0; t < n; t++) {
-                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / page_tokens];
                 if (page < 0 || page >= num_pages) { free(K); free(V); free(lg); return -1; }
-                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
-                kvqo_dequant_slot_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+                const int r = (int)(t % page_tokens);
+                const uint8_t *region = token_region(pool, page, kvh, num_kv_heads, r, page_tokens, region_bytes);
+                kvqo_dequant_slot_fmt(kbits, vbits, region, r % KVQO_PAGE, K + t * KVQO_D, V + t * KVQO_D);
             }
             for (int g = 0; g < G; g++) {
                 int hq = kvh * G + g;
@@ -544,6 +572,17 @@ int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t
     return 0;
 }
 
+int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
+                              int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              const uint16_t *query, double scale,
+                              const uint8_t *head_mask, double *out)
+{
+    return kvqo_decode_attention_paged(kbits, vbits, KVQO_PAGE, pool, num_pages, num_kv_heads, block_tables,
+                                       max_pages_per_seq, seq_lens, num_seqs, num_q_heads, query, scale,
+                                       head_mask, out);
+}
+
 int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
                           const int32_t *block_tables, int32_t max_pages_per_seq,
                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -565,27 +604,28 @@ int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv
  * no token (n - q_len + m < 0) is zero.  Returns 0, or -1 on an invalid shape
  * or page id.
  */
-int kvqo_decode_attention_mq_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
-                                 int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
-                                 const int32_t *seq_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
-                                 const uint16_t *query, double scale, double *out)
+int kvqo_decode_attention_mq_paged(int kbits, int vbits, int page_tokens, const uint8_t *pool, int64_t num_pages,
+                                   int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                   const int32_t *seq_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                                   const uint16_t *query, double scale, double *out)
 {
-    if (!fmt_ok(kbits, vbits) || q_len <= 0) return -1;
+    if (!fmt_ok(kbits, vbits) || !page_ok(page_tokens) || q_len <= 0) return -1;
     const int64_t region_bytes = kvqo_region_bytes(kbits, vbits);
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
     const int G = num_q_heads / num_kv_heads;
     for (int b = 0; b < num_seqs; b++) {
         const int64_t n = seq_lens[b];
-        if (n < 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        if (n < 0 || n > (int64_t)max_pages_per_seq * page_tokens) return -1;
         for (int kvh = 0; kvh < num_kv_heads; kvh++) {
             double *K = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
             double *V = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
             if (!K || !V) { free(K); free(V); return -1; }
             for (int64_t t = 0; t < n; t++) {
-                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / page_tokens];
                 if (page < 0 || page >= num_pages) { free(K); free(V); return -1; }
-                const uint8_t *region = pool + ((int64_t)page * num_kv_heads + kvh) * region_bytes;
-                kvqo_dequant_slot_fmt(kbits, vbits, region, (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+                const int r = (int)(t % page_tokens);
+                const uint8_t *region = token_region(pool, page, kvh, num_kv_heads, r, page_tokens, region_bytes);
+                kvqo_dequant_slot_fmt(kbits, vbits, region, r % KVQO_PAGE, K + t * KVQO_D, V + t * KVQO_D);
             }
             for (int m = 0; m < q_len; m++) {
                 const int64_t visible = n - q_len + m + 1;        /* tokens 0 .. n - q_len + m */
@@ -600,6 +640,16 @@ int kvqo_decode_attention_mq_fmt(int kbits, int vbits, const uint8_t *pool, int6
         }
     }
     return 0;
+}
+
+int kvqo_decode_attention_mq_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
+                                 int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                                 const uint16_t *query, double scale, double *out)
+{
+    return kvqo_decode_attention_mq_paged(kbits, vbits, KVQO_PAGE, pool, num_pages, num_kv_heads, block_tables,
+                                          max_pages_per_seq, seq_lens, num_seqs, q_len, num_q_heads, query,
+                                          scale, out);
 }
 
 /*

@@ -17,6 +17,7 @@ import kvq_inputs as inp
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 D = 128
+SCALE = 1.0 / math.sqrt(128)
 
 
 def _read_fixture(name):
@@ -823,3 +824,50 @@ def test_value_mean_cancellation_stays_tiny():
         assert np.array_equal(codes, c) and oracle.half_to_double(s) == 2.0 ** -4
         assert abs(oracle.half_to_double(mu)) <= 4 * 2.0 ** -24
         hits += 1
+
+
+# --------------------------------------------------------------------------
+# Pages of 32, 64 and 128 tokens
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P,fmt", [(32, (4, 2)), (64, (8, 4)), (128, (4, 4))])
+def test_larger_pages_are_relabelled_16_token_pages(P, fmt):
+    """A pool of P-token pages, u8 [N][H][P/16][region], is a pool of 16-token
+    pages laid out [N*P/16][H][region] with 16-token page p*S + s holding
+    sub-region s of page p (S = P/16).  The append and both attention calls at
+    page size P must agree with the 16-token ones under that relabelling."""
+    S = P // 16
+    rng = np.random.default_rng(P + fmt[0])
+    B, Hq, Hkv, lens = 3, 8, 2, [P * 2 + 5, 17, P - 1]
+    R = oracle.region_bytes(fmt)
+    pages = [-(-n // P) for n in lens]
+    N = sum(pages) + 1
+    perm = rng.permutation(N)
+    bt = np.zeros((B, max(pages)), np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    # the 16-token relabelling of the same pages
+    bt16 = np.zeros((B, max(pages) * S), np.int32)
+    for b in range(B):
+        for j in range(pages[b] * S):
+            bt16[b, j] = bt[b, j // S] * S + j % S
+    pool = np.zeros((N, Hkv, S * R), np.uint8)
+    pool16 = np.zeros((N * S, Hkv, R), np.uint8)
+    for b, n in enumerate(lens):
+        k = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        t = np.arange(n)
+        oracle.quantize_append(k, v, bt[b, t // P].astype(np.int64) * P + t % P, pool, fmt=fmt, page_tokens=P)
+        oracle.quantize_append(k, v, bt16[b, t // 16].astype(np.int64) * 16 + t % 16, pool16, fmt=fmt)
+    relabelled = pool.reshape(N, Hkv, S, R).transpose(0, 2, 1, 3).reshape(N * S, Hkv, R)
+    assert np.array_equal(relabelled, pool16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    a = oracle.decode_attention(pool, bt, np.array(lens), q, SCALE, fmt=fmt, page_tokens=P)
+    b16 = oracle.decode_attention(pool16, bt16, np.array(lens), q, SCALE, fmt=fmt)
+    assert np.array_equal(a, b16)
+    qm = rng.standard_normal((B, 3, Hq, D)).astype(np.float16)
+    am = oracle.decode_attention_mq(pool, bt, np.array(lens), qm, SCALE, fmt=fmt, page_tokens=P)
+    bm = oracle.decode_attention_mq(pool16, bt16, np.array(lens), qm, SCALE, fmt=fmt)
+    assert np.array_equal(am, bm)
