@@ -120,9 +120,15 @@ typedef enum kvq_status {
     KVQ_ERR_HIP = 6           /* the HIP runtime reported an error             */
 } kvq_status;
 
-/* Format descriptor: {128, 128, k_bits, v_bits, 16} with k_bits in {4, 8} and
- * v_bits in {2, 4} ({128, 128, 4, 2, 16} is K4V2 v1), or {128, 128, 16, 16, 16}
- * (the fp16 baseline). */
+/* Format descriptor: {128, 128, k_bits, v_bits, block_size} with k_bits in
+ * {4, 8}, v_bits in {2, 4} and block_size in {16, 32, 64, 128} tokens per page
+ * ({128, 128, 4, 2, 16} is K4V2 v1), or {128, 128, 16, 16, 16} (the fp16
+ * baseline).  A page of block_size tokens holds, per KV head, block_size / 16
+ * consecutive 16-token regions of the layout above: the pool is u8
+ * [num_pages][num_kv_heads][block_size / 16][region], and token r of a page
+ * (slot = page * block_size + r) sits in region r / 16, slot r % 16 (the
+ * variable page size [KVARN-P] announces, read this way).  Block tables index
+ * pages of block_size tokens. */
 typedef struct kvq_format {
     int32_t head_dim;    /* channels per head                    */
     int32_t group_size;  /* channels per quantisation group      */
@@ -140,9 +146,9 @@ typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
  * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
 
-/* Bytes of one (page, KV head) region: 256 * (k_bits + v_bits) + 128 for a
- * quantised format (1664 for K4V2 v1), 8192 for fp16; 0 for an unsupported
- * format or NULL. */
+/* Bytes of one (page, KV head): block_size / 16 regions of 256 * (k_bits +
+ * v_bits) + 128 bytes for a quantised format (1664 for K4V2 v1), 8192 for
+ * fp16; 0 for an unsupported format or NULL. */
 size_t kvq_page_bytes(const kvq_format *fmt);
 
 /* Bytes of a pool of num_pages pages and num_kv_heads heads; 0 on invalid input. */

@@ -118,9 +118,14 @@ def version() -> str:
     return load().kvq_version().decode()
 
 
-def format_from_string(preset: str = "kvarn_k4v2_g128") -> Format:
+def format_from_string(preset: str = "kvarn_k4v2_g128", page_tokens: int = 16) -> Format:
+    """The preset's format; page_tokens (16, 32, 64, 128 for the quantised
+    presets) sets tokens per page (block_size)."""
     f = Format()
     _check(load().kvq_format_from_string(preset.encode(), ctypes.byref(f)), "format_from_string")
+    f.block_size = page_tokens
+    if page_bytes(f) == 0:
+        raise KvqError(3, f"page size {page_tokens} not supported for {preset}")
     return f
 
 

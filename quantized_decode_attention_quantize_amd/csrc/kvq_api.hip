@@ -11,22 +11,36 @@ namespace {
 thread_local int g_last_hip_error = 0;
 thread_local kvq::LaunchEvents g_split_events;
 
-bool is_g128(const kvq_format *f) {
-    return f && f->head_dim == 128 && f->group_size == 128 && f->block_size == 16;
+bool is_g128(const kvq_format *f) { return f && f->head_dim == 128 && f->group_size == 128; }
+
+// log2 of the 16-token regions per page: pages of 16, 32, 64 or 128 tokens
+int page_log2s(const kvq_format *f) {
+    switch (f->block_size) {
+    case 16: return 0;
+    case 32: return 1;
+    case 64: return 2;
+    case 128: return 3;
+    default: return -1;
+    }
 }
 
-// A quantised cache: 4- or 8-bit keys, 2- or 4-bit values (4/2 is KVarN's).
+// A quantised cache: 4- or 8-bit keys, 2- or 4-bit values (4/2 is KVarN's),
+// pages of 16 to 128 tokens.
 bool is_quant(const kvq_format *f) {
-    return is_g128(f) && (f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4);
+    return is_g128(f) && (f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4) &&
+           page_log2s(f) >= 0;
 }
 
-// The uncompressed fp16 baseline cache.
-bool is_fp16(const kvq_format *f) { return is_g128(f) && f->k_bits == 16 && f->v_bits == 16; }
+// The uncompressed fp16 baseline cache (16-token pages).
+bool is_fp16(const kvq_format *f) {
+    return is_g128(f) && f->k_bits == 16 && f->v_bits == 16 && f->block_size == 16;
+}
 
 bool is_known(const kvq_format *f) { return is_quant(f) || is_fp16(f); }
 
+// Bytes of one (page, KV head): its 16-token regions.
 size_t region_bytes(const kvq_format *f) {
-    return is_quant(f) ? (size_t)(256 * (f->k_bits + f->v_bits) + 128)
+    return is_quant(f) ? (size_t)(256 * (f->k_bits + f->v_bits) + 128) << page_log2s(f)
                        : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
 }
 
@@ -100,7 +114,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
         (pages_per_split % 2) || pages_per_split > max_pps(fp16))
         return KVQ_ERR_SHAPE;
     if (max_pages_per_seq >= 0 &&
-        (max_pages_per_seq == 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * kvq::kPage))
+        (max_pages_per_seq == 0 || (int64_t)max_seq_len > (int64_t)max_pages_per_seq * fmt->block_size))
         return KVQ_ERR_SHAPE;
     if ((uintptr_t)seq_lens & 3u) return KVQ_ERR_ALIGN;
     const int32_t pps = pages_per_split ? pages_per_split
@@ -115,6 +129,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     a.rotated = fp16 ? 0 : 1;
     a.k_bits = fmt->k_bits;
     a.v_bits = fmt->v_bits;
+    a.page_log2s = fp16 ? 0 : page_log2s(fmt);
     a.max_seq_len = max_seq_len;
     a.seq_lens = seq_lens;
     a.num_seqs = num_seqs;
@@ -246,6 +261,7 @@ kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const
     a.num_pages = num_pages;
     a.k_bits = fmt->k_bits;
     a.v_bits = fmt->v_bits;
+    a.page_log2s = is_fp16(fmt) ? 0 : page_log2s(fmt);
     return hip_status(is_fp16(fmt) ? kvq::launch_fp16_append(a, (hipStream_t)stream)
                                    : kvq::launch_append(a, (hipStream_t)stream));
 }

@@ -38,14 +38,16 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(AppendArgs a) {
 
     const int64_t slot = a.slots[tok];
     if (slot < 0) return;
-    const int64_t page = slot / kPage;
-    const int off = (int)(slot % kPage);
+    const int64_t page = slot >> (4 + a.page_log2s);                 // slot = page * page_tokens + t
+    const int t = (int)(slot & ((16 << a.page_log2s) - 1));
     if (page >= a.num_pages) return;
 
     const uint16_t *src = is_v ? a.value + tok * a.value_stride + (int64_t)head * kHeadDim
                                : a.key + tok * a.key_stride + (int64_t)head * kHeadDim;
-    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)Layout<KB, VB>::kBytes;
-    encode_group_fmt<KB, VB>(src, is_v, r, region, off);
+    // region t / 16 of the (page, head) run
+    uint8_t *region = a.cache + (((page * a.num_kv_heads + head) << a.page_log2s) + (t >> 4)) *
+                                    (int64_t)Layout<KB, VB>::kBytes;
+    encode_group_fmt<KB, VB>(src, is_v, r, region, t & 15);
 }
 
 // Groups per lane-kernel work-group: waves 0 and 1 encode the keys of 128
@@ -185,10 +187,12 @@ __global__ __launch_bounds__(256) void quantize_append_lanes(AppendArgs a) {
     const int head = (int)(rowi % a.num_kv_heads);
     const int64_t slot = a.slots[tok];
     if (slot < 0) return;
-    const int64_t page = slot / kPage;
-    const int off = (int)(slot % kPage);
+    const int64_t page = slot >> (4 + a.page_log2s);
+    const int t = (int)(slot & ((16 << a.page_log2s) - 1));
+    const int off = t & 15;
     if (page >= a.num_pages) return;
-    uint8_t *region = a.cache + (page * a.num_kv_heads + head) * (int64_t)Layout<KB, VB>::kBytes;
+    uint8_t *region = a.cache + (((page * a.num_kv_heads + head) << a.page_log2s) + (t >> 4)) *
+                                    (int64_t)Layout<KB, VB>::kBytes;
     if (wave >> 1)
         encode_lane<KB, VB, true>(a.value + tok * a.value_stride + (int64_t)head * kHeadDim, region, off);
     else

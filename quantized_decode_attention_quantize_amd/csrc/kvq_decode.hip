@@ -299,7 +299,7 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
     }
 }
 
-template <int KB, int VB, bool kMQ>
+template <int KB, int VB, bool kMQ, bool kPaged>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     using Lay = Layout<KB, VB>;
     int split, kvh, hg, b;
@@ -339,8 +339,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     {
         const int last = a.bt_stride - 1;
         const int pa = split * a.pages_per_split + 2 * (wave + kWaves * lane);
-        bt_a = bt[pa < last ? pa : last];
-        bt_b = bt[pa + 1 < last ? pa + 1 : last];
+        // with pages of several 16-token regions, entry pa >> log2s holds region pa
+        const int ea = kPaged ? pa >> a.page_log2s : pa;
+        const int eb = kPaged ? (pa + 1) >> a.page_log2s : pa + 1;
+        bt_a = bt[ea < last ? ea : last];
+        bt_b = bt[eb < last ? eb : last];
     }
 
     const int max_len = a.max_seq_len;
@@ -368,17 +371,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
-    const int64_t head_off = (int64_t)kvh * Lay::kBytes;
-    const int64_t page_stride = (int64_t)a.num_kv_heads * Lay::kBytes;
+    const int log2s = kPaged ? a.page_log2s : 0;
+    const int64_t head_off = ((int64_t)kvh * Lay::kBytes) << log2s;
+    const int64_t page_stride = ((int64_t)a.num_kv_heads * Lay::kBytes) << log2s;
+    const int sub_mask = (1 << log2s) - 1;
 
     // A page id outside the pool is read as page 0: never an out-of-bounds
     // access (the output is unspecified under that precondition violation).
     const LaneOffsets<KB, VB> lo(lane);
     const uint32_t num_pages32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
-    auto region_of = [&](int32_t page_id) -> const uint8_t * {
+    // region of 16-token page pa (of the sequence) in block-table page page_id
+    auto region_of = [&](int32_t page_id, int pa) -> const uint8_t * {
         uint32_t id = (uint32_t)page_id;
         if (id >= num_pages32) id = 0;           // also catches negative ids
-        return a.cache + (int64_t)id * page_stride + head_off;
+        const uint8_t *r = a.cache + (int64_t)id * page_stride + head_off;
+        return kPaged ? r + (int64_t)(pa & sub_mask) * Lay::kBytes : r;
     };
 
     // Pairs of this split: the leading ones are full (both pages inside the
@@ -397,8 +404,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // registers, leaving the current pair's loads as the newest in flight).
     auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, int i) {
         const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
-        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j)), lo, A);
-        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j)), lo, B);
+        const int pa = kPaged ? p_begin + 2 * (wave + kWaves * j) : 0;
+        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j), pa), lo, A);
+        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1), lo, B);
         __builtin_amdgcn_sched_barrier(0);
     };
     // Fused append: a work-group whose split holds the sequence's last token
@@ -411,13 +419,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int pnew = pos / kPage;
         if (pnew >= p_begin && pnew < p_end) {
             if (wave == 0 && lane < 32) {
-                const uint32_t id = (uint32_t)bt[pnew];
+                const uint32_t id = (uint32_t)bt[kPaged ? pnew >> log2s : pnew];
                 if (id < num_pages32) {
                     const int is_v = lane >> 4;
                     const uint16_t *src = is_v
                         ? a.new_value + (int64_t)b * a.new_value_stride + (int64_t)kvh * kHeadDim
                         : a.new_key + (int64_t)b * a.new_key_stride + (int64_t)kvh * kHeadDim;
-                    uint8_t *region = const_cast<uint8_t *>(a.cache) + (int64_t)id * page_stride + head_off;
+                    uint8_t *region = const_cast<uint8_t *>(region_of((int32_t)id, pnew));
                     encode_group_fmt<KB, VB>(src, is_v, lane & 15, region, pos % kPage);
                 }
             }
@@ -560,8 +568,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const bool has_b = pa + 1 < p_end;
         const int j = i / kWaves;               // the pair's lane in bt_a / bt_b
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
-        load_page(region_of(id_a), lo, tA);
-        load_page(region_of(has_b ? __builtin_amdgcn_readlane(bt_b, j) : id_a), lo, tB);
+        load_page(region_of(id_a, pa), lo, tA);
+        load_page(has_b ? region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1) : region_of(id_a, pa), lo, tB);
         const int tok_b = has_b ? (pa + 1) * kPage : n_tokens;
         if (nk == 0)
             process_pair<KB, VB, true, true>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
@@ -652,7 +660,7 @@ int resident_workgroups() {
     if (cached[dev] > 0) return cached[dev];
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false>, 256, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -661,7 +669,7 @@ int resident_workgroups() {
     return cached[dev];
 }
 
-template <int KB, int VB, bool kMQ>
+template <int KB, int VB, bool kMQ, bool kPaged>
 hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
     if (kMQ) {
@@ -672,18 +680,21 @@ hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const La
         grid = dim3((unsigned)blocks, 1, 1);
     }
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ>), grid, dim3(256), 0, stream, ev.start,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged>), grid, dim3(256), 0, stream, ev.start,
                               ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 // One query row per sequence, or several (causal among them).
 template <int KB, int VB>
 hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
-    return a.q_len > 1 ? launch_split_kernel<KB, VB, true>(a, stream, ev)
-                       : launch_split_kernel<KB, VB, false>(a, stream, ev);
+    if (a.page_log2s > 0)
+        return a.q_len > 1 ? launch_split_kernel<KB, VB, true, true>(a, stream, ev)
+                           : launch_split_kernel<KB, VB, false, true>(a, stream, ev);
+    return a.q_len > 1 ? launch_split_kernel<KB, VB, true, false>(a, stream, ev)
+                       : launch_split_kernel<KB, VB, false, false>(a, stream, ev);
 }
 
 }  // namespace

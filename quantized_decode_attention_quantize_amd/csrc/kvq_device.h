@@ -93,6 +93,7 @@ struct AppendArgs {
     int64_t num_pages;
     int32_t k_bits;    // 4 or 8
     int32_t v_bits;    // 2 or 4
+    int32_t page_log2s;   // pages of 16 << page_log2s tokens: 2^page_log2s 16-token regions each
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
@@ -122,6 +123,8 @@ struct DecodeArgs {
     float alpha;              // softmax_scale * log2(e) / 128
     float *partials;          // [num_seqs][num_q_heads][splits][132]
     int32_t k_bits, v_bits;   // quantised cache: 4|8, 2|4 (16, 16: fp16 baseline)
+    int32_t page_log2s;       // block-table pages of 16 << page_log2s tokens, each a run of
+                              // 2^page_log2s 16-token regions per KV head (0: 16-token pages)
     int32_t rotated;          // 1: quantised (Hadamard epilogue); 0: fp16 baseline
     int32_t slot_offset;      // partial of split s goes to slot slot_offset + s ...
     int32_t slot_stride;      // ... of rows holding slot_stride slots each

@@ -43,7 +43,7 @@ def test_format_and_sizes():
     assert 3.0 <= ratio <= 5.0 and abs(ratio - 4.923) < 1e-3
     assert kvq.cache_bytes(10, 8) == 10 * 8 * 1664
     for bad in (kvq.Format(128, 128, 8, 8, 16), kvq.Format(128, 128, 2, 2, 16), kvq.Format(128, 64, 4, 2, 16),
-                kvq.Format(128, 128, 4, 2, 32)):
+                kvq.Format(128, 128, 4, 2, 48), kvq.Format(128, 128, 4, 2, 256), kvq.Format(128, 128, 16, 16, 32)):
         assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
         assert lib.kvq_cache_bytes(ctypes.byref(bad), 10, 8) == 0
 
@@ -276,3 +276,24 @@ def test_multi_query_validation_launches_nothing():
     assert call(out=None) == 1
     assert call(wsb=ws - 1) == 5                              # the workspace of q_len * Hq heads
     assert call(q=P(0x10008)) == 4
+
+
+@pytest.mark.parametrize("P", [16, 32, 64, 128])
+def test_page_sizes(P):
+    """Pages of P tokens: P / 16 regions per (page, KV head)."""
+    f = kvq.format_from_string("k4v2_g128", page_tokens=P)
+    assert f.block_size == P and kvq.page_bytes(f) == P // 16 * 1664
+    f84 = kvq.format_from_string("k8v4_g128", page_tokens=P)
+    assert kvq.page_bytes(f84) == P // 16 * 3200
+    with pytest.raises(kvq.KvqError):
+        kvq.format_from_string("fp16", page_tokens=32)
+    # max_seq_len may reach max_pages_per_seq * P
+    lib = kvq.load()
+    g = ctypes.c_void_p(0x10000)
+    ws = kvq.decode_workspace_bytes(2, 8, 2, 4 * P, fmt=f)
+    st = lib.kvq_decode_attention_ex(ctypes.byref(f), None, 1, g, g, 10, g, 4, g, 2, 8, 2, 4 * P, 0.088, g,
+                                     ws, 0, None)
+    assert st == 1                      # the sizes pass; the NULL output is reported
+    st = lib.kvq_decode_attention_ex(ctypes.byref(f), None, 1, g, g, 10, g, 4, g, 2, 8, 2, 4 * P + 1, 0.088, g,
+                                     ws, 0, None)
+    assert st == 2                      # 4 pages of P tokens hold at most 4 P

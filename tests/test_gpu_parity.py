@@ -947,3 +947,111 @@ def test_multi_query_decode_matches_oracle(dev, B, Hq, Hkv, lens, M, pps, fmt):
     one = kvq.decode_attention_mq(qd[:, -1:].contiguous(), cache, btd, ld, L, pages_per_split=pps, fmt=kf)
     plain = kvq.decode_attention(qd[:, -1].contiguous(), cache, btd, ld, L, pages_per_split=pps, fmt=kf)
     assert torch.equal(one[:, 0], plain)
+
+
+# --------------------------------------------------------------------------
+# Pages of 32, 64 and 128 tokens
+# --------------------------------------------------------------------------
+
+def _build_case_paged(dev, B, Hq, Hkv, lens, seed, P, fmt=(4, 2), append_last=True):
+    """Pool of P-token pages, the first lens[b] (or lens[b] - 1) tokens of every
+    sequence appended on the GPU and by the oracle."""
+    rng = np.random.default_rng(seed)
+    kf = kvq.format_from_string(f"k{fmt[0]}v{fmt[1]}_g128", page_tokens=P)
+    pb = kvq.page_bytes(kf)
+    pages = [-(-n // P) for n in lens]
+    N = sum(pages) + 2
+    perm = rng.permutation(N)
+    bt = np.full((B, max(pages) + 1), -1, np.int32)
+    o = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[o:o + p]
+        o += p
+    cache = torch.full((N, Hkv, pb), 0xFF, dtype=torch.uint8, device=dev)
+    pool = np.full((N, Hkv, pb), 0xFF, np.uint8)
+    kv = []
+    for b, n in enumerate(lens):
+        k = (rng.standard_normal((n, Hkv, D)) * rng.choice([0.5, 2])).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        k[:, :, rng.integers(0, D, 3)] *= 10
+        kv.append((k, v))
+        m = n if append_last else n - 1
+        if m > 0:
+            t = np.arange(m)
+            slots = bt[b, t // P].astype(np.int64) * P + t % P
+            gpu_append(torch.from_numpy(k[:m]).to(dev), torch.from_numpy(v[:m]).to(dev),
+                       torch.from_numpy(slots).to(dev), cache, fmt=kf)
+            oracle.quantize_append(k[:m], v[:m], slots, pool, fmt=fmt, page_tokens=P)
+    q = (rng.standard_normal((B, Hq, D)) * 1.5).astype(np.float16)
+    return cache, pool, bt, kv, q, kf
+
+
+@pytest.mark.parametrize("P,fmt,B,Hq,Hkv,lens", [
+    (32, (4, 2), 3, 8, 1, [100, 1, 257]),
+    (64, (4, 2), 2, 64, 8, [513, 77]),
+    (128, (8, 4), 2, 16, 2, [1000, 129]),
+    (64, (4, 4), 4, 12, 4, [64, 65, 127, 300]),
+])
+def test_paged_decode_matches_oracle(dev, P, fmt, B, Hq, Hkv, lens):
+    log(f"paged decode P={P} fmt={fmt} B={B} Hq={Hq} Hkv={Hkv} lens={lens}")
+    cache, pool, bt, _, q, kf = _build_case_paged(dev, B, Hq, Hkv, lens, seed=P + sum(lens), P=P, fmt=fmt)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    lens_np = np.asarray(lens, np.int64)
+    ref = oracle.decode_attention(pool, bt, lens_np, q, SCALE, fmt=fmt, page_tokens=P)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (0, 2, 6):            # splits of 2 or 6 regions cut pages of 32+ tokens
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=kf).cpu().numpy()
+        err = np.max(np.abs(out - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+    # several query rows on the same pool
+    M = 3
+    qm = (np.random.default_rng(P).standard_normal((B, M, Hq, D))).astype(np.float16)
+    refm = oracle.decode_attention_mq(pool, bt, lens_np, qm, SCALE, fmt=fmt, page_tokens=P)
+    outm = kvq.decode_attention_mq(torch.from_numpy(qm).to(dev), cache, btd, ld, L, fmt=kf).cpu().numpy()
+    assert np.max(np.abs(outm - refm)) <= TOL
+
+
+@pytest.mark.parametrize("P,H,T,seed", [(32, 3, 300, 1), (128, 8, 8200, 2), (64, 8, 9000, 3)])
+def test_paged_append_bit_exact(dev, P, H, T, seed):
+    """Both append kernels (the last two cases select the one-lane-per-group
+    kernel) at page sizes above 16, with skipped and out-of-pool slots."""
+    rng = np.random.default_rng(500 + seed)
+    log(f"paged append P={P} H={H} T={T}")
+    fmt = (4, 2) if seed != 3 else (8, 4)
+    kf = kvq.format_from_string(f"k{fmt[0]}v{fmt[1]}_g128", page_tokens=P)
+    pb = kvq.page_bytes(kf)
+    N = -(-T // P) + 3
+    k = _mixed_tokens(rng, T, H)
+    v = _mixed_tokens(rng, T, H)
+    slots = rng.permutation(N * P)[:T].astype(np.int64)
+    slots[rng.integers(0, T, 5)] = -1
+    slots[0] = N * P + 3
+    cache = torch.full((N, H, pb), 0x3C, dtype=torch.uint8, device=dev)
+    gpu_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(slots).to(dev), cache,
+               fmt=kf)
+    pool = np.full((N, H, pb), 0x3C, np.uint8)
+    ok = (slots >= 0) & (slots < N * P)
+    oracle.quantize_append(k[ok], v[ok], slots[ok], pool, fmt=fmt, page_tokens=P)
+    diff = np.argwhere(cache.cpu().numpy() != pool)
+    assert diff.size == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
+
+
+@pytest.mark.parametrize("P,pps", [(64, 0), (32, 2), (128, 4)])
+def test_paged_fused_append_decode(dev, P, pps):
+    B, Hq, Hkv, lens = 3, 16, 2, [400, 33, 777]
+    log(f"paged fused append P={P} pps={pps}")
+    cache, pool, bt, kv, q, kf = _build_case_paged(dev, B, Hq, Hkv, lens, seed=P * 3 + pps, P=P,
+                                                   append_last=False)
+    new_k = np.stack([kv[b][0][n - 1] for b, n in enumerate(lens)])
+    new_v = np.stack([kv[b][1][n - 1] for b, n in enumerate(lens)])
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out = kvq.append_decode_attention(torch.from_numpy(new_k).to(dev), torch.from_numpy(new_v).to(dev), qd, cache,
+                                      btd, ld, max(lens), pages_per_split=pps, fmt=kf).cpu().numpy()
+    last = np.array([bt[b, (n - 1) // P] * P + (n - 1) % P for b, n in enumerate(lens)], np.int64)
+    oracle.quantize_append(new_k, new_v, last, pool, page_tokens=P)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention(pool, bt, np.asarray(lens), q, SCALE, page_tokens=P)
+    assert np.max(np.abs(out - ref)) <= TOL
