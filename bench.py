@@ -375,8 +375,9 @@ def main():
         result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
 
     if not args.no_presets:
-        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p)
-                             for p in ("k4v4_g128", "k8v2_g128", "k8v4_g128")]
+        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt)
+                             for p, pt in (("k4v4_g128", 16), ("k8v2_g128", 16), ("k8v4_g128", 16),
+                                           ("k4v2_g128", 32), ("k4v2_g128", 64), ("k4v2_g128", 128))]
 
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
@@ -481,24 +482,33 @@ def multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, 
     return res
 
 
-def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset):
+def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16):
     """The benchmark step (fused append + decode split kernel, then the
-    combine) on the same workload with another preset's bit widths; the split
-    kernel alone is then timed back to back between two events."""
+    combine) on the same workload with another preset's bit widths or page
+    size; the split kernel alone is then timed back to back between two
+    events."""
+    import numpy as np
     w = inp.workload("qwen3_32b_16k")
     B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
     ctx, n = w.context, w.context + 1
-    fmt = kvq.format_from_string(preset)
+    fmt = kvq.format_from_string(preset, page_tokens=page_tokens)
     region = kvq.page_bytes(fmt)
-    bt_np, num_pages = inp.page_table(w)
+    if page_tokens == 16:
+        bt_np, num_pages = inp.page_table(w)
+    else:        # a random permutation of pages of page_tokens tokens
+        per_seq = -(-n // page_tokens)
+        num_pages = B * per_seq
+        perm = np.random.default_rng(20260605 + page_tokens).permutation(num_pages).astype(np.int32)
+        bt_np = perm.reshape(B, per_seq)
     bt = torch.from_numpy(bt_np).to(dev)
     lens = torch.full((B,), n, dtype=torch.int32, device=dev)
     base = torch.zeros((num_pages, Hkv, region), dtype=torch.uint8, device=dev)
     nk, nv = [], []
     for b in range(B):
         k, v = inp.sequence_kv(w, b, 0, n, device=dev)
-        kvq.quantize_append(k[:ctx], v[:ctx], torch.from_numpy(inp.slot_mapping(bt_np, b, 0, ctx)).to(dev), base,
-                            fmt=fmt)
+        t = np.arange(ctx)
+        slots = bt_np[b, t // page_tokens].astype(np.int64) * page_tokens + t % page_tokens
+        kvq.quantize_append(k[:ctx], v[:ctx], torch.from_numpy(slots).to(dev), base, fmt=fmt)
         nk.append(k[ctx:])
         nv.append(v[ctx:])
         del k, v
@@ -536,7 +546,8 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset):
     per_token_head = 16 * (fmt.k_bits + fmt.v_bits) + 8
     kv_bytes = B * n * Hkv * per_token_head
     del pools, base
-    return {"preset": preset, "bytes_per_token_head": per_token_head, "ms_per_step": round(ms, 5),
+    return {"preset": preset, "page_tokens": page_tokens, "bytes_per_token_head": per_token_head,
+            "ms_per_step": round(ms, 5),
             "step_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "split_kernel_ms": round(kern, 5),
             "kernel_GBps": round(kv_bytes / (kern * 1e-3) / 1e9, 2),
             "kernel_pct_hbm_peak": round(100 * kv_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
