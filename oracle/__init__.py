@@ -120,6 +120,8 @@ def _load():
     lib.kvqo_decode_attention_mq_paged.argtypes = [ci, ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
                                                    ctypes.c_double, P]
     lib.kvqo_decode_attention_mq_paged.restype = ctypes.c_int
+    lib.kvqo_block_variant.argtypes = [P, ci, ci, ci, P, P]
+    lib.kvqo_block_variant.restype = None
     _lib = lib
     return lib
 
@@ -323,3 +325,17 @@ def attention_f64(k, v, q_f16, scale):
     _load().kvqo_attention_f64(_ptr(k), _ptr(v), k.shape[0], _ptr(q), q.shape[0], float(scale), _ptr(out))
     return out
 
+
+
+def block_variant(x_f16, bits: int, iters: int):
+    """Variance-normalisation variant on a block of tokens (see
+    kvqo_block_variant): x float16 [T][128] -> (codes uint8 [T][128], the
+    rebuilt original-domain block float64 [T][128]).  iters = 0 is the
+    per-token encoder."""
+    x = _c(x_f16, np.float16)
+    T = x.shape[0]
+    assert x.shape == (T, D)
+    codes = np.empty((T, D), np.uint8)
+    out = np.empty((T, D), np.float64)
+    _load().kvqo_block_variant(_ptr(x.view(np.uint16)), T, int(bits), int(iters), _ptr(codes), _ptr(out))
+    return codes, out

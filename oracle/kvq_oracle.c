@@ -786,3 +786,102 @@ void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const u
     free(kd);
     free(vd);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Variance-normalisation variants (a study, not part of the format).        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages name variance normalisation as stage 2 of the pipeline [KVARN-P
+ * stage 2; KVARN-HN] without a formula; the Persian page's wording reads as
+ * an iterative ("repeated") normalisation of the variance.  The format's
+ * reading (divide each group by its RMS) is inert in exact arithmetic, since
+ * min/max RTN is scale-equivariant.  These variants act on a block of T
+ * tokens (a page of one KV head, keys or values) and do change the codes:
+ *
+ *   Y = the rows' rotations (fp32 FWHT, as the encoder), r = 1, c = 1;
+ *   iters rounds of   c_j = RMS over t of Y_tj / r_t   (per channel)
+ *                     r_t = RMS over j of Y_tj / c_j   (per token)
+ *   (a Sinkhorn-style balancing of the block's second moments, fp64);
+ *   each row of Y / (r c) (fp32) then goes through the encoder's own steps
+ *   (RMS, min/max, RTN with ties to even, clamp), its metadata folds r_t in,
+ *   s_t = fp16(delta sigma r_t), z_t = fp16(m sigma r_t), and the column
+ *   scales are stored as fp16(c_j);
+ *   the block is rebuilt as  Y'_tj = c_j (s_t code_tj + z_t)  and returned
+ *   in the original domain, H Y' / 128, in fp64.
+ *
+ * iters = 0 is the per-token encoder (keys' zero offset): the same codes and
+ * metadata, bit for bit.  x: fp16 [T][128]; codes (optional): u8 [T][128];
+ * out: fp64 [T][128].
+ */
+void kvqo_block_variant(const uint16_t *x, int T, int bits, int iters, uint8_t *codes_out, double *out)
+{
+    const int L = (1 << bits) - 1;
+    float *Y = malloc(sizeof(float) * KVQO_D * (T > 0 ? T : 1));
+    double *r = malloc(sizeof(double) * (T > 0 ? T : 1));
+    double c[KVQO_D];
+    if (!Y || !r) { free(Y); free(r); return; }
+    for (int t = 0; t < T; t++) {
+        for (int i = 0; i < KVQO_D; i++) Y[t * KVQO_D + i] = kvqo_half_to_float(x[t * KVQO_D + i]);
+        kvqo_fwht_f32(Y + t * KVQO_D);
+        r[t] = 1.0;
+    }
+    for (int i = 0; i < KVQO_D; i++) c[i] = 1.0;
+    for (int it = 0; it < iters; it++) {
+        for (int j = 0; j < KVQO_D; j++) {
+            double ss = 0.0;
+            for (int t = 0; t < T; t++) { double v = Y[t * KVQO_D + j] / r[t]; ss += v * v; }
+            c[j] = ss > 0.0 ? sqrt(ss / T) : 1.0;
+        }
+        for (int t = 0; t < T; t++) {
+            double ss = 0.0;
+            for (int j = 0; j < KVQO_D; j++) { double v = Y[t * KVQO_D + j] / c[j]; ss += v * v; }
+            r[t] = ss > 0.0 ? sqrt(ss / KVQO_D) : 1.0;
+        }
+    }
+    double cs[KVQO_D];
+    for (int j = 0; j < KVQO_D; j++) cs[j] = iters > 0 ? kvqo_half_to_double(kvqo_float_to_half((float)c[j])) : 1.0;
+    for (int t = 0; t < T; t++) {
+        float y[KVQO_D], p[KVQO_D];
+        for (int j = 0; j < KVQO_D; j++)
+            y[j] = iters > 0 ? (float)(Y[t * KVQO_D + j] / (r[t] * c[j])) : Y[t * KVQO_D + j];
+        /* the encoder's steps on the (scaled) rotated row */
+        for (int j = 0; j < KVQO_D; j++) p[j] = y[j] * y[j];
+        for (int h = KVQO_D / 2; h >= 1; h >>= 1)
+            for (int j = 0; j < h; j++) p[j] = p[j] + p[j + h];
+        uint8_t code[KVQO_D];
+        memset(code, 0, sizeof(code));
+        float sm = 0.0f, zm = 0.0f;
+        if (p[0] != 0.0f) {
+            float sigma = sqrtf(p[0] * 0x1p-7f);
+            float rcp = 1.0f / sigma;
+            float yh[KVQO_D];
+            for (int j = 0; j < KVQO_D; j++) yh[j] = y[j] * rcp;
+            float m = yh[0], M = yh[0];
+            for (int j = 1; j < KVQO_D; j++) { if (yh[j] < m) m = yh[j]; if (yh[j] > M) M = yh[j]; }
+            float delta = 0.0f;
+            if (M != m) {
+                delta = (M - m) / (float)L;
+                float inv = (float)L / (M - m);
+                for (int j = 0; j < KVQO_D; j++) {
+                    float cc = rintf((yh[j] - m) * inv);
+                    code[j] = (uint8_t)(cc > (float)L ? L : (int)cc);
+                }
+            }
+            sm = delta * sigma;
+            zm = m * sigma;
+        }
+        /* fold the row scale into the fp16 metadata (exactly as the encoder when r = 1) */
+        uint16_t s16 = kvqo_float_to_half(iters > 0 ? (float)(sm * r[t]) : sm);
+        uint16_t z16 = kvqo_float_to_half(iters > 0 ? (float)(zm * r[t]) : zm);
+        if (z16 == 0x8000) z16 = 0;
+        double yt[KVQO_D];
+        for (int j = 0; j < KVQO_D; j++)
+            yt[j] = cs[j] * (kvqo_half_to_double(s16) * code[j] + kvqo_half_to_double(z16));
+        kvqo_hadamard_matvec_f64(yt, out + (int64_t)t * KVQO_D);
+        for (int j = 0; j < KVQO_D; j++) out[(int64_t)t * KVQO_D + j] /= 128.0;
+        if (codes_out) memcpy(codes_out + (int64_t)t * KVQO_D, code, KVQO_D);
+    }
+    free(Y);
+    free(r);
+}
