@@ -72,6 +72,8 @@ def parse():
                     help="skip the k4v4 / k8v2 / k8v4 presets on the same workload")
     ap.add_argument("--no-multi-query", action="store_true",
                     help="skip the multi-row (speculative draft) decode on the same cache")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the decode of the other workload shapes (Qwen3-4B, Qwen3-30B-A3B, Llama-3.1-70B)")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
@@ -368,6 +370,10 @@ def main():
     if not args.no_fp16_baseline:
         result["fp16_baseline"] = fp16_baseline(torch, inp, kvq, lib, dev, stream, args, ms_per_step)
 
+    if not args.no_workloads:
+        result["other_workloads"] = [workload_bench(torch, inp, kvq, lib, dev, stream, args, name)
+                                     for name in ("qwen3_4b_64k", "qwen3_30b_a3b_128k", "llama31_70b_128k")]
+
     if not args.no_multi_query:
         result["multi_query"] = multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, n)
 
@@ -442,6 +448,70 @@ def fp16_baseline(torch, inp, kvq, lib, dev, stream, args, k4v2_ms_per_step):
             "kernel_GBps": round(fp16_bytes / (kern * 1e-3) / 1e9, 2),
             "kernel_pct_hbm_peak": round(100 * fp16_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
             "k4v2_step_speedup": round(ms / k4v2_ms_per_step, 3)}
+
+
+def workload_bench(torch, inp, kvq, lib, dev, stream, args, name):
+    """Decode (split kernel + combine, no append) over another workload's K4V2
+    cache at full size, inputs resident in HBM; the split kernel alone is also
+    timed back to back.  The Llama-shaped prompt is one sequence of 131072
+    tokens; the others hold 4 x 131072 and 32 ragged sequences of 32K-64K."""
+    import numpy as np
+    w = inp.workload(name)
+    B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
+    lens_np = inp.seq_lens(w)
+    bt_np, num_pages = inp.page_table(w)
+    fmt = kvq.format_from_string("k4v2_g128")
+    cache = torch.zeros((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    for b in range(B):
+        n = int(lens_np[b])
+        for s0 in range(0, n, 32768):          # bounded chunks of generated fp16 rows
+            cnt = min(32768, n - s0)
+            k, v = inp.sequence_kv(w, b, s0, cnt, device=dev)
+            kvq.quantize_append(k, v, torch.from_numpy(inp.slot_mapping(bt_np, b, s0, cnt)).to(dev), cache)
+            del k, v
+    pools = [cache]
+    kv_bytes = int(lens_np.sum()) * Hkv * KV_BYTES_PER_TOKEN_HEAD
+    if kv_bytes < 3 * (256 << 20):             # keep the pools beyond the 256 MB cache
+        pools += [cache.clone() for _ in range(-(-3 * (256 << 20) // kv_bytes) - 1)]
+    bt = torch.from_numpy(bt_np).to(dev)
+    lens = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    q = inp.queries(w, 0, device=dev).contiguous()
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    ws = kvq.alloc_workspace(B, Hq, Hkv, L)
+    call = DecodeCall(kvq, lib, fmt, stream.cuda_stream)
+    part = [call.partials_args(q, p, bt, lens, L, ws, 0) for p in pools]
+    comb = call.combine_args(out, lens, Hq, Hkv, L, ws, 0)
+    pf, cfn = lib.kvq_decode_partials, lib.kvq_decode_combine
+    for i in range(5):
+        pf(*part[i % len(pools)]); cfn(*comb)
+    torch.cuda.synchronize()
+    steps = max(20, args.steps // 4)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if pf(*part[i % len(pools)]) | cfn(*comb):
+            raise RuntimeError(f"{name} decode failed")
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    hev = HipEvents(2)
+    nl = max(1, args.kernel_launches // 4)
+    hev.record(0, stream.cuda_stream)
+    bad = 0
+    for i in range(nl):
+        bad |= pf(*part[i % len(pools)])
+    hev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError(f"{name} decode failed")
+    kern = hev.elapsed_ms(0, 1) / nl
+    hev.close()
+    del pools, cache
+    return {"workload": name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "tokens": int(lens_np.sum()), "kv_bytes": kv_bytes, "ms_per_call": round(ms, 5),
+            "call_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "split_kernel_ms": round(kern, 5),
+            "kernel_GBps": round(kv_bytes / (kern * 1e-3) / 1e9, 2),
+            "kernel_pct_hbm_peak": round(100 * kv_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "pages_per_split": kvq.decode_pages_per_split(B, Hq, Hkv, L)}
 
 
 def multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, n):

@@ -647,6 +647,88 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     finalize_head(o4, l, z, l32, a.out, a.out_f32, orow, a.rotated);
 }
 
+// The combine for rows of many split slots (more than 8): one work-group per
+// row; thread (g, c) with split group g = tid / 32 and channel quad c merges
+// splits g, g + 8, g + 16, ... (issuing every load at once: one memory round
+// trip, where the row-per-32-lanes kernel above takes one per 8 splits), then
+// the 8 split groups merge in LDS and group 0 applies the epilogue.
+constexpr int kWideGroups = 8;
+constexpr int kWideMaxPerGroup = 8;   // up to 64 slots in one round
+
+__global__ __launch_bounds__(256) void combine_wide_kernel(DecodeArgs a) {
+    const int tid = threadIdx.x;
+    const int l32 = tid & 31;
+    const int grp = tid >> 5;
+    const int64_t row = blockIdx.x;
+    const int nsplit = a.slot_stride;
+    const float *base = a.partials + row * a.slot_stride * kPartialFloats;
+    const int c0 = 4 * l32;
+    float M = -INFINITY, l = 0.0f, z = 0.0f;
+    float o4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = grp; s0 < nsplit; s0 += kWideGroups * kWideMaxPerGroup) {
+        float4 meta[kWideMaxPerGroup], v[kWideMaxPerGroup];
+#pragma unroll
+        for (int u = 0; u < kWideMaxPerGroup; u++) {
+            const int sp0 = s0 + u * kWideGroups;
+            const int sp = sp0 < nsplit ? sp0 : grp;    // in range; duplicates get weight 0
+            meta[u] = *reinterpret_cast<const float4 *>(base + sp * kPartialFloats);
+            v[u] = *reinterpret_cast<const float4 *>(base + sp * kPartialFloats + 4 + c0);
+        }
+        float mc = M;
+#pragma unroll
+        for (int u = 0; u < kWideMaxPerGroup; u++)
+            mc = s0 + u * kWideGroups < nsplit ? fmaxf(mc, meta[u].x) : mc;
+        if (mc != M) {
+            const float f = M == -INFINITY ? 0.0f : fast_exp2(M - mc);
+            l *= f;
+            z *= f;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o4[e] *= f;
+            M = mc;
+        }
+#pragma unroll
+        for (int u = 0; u < kWideMaxPerGroup; u++) {
+            const bool live = s0 + u * kWideGroups < nsplit && meta[u].x != -INFINITY;
+            const float f = live ? fast_exp2(meta[u].x - M) : 0.0f;
+            l += f * meta[u].y;
+            z += f * meta[u].z;
+            o4[0] += f * v[u].x;
+            o4[1] += f * v[u].y;
+            o4[2] += f * v[u].z;
+            o4[3] += f * v[u].w;
+        }
+    }
+    __shared__ float s_m[kWideGroups], s_l[kWideGroups], s_z[kWideGroups];
+    __shared__ float s_acc[kWideGroups][kHeadDim];
+    if (l32 == 0) {
+        s_m[grp] = M;
+        s_l[grp] = l;
+        s_z[grp] = z;
+    }
+    *reinterpret_cast<float4 *>(&s_acc[grp][c0]) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+    __syncthreads();
+    if (grp != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int g2 = 0; g2 < kWideGroups; g2++) Mt = fmaxf(Mt, s_m[g2]);
+    float lt = 0.0f, zt = 0.0f, acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g2 = 0; g2 < kWideGroups; g2++) {
+        const float mw = s_m[g2];
+        const float f = mw == -INFINITY ? 0.0f : fast_exp2(mw - Mt);
+        lt += f * s_l[g2];
+        zt += f * s_z[g2];
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc4[e] += f * s_acc[g2][c0 + e];
+    }
+    int64_t orow = row;
+    if (a.q_len > 1) {
+        const int bb = (int)(row / a.num_q_heads), vv = (int)(row % a.num_q_heads);
+        orow = io_row<true>(a, bb, vv / a.gqa, vv % a.gqa);
+    }
+    finalize_head(acc4, lt, zt, l32, a.out, a.out_f32, orow, a.rotated);
+}
+
 // Work-groups of decode_kernel<KB, VB> the current device holds at once
 // (compute units x occupancy), queried once per device; 512 without a device.
 template <int KB, int VB>
@@ -717,6 +799,11 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const La
 
 hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+    if (a.slot_stride > 8) {     // many slots per row: one work-group per row, one round of loads
+        if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(combine_wide_kernel, dim3((unsigned)rows), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t blocks = (rows + 2 * kWaves - 1) / (2 * kWaves);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
