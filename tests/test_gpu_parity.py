@@ -1055,3 +1055,50 @@ def test_paged_fused_append_decode(dev, P, pps):
     assert np.array_equal(cache.cpu().numpy(), pool)
     ref = oracle.decode_attention(pool, bt, np.asarray(lens), q, SCALE, page_tokens=P)
     assert np.max(np.abs(out - ref)) <= TOL
+
+
+def test_pool_beyond_4_gib(dev):
+    """Page ids whose byte offsets exceed 2^32 (a 4.4 GB pool of 8-head
+    pages): append and decode address them with 64-bit arithmetic.  Only a
+    few pages at the top of the pool are used; the oracle gets them
+    relabelled to a small pool."""
+    Hkv, Hq, B = 8, 64, 2
+    num_pages = (5 << 30) // (Hkv * 1664)               # ~5 GiB
+    lens = [100, 37]
+    rng = np.random.default_rng(4096)
+    log(f"pool beyond 4 GiB: {num_pages} pages")
+    cache = torch.empty((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    top = np.arange(num_pages - 12, num_pages, dtype=np.int32)
+    rng.shuffle(top)
+    pages = [-(-n // 16) for n in lens]
+    bt = np.full((B, max(pages)), -1, np.int32)
+    bt[0, :pages[0]] = top[:pages[0]]
+    bt[1, :pages[1]] = top[pages[0]:pages[0] + pages[1]]
+    assert int(bt.max()) * Hkv * 1664 > (1 << 32)
+    small = {int(p): i for i, p in enumerate(top)}
+    bt_small = np.vectorize(lambda p: small.get(int(p), -1))(bt).astype(np.int32)
+    pool = np.zeros((len(top), Hkv, 1664), np.uint8)
+    for b, n in enumerate(lens):
+        k = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((n, Hkv, D)).astype(np.float16)
+        gpu_append(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                   torch.from_numpy(inp.slot_mapping(bt, b, 0, n)).to(dev), cache)
+        oracle.quantize_append(k, v, inp.slot_mapping(bt_small, b, 0, n), pool)
+    got = cache[torch.from_numpy(top.astype(np.int64)).to(dev)].cpu().numpy()
+    used = np.zeros(len(top), bool)
+    used[[small[int(p)] for p in bt[bt >= 0]]] = True
+    for i in np.nonzero(used)[0]:
+        r = 0
+        # compare the written token slots only (the rest of the pool is uninitialised)
+        b = 0 if top[i] in bt[0] else 1
+        j = list(bt[b]).index(top[i])
+        r = min(16, lens[b] - 16 * j)
+        m = valid_byte_mask(r)
+        assert np.array_equal(got[i][:, m], pool[i][:, m])
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    out = kvq.decode_attention(torch.from_numpy(q).to(dev), cache, torch.from_numpy(bt).to(dev),
+                               torch.tensor(lens, dtype=torch.int32, device=dev), max(lens)).cpu().numpy()
+    ref = oracle.decode_attention(pool, bt_small, np.array(lens), q, SCALE)
+    assert np.max(np.abs(out - ref)) <= TOL
+    del cache
+    torch.cuda.empty_cache()
