@@ -49,6 +49,14 @@
 // device-scope release and acquire per work-group, i.e. a write-back and an
 // invalidate of the XCD's L2 each time; measured, that cost several times
 // the whole page stream.)
+//
+// Variants, all instantiations of the same kernel template: 8-bit keys and
+// 4-bit values (KB, VB: other key-operand and value-operand unpacking, the
+// same algebra); several causal query rows per sequence (kMQ: (row, head)
+// pairs take the MFMA columns, per-lane token limits in the masked tail
+// pairs, an XCD-aware grid); pages of 32-128 tokens (kPaged: a block-table
+// entry covers several 16-token regions).  The K4V2 single-row 16-token
+// instantiation is the hot path above.
 #include <hip/hip_ext.h>
 #include <math.h>
 

@@ -14,7 +14,7 @@ constexpr float kLazyThreshold = 8.0f;   // log2 of the largest unnormalised wei
 struct State {
     float m;        // running max (base 2) of this lane's column
     float l;        // partial sum of weights over this lane's tokens
-    float z;        // partial sum of weight * value mean (K4V2 only)
+    float z;        // partial sum of weight * value mean (quantised caches)
     v4f acc[8];     // value accumulators, channel 16j + 4g + i, column n
 };
 

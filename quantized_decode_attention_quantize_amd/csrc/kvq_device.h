@@ -1,8 +1,8 @@
 // Internal definitions of libkvq (gfx950).  Not part of the public ABI.
 //
-// Cache format "kvq-k4v2-g128 v1": one 1664-byte region per (page, KV head);
-// 16 tokens per page; 128 channels per head; see include/kvq.h for the layout.
-// The same layout family holds 8-bit keys and 4-bit values (Layout below).
+// Cache format "kvq-k4v2-g128 v1": one 1664-byte region per 16 tokens of one
+// KV head; 128 channels per head; see include/kvq.h for the layout.  The same
+// layout family holds 8-bit keys and 4-bit values (Layout below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,11 +12,6 @@ namespace kvq {
 
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
-constexpr int kRegion = 1664;
-constexpr int kKCodes = 0;      // token o: 64 bytes at 64*o
-constexpr int kVCodes = 1024;   // quad g, slot i, m: u16 at 1024 + 128g + 8m + 2i
-constexpr int kKMeta = 1536;    // token o: (s, z) fp16 at 1536 + 4o
-constexpr int kVMeta = 1600;    // token o: (s, z) fp16 at 1600 + 4o
 
 // Region of KB-bit keys (4 or 8) and VB-bit values (2 or 4): key codes (16
 // tokens x 16 KB bytes, token-major), value codes (16 x 16 VB bytes), key and
@@ -32,6 +27,12 @@ struct Layout {
     static constexpr int kKL = (1 << KB) - 1;   // largest key code
     static constexpr int kVL = (1 << VB) - 1;   // largest value code
 };
+// K4V2: key codes [0, 1024) (token o at 64 o), value codes [1024, 1536) (the
+// u16 of quad g, channel m, slot i at 1024 + 128 g + 8 m + 2 i), key (s, z)
+// at 1536 + 4 o, value (s, mu) at 1600 + 4 o.
+static_assert(Layout<4, 2>::kVCodes == 1024 && Layout<4, 2>::kKMeta == 1536 && Layout<4, 2>::kVMeta == 1600 &&
+                  Layout<4, 2>::kBytes == 1664,
+              "the K4V2 region");
 
 // Decode work decomposition.
 constexpr int kWaves = 4;           // waves per work-group
