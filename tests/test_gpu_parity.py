@@ -1102,3 +1102,25 @@ def test_pool_beyond_4_gib(dev):
     assert np.max(np.abs(out - ref)) <= TOL
     del cache
     torch.cuda.empty_cache()
+
+
+def test_checkpoint_and_resume(dev):
+    """The cache state is the caller's byte pool plus block tables: a pool
+    dumped to host memory and loaded into a fresh device buffer decodes to the
+    same bits, and keeps accepting appends exactly as the original."""
+    B, Hq, Hkv, lens = 2, 16, 2, [300, 77]
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=31)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    before = kvq.decode_attention(qd, cache, btd, ld, max(lens)).cpu()
+    host = cache.cpu().numpy().copy()                       # checkpoint
+    restored = torch.from_numpy(host).to(dev)               # resume into a new buffer
+    assert torch.equal(kvq.decode_attention(qd, restored, btd, ld, max(lens)).cpu(), before)
+    # one more token per sequence into both: identical bytes
+    rng = np.random.default_rng(32)
+    kn = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float16)).to(dev)
+    vn = torch.from_numpy(rng.standard_normal((B, Hkv, D)).astype(np.float16)).to(dev)
+    slots = torch.tensor([int(bt[b, n // 16]) * 16 + n % 16 for b, n in enumerate(lens)], device=dev)
+    gpu_append(kn, vn, slots, cache)
+    gpu_append(kn, vn, slots, restored)
+    assert torch.equal(cache.cpu(), restored.cpu())
