@@ -76,6 +76,8 @@ def parse():
                     help="skip the labelled warm-cache timing of the split kernel")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the decode of the other workload shapes (Qwen3-4B, Qwen3-30B-A3B, Llama-3.1-70B)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the measured streaming-read ceiling (kvq_stream_read_probe)")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
@@ -186,6 +188,45 @@ class DecodeCall:
                 ctypes.c_int32(lens.numel()), ctypes.c_int32(num_q_heads), ctypes.c_int32(num_kv_heads),
                 ctypes.c_int32(max_len), P(ws.data_ptr()), ctypes.c_size_t(ws.numel()), ctypes.c_int32(pps),
                 self.stream)
+
+
+def read_ceiling(torch, lib, dev, stream, nbytes, copies, launches):
+    """The plain streaming-read rate of this device (kvq_stream_read_probe):
+    `copies` buffers of the decode's KV bytes read in turn, back to back (the
+    same rotation through more memory than the 256 MB Infinity Cache holds
+    as the decode's pool copies), and a 2 GiB read for the steady state."""
+    nb = (nbytes + 15) // 16 * 16
+    bufs = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    big = torch.zeros(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fn = lib.kvq_stream_read_probe
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    args = [(P(b.data_ptr()), ctypes.c_size_t(nb), P(sink.data_ptr()), sp) for b in bufs]
+    big_args = (P(big.data_ptr()), ctypes.c_size_t(big.numel()), P(sink.data_ptr()), sp)
+    torch.cuda.synchronize()
+    bad = 0
+    for i in range(5):
+        bad |= fn(*args[i % copies])
+    ev = HipEvents(4)
+    ev.record(0, stream.cuda_stream)
+    for i in range(launches):
+        bad |= fn(*args[i % copies])
+    ev.record(1, stream.cuda_stream)
+    nbig = 10
+    for i in range(nbig):
+        bad |= fn(*big_args)
+    ev.record(2, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError("kvq_stream_read_probe failed")
+    us = ev.elapsed_ms(0, 1) / launches * 1e3
+    big_us = ev.elapsed_ms(1, 2) / nbig * 1e3
+    ev.close()
+    del bufs, big
+    return {"kernel": "stream_read_kernel", "bytes_per_launch": nb, "us_per_launch": round(us, 3),
+            "GBps": round(nb / us / 1e3, 1), "steady_2GiB_GBps": round((2 << 30) / big_us / 1e3, 1),
+            "launches": launches}
 
 
 def cpu_model() -> str:
@@ -369,6 +410,9 @@ def main():
         warm_ms = hw.elapsed_ms(0, 1) / nl
         hw.close()
     traffic, traffic_note = recorded_traffic()
+    ceiling = None
+    if not args.no_read_ceiling:
+        ceiling = read_ceiling(torch, lib, dev, stream, B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD, len(pools), nl)
 
     kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -393,6 +437,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "decode_kernel", "bytes_per_launch": kv_bytes, "traffic_note": traffic_note},
     }
+    if ceiling:
+        # the same bytes read front to back by a plain streaming kernel on this
+        # device: the rate the decode's page walk is measured against
+        ceiling["decode_frac_of_it"] = round(achieved / ceiling["GBps"], 4)
+        result["roofline"]["measured_read_ceiling"] = ceiling
 
     if ev_ms:
         result["kernel_events_in_steps"] = {

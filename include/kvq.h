@@ -400,6 +400,20 @@ int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,
  * (NULL, NULL) clears the hook.  Always returns KVQ_OK. */
 kvq_status kvq_set_split_kernel_events(void *start_event, void *stop_event);
 
+/* Measurement aid, not part of the decode path: one launch that reads
+ * `bytes` of device memory from `buffer` front to back (16-byte loads, two
+ * work-groups of 256 lanes per compute unit, grid-stride), so that a caller
+ * can time the plain streaming-read rate of the device the decode runs on
+ * and set the decode's bytes per second against it (decode moves the whole
+ * cache through HBM per token [KV-INFRA]).
+ *   buffer  (device) 16-byte aligned; bytes a positive multiple of 16
+ *           (at most 2^40; else KVQ_ERR_SHAPE).
+ *   sink    (device) one uint32, written only in the rare case that the
+ *           XOR of everything read equals a fixed constant (it keeps the
+ *           loads from being optimised away); may hold anything.
+ * Nothing is allocated; the call is enqueued on `stream`. */
+kvq_status kvq_stream_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kvq_status_string(kvq_status status);
 

@@ -33,6 +33,7 @@ SOURCES = {
     "kvq_decode.hip": [],
     "kvq_fp16.hip": [],
     "kvq_api.hip": [],
+    "kvq_probe.hip": [],
 }
 
 

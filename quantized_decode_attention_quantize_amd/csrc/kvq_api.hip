@@ -5,6 +5,7 @@
 
 #include "../../include/kvq.h"
 #include "kvq_device.h"
+#include "kvq_probe.h"
 
 namespace {
 
@@ -468,6 +469,13 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype 
     return kvq_decode_attention_ex(fmt, out, out_dtype, query, cache, num_pages, block_tables,
                                    max_pages_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
                                    max_seq_len, softmax_scale, workspace, workspace_bytes, 0, stream);
+}
+
+kvq_status kvq_stream_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buffer || !sink) return KVQ_ERR_NULL;
+    if (bytes == 0 || (bytes % 16) || bytes > ((size_t)1 << 40)) return KVQ_ERR_SHAPE;
+    if (!aligned16(buffer) || ((uintptr_t)sink & 3u)) return KVQ_ERR_ALIGN;
+    return hip_status(kvq::launch_stream_read(buffer, (int64_t)bytes, sink, (hipStream_t)stream));
 }
 
 kvq_status kvq_set_split_kernel_events(void *start_event, void *stop_event) {

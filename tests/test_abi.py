@@ -297,3 +297,16 @@ def test_page_sizes(P):
     st = lib.kvq_decode_attention_ex(ctypes.byref(f), None, 1, g, g, 10, g, 4, g, 2, 8, 2, 4 * P + 1, 0.088, g,
                                      ws, 0, None)
     assert st == 2                      # 4 pages of P tokens hold at most 4 P
+
+
+def test_stream_read_probe_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g = P(0x10000)
+    assert lib.kvq_stream_read_probe(None, 16, g, None) == 1
+    assert lib.kvq_stream_read_probe(g, 16, None, None) == 1
+    assert lib.kvq_stream_read_probe(g, 0, g, None) == 2
+    assert lib.kvq_stream_read_probe(g, 24, g, None) == 2
+    assert lib.kvq_stream_read_probe(g, (1 << 40) + 16, g, None) == 2
+    assert lib.kvq_stream_read_probe(P(0x10008), 16, g, None) == 4
+    assert lib.kvq_stream_read_probe(g, 16, P(0x10002), None) == 4

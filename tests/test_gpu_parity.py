@@ -408,6 +408,30 @@ def test_split_kernel_events_hook(dev):
     hip.hipEventDestroy(e1)
 
 
+@pytest.mark.parametrize("n16", [1, 7, 4096, 1000003])
+def test_stream_read_probe_reads_every_word(dev, n16):
+    """kvq_stream_read_probe (the bench's measured read ceiling) reads every
+    16-byte word: one marked word anywhere in the buffer reaches the sink."""
+    lib = kvq.load()
+    buf = torch.zeros(n16 * 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    mark = np.int32(np.uint32(0x9E3779B9).view(np.int32))
+    log(f"stream read probe n16={n16}")
+    for w in sorted({0, 3, (n16 // 2) * 4 + 1, n16 * 4 - 1}):
+        buf.zero_()
+        sink.zero_()
+        buf[w] = int(mark)
+        st = lib.kvq_stream_read_probe(ctypes.c_void_p(buf.data_ptr()), n16 * 16,
+                                       ctypes.c_void_p(sink.data_ptr()), None)
+        assert st == 0
+        assert int(sink.cpu()[0]) == int(mark), f"word {w} not read"
+    buf.zero_()
+    sink.zero_()
+    assert lib.kvq_stream_read_probe(ctypes.c_void_p(buf.data_ptr()), n16 * 16,
+                                     ctypes.c_void_p(sink.data_ptr()), None) == 0
+    assert int(sink.cpu()[0]) == 0
+
+
 def test_decode_zero_query_gives_mean_value(dev):
     B, Hq, Hkv, lens = 1, 4, 1, [123]
     cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=9)
