@@ -171,6 +171,12 @@ def _stream_ptr(stream) -> ctypes.c_void_p:
 
 
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    """Device address of a tensor that lives on the current GPU (the kernels
+    dereference it on the device, so a host tensor is refused here)."""
+    if not t.is_cuda:
+        raise ValueError("kvq operates on GPU tensors; got a tensor on " + str(t.device))
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(t.data_ptr())
 
 

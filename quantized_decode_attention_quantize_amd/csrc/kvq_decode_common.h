@@ -18,10 +18,6 @@ struct State {
     v4f acc[8];     // value accumulators, channel 16j + 4g + i, column n
 };
 
-// Output of one head from merged sums: 32 lanes (lane32 = lane & 31) hold
-// channels 4*lane32 .. +3.  rotated (the K4V2 path): o_j = (H acc)_j / (128 l)
-// for j >= 1 and o_0 = z / l (the FWHT runs 2 stages in-lane and 5 across);
-// otherwise o = acc / l.  l = 0 gives a zero row.
 // In-place unnormalised Hadamard transform of one head's 128 values held by
 // 32 lanes (lane32 = lane & 31), 4 channels each: 2 stages in-lane, 5 across.
 __device__ __forceinline__ void hadamard_128(float (&y)[4], int lane32) {
@@ -42,6 +38,10 @@ __device__ __forceinline__ void hadamard_128(float (&y)[4], int lane32) {
     }
 }
 
+// Output of one head from merged sums: 32 lanes (lane32 = lane & 31) hold
+// channels 4*lane32 .. +3.  rotated (the K4V2 path): o_j = (H acc)_j / (128 l)
+// for j >= 1 and o_0 = z / l (the FWHT runs 2 stages in-lane and 5 across);
+// otherwise o = acc / l.  l = 0 gives a zero row.
 __device__ __forceinline__ void finalize_head(const float (&acc)[4], float l, float z, int lane32,
                                               void *out, int out_f32, int64_t row, int rotated) {
     float y[4] = {acc[0], acc[1], acc[2], acc[3]};

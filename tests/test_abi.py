@@ -310,3 +310,12 @@ def test_stream_read_probe_validation_launches_nothing():
     assert lib.kvq_stream_read_probe(g, (1 << 40) + 16, g, None) == 2
     assert lib.kvq_stream_read_probe(P(0x10008), 16, g, None) == 4
     assert lib.kvq_stream_read_probe(g, 16, P(0x10002), None) == 4
+
+
+def test_binding_refuses_host_tensors():
+    """The binding never hands a host pointer to a kernel."""
+    k = torch.zeros((1, 1, 128), dtype=torch.float16)
+    slots = torch.zeros(1, dtype=torch.int64)
+    cache = torch.zeros((1, 1, 1664), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kvq.quantize_append(k, k, slots, cache)
