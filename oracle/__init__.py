@@ -23,9 +23,10 @@ Functions and the passages they follow (pages cited by title and section):
   made of page_tokens / 16 consecutive 16-token regions (the variable page
   size the dothoosh.com page announces in its closing list).
 * ``fmt=(kbits, vbits)`` -- the same pipeline at the other bit widths the pages
-  report (8-bit keys with 4-bit values, 4-bit both: dzen.ru summary of the
-  vLLM TurboQuant post, sections on accuracy and memory); keys 4 or 8 bits,
-  values 2 or 4 bits.  The default (4, 2) is the KVarN preset.
+  report (8-bit keys with 4-bit values, 4-bit both, and 3-bit codes: dzen.ru
+  summary of the vLLM TurboQuant post, sections on accuracy and memory); keys
+  4 or 8 bits with values 2 or 4 bits, or 3 bits both (stored as bit
+  planes).  The default (4, 2) is the KVarN preset.
 """
 from __future__ import annotations
 

@@ -44,10 +44,12 @@
 
 /* Bit widths.  The pages name the KVarN preset with 4-bit keys and 2-bit
  * values, and report presets of other widths (8-bit keys with 4-bit values,
- * 4-bit both) as nearly lossless next to fp16 (dzen.ru summary of the vLLM
- * TurboQuant post, the sections on accuracy and on memory).  The same KVarN
- * pipeline is applied at those widths: keys take kbits in {4, 8}, values
- * vbits in {2, 4}.  A (page, KV head) region then holds, in this order:
+ * 4-bit both) as nearly lossless next to fp16, and 3-bit codes as
+ * noticeably worse (dzen.ru summary of the vLLM TurboQuant post, the sections
+ * on accuracy and on memory).  The same KVarN pipeline is applied at those
+ * widths: keys take kbits in {4, 8}, values vbits in {2, 4}, and 3 bits for
+ * both (kbits = vbits = 3).  A (page, KV head) region then holds, in this
+ * order:
  *   key codes    16 tokens x 16*kbits bytes   at 0
  *   value codes  16 tokens x 16*vbits bytes   at 256*kbits
  *   key (s, z)   16 tokens x 4 bytes          at 256*(kbits+vbits)
@@ -55,8 +57,24 @@
  * i.e. 256*(kbits+vbits) + 128 bytes (1664 at 4/2, a multiple of 128). */
 static int fmt_ok(int kbits, int vbits)
 {
-    return (kbits == 4 || kbits == 8) && (vbits == 2 || vbits == 4);
+    return ((kbits == 4 || kbits == 8) && (vbits == 2 || vbits == 4)) || (kbits == 3 && vbits == 3);
 }
+
+/* Little-endian u32 at p. */
+static void put_u32(uint8_t *p, uint32_t w)
+{
+    p[0] = (uint8_t)w; p[1] = (uint8_t)(w >> 8); p[2] = (uint8_t)(w >> 16); p[3] = (uint8_t)(w >> 24);
+}
+
+static uint32_t get_u32(const uint8_t *p)
+{
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+/* 3-bit codes are stored as bit planes: bit p (0, 1, 2) of every code of a
+ * set of channels in one word per plane.  Token slot i of a quad of 4 takes
+ * byte K3V3_SLOT_BYTE[i] of a value plane word. */
+static const int K3V3_SLOT_BYTE[4] = {0, 2, 1, 3};
 
 int64_t kvqo_region_bytes(int kbits, int vbits)
 {
@@ -281,12 +299,18 @@ void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
  *                code of channel c at bits kbits*c .. kbits*c+kbits-1 of the
  *                row, least significant bit first (4 bits: byte b = code[2b]
  *                | code[2b+1] << 4; 8 bits: byte c = code[c]).
+ *     3 bits (bit planes): for G = 0..3 and p = 0..2 the little-endian u32
+ *                at 12G + 4p of the 48-byte row holds, at bit x, bit p of
+ *                the code of channel 32G + x.
  *   value codes, for quad g = off/4, slot i = off%4 and channel c = 16j + m:
  *     2 bits: the 16-bit little-endian word at vbase + 128g + 8m + 2i holds
  *             the code of channel 16j + m in bits 2j..2j+1 (j = 0..7);
  *     4 bits: with j = 4h + k (h = 0, 1; k = 0..3), the 16-bit word at
  *             vbase + 256g + 16m + 8(i/2) + 4h + 2(i%2) holds the code of
- *             channel 16j + m in bits 4k..4k+3.
+ *             channel 16j + m in bits 4k..4k+3;
+ *     3 bits (bit planes): byte K3V3_SLOT_BYTE[i] of the little-endian u32 at
+ *             vbase + 12(16g + m) + 4p holds, at bit j, bit p of the code of
+ *             channel 16j + m.
  *   metadata:    fp16 s then fp16 offset, little-endian, 4 bytes per token at
  *                kmeta + 4*off (keys) and kmeta + 64 + 4*off (values).
  * (vbase = 256*kbits, kmeta = 256*(kbits+vbits).) */
@@ -299,13 +323,31 @@ void kvqo_store_token_fmt(int kbits, int vbits, uint8_t *region, int off,
 
     uint8_t *kb = region + 16 * kbits * off;
     memset(kb, 0, (size_t)(16 * kbits));
-    for (int c = 0; c < KVQO_D; c++) {
-        int bit = kbits * c;
-        kb[bit / 8] |= (uint8_t)((kc[c] & kmask) << (bit % 8));
+    if (kbits == 3) {
+        for (int G = 0; G < 4; G++)
+            for (int p = 0; p < 3; p++) {
+                uint32_t w = 0;
+                for (int x = 0; x < 32; x++)
+                    w |= (uint32_t)((kc[32 * G + x] >> p) & 1u) << x;
+                put_u32(kb + 12 * G + 4 * p, w);
+            }
+    } else {
+        for (int c = 0; c < KVQO_D; c++) {
+            int bit = kbits * c;
+            kb[bit / 8] |= (uint8_t)((kc[c] & kmask) << (bit % 8));
+        }
     }
 
     int g = off / 4, i = off % 4;
-    if (vbits == 2) {
+    if (vbits == 3) {
+        for (int m = 0; m < 16; m++)
+            for (int p = 0; p < 3; p++) {
+                unsigned b = 0;
+                for (int j = 0; j < 8; j++)
+                    b |= ((vc[16 * j + m] >> p) & 1u) << j;
+                region[vbase + 12 * (16 * g + m) + 4 * p + K3V3_SLOT_BYTE[i]] = (uint8_t)b;
+            }
+    } else if (vbits == 2) {
         for (int m = 0; m < 16; m++) {
             unsigned w = 0;
             for (int j = 0; j < 8; j++)
@@ -343,12 +385,30 @@ void kvqo_load_token_fmt(int kbits, int vbits, const uint8_t *region, int off,
     const unsigned kmask = (1u << kbits) - 1, vmask = (1u << vbits) - 1;
 
     const uint8_t *kb = region + 16 * kbits * off;
-    for (int c = 0; c < KVQO_D; c++) {
-        int bit = kbits * c;
-        kc[c] = (uint8_t)((kb[bit / 8] >> (bit % 8)) & kmask);
+    if (kbits == 3) {
+        for (int G = 0; G < 4; G++)
+            for (int x = 0; x < 32; x++) {
+                unsigned c = 0;
+                for (int p = 0; p < 3; p++)
+                    c |= ((get_u32(kb + 12 * G + 4 * p) >> x) & 1u) << p;
+                kc[32 * G + x] = (uint8_t)c;
+            }
+    } else {
+        for (int c = 0; c < KVQO_D; c++) {
+            int bit = kbits * c;
+            kc[c] = (uint8_t)((kb[bit / 8] >> (bit % 8)) & kmask);
+        }
     }
     int g = off / 4, i = off % 4;
-    if (vbits == 2) {
+    if (vbits == 3) {
+        for (int m = 0; m < 16; m++)
+            for (int j = 0; j < 8; j++) {
+                unsigned c = 0;
+                for (int p = 0; p < 3; p++)
+                    c |= ((region[vbase + 12 * (16 * g + m) + 4 * p + K3V3_SLOT_BYTE[i]] >> j) & 1u) << p;
+                vc[16 * j + m] = (uint8_t)c;
+            }
+    } else if (vbits == 2) {
         for (int m = 0; m < 16; m++) {
             const uint8_t *vb = region + vbase + 128 * g + 8 * m + 2 * i;
             unsigned w = (unsigned)vb[0] | ((unsigned)vb[1] << 8);

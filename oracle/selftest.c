@@ -102,9 +102,9 @@ static int check_format(int kbits, int vbits, int page_tokens)
 
 int main(void)
 {
-    const int fmts[4][2] = {{4, 2}, {4, 4}, {8, 2}, {8, 4}};
+    const int fmts[5][2] = {{4, 2}, {4, 4}, {8, 2}, {8, 4}, {3, 3}};
     const int pages[4] = {16, 32, 64, 128};
-    for (int f = 0; f < 4; f++)
+    for (int f = 0; f < 5; f++)
         for (int p = 0; p < 4; p++) {
             int rc = check_format(fmts[f][0], fmts[f][1], pages[p]);
             if (rc) {

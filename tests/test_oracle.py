@@ -518,7 +518,7 @@ def test_attention_f64_matches_torch_sdpa_and_concatenation():
 # Other bit widths: 8-bit or 4-bit keys, 4-bit or 2-bit values
 # --------------------------------------------------------------------------
 
-PRESETS = [(4, 2), (4, 4), (8, 2), (8, 4)]
+PRESETS = [(4, 2), (4, 4), (8, 2), (8, 4), (3, 3)]
 
 
 def test_region_sizes():
@@ -549,6 +549,31 @@ def test_layout_golden_k8v4():
             expect[base + 16 * m + 4 * h + 1] = v >> 8
     expect[3096:3100] = np.frombuffer(bytes.fromhex(f["key_meta_at_3096"]), np.uint8)
     expect[3160:3164] = np.frombuffer(bytes.fromhex(f["value_meta_at_3160"]), np.uint8)
+    assert np.array_equal(region, expect)
+
+
+def test_layout_golden_k3v3():
+    """3-bit codes as bit planes, against the hand-derived image of one slot."""
+    f = _read_fixture("layout_k3v3.txt")
+    off, size = int(f["off"]), int(f["region_bytes"])
+    region = np.zeros(size, np.uint8)
+    c = np.arange(D)
+    kc = (c % 8) ^ (c // 32)
+    vc = (c // 16) ^ (c % 16 % 8)
+    oracle.store_token(region, off, kc, 0x1234, 0x5678, vc, 0x9ABC, 0xDEF0, fmt=(3, 3))
+    expect = np.zeros(size, np.uint8)
+    ko = int(f["key_row_offset"])
+    for G in range(4):
+        planes = [int(b, 16) for b in f[f"key_plane_bytes_G{G}"].split()]
+        for p in range(3):
+            expect[ko + 12 * G + 4 * p:ko + 12 * G + 4 * p + 4] = planes[p]
+    vb = int(f["value_byte_base"])
+    for m in range(16):
+        planes = [int(b, 16) for b in f[f"value_plane_bytes_m{m % 8}"].split()]
+        for p in range(3):
+            expect[vb + 12 * m + 4 * p] = planes[p]
+    expect[1556:1560] = np.frombuffer(bytes.fromhex(f["key_meta_at_1556"]), np.uint8)
+    expect[1620:1624] = np.frombuffer(bytes.fromhex(f["value_meta_at_1620"]), np.uint8)
     assert np.array_equal(region, expect)
 
 
@@ -620,7 +645,7 @@ def _sparse_on_grid_8bit(rng, delta=2.0 ** -4, zero=-0.5):
     return x16, c, delta, zero
 
 
-@pytest.mark.parametrize("bits,mode", [(8, 0), (4, 1), (8, 1)])
+@pytest.mark.parametrize("bits,mode", [(8, 0), (4, 1), (8, 1), (3, 0), (3, 1)])
 def test_on_grid_round_trip_exact_other_widths(bits, mode):
     """8-bit keys and 4-bit (or 8-bit) groups with the value offset (the group
     mean): codes, scale and offset come back exactly."""
@@ -637,7 +662,7 @@ def test_on_grid_round_trip_exact_other_widths(bits, mode):
         assert np.array_equal(rec, zero + delta * c)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 3])
 def test_error_bound_and_brute_force_nearest_level_other_widths(bits):
     rng = np.random.default_rng(70 + bits)
     L = (1 << bits) - 1
@@ -665,10 +690,11 @@ def test_error_bound_and_brute_force_nearest_level_other_widths(bits):
 
 
 def test_wider_codes_lower_the_error():
-    """Same groups at 2, 4 and 8 bits: the mean squared reconstruction error
-    falls by about 4x per extra bit (uniform quantiser, step ~ range / L)."""
+    """Same groups at 2, 3, 4 and 8 bits: the mean squared reconstruction
+    error falls by about 4x per extra bit (uniform quantiser, step ~ range /
+    L, so the ratio between widths is about (L_wide / L_narrow)^2)."""
     rng = np.random.default_rng(80)
-    err = {2: 0.0, 4: 0.0, 8: 0.0}
+    err = {2: 0.0, 3: 0.0, 4: 0.0, 8: 0.0}
     for _ in range(200):
         x16 = rng.standard_normal(D).astype(np.float16)
         y = H @ x16.astype(np.float64)
@@ -677,10 +703,12 @@ def test_wider_codes_lower_the_error():
             rec = oracle.half_to_double(s) * codes + oracle.group_zero(codes, s, z, is_value=True)
             err[bits] += np.mean((y - rec) ** 2)
     assert err[4] < err[2] / 16 * 2.5 and err[4] > err[2] / 16 / 2.5
+    assert err[3] < err[2] / (7 / 3) ** 2 * 2.5 and err[3] > err[2] / (7 / 3) ** 2 / 2.5
+    assert err[4] < err[3] / (15 / 7) ** 2 * 2.5 and err[4] > err[3] / (15 / 7) ** 2 / 2.5
     assert err[8] < err[4] / 256 * 2.5
 
 
-@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4), (3, 3)])
 def test_append_per_token_and_idempotent_presets(fmt):
     w = inp.workload("tiny", context=48)
     k, v = inp.sequence_kv(w, 0)
@@ -721,7 +749,7 @@ def _small_case_fmt(fmt, num_seqs=2, hq=4, hkv=2, lens=(37, 70), seed=5, on_grid
     for b in range(num_seqs):
         n = int(lens[b])
         if on_grid:
-            gk = (lambda: _sparse_on_grid_8bit(rng)[0]) if kb == 8 else (lambda: _on_grid(rng, 15)[0])
+            gk = (lambda: _sparse_on_grid_8bit(rng)[0]) if kb == 8 else (lambda: _on_grid(rng, (1 << kb) - 1)[0])
             k = np.stack([[gk() for _ in range(hkv)] for _ in range(n)])
             v = np.stack([[_on_grid(rng, (1 << vb) - 1)[0] for _ in range(hkv)] for _ in range(n)])
         else:
@@ -734,7 +762,7 @@ def _small_case_fmt(fmt, num_seqs=2, hq=4, hkv=2, lens=(37, 70), seed=5, on_grid
     return pool, bt, np.asarray(lens, np.int64), q, ks, vs
 
 
-@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4), (3, 3)])
 def test_attention_on_grid_equals_sdpa_presets(fmt):
     pool, bt, lens, q, ks, vs = _small_case_fmt(fmt, on_grid=True, seed=9)
     scale = 1 / np.sqrt(D)
@@ -748,7 +776,7 @@ def test_attention_on_grid_equals_sdpa_presets(fmt):
         assert np.max(np.abs(out[b] - ref.numpy())) < 1e-12
 
 
-@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4)])
+@pytest.mark.parametrize("fmt", [(4, 4), (8, 2), (8, 4), (3, 3)])
 def test_attention_folded_equals_plain_presets(fmt):
     pool, bt, lens, q, _, _ = _small_case_fmt(fmt, seed=11, lens=(1, 129))
     scale = 1 / np.sqrt(D)
