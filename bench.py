@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--no-mixed-window", action="store_true",
                     help="skip the fp16 sink + recent window beside the K4V2 history")
     ap.add_argument("--no-presets", action="store_true",
-                    help="skip the k4v4 / k8v2 / k8v4 presets on the same workload")
+                    help="skip the k4v4 / k8v2 / k8v4 / k3v3 presets on the same workload")
     ap.add_argument("--no-multi-query", action="store_true",
                     help="skip the multi-row (speculative draft) decode on the same cache")
     ap.add_argument("--no-warm", action="store_true",
@@ -464,7 +464,8 @@ def main():
     if not args.no_presets:
         result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt)
                              for p, pt in (("k4v4_g128", 16), ("k8v2_g128", 16), ("k8v4_g128", 16),
-                                           ("k4v2_g128", 32), ("k4v2_g128", 64), ("k4v2_g128", 128))]
+                                           ("k3v3_g128", 16), ("k4v2_g128", 32), ("k4v2_g128", 64),
+                                           ("k4v2_g128", 128))]
 
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
@@ -664,7 +665,10 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
         nv.append(v[ctx:])
         del k, v
     nk, nv = torch.cat(nk).contiguous(), torch.cat(nv).contiguous()
-    pools = [base] + [base.clone() for _ in range(2)]     # >= 3 x 139 MB: beyond the 256 MB cache
+    # copies cycled so that each launch reads a pool the 256 MB Infinity Cache
+    # does not hold: at least 640 MB in all
+    copies = max(3, -(-640_000_000 // base.numel()))
+    pools = [base] + [base.clone() for _ in range(copies - 1)]
     q = inp.queries(w, 0, device=dev).contiguous()
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
     ws = kvq.alloc_workspace(B, Hq, Hkv, n, fmt=fmt)
@@ -674,11 +678,11 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
     pf, cfn = lib.kvq_append_decode_partials, lib.kvq_decode_combine
     steps = max(20, args.steps // 2)
     for i in range(5):
-        pf(*part[i % 3]); cfn(*comb)
+        pf(*part[i % len(part)]); cfn(*comb)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        if pf(*part[i % 3]) | cfn(*comb):
+        if pf(*part[i % len(part)]) | cfn(*comb):
             raise RuntimeError(f"{preset} decode call failed")
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -687,7 +691,7 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
     hev.record(0, stream.cuda_stream)
     bad = 0
     for i in range(nl):
-        bad |= pf(*part[i % 3])
+        bad |= pf(*part[i % len(part)])
     hev.record(1, stream.cuda_stream)
     torch.cuda.synchronize()
     if bad:

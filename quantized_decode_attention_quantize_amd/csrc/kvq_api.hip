@@ -25,10 +25,12 @@ int page_log2s(const kvq_format *f) {
     }
 }
 
-// A quantised cache: 4- or 8-bit keys, 2- or 4-bit values (4/2 is KVarN's),
-// pages of 16 to 128 tokens.
+// A quantised cache: 4- or 8-bit keys with 2- or 4-bit values (4/2 is
+// KVarN's), or 3 bits both; pages of 16 to 128 tokens.
 bool is_quant(const kvq_format *f) {
-    return is_g128(f) && (f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4) &&
+    return is_g128(f) &&
+           (((f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4)) ||
+            (f->k_bits == 3 && f->v_bits == 3)) &&
            page_log2s(f) >= 0;
 }
 
@@ -213,6 +215,7 @@ kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
     } presets[] = {
         {"k4v2_g128", 4, 2}, {"kvarn_k4v2_g128", 4, 2}, {"k4v4_g128", 4, 4}, {"kvarn_k4v4_g128", 4, 4},
         {"k8v2_g128", 8, 2}, {"kvarn_k8v2_g128", 8, 2}, {"k8v4_g128", 8, 4}, {"kvarn_k8v4_g128", 8, 4},
+        {"k3v3_g128", 3, 3}, {"kvarn_k3v3_g128", 3, 3},
         {"fp16", 16, 16},
     };
     for (const auto &p : presets) {

@@ -1,5 +1,6 @@
 // Quantise-on-write of new key/value tokens into the g128 paged cache (4/8-bit
-// keys, 2/4-bit values; the KVarN preset is 4-bit keys and 2-bit values).
+// keys with 2/4-bit values, or 3 bits both; the KVarN preset is 4-bit keys
+// and 2-bit values).
 //
 // Two kernels encode the same bytes:
 //   quantize_append_kernel   one 16-lane row per group = (token, KV head,
@@ -101,9 +102,10 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
         ss = p[0];
     }
     constexpr int L = kValue ? Lay::kVL : Lay::kKL;
-    // keys: the token's code row as dwords (16 of nibbles or 32 of bytes);
-    // values: the 16-bit words of the layout (16 of crumbs or 32 of nibbles)
-    constexpr int kWords = kValue ? (VB == 2 ? 16 : 32) : (KB == 4 ? 16 : 32);
+    // keys: the token's code row as dwords (16 of nibbles, 32 of bytes, or
+    // 12 bit-plane words); values: the 16-bit words of the layout (16 of
+    // crumbs or 32 of nibbles), or 48 bit-plane bytes (3 per m)
+    constexpr int kWords = kValue ? (VB == 2 ? 16 : VB == 3 ? 48 : 32) : (KB == 4 ? 16 : KB == 3 ? 12 : 32);
     uint32_t packed[kWords];
 #pragma unroll
     for (int d = 0; d < kWords; d++) packed[d] = 0;
@@ -130,10 +132,19 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
                 const uint32_t code = (uint32_t)fminf(rintf((y[i] - lo) * inv), (float)L);
                 if (kValue) {
                     csum += code;
-                    if (VB == 2)
+                    if (VB == 2) {
                         packed[i & 15] |= code << (2 * (i >> 4));     // word m: channel 16j + m at bits 2j
-                    else   // word 2m + h: channel 16(4h + k) + m at bits 4k
+                    } else if (VB == 3) {
+                        // byte 3m + p: bit p of channel 16j + m's code at bit j
+#pragma unroll
+                        for (int p = 0; p < 3; p++) packed[3 * (i & 15) + p] |= ((code >> p) & 1u) << (i >> 4);
+                    } else {   // word 2m + h: channel 16(4h + k) + m at bits 4k
                         packed[2 * (i & 15) + (i >> 6)] |= code << (4 * ((i >> 4) & 3));
+                    }
+                } else if (KB == 3) {
+                    // plane word 3G + p (G = i / 32): bit p of the code at bit i % 32
+#pragma unroll
+                    for (int p = 0; p < 3; p++) packed[3 * (i >> 5) + p] |= ((code >> p) & 1u) << (i & 31);
                 } else if (KB == 4) {
                     packed[i >> 3] |= code << (4 * (i & 7));      // byte b = c[2b] | c[2b+1] << 4
                 } else {
@@ -160,6 +171,15 @@ __device__ __forceinline__ void encode_lane(const uint16_t *src, uint8_t *region
         for (int q = 0; q < kWords / 4; q++)
             dst[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
         *reinterpret_cast<uint32_t *>(region + Lay::kKMeta + 4 * off) = s16 | (z16 << 16);
+    } else if (VB == 3) {
+        // byte (0, 2, 1, 3)[i] of plane word p at 12 (16g + m) + 4p
+        const int i = off & 3;
+        uint8_t *vb = region + Lay::kVCodes + 192 * (off >> 2) + (((i & 1) << 1) | (i >> 1));
+#pragma unroll
+        for (int m = 0; m < 16; m++)
+#pragma unroll
+            for (int p = 0; p < 3; p++) vb[12 * m + 4 * p] = (uint8_t)packed[3 * m + p];
+        *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     } else if (VB == 2) {
         uint8_t *vb = region + Lay::kVCodes + 128 * (off >> 2) + 2 * (off & 3);
 #pragma unroll
@@ -225,6 +245,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t stream) {
     if (a.k_bits == 4 && a.v_bits == 4) return launch_append_fmt<4, 4>(a, stream);
     if (a.k_bits == 8 && a.v_bits == 2) return launch_append_fmt<8, 2>(a, stream);
     if (a.k_bits == 8 && a.v_bits == 4) return launch_append_fmt<8, 4>(a, stream);
+    if (a.k_bits == 3 && a.v_bits == 3) return launch_append_fmt<3, 3>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -72,8 +72,10 @@ namespace {
 template <int KB, int VB>
 struct PageRegs {
     uint32_t k[KB];   // key codes: token (lane & 15), channels 32g..32g+31 (g = lane >> 4),
-                      // the 4*KB bytes at 4*KB*g of the token's code row
-    uint32_t v[VB];   // value codes: the 4*VB bytes at 4*VB*lane (quad g, channel lane & 15)
+                      // the 4*KB bytes at 4*KB*g of the token's code row (3 bits: the
+                      // three bit-plane words of those channels)
+    uint32_t v[VB];   // value codes: the 4*VB bytes at 4*VB*lane (quad g, channel lane & 15;
+                      // 3 bits: the three bit-plane words)
     uint4 km;         // key (s, z) of tokens 4g..4g+3
     uint4 vm;         // value (s, mu) of tokens 4g..4g+3
 };
@@ -90,6 +92,7 @@ struct LaneOffsets {
 };
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v3u __attribute__((ext_vector_type(3)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 // `region` is wave-uniform: it becomes a buffer resource in scalar registers
@@ -101,6 +104,10 @@ __device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffse
                                           PageRegs<KB, VB> &r) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(region), (short)0, Layout<KB, VB>::kBytes, 0x00020000);
+    if (KB == 3) {
+        const v3u k = __builtin_amdgcn_raw_buffer_load_b96(rs, o.k, 0, 0);
+        r.k[0] = k.x; r.k[1] = k.y; r.k[KB > 2 ? 2 : 0] = k.z;
+    }
 #pragma unroll
     for (int h = 0; h < KB / 4; h++) {
         const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 16 * h, 0, 0);
@@ -109,6 +116,9 @@ __device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffse
     if (VB == 2) {
         const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.v, 0, 0);
         r.v[0] = v.x; r.v[1] = v.y;
+    } else if (VB == 3) {
+        const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, o.v, 0, 0);
+        r.v[0] = v.x; r.v[1] = v.y; r.v[VB > 2 ? 2 : 0] = v.z;
     } else {
         const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v, 0, 0);
         r.v[0] = v.x; r.v[1] = v.y; r.v[VB > 2 ? 2 : 0] = v.z; r.v[VB > 2 ? 3 : 1] = v.w;
@@ -141,6 +151,26 @@ __device__ __forceinline__ v8h key_codes8(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(v8h, u);
 }
 
+// 3-bit keys: the A operand of k-step d (0..3) from the lane's three
+// bit-plane words (bit x of word p = bit p of the code of channel 32g + x).
+// Dword k holds channel x = 8 (d >> 1) + j, j = 4 (d & 1) + k, in its low
+// half and channel x + 16 in its high half, each code at mantissa bits
+// j..j+2: the fp16 subnormal c * 2^(j - 24).  Planes 1 and 2 are shifted up
+// by 1 and 2 first, so a code takes one AND and two AND-ORs per pair of
+// channels.  The query operand carries the matching order and 2^-j.
+__device__ __forceinline__ v8h key_codes3(const uint32_t (&pl)[3], int d) {
+    const int sh = 8 * (d >> 1);
+    const uint32_t a = pl[0] >> sh, b = (pl[1] >> sh) << 1, c = (pl[2] >> sh) << 2;
+    uint32_t u[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const int j = 4 * (d & 1) + k;
+        const uint32_t m = (1u << j) | (1u << (16 + j));
+        u[k] = (a & m) | (b & (m << 1)) | (c & (m << 2));
+    }
+    return __builtin_bit_cast(v8h, make_uint4(u[0], u[1], u[2], u[3]));
+}
+
 // Folded base-2 scores of the lane's 4 tokens of one page:
 // v_mfma_f32_16x16x32_f16 x 4 (32 channels per instruction and lane-group),
 // columns n < 8 the fp16 query q_hi of head n, columns n >= 8 its residual
@@ -152,7 +182,13 @@ __device__ __forceinline__ void page_scores(const PageRegs<KB, VB> &r, const v8h
     v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        const v8h a = KB == 4 ? key_codes(r.k[q]) : key_codes8(r.k[(2 * q) % KB], r.k[(2 * q + 1) % KB]);
+        v8h a;
+        if (KB == 3) {
+            const uint32_t pl[3] = {r.k[0], r.k[1 % KB], r.k[2 % KB]};
+            a = key_codes3(pl, q);
+        } else {
+            a = KB == 4 ? key_codes(r.k[q]) : key_codes8(r.k[(2 * q) % KB], r.k[(2 * q + 1) % KB]);
+        }
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[q], d, 0, 0, 0);
     }
     const uint32_t km[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
@@ -212,6 +248,31 @@ __device__ __forceinline__ uint32_t value_code4(uint32_t u, int k) {
     default: return (u >> 8) & kBits47;
     }
 }
+
+// 3-bit values: the three bit-plane words of one page for one lane (quad g,
+// channel m; byte (0, 2, 1, 3)[i] of word p holds bit p of the codes of
+// token slot i, channel block j at bit j).  Returns the dword of channel
+// block j for token slots 0, 1 (hi = 0) or 2, 3 (hi = 1), each code at
+// mantissa bits pos..pos+2 with pos = 4 + (j & 3): the fp16 subnormal
+// c * 2^(pos - 24).  Each plane is shifted so that block j's bit of both
+// slots lands at pos + p and pos + p + 16; then one AND and two AND-ORs.
+__device__ __forceinline__ uint32_t value_code3(const uint32_t (&w)[3], int j, int hi) {
+    const int pos = 4 + (j & 3);
+    uint32_t x[3];
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+        // the slot's byte (0 or 2 for slots 0/1, 1 or 3 for slots 2/3) has
+        // block j at bit j (+ 8 for slots 2/3); move it to pos + p
+        const int from = j + (hi ? 8 : 0);
+        const int to = pos + p;
+        x[p] = to >= from ? (w[p] << (to - from)) : (w[p] >> (from - to));
+    }
+    const uint32_t m = (1u << pos) | (1u << (16 + pos));
+    return (x[0] & m) | (x[1] & (m << 1)) | (x[2] & (m << 2));
+}
+
+// log2 of the factor that removes the code scaling of channel block j (3 bits)
+__device__ __forceinline__ constexpr int value3_unscale_log2(int j) { return 20 - (j & 3); }
 
 struct LaneConsts {
     float c1, c2;          // folded score constants of head n & 7
@@ -297,6 +358,10 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
         uint4 packed;
         if (VB == 2) {
             packed = {value_code(A.v[0], j), value_code(A.v[1], j), value_code(B.v[0], j), value_code(B.v[1], j)};
+        } else if (VB == 3) {
+            const uint32_t wa[3] = {A.v[0], A.v[1 % VB], A.v[2 % VB]};
+            const uint32_t wb[3] = {B.v[0], B.v[1 % VB], B.v[2 % VB]};
+            packed = {value_code3(wa, j, 0), value_code3(wa, j, 1), value_code3(wb, j, 0), value_code3(wb, j, 1)};
         } else {
             const int h = j >> 2, k = j & 3;
             packed = {value_code4(A.v[h], k), value_code4(A.v[(2 + h) % VB], k), value_code4(B.v[h], k),
@@ -505,15 +570,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const int ch = c0 + e;
             const int r8 = ch & 7;
             // slot of channel ch in the key operand's order (see key_codes,
-            // key_codes8); 4-bit keys in slots 2, 3, 6, 7 carry 2^-20
-            int slot, hi_nibble = 0;
+            // key_codes8, key_codes3) and log2 of the code scaling it
+            // carries: 4-bit keys in slots 2, 3, 6, 7 carry 2^-20 (down = 4);
+            // a 3-bit key at mantissa bits j..j+2 carries 2^(j - 24)
+            int slot, down = 0;
             if (KB == 4) {
                 slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
-                hi_nibble = (slot >> 1) & 1;
+                down = 4 * ((slot >> 1) & 1);
+            } else if (KB == 3) {
+                const int x = ch & 31, r16 = x & 15;   // channel 32g + x; x = 16 hi + r16
+                slot = (ch & ~31) + 8 * (2 * (r16 >> 3) + ((r16 >> 2) & 1)) + 2 * (r16 & 3) + (x >> 4);
+                down = r16 & 7;
             } else {
                 slot = (ch & ~7) + ((r8 & 4) | ((r8 & 1) << 1) | ((r8 >> 1) & 1));
             }
-            const float v = __builtin_ldexpf(q[e], shift - 4 * hi_nibble);
+            const float v = __builtin_ldexpf(q[e], shift - down);
             const _Float16 vh = (_Float16)v;
             s_qb[hh][slot] = vh;
             s_qb[8 + hh][slot] = (_Float16)(v - (float)vh);
@@ -589,7 +660,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // ---- merge the 4 waves; write the partial (or the output) ----
     merge_and_store<kMQ>(st, s_merge, a, 1,
-                    [](int j) { return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : 20); },
+                    [](int j) {
+                        return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : VB == 3 ? value3_unscale_log2(j) : 20);
+                    },
                     wave, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
 }
 
@@ -797,6 +870,7 @@ int decode_resident_workgroups(int k_bits, int v_bits) {
     if (k_bits == 4 && v_bits == 4) return resident_workgroups<4, 4>();
     if (k_bits == 8 && v_bits == 2) return resident_workgroups<8, 2>();
     if (k_bits == 8 && v_bits == 4) return resident_workgroups<8, 4>();
+    if (k_bits == 3 && v_bits == 3) return resident_workgroups<3, 3>();
     return 512;
 }
 
@@ -805,6 +879,7 @@ hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const La
     if (a.k_bits == 4 && a.v_bits == 4) return launch_split_fmt<4, 4>(a, stream, ev);
     if (a.k_bits == 8 && a.v_bits == 2) return launch_split_fmt<8, 2>(a, stream, ev);
     if (a.k_bits == 8 && a.v_bits == 4) return launch_split_fmt<8, 4>(a, stream, ev);
+    if (a.k_bits == 3 && a.v_bits == 3) return launch_split_fmt<3, 3>(a, stream, ev);
     return hipErrorInvalidValue;
 }
 

@@ -13,12 +13,13 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 
-// Region of KB-bit keys (4 or 8) and VB-bit values (2 or 4): key codes (16
-// tokens x 16 KB bytes, token-major), value codes (16 x 16 VB bytes), key and
-// value metadata (16 x 4 bytes each).  Layout<4, 2> is the 1664-byte region.
+// Region of KB-bit keys (4 or 8) and VB-bit values (2 or 4), or 3-bit keys
+// and values (bit planes): key codes (16 tokens x 16 KB bytes, token-major),
+// value codes (16 x 16 VB bytes), key and value metadata (16 x 4 bytes each).
+// Layout<4, 2> and Layout<3, 3> are 1664-byte regions.
 template <int KB, int VB>
 struct Layout {
-    static_assert((KB == 4 || KB == 8) && (VB == 2 || VB == 4), "unsupported bit widths");
+    static_assert(((KB == 4 || KB == 8) && (VB == 2 || VB == 4)) || (KB == 3 && VB == 3), "unsupported bit widths");
     static constexpr int kKCodes = 0;
     static constexpr int kVCodes = 256 * KB;
     static constexpr int kKMeta = 256 * (KB + VB);
@@ -92,8 +93,8 @@ struct AppendArgs {
     int32_t num_kv_heads;
     uint8_t *cache;
     int64_t num_pages;
-    int32_t k_bits;    // 4 or 8
-    int32_t v_bits;    // 2 or 4
+    int32_t k_bits;    // 4 or 8 (3 with v_bits 3)
+    int32_t v_bits;    // 2 or 4 (3 with k_bits 3)
     int32_t page_log2s;   // pages of 16 << page_log2s tokens: 2^page_log2s 16-token regions each
 };
 

@@ -1,6 +1,6 @@
 // Encoder of one g128 group (one token of one KV head, keys or values) at
-// 4/8-bit keys and 2/4-bit values, shared by the quantise-append kernel and
-// the fused append-and-decode path.
+// 4/8-bit keys and 2/4-bit values, or 3 bits both, shared by the
+// quantise-append kernel and the fused append-and-decode path.
 //
 // Method: the KVarN write path -- Hadamard rotation, variance normalisation,
 // asymmetric round-to-nearest to 4-bit keys / 2-bit values (dothoosh.com,
@@ -149,7 +149,20 @@ __device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, 
     if (z16 == 0x8000u) z16 = 0;   // a zero offset is stored as +0
 
     if (!is_v) {
-        if (KB == 4) {
+        if (KB == 3) {
+            // keys as bit planes: lane r holds channels 32G + x, G = r / 4,
+            // x = 8 (r % 4) + e, so byte r % 4 of plane word (G, p) at
+            // 12G + 4p of the token's 48-byte row is this lane's bit p of
+            // codes e = 0..7
+            uint8_t *row = region + Lay::kKCodes + 48 * off + 12 * (r >> 2) + (r & 3);
+#pragma unroll
+            for (int p = 0; p < 3; p++) {
+                uint32_t b = 0;
+#pragma unroll
+                for (int e = 0; e < 8; e++) b |= ((code[e] >> p) & 1u) << e;
+                row[4 * p] = (uint8_t)b;
+            }
+        } else if (KB == 4) {
             // keys: byte b of the token's 64 = code[2b] | code[2b+1] << 4
             uint32_t packed = 0;
 #pragma unroll
@@ -163,6 +176,43 @@ __device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, 
         }
         if (r == 0)
             *reinterpret_cast<uint32_t *>(region + Lay::kKMeta + 4 * off) = s16 | (z16 << 16);
+    } else if (VB == 3) {
+        // values as bit planes: for channel 16j + m, byte p of the word for
+        // m collects bit p of the code at bit j.  Lane r has channels
+        // 8r..8r+7, i.e. j = r/2 and m = 8(r&1) + e; the 8 lanes that share
+        // r&1 are OR-reduced with the transpose used for 2-bit values, which
+        // leaves each lane the word of one m.  Its byte p goes to byte
+        // (0, 2, 1, 3)[i] of plane word p at 12 (16g + m) + 4p.
+        const int j = r >> 1;
+        uint32_t v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            v8[e] = ((code[e] & 1u) << j) | (((code[e] >> 1) & 1u) << (8 + j)) | (((code[e] >> 2) & 1u) << (16 + j));
+        const bool b1 = (r & 2) != 0, b2 = (r & 4) != 0, b3 = (r & 8) != 0;
+        uint32_t v4[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t send = b1 ? v8[k] : v8[4 + k];
+            const uint32_t keep = b1 ? v8[4 + k] : v8[k];
+            v4[k] = keep | xor_lane_u(send, 2);
+        }
+        uint32_t v2[2];
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const uint32_t send = b2 ? v4[k] : v4[2 + k];
+            const uint32_t keep = b2 ? v4[2 + k] : v4[k];
+            v2[k] = keep | xor_lane_u(send, 4);
+        }
+        const uint32_t send = b3 ? v2[0] : v2[1];
+        const uint32_t keep = b3 ? v2[1] : v2[0];
+        const uint32_t word = keep | xor_lane_u(send, 8);
+        const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + (int)b3;
+        const int g = off >> 2, i = off & 3;
+        uint8_t *vb = region + Lay::kVCodes + 12 * (16 * g + m) + (((i & 1) << 1) | (i >> 1));
+#pragma unroll
+        for (int p = 0; p < 3; p++) vb[4 * p] = (uint8_t)(word >> (8 * p));
+        if (r == 0)
+            *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     } else if (VB == 4) {
         // values: with channel 16j + m and j = 4h + k, the u16 word for
         // (m, h) holds code(16j + m) << 4k, k = 0..3.  Lane r has channels

@@ -43,13 +43,15 @@ def test_format_and_sizes():
     assert 3.0 <= ratio <= 5.0 and abs(ratio - 4.923) < 1e-3
     assert kvq.cache_bytes(10, 8) == 10 * 8 * 1664
     for bad in (kvq.Format(128, 128, 8, 8, 16), kvq.Format(128, 128, 2, 2, 16), kvq.Format(128, 64, 4, 2, 16),
+                kvq.Format(128, 128, 3, 2, 16), kvq.Format(128, 128, 4, 3, 16), kvq.Format(128, 128, 3, 4, 16),
                 kvq.Format(128, 128, 4, 2, 48), kvq.Format(128, 128, 4, 2, 256), kvq.Format(128, 128, 16, 16, 32)):
         assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
         assert lib.kvq_cache_bytes(ctypes.byref(bad), 10, 8) == 0
 
 
 @pytest.mark.parametrize("preset,kb,vb", [("k4v4_g128", 4, 4), ("kvarn_k4v4_g128", 4, 4), ("k8v2_g128", 8, 2),
-                                          ("k8v4_g128", 8, 4), ("kvarn_k8v4_g128", 8, 4)])
+                                          ("k8v4_g128", 8, 4), ("kvarn_k8v4_g128", 8, 4), ("k3v3_g128", 3, 3),
+                                          ("kvarn_k3v3_g128", 3, 3)])
 def test_other_bit_width_presets(preset, kb, vb):
     """Presets of the same pipeline at other widths: region = key codes (16 x
     16 kb bytes) + value codes (16 x 16 vb) + two 16 x 4 metadata arrays."""

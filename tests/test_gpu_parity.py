@@ -55,7 +55,7 @@ def gpu_append(k, v, slots, cache, fmt=None):
 
 
 # bit widths (keys, values) of the quantised presets; (4, 2) is KVarN's
-PRESET_FMTS = [(4, 4), (8, 2), (8, 4)]
+PRESET_FMTS = [(4, 4), (8, 2), (8, 4), (3, 3)]
 
 
 def _kfmt(fmt):
@@ -796,7 +796,7 @@ def test_rotated_fp16_partials_alone(dev):
 
 
 # --------------------------------------------------------------------------
-# Other bit widths: 4/8-bit keys, 2/4-bit values
+# Other bit widths: 4/8-bit keys with 2/4-bit values, 3 bits both
 # --------------------------------------------------------------------------
 
 # 65600 (token, KV head) rows select the one-lane-per-group append kernel
@@ -947,6 +947,7 @@ MQ_CASES = [
     (2, 8, 2, [513, 31], 5, 0, (8, 4)),
     (2, 4, 1, [77, 200], 6, 2, (4, 4)),
     (2, 4, 1, [34, 66], 5, 0, (4, 2)),         # two masked page pairs in one split
+    (2, 16, 2, [200, 45], 4, 0, (3, 3)),
 ]
 
 
@@ -1015,6 +1016,7 @@ def _build_case_paged(dev, B, Hq, Hkv, lens, seed, P, fmt=(4, 2), append_last=Tr
     (64, (4, 2), 2, 64, 8, [513, 77]),
     (128, (8, 4), 2, 16, 2, [1000, 129]),
     (64, (4, 4), 4, 12, 4, [64, 65, 127, 300]),
+    (32, (3, 3), 2, 16, 2, [333, 48]),
 ])
 def test_paged_decode_matches_oracle(dev, P, fmt, B, Hq, Hkv, lens):
     log(f"paged decode P={P} fmt={fmt} B={B} Hq={Hq} Hkv={Hkv} lens={lens}")
