@@ -1,7 +1,7 @@
 /*
  * kvq.h -- C ABI of libkvq: K4V2 group-128 quantised paged KV cache (and the
- * same pipeline at 8-bit keys / 4-bit values) for AMD Instinct MI355X
- * (gfx950).
+ * same pipeline at 4/8-bit keys with 2/4-bit values, and at 3 bits both) for
+ * AMD Instinct MI355X (gfx950).
  *
  * Two operations on a paged KV cache:
  *   kvq_quantize_append   quantise-on-write of new key/value tokens
@@ -68,6 +68,17 @@
  *                     4k..4k+3
  *       key (s, z)    16 x 4 bytes at 256*(k_bits + v_bits)
  *       value (s, mu) 16 x 4 bytes after them
+ * 3 bits both ("k3v3_g128", also "kvarn_k3v3_g128"; the pages rank 3-bit codes
+ * as noticeably less accurate than the widths above [TQ]): L = 7, codes
+ * stored as bit planes, again 1664 bytes per region in the same order:
+ *       key codes     the token's 48-byte row at 48*o: for G = 0..3 and
+ *                     p = 0..2 the little-endian u32 at 12G + 4p holds, at
+ *                     bit x, bit p of the code of channel 32G + x
+ *       value codes   at 768: for quad g = o/4, slot i = o%4, channel
+ *                     16j + m, byte (0, 2, 1, 3)[i] of the little-endian u32
+ *                     at 768 + 12(16g + m) + 4p holds, at bit j, bit p of the
+ *                     code
+ *       key (s, z)    at 1536 + 4*o; value (s, mu) at 1600 + 4*o
  *
  * Baseline format "fp16" (k_bits = v_bits = 16): the uncompressed cache the
  * K4V2 format is measured against (the pages compare KVarN with fp16 on
