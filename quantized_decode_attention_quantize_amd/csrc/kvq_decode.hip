@@ -418,6 +418,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         bt_a = bt[ea < last ? ea : last];
         bt_b = bt[eb < last ? eb : last];
     }
+    // This lane's slice of the query (head 2 wave + lane / 32 of the head
+    // group, channels 4 (lane % 32) ..+3) is requested with the page ids,
+    // before any page: loads return in issue order, so a query load issued
+    // after the first pages would hold the query prologue until those pages
+    // had arrived (measured: the prologue then ended ~4.4 us after the wave
+    // started, against ~1 us for the page ids).
+    const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
+    uint2 qraw = make_uint2(0u, 0u);
+    {
+        const int hh = 2 * wave + (lane >> 5);
+        if (hh < nh)
+            qraw = *reinterpret_cast<const uint2 *>(a.query + io_row<kMQ>(a, b, kvh, hg * kHeadsPerGroup + hh) * kHeadDim +
+                                                    4 * (lane & 31));
+    }
 
     const int max_len = a.max_seq_len;
     int n_tokens = a.seq_lens[b];
@@ -430,7 +444,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int npages = (n_tokens + kPage - 1) / kPage;
     const int pps = a.pages_per_split;
     const int p_begin = split * pps;
-    const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
 
     if (p_begin >= npages) {         // an empty sequence, or a split past its end
         write_empty<kMQ>(a, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
@@ -531,15 +544,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int hh = 2 * wave + (lane >> 5);
         const int l32 = lane & 31;
         const int c0 = 4 * l32;
-        float q[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (hh < nh) {
-            const uint2 raw = *reinterpret_cast<const uint2 *>(
-                a.query + io_row<kMQ>(a, b, kvh, hg * kHeadsPerGroup + hh) * kHeadDim + c0);
-            q[0] = half_bits_to_float(raw.x & 0xffffu);
-            q[1] = half_bits_to_float(raw.x >> 16);
-            q[2] = half_bits_to_float(raw.y & 0xffffu);
-            q[3] = half_bits_to_float(raw.y >> 16);
-        }
+        float q[4];
+        q[0] = half_bits_to_float(qraw.x & 0xffffu);   // zero for heads past the group
+        q[1] = half_bits_to_float(qraw.x >> 16);
+        q[2] = half_bits_to_float(qraw.y & 0xffffu);
+        q[3] = half_bits_to_float(qraw.y >> 16);
         {
             float p = q[0], r = q[1]; q[0] = p + r; q[1] = p - r;
             p = q[2]; r = q[3]; q[2] = p + r; q[3] = p - r;
