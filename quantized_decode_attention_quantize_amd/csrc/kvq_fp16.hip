@@ -209,6 +209,13 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
         load_page16(region_of(__builtin_amdgcn_readlane(bt_p, j)), koff, voff, A);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // The query slice is requested before any page: loads return in issue
+    // order, so a later query load would wait for the first pages.
+    const int hh_q = 2 * wave + (lane >> 5);
+    const int c0_q = 4 * (lane & 31);
+    uint2 qraw = make_uint2(0, 0);
+    if (hh_q < nh)
+        qraw = *reinterpret_cast<const uint2 *>(a.query + ((int64_t)b * a.num_q_heads + hq0 + hh_q) * kHeadDim + c0_q);
     asm volatile("" ::"v"(bt_p));
     Page16 r0, r1, r2;
     if (nk > 0) {
@@ -217,14 +224,7 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
     }
 
     // ---- query: wave w copies heads 2w and 2w + 1 to LDS (zero past nh) ----
-    {
-        const int hh = 2 * wave + (lane >> 5);
-        const int c0 = 4 * (lane & 31);
-        uint2 raw = make_uint2(0, 0);
-        if (hh < nh)
-            raw = *reinterpret_cast<const uint2 *>(a.query + ((int64_t)b * a.num_q_heads + hq0 + hh) * kHeadDim + c0);
-        *reinterpret_cast<uint2 *>(&s_q[hh][c0]) = raw;
-    }
+    *reinterpret_cast<uint2 *>(&s_q[hh_q][c0_q]) = qraw;
     __syncthreads();
     const int n16 = lane & 15;
     const int g = lane >> 4;
