@@ -90,7 +90,8 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_qwen3_32b_16k_traffic.txt")
 DECODE_SOURCES = [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_decode_common.h", "kvq_device.h", "kvq_quant.h")]
+                  for f in ("kvq_decode.hip", "kvq_decode_common.h", "kvq_device.h", "kvq_quant.h")] + \
+                 [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "build.py")]   # compile flags
 
 
 def decode_source_hash() -> str:
