@@ -171,14 +171,13 @@ __device__ __forceinline__ v8h key_codes3(const uint32_t (&pl)[3], int d) {
     return __builtin_bit_cast(v8h, make_uint4(u[0], u[1], u[2], u[3]));
 }
 
-// Folded base-2 scores of the lane's 4 tokens of one page:
+// Code-domain dot products of the lane's 4 tokens (4g..4g+3) of one page:
 // v_mfma_f32_16x16x32_f16 x 4 (32 channels per instruction and lane-group),
 // columns n < 8 the fp16 query q_hi of head n, columns n >= 8 its residual
-// q_lo = q' - q_hi; adding the partner column (lane n ^ 8, one DPP move)
-// gives both lanes of a pair the same score for head n & 7.
+// q_lo = q' - q_hi.  Adding the partner column (lane n ^ 8, one DPP move)
+// gives the full dot q' . c of head n & 7.
 template <int KB, int VB>
-__device__ __forceinline__ void page_scores(const PageRegs<KB, VB> &r, const v8h (&bq)[4],
-                                            float c1, float c2, float mref, float *lg) {
+__device__ __forceinline__ v4f page_dots(const PageRegs<KB, VB> &r, const v8h (&bq)[4]) {
     v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -191,16 +190,7 @@ __device__ __forceinline__ void page_scores(const PageRegs<KB, VB> &r, const v8h
         }
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[q], d, 0, 0, 0);
     }
-    const uint32_t km[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float dot = d[i] + row_swap8(d[i]);     // q_hi . c + q_lo . c
-        const float ks = half_bits_to_float(km[i] & 0xffffu);
-        const float kz = half_bits_to_float(km[i] >> 16);
-        // base-2 logit minus the reference mref; the fp16 operands feed
-        // mixed-precision FMAs directly
-        lg[i] = __builtin_fmaf(dot * c1, ks, __builtin_fmaf(c2, kz, -mref));
-    }
+    return d;
 }
 
 // Value-code A operands of one page for one lane: u = two 16-bit words
@@ -276,7 +266,7 @@ __device__ __forceinline__ constexpr int value3_unscale_log2(int j) { return 20 
 
 struct LaneConsts {
     float c1, c2;          // folded score constants of head n & 7
-    float res_k;           // 0 (lanes n < 8: weight) or -1 (lanes n >= 8: residual)
+    bool hb;               // lane n >= 8 (weights page B's tokens; n < 8: page A's)
 };
 
 // One page pair.  kMasked: tokens at or beyond this lane's limit `lim` (the
@@ -290,31 +280,47 @@ struct LaneConsts {
 // maximum; 0 before the first pair), so the weights are exp2 of them
 // directly.  When a score exceeds the reference (some logit beats m by more
 // than 8), the state is rescaled and the scores shifted to the new reference.
+//
+// Lanes n and n ^ 8 hold the same tokens of the same head (the query's two
+// fp16 terms sit in their columns), so the per-token softmax work is split
+// between them: lane n < 8 folds, weights and sums page A's 4 tokens, lane
+// n + 8 page B's.  Each lane turns its weights w into w_hi = fp16(w) and
+// w_lo = fp16(w - w_hi); one bank-masked DPP move per dword then hands the
+// partner the half it lacks, so that column n < 8 again holds w_hi and
+// column n + 8 w_lo for all 8 tokens.  l and zacc are per-lane halves,
+// added across the pair before the merge.
 template <int KB, int VB, bool kMasked, bool kFirst>
 __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
                                              int tokB,
                                              int lim, const v8h (&bq)[4], const LaneConsts &lc,
                                              int g, State &st) {
     constexpr bool first = kFirst;
+    const bool hb = lc.hb;
     const float mref = first ? 0.0f : st.m + kLazyThreshold;
-    float lg[8];
-    page_scores<KB, VB>(A, bq, lc.c1, lc.c2, mref, lg);
-    page_scores<KB, VB>(B, bq, lc.c1, lc.c2, mref, lg + 4);
-    bool valid[8];
-    if (kMasked) {
+    const v4f dA = page_dots<KB, VB>(A, bq);
+    const v4f dB = page_dots<KB, VB>(B, bq);
+    const uint32_t kmA[4] = {A.km.x, A.km.y, A.km.z, A.km.w}, kmB[4] = {B.km.x, B.km.y, B.km.z, B.km.w};
+    const uint32_t vmA[4] = {A.vm.x, A.vm.y, A.vm.z, A.vm.w}, vmB[4] = {B.vm.x, B.vm.y, B.vm.z, B.vm.w};
+    float lg[4];
+    bool valid[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            valid[i] = tokA + 4 * g + i < lim;
-            valid[4 + i] = tokB + 4 * g + i < lim;
+    for (int i = 0; i < 4; i++) {
+        const float sA = dA[i] + row_swap8(dA[i]);     // q_hi . c + q_lo . c
+        const float sB = dB[i] + row_swap8(dB[i]);
+        const float dot = hb ? sB : sA;
+        const uint32_t km = hb ? kmB[i] : kmA[i];
+        const float ks = half_bits_to_float(km & 0xffffu);
+        const float kz = half_bits_to_float(km >> 16);
+        lg[i] = __builtin_fmaf(dot * lc.c1, ks, __builtin_fmaf(lc.c2, kz, -mref));
+        if (kMasked) {
+            valid[i] = (hb ? tokB : tokA) + 4 * g + i < lim;
+            lg[i] = valid[i] ? lg[i] : -INFINITY;
         }
-#pragma unroll
-        for (int i = 0; i < 8; i++) lg[i] = valid[i] ? lg[i] : -INFINITY;
     }
-    float lmax = lg[0];
-#pragma unroll
-    for (int i = 1; i < 8; i++) lmax = fmaxf(lmax, lg[i]);
+    float lmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
     if (first || __any(lmax > 0.0f)) {
-        float cm = fmaxf(lmax, xor_lane(lmax, 16));
+        float cm = fmaxf(lmax, row_swap8(lmax));
+        cm = fmaxf(cm, xor_lane(cm, 16));
         cm = fmaxf(cm, xor_lane(cm, 32));
         const float m_new = first ? cm : fmaxf(st.m, cm + mref);
         const float f = first ? 0.0f : fast_exp2(st.m - m_new);
@@ -325,33 +331,43 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
         st.m = m_new;
         const float shift = (kMasked && first && m_new == -INFINITY) ? 0.0f : (m_new + kLazyThreshold) - mref;
 #pragma unroll
-        for (int i = 0; i < 8; i++) lg[i] -= shift;
+        for (int i = 0; i < 4; i++) lg[i] -= shift;
     }
     // Weights are exp2(l - m - 8) <= 1 (the lazy threshold is folded into the
     // exponent), so w = p * s_v <= s_v stays inside fp16 for any value scale
     // the format can store; l and zacc carry the same factor, which cancels.
-    const uint32_t vm[8] = {A.vm.x, A.vm.y, A.vm.z, A.vm.w, B.vm.x, B.vm.y, B.vm.z, B.vm.w};
-    v8h bw;
+    _Float16 wh[4], wl[4];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < 4; i++) {
         const float p = fast_exp2(lg[i]);
-        const float vs = half_bits_to_float(vm[i] & 0xffffu);
-        const float vz = half_bits_to_float(vm[i] >> 16);
-        float w;
+        const uint32_t vm = hb ? vmB[i] : vmA[i];
+        const float vs = half_bits_to_float(vm & 0xffffu);
+        const float vz = half_bits_to_float(vm >> 16);
+        st.l += p;
+        // w = p s_v as fp16 plus the residual fl(p s_v - fp16(w)): the value
+        // sum is carried to ~2^-22
+        _Float16 h = (_Float16)__builtin_fmaf(p, vs, 0.0f);
+        _Float16 r = (_Float16)__builtin_fmaf(p, vs, -(float)h);
         if (kMasked) {
-            st.l += p;
             st.z += valid[i] ? p * vz : 0.0f;
-            w = valid[i] ? __builtin_fmaf(p, vs, 0.0f) : 0.0f;
+            h = valid[i] ? h : (_Float16)0.0f;
+            r = valid[i] ? r : (_Float16)0.0f;
         } else {
-            st.l += p;
             st.z = __builtin_fmaf(p, vz, st.z);
-            w = __builtin_fmaf(p, vs, 0.0f);
         }
-        // columns n < 8 take fp16(w), columns n >= 8 the exact residual
-        // w - fp16(w), so that the value sum is carried to ~2^-22
-        const _Float16 w_hi = (_Float16)w;
-        bw[i] = (_Float16)fmaf((float)w_hi, lc.res_k, w);
+        wh[i] = h;
+        wl[i] = r;
     }
+    const int own_hi[2] = {__builtin_bit_cast(int, v2h{wh[0], wh[1]}), __builtin_bit_cast(int, v2h{wh[2], wh[3]})};
+    const int own_lo[2] = {__builtin_bit_cast(int, v2h{wl[0], wl[1]}), __builtin_bit_cast(int, v2h{wl[2], wl[3]})};
+    // page A's dwords: lanes n + 8 (banks 2, 3 of a row) take w_lo from lane
+    // n; page B's: lanes n < 8 (banks 0, 1) take w_hi from lane n + 8
+    uint4 bwu;
+    bwu.x = (uint32_t)__builtin_amdgcn_update_dpp(own_hi[0], own_lo[0], 0x128, 0xF, 0xC, false);
+    bwu.y = (uint32_t)__builtin_amdgcn_update_dpp(own_hi[1], own_lo[1], 0x128, 0xF, 0xC, false);
+    bwu.z = (uint32_t)__builtin_amdgcn_update_dpp(own_lo[0], own_hi[0], 0x128, 0xF, 0x3, false);
+    bwu.w = (uint32_t)__builtin_amdgcn_update_dpp(own_lo[1], own_hi[1], 0x128, 0xF, 0x3, false);
+    const v8h bw = __builtin_bit_cast(v8h, bwu);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         // tokens 4g, 4g+1 | 4g+2, 4g+3 of page A, then of page B
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     LaneConsts lc;
     lc.c1 = s_c1[n16 & 7];
     lc.c2 = s_c2[n16 & 7];
-    lc.res_k = n16 < 8 ? 0.0f : -1.0f;
+    lc.hb = n16 >= 8;
 
     State st;
     st.m = -INFINITY;
@@ -668,6 +684,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kWaves) masked_pair(npairs - 2);
 
     // ---- merge the 4 waves; write the partial (or the output) ----
+    st.l += row_swap8(st.l);     // the two halves of the lane pair's tokens
+    st.z += row_swap8(st.z);
     merge_and_store<kMQ>(st, s_merge, a, 1,
                     [](int j) {
                         return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : VB == 3 ? value3_unscale_log2(j) : 20);
@@ -840,6 +858,11 @@ int resident_workgroups() {
         (void)hipGetLastError();
         return 512;
     }
+    // Plan for two work-groups per CU even where three would fit (k4v2 at
+    // 166 VGPRs): measured at 16K and 128K, three per CU made the split
+    // kernel ~1.2 us slower, and the extra splits push the combine onto its
+    // wide path.
+    if (per_cu > 2) per_cu = 2;
     cached[dev] = cus * per_cu;
     return cached[dev];
 }
