@@ -104,24 +104,25 @@ __device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffse
                                           PageRegs<KB, VB> &r) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(region), (short)0, Layout<KB, VB>::kBytes, 0x00020000);
-    if (KB == 3) {
+    if constexpr (KB == 3) {
         const v3u k = __builtin_amdgcn_raw_buffer_load_b96(rs, o.k, 0, 0);
-        r.k[0] = k.x; r.k[1] = k.y; r.k[KB > 2 ? 2 : 0] = k.z;
-    }
+        r.k[0] = k.x; r.k[1] = k.y; r.k[2] = k.z;
+    } else {
 #pragma unroll
-    for (int h = 0; h < KB / 4; h++) {
-        const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 16 * h, 0, 0);
-        r.k[4 * h] = k.x; r.k[4 * h + 1] = k.y; r.k[4 * h + 2] = k.z; r.k[4 * h + 3] = k.w;
+        for (int h = 0; h < KB / 4; h++) {
+            const v4u k = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k + 16 * h, 0, 0);
+            r.k[4 * h] = k.x; r.k[4 * h + 1] = k.y; r.k[4 * h + 2] = k.z; r.k[4 * h + 3] = k.w;
+        }
     }
-    if (VB == 2) {
+    if constexpr (VB == 2) {
         const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, o.v, 0, 0);
         r.v[0] = v.x; r.v[1] = v.y;
-    } else if (VB == 3) {
+    } else if constexpr (VB == 3) {
         const v3u v = __builtin_amdgcn_raw_buffer_load_b96(rs, o.v, 0, 0);
-        r.v[0] = v.x; r.v[1] = v.y; r.v[VB > 2 ? 2 : 0] = v.z;
+        r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z;
     } else {
         const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v, 0, 0);
-        r.v[0] = v.x; r.v[1] = v.y; r.v[VB > 2 ? 2 : 0] = v.z; r.v[VB > 2 ? 3 : 1] = v.w;
+        r.v[0] = v.x; r.v[1] = v.y; r.v[2] = v.z; r.v[3] = v.w;
     }
     const v4u km = __builtin_amdgcn_raw_buffer_load_b128(rs, o.km, 0, 0);
     const v4u vm = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vm, 0, 0);
