@@ -31,6 +31,10 @@
 //     column n; a DPP row rotation by 8 adds the partner column.
 //   Softmax: base 2, fp32, running max per head, rescaled lazily (only when a
 //     page's score exceeds the running max by more than 8, i.e. p <= 256).
+//     The per-token work (fold, exp, weight, sums) is split between the two
+//     lanes of a column pair: lane n < 8 takes page A's 4 tokens, lane n + 8
+//     page B's, and one bank-masked DPP move per dword hands each lane the
+//     weight half it lacks.
 //   Values: v_mfma_f32_16x16x32_f16, A = value codes (row = channel 16j + m,
 //     k = 8 tokens: 4 of each page), B = w = p * s_v (k = the same 8 tokens):
 //     column n < 8 holds fp16(w) of head n, column n + 8 the residual
