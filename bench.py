@@ -77,7 +77,7 @@ def parse():
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the decode of the other workload shapes (Qwen3-4B, Qwen3-30B-A3B, Llama-3.1-70B)")
     ap.add_argument("--no-read-ceiling", action="store_true",
-                    help="skip the measured streaming-read ceiling (kvq_stream_read_probe)")
+                    help="skip the measured read ceilings (kvq_stream_read_probe, kvq_page_walk_probe)")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
@@ -228,6 +228,37 @@ def read_ceiling(torch, lib, dev, stream, nbytes, copies, launches):
     return {"kernel": "stream_read_kernel", "bytes_per_launch": nb, "us_per_launch": round(us, 3),
             "GBps": round(nb / us / 1e3, 1), "steady_2GiB_GBps": round((2 << 30) / big_us / 1e3, 1),
             "launches": launches}
+
+
+def page_walk_ceiling(torch, lib, fmt, dev, stream, pools, bt, lens, B, Hkv, max_len, pps, launches):
+    """The decode's own page walk without its arithmetic (kvq_page_walk_probe):
+    the same pool copies, block table, sequence lengths and split size, the
+    same work decomposition and bytes, launched back to back.  The rate of
+    the decode's access pattern (random page regions), beside the plain
+    sequential read."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    P = ctypes.c_void_p
+    sp = P(stream.cuda_stream)
+    fn = lib.kvq_page_walk_probe
+    args = [(ctypes.byref(fmt), P(p.data_ptr()), ctypes.c_int64(p.shape[0]), P(bt.data_ptr()),
+             ctypes.c_int32(bt.shape[1]), P(lens.data_ptr()), ctypes.c_int32(B), ctypes.c_int32(Hkv),
+             ctypes.c_int32(max_len), ctypes.c_int32(pps), P(sink.data_ptr()), sp) for p in pools]
+    torch.cuda.synchronize()
+    bad = 0
+    for i in range(5):
+        bad |= fn(*args[i % len(args)])
+    ev = HipEvents(2)
+    ev.record(0, stream.cuda_stream)
+    for i in range(launches):
+        bad |= fn(*args[i % len(args)])
+    ev.record(1, stream.cuda_stream)
+    torch.cuda.synchronize()
+    if bad:
+        raise RuntimeError("kvq_page_walk_probe failed")
+    us = ev.elapsed_ms(0, 1) / launches * 1e3
+    ev.close()
+    return {"kernel": "page_walk_kernel", "us_per_launch": round(us, 3), "launches": launches,
+            "pages_per_split": pps}
 
 
 def cpu_model() -> str:
@@ -411,9 +442,11 @@ def main():
         warm_ms = hw.elapsed_ms(0, 1) / nl
         hw.close()
     traffic, traffic_note = recorded_traffic()
-    ceiling = None
+    ceiling = walk = None
     if not args.no_read_ceiling:
         ceiling = read_ceiling(torch, lib, dev, stream, B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD, len(pools), nl)
+        walk = page_walk_ceiling(torch, lib, fmt, dev, stream, pools, bt, lens, B, Hkv, n,
+                                 pps or kvq.decode_pages_per_split(B, Hq, Hkv, n), nl)
 
     kv_bytes = B * n * Hkv * KV_BYTES_PER_TOKEN_HEAD
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -443,6 +476,13 @@ def main():
         # device: the rate the decode's page walk is measured against
         ceiling["decode_frac_of_it"] = round(achieved / ceiling["GBps"], 4)
         result["roofline"]["measured_read_ceiling"] = ceiling
+    if walk:
+        # the decode's own reads (same pages, order and decomposition) with
+        # no arithmetic: the ceiling of its access pattern
+        walk["bytes_per_launch"] = kv_bytes
+        walk["GBps"] = round(kv_bytes / walk["us_per_launch"] / 1e3, 1)
+        walk["decode_frac_of_it"] = round(achieved / walk["GBps"], 4)
+        result["roofline"]["measured_page_walk_ceiling"] = walk
 
     if ev_ms:
         result["kernel_events_in_steps"] = {

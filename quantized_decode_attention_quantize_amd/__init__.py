@@ -93,6 +93,7 @@ def load():
                                                    i32, i32, ctypes.c_float, P, sz, i32, P]),
         "kvq_set_split_kernel_events": (ctypes.c_int, [P, P]),
         "kvq_stream_read_probe": (ctypes.c_int, [P, sz, P, P]),
+        "kvq_page_walk_probe": (ctypes.c_int, [FP, P, i64, P, i32, P, i32, i32, i32, i32, P, P]),
         "kvq_decode_split_slots": (i32, [FP, i32, i32, i32, i32, i32]),
         "kvq_decode_partials_slots": (ctypes.c_int, [FP, P, P, i64, P, i32, P, i32, i32, i32, i32,
                                                      ctypes.c_float, P, sz, i32, i32, i32, i32, P]),

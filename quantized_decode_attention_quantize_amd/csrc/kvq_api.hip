@@ -474,6 +474,37 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, void *out, kvq_out_dtype 
                                    max_seq_len, softmax_scale, workspace, workspace_bytes, 0, stream);
 }
 
+kvq_status kvq_page_walk_probe(const kvq_format *fmt, const uint8_t *cache, int64_t num_pages,
+                               const int32_t *block_tables, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                               int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                               int32_t pages_per_split, uint32_t *sink, void *stream) {
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_quant(fmt) || fmt->block_size != 16) return KVQ_ERR_UNSUPPORTED;
+    if (!cache || !block_tables || !seq_lens || !sink) return KVQ_ERR_NULL;
+    if (num_pages <= 0 || num_seqs <= 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
+        max_seq_len <= 0 || max_pages_per_seq <= 0 ||
+        (int64_t)max_seq_len > (int64_t)max_pages_per_seq * fmt->block_size || pages_per_split < 2 ||
+        (pages_per_split % 2) || pages_per_split > kvq::kMaxPagesPerSplit)
+        return KVQ_ERR_SHAPE;
+    if (!aligned16(cache) || ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u) ||
+        ((uintptr_t)sink & 3u))
+        return KVQ_ERR_ALIGN;
+    const int64_t splits = ceil_div(ceil_div(max_seq_len, kvq::kPage), pages_per_split);
+    if (splits > 65535) return KVQ_ERR_SHAPE;
+    kvq::PageWalkArgs a;
+    a.cache = cache;
+    a.num_pages = num_pages;
+    a.region16 = (int32_t)(region_bytes(fmt) / 16);
+    a.num_kv_heads = num_kv_heads;
+    a.block_tables = block_tables;
+    a.bt_stride = max_pages_per_seq;
+    a.seq_lens = seq_lens;
+    a.max_seq_len = max_seq_len;
+    a.pages_per_split = pages_per_split;
+    a.sink = sink;
+    return hip_status(kvq::launch_page_walk(a, (int32_t)splits, num_seqs, (hipStream_t)stream));
+}
+
 kvq_status kvq_stream_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream) {
     if (!buffer || !sink) return KVQ_ERR_NULL;
     if (bytes == 0 || (bytes % 16) || bytes > ((size_t)1 << 40)) return KVQ_ERR_SHAPE;

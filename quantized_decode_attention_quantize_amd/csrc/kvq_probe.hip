@@ -3,7 +3,9 @@
 // ceiling that this machine reaches and not only against the vendor peak
 // (decode streams the whole cache through HBM once per token: encorp.ai,
 // "KV cache compression is an infrastructure decision, not a model debate",
-// section on the HBM ceiling).  Not part of the decode path.
+// section on the HBM ceiling); and a page-walk probe, the decode's own reads
+// without its arithmetic, for the ceiling of its access pattern.  Neither is
+// part of the decode path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,7 +38,92 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *src, int6
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Page-walk read: the bytes a decode split kernel reads, in its work
+// decomposition, without its arithmetic.  Work-group (split, KV head,
+// sequence) of 4 waves; wave w walks page pairs w, w + 4, ... of the split
+// with the page ids of the block table, each lane holding the ids of one of
+// its pairs (as the decode kernel does), and three pairs' loads in flight.
+// A 16-token region of region16 16-byte words is read with lanes striding
+// over its words (up to kWalkWords per lane).
+constexpr int kWalkWaves = 4;
+constexpr int kWalkWords = 4;          // 16-byte words per lane and region (regions up to 4 KB)
+
+struct WalkRegs {
+    uint4 w[2][kWalkWords];
+};
+
+__global__ __launch_bounds__(256) void page_walk_kernel(PageWalkArgs a) {
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > a.max_seq_len ? a.max_seq_len : n);
+    const int npages = (n + 15) / 16;
+    const int p_begin = split * a.pages_per_split;
+    if (p_begin >= npages) return;
+    const int p_end = min(p_begin + a.pages_per_split, npages);
+    const int32_t *bt = a.block_tables + (int64_t)b * a.bt_stride;
+    const int last = a.bt_stride - 1;
+    int32_t id_a, id_b;
+    {
+        const int pa = p_begin + 2 * (wave + kWalkWaves * lane);
+        id_a = bt[pa < last ? pa : last];
+        id_b = bt[pa + 1 < last ? pa + 1 : last];
+    }
+    const int npairs = (p_end - p_begin + 1) / 2;
+    const int nk = npairs > wave ? (npairs - wave + kWalkWaves - 1) / kWalkWaves : 0;
+    if (nk == 0) return;
+    const int64_t page_stride = (int64_t)a.num_kv_heads * a.region16 * 16;
+    const uint32_t np32 = a.num_pages < 0x7fffffff ? (uint32_t)a.num_pages : 0x7fffffffu;
+    auto issue = [&](WalkRegs &r, int j) {
+        j = j < nk ? j : nk - 1;                // past the end: repeat the wave's last pair
+        const int pa = p_begin + 2 * (wave + kWalkWaves * j);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t id = (uint32_t)__builtin_amdgcn_readlane(h && pa + 1 < p_end ? id_b : id_a, j);
+            if (id >= np32) id = 0;
+            const uint4 *reg = reinterpret_cast<const uint4 *>(a.cache + (int64_t)id * page_stride +
+                                                               (int64_t)kvh * a.region16 * 16);
+#pragma unroll
+            for (int u = 0; u < kWalkWords; u++) {
+                const int wd = lane + 64 * u;
+                r.w[h][u] = wd < a.region16 ? reg[wd] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    uint32_t acc = 0;
+    auto fold = [&](const WalkRegs &r) {
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int u = 0; u < kWalkWords; u++) acc ^= r.w[h][u].x ^ r.w[h][u].y ^ r.w[h][u].z ^ r.w[h][u].w;
+    };
+    WalkRegs r0, r1, r2;
+    issue(r0, 0);
+    issue(r1, 1);
+    issue(r2, 2);
+    fold(r0);
+    for (int i = 1; i < nk; i += 3) {
+        issue(r0, i + 2);
+        fold(r1);
+        if (i + 1 >= nk) break;
+        issue(r1, i + 3);
+        fold(r2);
+        if (i + 2 >= nk) break;
+        issue(r2, i + 4);
+        fold(r0);
+    }
+    if (acc == 0x9E3779B9u) a.sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_page_walk(const PageWalkArgs &a, int32_t splits, int32_t num_seqs, hipStream_t stream) {
+    hipLaunchKernelGGL(page_walk_kernel, dim3((unsigned)splits, (unsigned)a.num_kv_heads, (unsigned)num_seqs),
+                       dim3(64 * kWalkWaves), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream) {
     int dev = 0, cus = 0;

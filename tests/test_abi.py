@@ -314,6 +314,38 @@ def test_stream_read_probe_validation_launches_nothing():
     assert lib.kvq_stream_read_probe(g, 16, P(0x10002), None) == 4
 
 
+def test_page_walk_probe_validation_launches_nothing():
+    lib = kvq.load()
+    P = ctypes.c_void_p
+    g, gs = P(0x10000), P(0x20000)
+    f = kvq.format_from_string()
+    fb = ctypes.byref(f)
+
+    def call(fmt=fb, cache=g, num_pages=64, bt=g, maxp=40, lens=g, B=2, Hkv=2, max_len=640, pps=8, sink=gs):
+        return lib.kvq_page_walk_probe(fmt, cache, num_pages, bt, maxp, lens, B, Hkv, max_len, pps, sink, None)
+
+    assert call(fmt=None) == 1
+    assert call(fmt=ctypes.byref(kvq.format_from_string("fp16"))) == 3
+    assert call(fmt=ctypes.byref(kvq.format_from_string(page_tokens=32))) == 3
+    assert call(cache=None) == 1
+    assert call(bt=None) == 1
+    assert call(lens=None) == 1
+    assert call(sink=None) == 1
+    assert call(num_pages=0) == 2
+    assert call(B=0) == 2
+    assert call(Hkv=0) == 2
+    assert call(max_len=0) == 2
+    assert call(maxp=0) == 2
+    assert call(max_len=641) == 2          # 40 pages of 16 tokens hold at most 640
+    for pps in (0, 1, 7, 514):
+        assert call(pps=pps) == 2
+    assert call(maxp=1 << 24, max_len=(1 << 24) * 16, pps=2) == 2    # more than 65535 splits
+    assert call(cache=P(0x10008)) == 4
+    assert call(bt=P(0x10002)) == 4
+    assert call(lens=P(0x10001)) == 4
+    assert call(sink=P(0x20002)) == 4
+
+
 def test_binding_refuses_host_tensors():
     """The binding never hands a host pointer to a kernel."""
     k = torch.zeros((1, 1, 128), dtype=torch.float16)

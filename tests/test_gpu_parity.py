@@ -432,6 +432,40 @@ def test_stream_read_probe_reads_every_word(dev, n16):
     assert int(sink.cpu()[0]) == 0
 
 
+def test_page_walk_probe_reads_the_decode_regions(dev):
+    """kvq_page_walk_probe (the bench's page-walk ceiling) reads every word of
+    every region the decode reads, and no other: a marked word in a region of
+    a block-table page reaches the sink; one in a page that no block table
+    names does not.  Page counts are even, so no page is read twice (a lone
+    last page is read as both halves of its pair, like the decode's)."""
+    lib = kvq.load()
+    fmt = kvq.format_from_string()
+    B, Hkv, num_pages, maxp, pps = 2, 2, 64, 40, 8
+    lens = [16 * 40, 16 * 17 + 5]                       # 40 and 18 pages
+    perm = np.random.default_rng(5).permutation(num_pages - 2)   # ids 62, 63 never named
+    bt = np.zeros((B, maxp), np.int32)
+    bt[0, :40] = perm[:40]
+    bt[1, :18] = perm[40:58]
+    pool = torch.zeros((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    words = pool.view(torch.int32)                      # [page][head][416]
+    bt_d = torch.from_numpy(bt).to(dev)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    mark = int(np.uint32(0x9E3779B9).view(np.int32))
+    P = ctypes.c_void_p
+    cases = [((int(bt[0, 0]), 0, 0), True), ((int(bt[0, 39]), 1, 415), True), ((int(bt[1, 17]), 1, 200), True),
+             ((int(bt[1, 5]), 0, 103), True), ((62, 0, 5), False), ((63, 1, 415), False)]
+    for (page, head, w), read in cases:
+        log(f"page walk probe mark page={page} head={head} word={w} read={read}")
+        words.zero_()
+        sink.zero_()
+        words[page, head, w] = mark
+        st = lib.kvq_page_walk_probe(ctypes.byref(fmt), P(pool.data_ptr()), num_pages, P(bt_d.data_ptr()), maxp,
+                                     P(lens_d.data_ptr()), B, Hkv, 640, pps, P(sink.data_ptr()), None)
+        assert st == 0
+        assert (int(sink.cpu()[0]) == mark) == read, (page, head, w)
+
+
 def test_decode_zero_query_gives_mean_value(dev):
     B, Hq, Hkv, lens = 1, 4, 1, [123]
     cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, lens, seed=9)
