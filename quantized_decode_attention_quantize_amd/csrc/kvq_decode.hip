@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const bool upper = (l32 & x) != 0;
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float other = xor_lane(q[e], x);
+                const float other = xor_lane_dpp(q[e], x);
                 q[e] = upper ? (other - q[e]) : (q[e] + other);
             }
         }
@@ -592,8 +592,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float qs = q[0] + q[1] + q[2] + q[3];
 #pragma unroll
         for (int x = 1; x < 32; x <<= 1) {
-            am = fmaxf(am, xor_lane(am, x));
-            qs += xor_lane(qs, x);
+            am = fmaxf(am, xor_lane_dpp(am, x));
+            qs += xor_lane_dpp(qs, x);
         }
         int ex = 0;
         if (am > 0.0f) (void)frexpf(am, &ex);          // am in [2^(ex-1), 2^ex)

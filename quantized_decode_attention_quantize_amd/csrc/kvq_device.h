@@ -74,6 +74,18 @@ __device__ __forceinline__ float row_swap8(float v) {
         __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
 }
 
+// Value of lane l ^ x for a constant x (the loops that call it are
+// unrolled): one DPP move for x = 1, 2 (quad permutes) and 8 (row rotation
+// by 8), a cross-lane permute through the LDS crossbar otherwise.  The
+// values are the same as xor_lane's; only the transport differs.
+__device__ __forceinline__ float xor_lane_dpp(float v, int x) {
+    const int b = __builtin_bit_cast(int, v);
+    return x == 1   ? __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false))
+           : x == 2 ? __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false))
+           : x == 8 ? __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false))
+                    : xor_lane(v, x);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
 }
