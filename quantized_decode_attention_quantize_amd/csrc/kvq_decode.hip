@@ -102,12 +102,14 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 // `region` is wave-uniform: it becomes a buffer resource in scalar registers
 // (the region's byte range, so the hardware bounds-checks every access) and
 // the per-lane 32-bit offsets are loop invariant, so a page costs four to six
-// buffer loads and no vector address arithmetic.
+// buffer loads and no vector address arithmetic.  live = false gives the
+// resource no bytes: every load is out of range and returns zeros without a
+// memory access (the prefetch past a wave's last pair).
 template <int KB, int VB>
 __device__ __forceinline__ void load_page(const uint8_t *region, const LaneOffsets<KB, VB> &o,
-                                          PageRegs<KB, VB> &r) {
+                                          PageRegs<KB, VB> &r, bool live = true) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(region), (short)0, Layout<KB, VB>::kBytes, 0x00020000);
+        const_cast<uint8_t *>(region), (short)0, live ? Layout<KB, VB>::kBytes : 0, 0x00020000);
     if constexpr (KB == 3) {
         const v3u k = __builtin_amdgcn_raw_buffer_load_b96(rs, o.k, 0, 0);
         r.k[0] = k.x; r.k[1] = k.y; r.k[2] = k.z;
@@ -499,8 +501,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // split, every token seen by every query row), the rest -- the last one
     // or two (query rows span at most 16 tokens) -- are masked.  Wave w takes
     // pairs w, w + 4, ...; full pairs run through a triple-buffered loop whose
-    // loads are always issued (past the end they repeat the wave's last pair),
-    // so two pairs are in flight while one is computed.  A masked pair is
+    // loads are always issued (past the end as loads that read nothing), so
+    // two pairs are in flight while one is computed.  A masked pair is
     // loaded and processed afterwards with per-token masking.
     const int full_end = min(p_end, n_min / kPage);       // pages below: full
     const int nfull = full_end > p_begin ? (full_end - p_begin) >> 1 : 0;
@@ -509,11 +511,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // The scheduling barrier keeps the compiler from sinking the prefetch
     // loads into the next pair's arithmetic (which it otherwise does to save
     // registers, leaving the current pair's loads as the newest in flight).
+    // Past the wave's last pair the loads stay in the instruction stream (so
+    // that every wait count in the loop is the same on every path) but read
+    // nothing: measured, 0.2 us per launch at 16K against re-reading the
+    // last pair, and ~14 MB less cache traffic per launch.
     auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, int i) {
         const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
         const int pa = kPaged ? p_begin + 2 * (wave + kWaves * j) : 0;
-        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j), pa), lo, A);
-        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1), lo, B);
+        const bool live = i < nk;
+        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j), pa), lo, A, live);
+        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1), lo, B, live);
         __builtin_amdgcn_sched_barrier(0);
     };
     // Fused append: a work-group whose split holds the sequence's last token
