@@ -19,7 +19,8 @@ struct State {
 };
 
 // In-place unnormalised Hadamard transform of one head's 128 values held by
-// 32 lanes (lane32 = lane & 31), 4 channels each: 2 stages in-lane, 5 across.
+// 32 lanes (lane32 = lane & 31), 4 channels each: 2 stages in-lane, 5 across
+// (partners 1, 2 and 8 lanes apart by DPP moves, 4 and 16 by permutes).
 __device__ __forceinline__ void hadamard_128(float (&y)[4], int lane32) {
     {
         float p = y[0], q = y[1]; y[0] = p + q; y[1] = p - q;
@@ -32,7 +33,7 @@ __device__ __forceinline__ void hadamard_128(float (&y)[4], int lane32) {
         const bool upper = (lane32 & x) != 0;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const float other = xor_lane(y[e], x);
+            const float other = xor_lane_dpp(y[e], x);
             y[e] = upper ? (other - y[e]) : (y[e] + other);
         }
     }
