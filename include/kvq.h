@@ -399,7 +399,12 @@ kvq_status kvq_decode_combine_slots(void *out, kvq_out_dtype out_dtype, int32_t 
                                     const void *workspace, size_t workspace_bytes, int32_t total_slots,
                                     int32_t rotated, void *stream);
 
-/* Pages per split the heuristic picks for these sizes (0 on invalid input). */
+/* Pages per split the heuristic picks for these sizes with the K4V2 format
+ * (0 on invalid input).  The heuristic plans one round of work-groups: the
+ * device's compute units times the work-groups per unit that fit (at most
+ * two), divided among the (sequence, KV head, head group) units, rounded up
+ * to whole page pairs and capped at 512 pages.  The other formats' choice
+ * shows in kvq_decode_split_slots and kvq_decode_workspace_bytes. */
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t max_seq_len);
 
