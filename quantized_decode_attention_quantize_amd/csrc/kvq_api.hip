@@ -62,14 +62,18 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerGroup); }
 
 // Split heuristic: one round of resident work-groups.  A (sequence, KV head,
-// head group) unit is cut into S = max(1, resident / units) splits of equal
+// work-group of head groups) unit is cut into S = max(1, resident / units) splits of equal
 // page count (rounded up to a page pair), so every work-group starts at once,
 // carries the same work, and pays its fixed cost (query rotation, wave merge,
 // partial write) once.
 int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
                       int32_t k_bits = 4, int32_t v_bits = 2) {
     const bool fp16 = k_bits == 16;
-    const int64_t units = (int64_t)num_seqs * num_kv_heads * head_groups(num_q_heads / num_kv_heads);
+    // work-groups per (sequence, KV head): the quantised kernel takes two head
+    // groups per work-group when there are several; the fp16 kernel one
+    const int64_t hgs = head_groups(num_q_heads / num_kv_heads);
+    const int64_t wgs = fp16 || hgs < 2 ? hgs : (hgs + 1) / 2;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * wgs;
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
     const int64_t resident = fp16 ? kvq::decode_fp16_resident_workgroups()
                                   : kvq::decode_resident_workgroups(k_bits, v_bits);

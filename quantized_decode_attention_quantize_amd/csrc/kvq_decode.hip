@@ -178,6 +178,16 @@ __device__ __forceinline__ v8h key_codes3(const uint32_t (&pl)[3], int d) {
     return __builtin_bit_cast(v8h, make_uint4(u[0], u[1], u[2], u[3]));
 }
 
+// Key-code A operand of k-step q (32 channels) of one page.
+template <int KB, int VB>
+__device__ __forceinline__ v8h key_operand(const PageRegs<KB, VB> &r, int q) {
+    if (KB == 3) {
+        const uint32_t pl[3] = {r.k[0], r.k[1 % KB], r.k[2 % KB]};
+        return key_codes3(pl, q);
+    }
+    return KB == 4 ? key_codes(r.k[q]) : key_codes8(r.k[(2 * q) % KB], r.k[(2 * q + 1) % KB]);
+}
+
 // Code-domain dot products of the lane's 4 tokens (4g..4g+3) of one page:
 // v_mfma_f32_16x16x32_f16 x 4 (32 channels per instruction and lane-group),
 // columns n < 8 the fp16 query q_hi of head n, columns n >= 8 its residual
@@ -187,16 +197,7 @@ template <int KB, int VB>
 __device__ __forceinline__ v4f page_dots(const PageRegs<KB, VB> &r, const v8h (&bq)[4]) {
     v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        v8h a;
-        if (KB == 3) {
-            const uint32_t pl[3] = {r.k[0], r.k[1 % KB], r.k[2 % KB]};
-            a = key_codes3(pl, q);
-        } else {
-            a = KB == 4 ? key_codes(r.k[q]) : key_codes8(r.k[(2 * q) % KB], r.k[(2 * q + 1) % KB]);
-        }
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[q], d, 0, 0, 0);
-    }
+    for (int q = 0; q < 4; q++) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_operand<KB, VB>(r, q), bq[q], d, 0, 0, 0);
     return d;
 }
 
@@ -276,7 +277,27 @@ struct LaneConsts {
     bool hb;               // lane n >= 8 (weights page B's tokens; n < 8: page A's)
 };
 
-// One page pair.  kMasked: tokens at or beyond this lane's limit `lim` (the
+// Value-code A operand of channel block j for the page pair: tokens 4g,
+// 4g+1 | 4g+2, 4g+3 of page A, then of page B.
+template <int KB, int VB>
+__device__ __forceinline__ v8h value_operand(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int j) {
+    uint4 packed;
+    if (VB == 2) {
+        packed = {value_code(A.v[0], j), value_code(A.v[1], j), value_code(B.v[0], j), value_code(B.v[1], j)};
+    } else if (VB == 3) {
+        const uint32_t wa[3] = {A.v[0], A.v[1 % VB], A.v[2 % VB]};
+        const uint32_t wb[3] = {B.v[0], B.v[1 % VB], B.v[2 % VB]};
+        packed = {value_code3(wa, j, 0), value_code3(wa, j, 1), value_code3(wb, j, 0), value_code3(wb, j, 1)};
+    } else {
+        const int h = j >> 2, k = j & 3;
+        packed = {value_code4(A.v[h], k), value_code4(A.v[(2 + h) % VB], k), value_code4(B.v[h], k),
+                  value_code4(B.v[(2 + h) % VB], k)};
+    }
+    return __builtin_bit_cast(v8h, packed);
+}
+
+// Softmax weights of one page pair for one head group, from the code-domain
+// dot products dA, dB of its pages.  kMasked: tokens at or beyond this lane's limit `lim` (the
 // tokens its query row sees; page A starts at token tokA, page B at tokB;
 // tokB >= every limit marks an absent page B) take no weight, whatever their
 // (possibly never written) slots hold.  kFirst: the wave's first pair, which
@@ -297,15 +318,12 @@ struct LaneConsts {
 // column n + 8 w_lo for all 8 tokens.  l and zacc are per-lane halves,
 // added across the pair before the merge.
 template <int KB, int VB, bool kMasked, bool kFirst>
-__device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
-                                             int tokB,
-                                             int lim, const v8h (&bq)[4], const LaneConsts &lc,
-                                             int g, State &st) {
+__device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, const v4f &dA,
+                                            const v4f &dB, int tokA, int tokB, int lim, const LaneConsts &lc,
+                                            int g, State &st) {
     constexpr bool first = kFirst;
     const bool hb = lc.hb;
     const float mref = first ? 0.0f : st.m + kLazyThreshold;
-    const v4f dA = page_dots<KB, VB>(A, bq);
-    const v4f dB = page_dots<KB, VB>(B, bq);
     const uint32_t kmA[4] = {A.km.x, A.km.y, A.km.z, A.km.w}, kmB[4] = {B.km.x, B.km.y, B.km.z, B.km.w};
     const uint32_t vmA[4] = {A.vm.x, A.vm.y, A.vm.z, A.vm.w}, vmB[4] = {B.vm.x, B.vm.y, B.vm.z, B.vm.w};
     float lg[4];
@@ -374,35 +392,62 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
     bwu.y = (uint32_t)__builtin_amdgcn_update_dpp(own_hi[1], own_lo[1], 0x128, 0xF, 0xC, false);
     bwu.z = (uint32_t)__builtin_amdgcn_update_dpp(own_lo[0], own_hi[0], 0x128, 0xF, 0x3, false);
     bwu.w = (uint32_t)__builtin_amdgcn_update_dpp(own_lo[1], own_hi[1], 0x128, 0xF, 0x3, false);
-    const v8h bw = __builtin_bit_cast(v8h, bwu);
+    return __builtin_bit_cast(v8h, bwu);
+}
+
+// One page pair for kG head groups of 8 query heads (kG = 2: 16 heads, when
+// a KV head has more than 8 query heads or query rows): the key and value
+// operands are unpacked once and feed every group's MFMAs; each group keeps
+// its own softmax state.  lim[h]: group h's token limit (kMasked).
+template <int KB, int VB, int kG, bool kMasked, bool kFirst>
+__device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
+                                             int tokB, const int (&lim)[kG], const v8h (&bq)[kG][4],
+                                             const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
+    v8h bw[kG];
+    if constexpr (kG == 1) {
+        const v4f dA = page_dots<KB, VB>(A, bq[0]);
+        const v4f dB = page_dots<KB, VB>(B, bq[0]);
+        bw[0] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim[0], lc[0], g, st[0]);
+    } else {
+        // each k-step's key operands feed every group's MFMAs as they are
+        // unpacked, so that only one operand per page is live at a time
+        v4f dA[kG], dB[kG];
+#pragma unroll
+        for (int h = 0; h < kG; h++) dA[h] = dB[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const v8h ka = key_operand<KB, VB>(A, q);
+            const v8h kb = key_operand<KB, VB>(B, q);
+#pragma unroll
+            for (int h = 0; h < kG; h++) {
+                dA[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, bq[h][q], dA[h], 0, 0, 0);
+                dB[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq[h][q], dB[h], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kG; h++)
+            bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], g, st[h]);
+    }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        // tokens 4g, 4g+1 | 4g+2, 4g+3 of page A, then of page B
-        uint4 packed;
-        if (VB == 2) {
-            packed = {value_code(A.v[0], j), value_code(A.v[1], j), value_code(B.v[0], j), value_code(B.v[1], j)};
-        } else if (VB == 3) {
-            const uint32_t wa[3] = {A.v[0], A.v[1 % VB], A.v[2 % VB]};
-            const uint32_t wb[3] = {B.v[0], B.v[1 % VB], B.v[2 % VB]};
-            packed = {value_code3(wa, j, 0), value_code3(wa, j, 1), value_code3(wb, j, 0), value_code3(wb, j, 1)};
-        } else {
-            const int h = j >> 2, k = j & 3;
-            packed = {value_code4(A.v[h], k), value_code4(A.v[(2 + h) % VB], k), value_code4(B.v[h], k),
-                      value_code4(B.v[(2 + h) % VB], k)};
-        }
-        const v8h av = __builtin_bit_cast(v8h, packed);
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw, st.acc[j], 0, 0, 0);
+        const v8h av = value_operand<KB, VB>(A, B, j);
+#pragma unroll
+        for (int h = 0; h < kG; h++)
+            st[h].acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[h], st[h].acc[j], 0, 0, 0);
     }
 }
 
-template <int KB, int VB, bool kMQ, bool kPaged>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+// kG: head groups (of 8 query heads, or (row, head) pairs) per work-group;
+// 2 when a KV head has more than 8, so that they share the page unpack.
+template <int KB, int VB, bool kMQ, bool kPaged, int kG>
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     using Lay = Layout<KB, VB>;
-    int split, kvh, hg, b;
+    const int sgroups = (a.head_groups + kG - 1) / kG;   // work-groups per (split, KV head, sequence)
+    int split, kvh, sg, b;
     if (!kMQ) {
         split = blockIdx.x;
-        kvh = blockIdx.y / a.head_groups;
-        hg = blockIdx.y % a.head_groups;
+        kvh = blockIdx.y / sgroups;
+        sg = blockIdx.y % sgroups;
         b = blockIdx.z;
     } else {
         // One-dimensional grid, XCD-aware: work-groups are dispatched to the 8
@@ -412,8 +457,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // served by that XCD's L2.  Blocks past the work (the grid is padded
         // to whole rounds) exit at once.
         const int L = blockIdx.x;
-        hg = (L >> 3) % a.head_groups;
-        const int64_t w = (int64_t)((L >> 3) / a.head_groups) * 8 + (L & 7);
+        sg = (L >> 3) % sgroups;
+        const int64_t w = (int64_t)((L >> 3) / sgroups) * 8 + (L & 7);
         const int64_t units = (int64_t)a.splits * a.num_kv_heads * a.num_seqs;
         if (w >= units) return;
         split = (int)(w % a.splits);
@@ -447,13 +492,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // after the first pages would hold the query prologue until those pages
     // had arrived (measured: the prologue then ended ~4.4 us after the wave
     // started, against ~1 us for the page ids).
-    const int nh = min(kHeadsPerGroup, a.gqa - hg * kHeadsPerGroup);
-    uint2 qraw = make_uint2(0u, 0u);
-    {
+    const int hg0 = sg * kG;                 // first head group of this work-group
+    int nh[kG];                              // heads of each group (0: a padding group)
+    uint2 qraw[kG];
+#pragma unroll
+    for (int h = 0; h < kG; h++) {
+        nh[h] = max(0, min(kHeadsPerGroup, a.gqa - (hg0 + h) * kHeadsPerGroup));
+        qraw[h] = make_uint2(0u, 0u);
         const int hh = 2 * wave + (lane >> 5);
-        if (hh < nh)
-            qraw = *reinterpret_cast<const uint2 *>(a.query + io_row<kMQ>(a, b, kvh, hg * kHeadsPerGroup + hh) * kHeadDim +
-                                                    4 * (lane & 31));
+        if (hh < nh[h])
+            qraw[h] = *reinterpret_cast<const uint2 *>(
+                a.query + io_row<kMQ>(a, b, kvh, (hg0 + h) * kHeadsPerGroup + hh) * kHeadDim + 4 * (lane & 31));
     }
 
     const int max_len = a.max_seq_len;
@@ -469,13 +518,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int p_begin = split * pps;
 
     if (p_begin >= npages) {         // an empty sequence, or a split past its end
-        write_empty<kMQ>(a, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
+#pragma unroll
+        for (int h = 0; h < kG; h++)
+            if (nh[h] > 0) write_empty<kMQ>(a, tid, b, kvh, (hg0 + h) * kHeadsPerGroup, nh[h], split);
         return;
     }
     const int p_end = min(p_begin + pps, npages);
 
-    __shared__ _Float16 s_qb[16][kHeadDim];   // [column][slot], slot = 32g + 8d + e
-    __shared__ float s_c1[kHeadsPerGroup], s_c2[kHeadsPerGroup];
+    __shared__ _Float16 s_qb[kG][16][kHeadDim];   // [group][column][slot], slot = 32g + 8d + e
+    __shared__ float s_c1[kG][kHeadsPerGroup], s_c2[kG][kHeadsPerGroup];
     __shared__ MergeLds s_merge;
 
     // ---- page-pair loop ----
@@ -567,19 +618,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         issue(r2A, r2B, 2);
     }
 
-    // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 ----
+    // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 of each group ----
     // q' = H q in fp32, scaled by a power of two so that max |q'| lies in
     // [2^13, 2^14), then written as q_hi = fp16(q'), q_lo = fp16(q' - q_hi):
     // the two-term query carries q' to about 2^-22 of each element.
-    {
+#pragma unroll
+    for (int hq = 0; hq < kG; hq++) {
         const int hh = 2 * wave + (lane >> 5);
         const int l32 = lane & 31;
         const int c0 = 4 * l32;
         float q[4];
-        q[0] = half_bits_to_float(qraw.x & 0xffffu);   // zero for heads past the group
-        q[1] = half_bits_to_float(qraw.x >> 16);
-        q[2] = half_bits_to_float(qraw.y & 0xffffu);
-        q[3] = half_bits_to_float(qraw.y >> 16);
+        q[0] = half_bits_to_float(qraw[hq].x & 0xffffu);   // zero for heads past the group
+        q[1] = half_bits_to_float(qraw[hq].x >> 16);
+        q[2] = half_bits_to_float(qraw[hq].y & 0xffffu);
+        q[3] = half_bits_to_float(qraw[hq].y >> 16);
         {
             float p = q[0], r = q[1]; q[0] = p + r; q[1] = p - r;
             p = q[2]; r = q[3]; q[2] = p + r; q[3] = p - r;
@@ -626,48 +678,51 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
             const float v = __builtin_ldexpf(q[e], shift - down);
             const _Float16 vh = (_Float16)v;
-            s_qb[hh][slot] = vh;
-            s_qb[8 + hh][slot] = (_Float16)(v - (float)vh);
+            s_qb[hq][hh][slot] = vh;
+            s_qb[hq][8 + hh][slot] = (_Float16)(v - (float)vh);
         }
         if (l32 == 0) {
             // dot(q', c) = D * 2^(24 - shift), D the MFMA sum with codes c * 2^-24
-            s_c1[hh] = a.alpha * __builtin_ldexpf(1.0f, 24 - shift);
-            s_c2[hh] = a.alpha * qs;
+            s_c1[hq][hh] = a.alpha * __builtin_ldexpf(1.0f, 24 - shift);
+            s_c2[hq][hh] = a.alpha * qs;
         }
     }
     __syncthreads();
 
     const int n16 = lane & 15;
     const int g = lane >> 4;
-    v8h bq[4];
+    v8h bq[kG][4];
+    LaneConsts lc[kG];
+    State st[kG];
+    const int lim0[kG] = {};                 // unused by unmasked pairs
 #pragma unroll
-    for (int d = 0; d < 4; d++) bq[d] = *reinterpret_cast<const v8h *>(&s_qb[n16][32 * g + 8 * d]);
-    LaneConsts lc;
-    lc.c1 = s_c1[n16 & 7];
-    lc.c2 = s_c2[n16 & 7];
-    lc.hb = n16 >= 8;
-
-    State st;
-    st.m = -INFINITY;
-    st.l = 0.0f;
-    st.z = 0.0f;
+    for (int h = 0; h < kG; h++) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) st.acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int d = 0; d < 4; d++) bq[h][d] = *reinterpret_cast<const v8h *>(&s_qb[h][n16][32 * g + 8 * d]);
+        lc[h].c1 = s_c1[h][n16 & 7];
+        lc[h].c2 = s_c2[h][n16 & 7];
+        lc[h].hb = n16 >= 8;
+        st[h].m = -INFINITY;
+        st[h].l = 0.0f;
+        st[h].z = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) st[h].acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     if (nk > 0) {
         // the wave's first pair sets the running maximum; the loop then
         // rotates the three buffers (pair i in r1, i + 1 in r2, i + 2 in r0)
-        process_pair<KB, VB, false, true>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+        process_pair<KB, VB, kG, false, true>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
         if (nk > 1) {
             for (int i = 1;; i += 3) {
                 issue(r0A, r0B, i + 2);
-                process_pair<KB, VB, false, false>(r1A, r1B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, kG, false, false>(r1A, r1B, 0, 0, lim0, bq, lc, g, st);
                 if (i + 1 >= nk) break;
                 issue(r1A, r1B, i + 3);
-                process_pair<KB, VB, false, false>(r2A, r2B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, kG, false, false>(r2A, r2B, 0, 0, lim0, bq, lc, g, st);
                 if (i + 2 >= nk) break;
                 issue(r2A, r2B, i + 4);
-                process_pair<KB, VB, false, false>(r0A, r0B, 0, 0, 0, bq, lc, g, st);
+                process_pair<KB, VB, kG, false, false>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
                 if (i + 3 >= nk) break;
             }
         }
@@ -675,11 +730,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // Masked pairs: the last pair, and with several query rows possibly the
     // one before it (each the last pair of its wave).
     auto masked_pair = [&](int i) {
-        int lim = n_tokens;                     // the tokens this lane's query row sees
-        if (kMQ) {
-            const int G = a.gqa / M;
-            const int mrow = min((hg * kHeadsPerGroup + (n16 & 7)) / G, M - 1);
-            lim = n_tokens - (M - 1 - mrow);
+        int lim[kG];                            // the tokens this lane's query row sees, per group
+#pragma unroll
+        for (int h = 0; h < kG; h++) {
+            lim[h] = n_tokens;
+            if (kMQ) {
+                const int G = a.gqa / M;
+                const int mrow = min(((hg0 + h) * kHeadsPerGroup + (n16 & 7)) / G, M - 1);
+                lim[h] = n_tokens - (M - 1 - mrow);
+            }
         }
         PageRegs<KB, VB> tA, tB;
         const int pa = p_begin + 2 * i;
@@ -690,21 +749,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         load_page(has_b ? region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1) : region_of(id_a, pa), lo, tB);
         const int tok_b = has_b ? (pa + 1) * kPage : n_tokens;
         if (nk == 0)
-            process_pair<KB, VB, true, true>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
+            process_pair<KB, VB, kG, true, true>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
         else
-            process_pair<KB, VB, true, false>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
+            process_pair<KB, VB, kG, true, false>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
     };
     if (nfull < npairs && wave == (npairs - 1) % kWaves) masked_pair(npairs - 1);
     if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kWaves) masked_pair(npairs - 2);
 
     // ---- merge the 4 waves; write the partial (or the output) ----
-    st.l += row_swap8(st.l);     // the two halves of the lane pair's tokens
-    st.z += row_swap8(st.z);
-    merge_and_store<kMQ>(st, s_merge, a, 1,
-                    [](int j) {
-                        return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : VB == 3 ? value3_unscale_log2(j) : 20);
-                    },
-                    wave, tid, b, kvh, hg * kHeadsPerGroup, nh, split);
+#pragma unroll
+    for (int h = 0; h < kG; h++) {
+        st[h].l += row_swap8(st[h].l);     // the two halves of the lane pair's tokens
+        st[h].z += row_swap8(st[h].z);
+        if (h > 0) __syncthreads();        // the previous group's merge has read s_merge
+        merge_and_store<kMQ>(st[h], s_merge, a, 1,
+                        [](int j) {
+                            return __builtin_ldexpf(1.0f, VB == 2 ? value_unscale_log2(j) : VB == 3 ? value3_unscale_log2(j) : 20);
+                        },
+                        wave, tid, b, kvh, (hg0 + h) * kHeadsPerGroup, nh[h], split);
+    }
 }
 
 // Merge the split partials of each (sequence, query head) and apply the
@@ -867,7 +930,7 @@ int resident_workgroups() {
     if (cached[dev] > 0) return cached[dev];
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1>, 256, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -881,32 +944,41 @@ int resident_workgroups() {
     return cached[dev];
 }
 
-template <int KB, int VB, bool kMQ, bool kPaged>
+template <int KB, int VB, bool kMQ, bool kPaged, int kG>
 hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
-    dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * a.head_groups), (unsigned)a.num_seqs);
+    const int sgroups = (a.head_groups + kG - 1) / kG;
+    dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * sgroups), (unsigned)a.num_seqs);
     if (kMQ) {
-        // one dimension: rounds of 8 (split, sequence, KV head) units x head groups
+        // one dimension: rounds of 8 (split, sequence, KV head) units x work-groups per unit
         const int64_t units = (int64_t)a.splits * a.num_kv_heads * a.num_seqs;
-        const int64_t blocks = (units + 7) / 8 * 8 * a.head_groups;
+        const int64_t blocks = (units + 7) / 8 * 8 * sgroups;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         grid = dim3((unsigned)blocks, 1, 1);
     }
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged>), grid, dim3(256), 0, stream, ev.start,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(256), 0, stream, ev.start,
                               ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 // One query row per sequence, or several (causal among them).
+template <int KB, int VB, int kG>
+hipError_t launch_split_groups(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+    if (a.page_log2s > 0)
+        return a.q_len > 1 ? launch_split_kernel<KB, VB, true, true, kG>(a, stream, ev)
+                           : launch_split_kernel<KB, VB, false, true, kG>(a, stream, ev);
+    return a.q_len > 1 ? launch_split_kernel<KB, VB, true, false, kG>(a, stream, ev)
+                       : launch_split_kernel<KB, VB, false, false, kG>(a, stream, ev);
+}
+
+// Two head groups per work-group whenever a KV head has more than one (the
+// split plan counts work-groups the same way: decode_groups_per_workgroup).
 template <int KB, int VB>
 hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
-    if (a.page_log2s > 0)
-        return a.q_len > 1 ? launch_split_kernel<KB, VB, true, true>(a, stream, ev)
-                           : launch_split_kernel<KB, VB, false, true>(a, stream, ev);
-    return a.q_len > 1 ? launch_split_kernel<KB, VB, true, false>(a, stream, ev)
-                       : launch_split_kernel<KB, VB, false, false>(a, stream, ev);
+    return a.head_groups >= 2 ? launch_split_groups<KB, VB, 2>(a, stream, ev)
+                              : launch_split_groups<KB, VB, 1>(a, stream, ev);
 }
 
 }  // namespace
