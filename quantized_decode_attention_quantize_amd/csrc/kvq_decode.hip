@@ -16,10 +16,11 @@
 // z_t (C_t = code sum), output channel 0 is simply sum p_t mu_t / sum p_t:
 // the large, nearly cancelling terms s_t C_t and 128 z_t never meet in fp32.
 //
-// Work decomposition.  Grid (split, kv head x head group, sequence); a
-// work-group of 4 waves owns `pages_per_split` consecutive pages of one
-// (sequence, KV head) and up to 8 query heads of that KV head.  Each wave
-// takes page pairs w, w+4, ... of the split.
+// Work decomposition.  Grid (split, KV head x work-group of head groups,
+// sequence); a work-group of 4 waves owns `pages_per_split` consecutive pages
+// of one (sequence, KV head) and up to 8 query heads of that KV head (one
+// head group), or 16 (two groups sharing the page unpack) when the KV head
+// has more.  Each wave takes page pairs w, w+4, ... of the split.
 //
 // Per page pair, per wave (64 lanes; n = lane & 15, g = lane >> 4):
 //   Scores: v_mfma_f32_16x16x32_f16 x 4, A = key codes (row = token n, the
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         b = blockIdx.z;
     } else {
         // One-dimensional grid, XCD-aware: work-groups are dispatched to the 8
-        // XCDs in turn, so block L runs on XCD L % 8.  The head groups of one
+        // XCDs in turn, so block L runs on XCD L % 8.  The work-groups of one
         // (split, sequence, KV head) take consecutive blocks of one XCD and
         // read the same pages at about the same time: the later reads are
         // served by that XCD's L2.  Blocks past the work (the grid is padded
@@ -974,7 +975,7 @@ hipError_t launch_split_groups(const DecodeArgs &a, hipStream_t stream, const La
 }
 
 // Two head groups per work-group whenever a KV head has more than one (the
-// split plan counts work-groups the same way: decode_groups_per_workgroup).
+// split heuristic of the C ABI counts work-groups the same way).
 template <int KB, int VB>
 hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     return a.head_groups >= 2 ? launch_split_groups<KB, VB, 2>(a, stream, ev)
