@@ -93,6 +93,26 @@ def test_workspace_sizing_and_heuristic():
     assert kvq.decode_pages_per_split(1, 8, 8, 1 << 24) <= 512
 
 
+def test_split_plan_counts_two_head_groups_per_workgroup():
+    """The quantised decode serves two head groups (16 query heads of a KV
+    head) per work-group, so the split plan counts work-groups, not head
+    groups: 16 heads per KV head plan like 8, and 24 or 32 heads like two
+    work-groups (half the splits of one).  The fp16 kernel keeps one group
+    per work-group."""
+    n = 1 << 16                                  # 4096 pages of one sequence
+    p8, p16, p24, p32 = (kvq.decode_pages_per_split(1, h, 1, n) for h in (8, 16, 24, 32))
+    assert p16 == p8
+    assert p24 == p32
+    assert p24 == kvq.decode_pages_per_split(2, 8, 1, n)       # two work-groups per unit
+    # slots per row: the same for 8 and 16 quantised heads; the fp16 kernel's
+    # two work-groups for 16 heads take half the splits each
+    k8, k16 = (kvq.decode_split_slots(1, h, 1, n) for h in (8, 16))
+    assert k16 == k8
+    f16 = kvq.format_from_string("fp16")
+    h8, h16 = (kvq.decode_split_slots(1, h, 1, n, fmt=f16) for h in (8, 16))
+    assert h16 < h8
+
+
 def _fmt():
     return ctypes.byref(kvq.format_from_string())
 
