@@ -81,6 +81,10 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
+    ap.add_argument("--dist-blocks", type=int, default=100,
+                    help="blocks timed for the per-step median and p10/p90 (0: skip)")
+    ap.add_argument("--dist-block-steps", type=int, default=10,
+                    help="steps per distribution block (one event between blocks)")
     ap.add_argument("--event-every", type=int, default=0,
                     help="also time the split kernel with kernel events on every N-th timed step (0: off)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -313,6 +317,9 @@ def cpu_baseline(w, groups: int, threads: int):
     kv_bytes = len(units) * n * KV_BYTES_PER_TOKEN_HEAD
     return {
         "value": kv_bytes / (t2 - t1) / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "oracle_form": "plain-definition oracle as written for parity: every cached token is dequantised "
+                       "and un-rotated by a dense fp64 128x128 Hadamard product (16384 multiply-adds per "
+                       "vector, not an O(896) FWHT), then fp64 softmax(q.k) v; not a tuned CPU decode",
         "sample": f"{len(units)} (sequence, KV head) groups of qwen3_32b_16k, {n} tokens each: quantise-append, "
                   f"then decode of {w.gqa} query heads per group (fp64 plain definition), one group per thread",
         "seconds": round(t2 - t0, 2),
@@ -425,6 +432,35 @@ def main():
     dec_avg_ms = hev.elapsed_ms(kl0, kl0 + 1) / nl
     ev_ms = [hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(sampled))]
     hev.close()
+
+    # spread of the per-step time: --dist-blocks blocks of --dist-block-steps
+    # steps each, one event between consecutive blocks (each event adds its
+    # own marker gap, ~1/block_steps of it per step); per-step time of a block
+    # = its elapsed time / block_steps.  The same for the split kernel alone.
+    dist = kdist = None
+    if args.dist_blocks > 0:
+        nb, bs = args.dist_blocks, max(1, args.dist_block_steps)
+
+        def blocks(fn_block):
+            he = HipEvents(nb + 1)
+            he.record(0, stream.cuda_stream)
+            failed = 0
+            for k in range(nb):
+                failed |= fn_block(k)
+                he.record(k + 1, stream.cuda_stream)
+            torch.cuda.synchronize()
+            if failed:
+                raise RuntimeError("kvq call failed in the distribution blocks")
+            per = np.array([he.elapsed_ms(k, k + 1) / bs for k in range(nb)])
+            he.close()
+            return {"median_ms": round(float(np.median(per)), 5),
+                    "p10_ms": round(float(np.percentile(per, 10)), 5),
+                    "p90_ms": round(float(np.percentile(per, 90)), 5),
+                    "mean_ms": round(float(per.mean()), 5), "blocks": nb, "steps_per_block": bs}
+
+        base_i = args.warmup + args.steps + nl
+        dist = blocks(lambda k: sum(step(base_i + k * bs + j) for j in range(bs)))
+        kdist = blocks(lambda k: sum(part_fn(*part_args[(base_i + k * bs + j) % len(pools)]) for j in range(bs)))
     # labelled warm figure: the same launches on one pool copy, whose 109 MB
     # stay in the 256 MB Infinity Cache between launches (not the headline)
     warm_ms = None
@@ -462,7 +498,12 @@ def main():
                    "pool_replicas": len(pools),
                    "pages_per_split": pps or kvq.decode_pages_per_split(B, Hq, Hkv, n)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "ms_per_step_median": None if dist is None else dist["median_ms"],
+        "ms_per_step_p10": None if dist is None else dist["p10_ms"],
+        "ms_per_step_p90": None if dist is None else dist["p90_ms"],
+        "step_distribution": dist,
         "decode_kernel_ms": round(dec_avg_ms, 5),
+        "decode_kernel_distribution": kdist,
         "decode_kernel_launches_timed": nl,
         "warm_cache_decode_kernel_ms": None if warm_ms is None else round(warm_ms, 5),
         "warm_cache_note": "one pool copy re-read back to back (resident in the 256 MB Infinity Cache); "

@@ -95,8 +95,12 @@
  *
  * Conventions for every call:
  *   - All buffers are owned by the caller.  The library never allocates,
- *     frees or synchronises device memory and keeps no global mutable state
- *     besides a thread-local last HIP error.
+ *     frees or synchronises device memory.  Its only global mutable state is
+ *     a thread-local last HIP error and, per device, the number of decode
+ *     work-groups the device holds at once (queried on first use, stored
+ *     atomically; concurrent first calls from several threads store the same
+ *     value).  The measurement aids declared in kvq_measure.h add one more:
+ *     a thread-local pair of timing events.
  *   - Pointers marked (device) are device pointers; (host) are host pointers.
  *     fp16 values are passed as their uint16_t bit patterns.
  *   - `stream` is a hipStream_t (NULL: the default stream).  Work is enqueued
@@ -132,9 +136,9 @@ typedef enum kvq_status {
 } kvq_status;
 
 /* Format descriptor: {128, 128, k_bits, v_bits, block_size} with k_bits in
- * {4, 8}, v_bits in {2, 4} and block_size in {16, 32, 64, 128} tokens per page
- * ({128, 128, 4, 2, 16} is K4V2 v1), or {128, 128, 16, 16, 16} (the fp16
- * baseline).  A page of block_size tokens holds, per KV head, block_size / 16
+ * {4, 8} and v_bits in {2, 4}, or k_bits = v_bits = 3, and block_size in
+ * {16, 32, 64, 128} tokens per page ({128, 128, 4, 2, 16} is K4V2 v1), or
+ * {128, 128, 16, 16, 16} (the fp16 baseline).  A page of block_size tokens holds, per KV head, block_size / 16
  * consecutive 16-token regions of the layout above: the pool is u8
  * [num_pages][num_kv_heads][block_size / 16][region], and token r of a page
  * (slot = page * block_size + r) sits in region r / 16, slot r % 16 (the
@@ -152,8 +156,9 @@ typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
 
 /* Parse a preset name ([KVARN-HN] flag value; [KVARN-P] kv_cache_dtype string).
  * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16}); "k4v4_g128",
- * "k8v2_g128", "k8v4_g128" (with or without the "kvarn_" prefix); and the
- * baseline "fp16" ({128, 128, 16, 16, 16}).  preset, out: (host).
+ * "k8v2_g128", "k8v4_g128" and "k3v3_g128" (each with or without the "kvarn_"
+ * prefix); and the baseline "fp16" ({128, 128, 16, 16, 16}).  Every preset
+ * has 16-token pages; set block_size afterwards for larger ones.  preset, out: (host).
  * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
 
@@ -170,7 +175,8 @@ size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_
  *   key, value        (device) fp16 [num_tokens][num_kv_heads][128]; token
  *                     strides in elements (>= num_kv_heads*128), head stride
  *                     128; 16-byte aligned; token strides multiples of 8.
- *   slot_mapping      (device) int64 [num_tokens]; slot = page*16 + offset.
+ *   slot_mapping      (device) int64 [num_tokens]; slot = page*block_size +
+ *                     offset (offset < block_size).
  *                     A negative slot skips the token; a slot whose page is
  *                     >= num_pages is skipped.  Slots must be distinct.
  *   cache             (device) u8 pool [num_pages][num_kv_heads][page bytes]
@@ -188,10 +194,13 @@ kvq_status kvq_quantize_append(const kvq_format *fmt,
                                void *stream);
 
 /* Workspace bytes the decode calls need for these sizes (0 on invalid
- * input).  pages_per_split = 0 selects the library's split heuristic; a
- * positive value forces that many pages per split (see _ex below).  The
- * workspace holds the split partials, fp32 [num_seqs][num_q_heads][splits][132]
- * with splits = ceil(ceil(max_seq_len / 16) / pages_per_split). */
+ * input).  The split plan depends on the KV-head count (it sets the number of
+ * (sequence, KV head) work units that share the device) and on the split
+ * size, so both are arguments: pages_per_split = 0 selects the library's
+ * split heuristic; a positive value forces that many pages per split (see _ex
+ * below).  The workspace holds the split partials, fp32
+ * [num_seqs][num_q_heads][splits][132] with splits = ceil(ceil(max_seq_len /
+ * 16) / pages_per_split). */
 size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_seq_len, int32_t pages_per_split);
@@ -407,55 +416,6 @@ kvq_status kvq_decode_combine_slots(void *out, kvq_out_dtype out_dtype, int32_t 
  * shows in kvq_decode_split_slots and kvq_decode_workspace_bytes. */
 int32_t kvq_decode_pages_per_split(int32_t num_seqs, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t max_seq_len);
-
-/* Timing hook.  While start_event / stop_event (hipEvent_t handles created
- * by the caller; either may be NULL) are set, every decode split kernel that
- * a kvq call on this thread launches records them at its own start and end
- * (hipExtLaunchKernel's kernel events: no extra packets on the stream, so the
- * elapsed time is the kernel's execution time).  kvq_set_split_kernel_events
- * (NULL, NULL) clears the hook.  Always returns KVQ_OK. */
-kvq_status kvq_set_split_kernel_events(void *start_event, void *stop_event);
-
-/* Measurement aid, not part of the decode path: one launch that reads
- * `bytes` of device memory from `buffer` front to back (16-byte loads, two
- * work-groups of 256 lanes per compute unit, grid-stride), so that a caller
- * can time the plain streaming-read rate of the device the decode runs on
- * and set the decode's bytes per second against it (decode moves the whole
- * cache through HBM per token [KV-INFRA]).
- *   buffer  (device) 16-byte aligned; bytes a positive multiple of 16
- *           (at most 2^40; else KVQ_ERR_SHAPE).
- *   sink    (device) one uint32, written only in the rare case that the
- *           XOR of everything read equals a fixed constant (it keeps the
- *           loads from being optimised away); may hold anything.
- * Nothing is allocated; the call is enqueued on `stream`. */
-kvq_status kvq_stream_read_probe(const void *buffer, size_t bytes, uint32_t *sink, void *stream);
-
-/* Measurement aid, not part of the decode path: one launch that reads the
- * bytes a decode split kernel reads for these arguments, in the same work
- * decomposition, and does nothing else.  Work-group (split, KV head,
- * sequence); 4 waves; wave w walks page pairs w, w + 4, ... of its split,
- * with the page ids that block_tables gives; each 16-token region of the
- * KV head is read whole (16-byte loads).  Timing it beside the decode sets
- * the decode against the cost of its own access pattern: random page
- * regions of a few KB rather than a sequential stream [KV-INFRA].
- *   fmt      (host) a quantised format with 16-token pages
- *            (else KVQ_ERR_UNSUPPORTED).
- *   cache, block_tables, seq_lens, num_pages, max_pages_per_seq, num_seqs,
- *   num_kv_heads, max_seq_len: as for kvq_decode_attention (the same
- *            preconditions on the device-resident arguments).
- *   pages_per_split  even, 2..512: the decode's split size
- *            (kvq_decode_pages_per_split gives the heuristic's).
- *   sink     (device) one uint32, written only in the rare case that the
- *            XOR of everything read equals a fixed constant; may hold
- *            anything.
- * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (sizes as above, or more than 65535
- * splits), KVQ_ERR_ALIGN (cache 16 bytes; block_tables, seq_lens and sink
- * 4 bytes), KVQ_ERR_HIP.  Nothing is allocated; the call is enqueued on
- * `stream`. */
-kvq_status kvq_page_walk_probe(const kvq_format *fmt, const uint8_t *cache, int64_t num_pages,
-                               const int32_t *block_tables, int32_t max_pages_per_seq, const int32_t *seq_lens,
-                               int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
-                               int32_t pages_per_split, uint32_t *sink, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kvq_status_string(kvq_status status);

@@ -261,7 +261,7 @@ def decode_attention(query: torch.Tensor, cache: torch.Tensor, block_tables: tor
         ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
         _ptr(query), _ptr(cache), cache.shape[0], _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), B, Hq, Hkv, int(max_seq_len), float(softmax_scale), _ptr(workspace),
-        workspace.numel(), int(pages_per_split), _stream_ptr(stream))
+        workspace.numel() * workspace.element_size(), int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_decode_attention")
     return out
 

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "../../include/kvq.h"
+#include "../../include/kvq_measure.h"
 #include "kvq_device.h"
 #include "kvq_probe.h"
 

@@ -63,6 +63,8 @@
 // entry covers several 16-token regions).  The K4V2 single-row 16-token
 // instantiation is the hot path above.
 #include <hip/hip_ext.h>
+
+#include <atomic>
 #include <math.h>
 
 #include "kvq_decode_common.h"
@@ -922,13 +924,16 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(DecodeArgs a) {
 // (compute units x occupancy), queried once per device; 512 without a device.
 template <int KB, int VB>
 int resident_workgroups() {
-    static int cached[64] = {0};
+    // one entry per device; several host threads may fill an entry at once,
+    // and they all store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return 512;
     }
-    if (cached[dev] > 0) return cached[dev];
+    const int known = cached[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1>, 256, 0) != hipSuccess ||
@@ -941,8 +946,8 @@ int resident_workgroups() {
     // kernel ~1.2 us slower, and the extra splits push the combine onto its
     // wide path.
     if (per_cu > 2) per_cu = 2;
-    cached[dev] = cus * per_cu;
-    return cached[dev];
+    cached[dev].store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
 }
 
 template <int KB, int VB, bool kMQ, bool kPaged, int kG>

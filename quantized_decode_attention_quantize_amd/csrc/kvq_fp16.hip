@@ -22,6 +22,8 @@
 // same scores), and P.V is v_mfma_f32_16x16x16_f16 of the values with the
 // weights split into fp16 and residual columns, as in the K4V2 kernel.
 #include <hip/hip_ext.h>
+
+#include <atomic>
 #include <math.h>
 
 #include "kvq_decode_common.h"
@@ -275,13 +277,16 @@ __global__ __launch_bounds__(256) void decode_fp16_kernel(DecodeArgs a) {
 }  // namespace
 
 int decode_fp16_resident_workgroups() {
-    static int cached[64] = {0};
+    // one entry per device; several host threads may fill an entry at once,
+    // and they all store the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
         return 512;
     }
-    if (cached[dev] > 0) return cached[dev];
+    const int known = cached[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_fp16_kernel, 256, 0) != hipSuccess ||
@@ -289,8 +294,8 @@ int decode_fp16_resident_workgroups() {
         (void)hipGetLastError();
         return 512;
     }
-    cached[dev] = cus * per_cu;
-    return cached[dev];
+    cached[dev].store(cus * per_cu, std::memory_order_relaxed);
+    return cus * per_cu;
 }
 
 hipError_t launch_fp16_append(const AppendArgs &a, hipStream_t stream) {

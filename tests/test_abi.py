@@ -10,13 +10,21 @@ import torch
 import quantized_decode_attention_quantize_amd as kvq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvq.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADER = os.path.join(INCLUDE, "kvq.h")
+
+
+def header_texts():
+    """Every public header (kvq.h and the measurement aids' kvq_measure.h)."""
+    return {f: open(os.path.join(INCLUDE, f)).read() for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")}
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for text in header_texts().values():
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -25,6 +33,45 @@ def test_library_exports_every_declared_symbol():
     assert "kvq_quantize_append" in names and "kvq_decode_attention" in names
     for name in names:
         assert hasattr(lib, name), name
+
+
+# every preset name the library accepts; the header must document each one
+PRESETS = {"k4v2_g128": (4, 2), "k4v4_g128": (4, 4), "k8v2_g128": (8, 2), "k8v4_g128": (8, 4),
+           "k3v3_g128": (3, 3)}
+
+
+def test_header_documents_every_accepted_preset():
+    """Each preset string the parser accepts (with and without the kvarn_
+    prefix) appears in kvq.h's description of kvq_format_from_string, and
+    the header's bit-width sentence names its key and value widths; a string
+    the parser rejects is not presented as a preset there."""
+    lib = kvq.load()
+    text = open(HEADER).read()
+    i = text.index("Parse a preset name")
+    doc = text[i:text.index("kvq_status kvq_format_from_string", i)]
+    f = kvq.Format()
+    for name, (kb, vb) in PRESETS.items():
+        for full in (name, "kvarn_" + name):
+            assert lib.kvq_format_from_string(full.encode(), ctypes.byref(f)) == 0, full
+            assert (f.k_bits, f.v_bits) == (kb, vb)
+        assert f'"{name}"' in doc, name
+        assert name in text[:text.index("#ifndef KVQ_H")], name
+    assert '"kvarn_"' in doc
+    assert lib.kvq_format_from_string(b"fp16", ctypes.byref(f)) == 0 and '"fp16"' in doc
+    for quoted in re.findall(r'"([a-z0-9_]+)"', doc):
+        if quoted == "kvarn_":
+            continue
+        assert lib.kvq_format_from_string(quoted.encode(), ctypes.byref(f)) == 0, quoted
+
+
+def test_measurement_aids_live_in_their_own_header():
+    """The timing hook and the read probes are declared in kvq_measure.h, not
+    beside the decode path in kvq.h."""
+    texts = header_texts()
+    assert set(texts) >= {"kvq.h", "kvq_measure.h"}
+    for name in ("kvq_set_split_kernel_events", "kvq_stream_read_probe", "kvq_page_walk_probe"):
+        assert name + "(" in texts["kvq_measure.h"].replace(" (", "(")
+        assert name not in texts["kvq.h"]
 
 
 def test_format_and_sizes():
