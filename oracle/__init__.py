@@ -65,27 +65,8 @@ def _load():
     lib.kvqo_fwht_f32.restype = None
     lib.kvqo_hadamard_matvec_f64.argtypes = [P, P]
     lib.kvqo_hadamard_matvec_f64.restype = None
-    lib.kvqo_quantize_group.argtypes = [P, ctypes.c_int, P, P, P]
-    lib.kvqo_quantize_group.restype = None
-    lib.kvqo_store_token.argtypes = [P, ctypes.c_int, P, ctypes.c_uint16, ctypes.c_uint16,
-                                     P, ctypes.c_uint16, ctypes.c_uint16]
-    lib.kvqo_store_token.restype = None
-    lib.kvqo_load_token.argtypes = [P, ctypes.c_int, P, P, P, P, P, P]
-    lib.kvqo_load_token.restype = None
-    lib.kvqo_quantize_append.argtypes = [P, P, i64, i64, P, i64, i32, P, i64]
-    lib.kvqo_quantize_append.restype = ctypes.c_int
-    lib.kvqo_dequant_slot.argtypes = [P, ctypes.c_int, P, P]
-    lib.kvqo_dequant_slot.restype = None
-    lib.kvqo_dequant_slot_rotated.argtypes = [P, ctypes.c_int, P, P]
-    lib.kvqo_dequant_slot_rotated.restype = None
     lib.kvqo_quantize_group_mode.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P]
     lib.kvqo_quantize_group_mode.restype = None
-    lib.kvqo_decode_attention.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
-                                          ctypes.c_double, P, P]
-    lib.kvqo_decode_attention.restype = ctypes.c_int
-    lib.kvqo_decode_attention_folded.argtypes = [P, i64, i32, P, i32, P, i32, i32, P,
-                                                 ctypes.c_double, P]
-    lib.kvqo_decode_attention_folded.restype = ctypes.c_int
     lib.kvqo_attention_f16.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
     lib.kvqo_attention_f16.restype = None
     lib.kvqo_attention_f64.argtypes = [P, P, i64, P, i32, ctypes.c_double, P]
@@ -98,21 +79,13 @@ def _load():
     lib.kvqo_store_token_fmt.restype = None
     lib.kvqo_load_token_fmt.argtypes = [ci, ci, P, ci, P, P, P, P, P, P]
     lib.kvqo_load_token_fmt.restype = None
-    lib.kvqo_quantize_append_fmt.argtypes = [ci, ci, P, P, i64, i64, P, i64, i32, P, i64]
-    lib.kvqo_quantize_append_fmt.restype = ctypes.c_int
     lib.kvqo_dequant_slot_fmt.argtypes = [ci, ci, P, ci, P, P]
     lib.kvqo_dequant_slot_fmt.restype = None
     lib.kvqo_dequant_slot_rotated_fmt.argtypes = [ci, ci, P, ci, P, P]
     lib.kvqo_dequant_slot_rotated_fmt.restype = None
-    lib.kvqo_decode_attention_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
-                                              ctypes.c_double, P, P]
-    lib.kvqo_decode_attention_fmt.restype = ctypes.c_int
     lib.kvqo_decode_attention_folded_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
                                                      ctypes.c_double, P]
     lib.kvqo_decode_attention_folded_fmt.restype = ctypes.c_int
-    lib.kvqo_decode_attention_mq_fmt.argtypes = [ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
-                                                 ctypes.c_double, P]
-    lib.kvqo_decode_attention_mq_fmt.restype = ctypes.c_int
     lib.kvqo_quantize_append_paged.argtypes = [ci, ci, ci, P, P, i64, i64, P, i64, i32, P, i64]
     lib.kvqo_quantize_append_paged.restype = ctypes.c_int
     lib.kvqo_decode_attention_paged.argtypes = [ci, ci, ci, P, i64, i32, P, i32, P, i32, i32, P,
@@ -121,8 +94,18 @@ def _load():
     lib.kvqo_decode_attention_mq_paged.argtypes = [ci, ci, ci, P, i64, i32, P, i32, P, i32, i32, i32, P,
                                                    ctypes.c_double, P]
     lib.kvqo_decode_attention_mq_paged.restype = ctypes.c_int
-    lib.kvqo_block_variant.argtypes = [P, ci, ci, ci, P, P]
-    lib.kvqo_block_variant.restype = None
+    lib.kvqo_block_variant.argtypes = [P, P, ci, ci, ci, P, P, P, P, P]
+    lib.kvqo_block_variant.restype = ci
+    lib.kvqo_quantize_append_pb.argtypes = [P, P, i64, i64, P, i64, i32, P, i64]
+    lib.kvqo_quantize_append_pb.restype = ci
+    lib.kvqo_dequant_slot_pb.argtypes = [P, ci, P, P]
+    lib.kvqo_dequant_slot_pb.restype = None
+    lib.kvqo_decode_attention_pb.argtypes = [P, i64, i32, P, i32, P, i32, i32, P, ctypes.c_double, P, P]
+    lib.kvqo_decode_attention_pb.restype = ci
+    lib.kvqo_pb_region_bytes.argtypes = []
+    lib.kvqo_pb_region_bytes.restype = ci
+    lib.kvqo_pb_iters.argtypes = []
+    lib.kvqo_pb_iters.restype = ci
     _lib = lib
     return lib
 
@@ -328,15 +311,74 @@ def attention_f64(k, v, q_f16, scale):
 
 
 
-def block_variant(x_f16, bits: int, iters: int):
-    """Variance-normalisation variant on a block of tokens (see
-    kvqo_block_variant): x float16 [T][128] -> (codes uint8 [T][128], the
-    rebuilt original-domain block float64 [T][128]).  iters = 0 is the
-    per-token encoder."""
+def block_variant(x_f16, bits: int, iters: int, present=None):
+    """Page-balanced variance normalisation of one block of T <= 16 tokens
+    (kvqo_block_variant): x float16 [T][128] -> (codes uint8 [T][128], the
+    rebuilt original-domain block float64 [T][128], s and z fp16 bits [T],
+    column exponents int [128]).  iters = number of column passes (0: the
+    per-token encoder); present (optional bool [T]) marks absent rows."""
     x = _c(x_f16, np.float16)
     T = x.shape[0]
-    assert x.shape == (T, D)
-    codes = np.empty((T, D), np.uint8)
-    out = np.empty((T, D), np.float64)
-    _load().kvqo_block_variant(_ptr(x.view(np.uint16)), T, int(bits), int(iters), _ptr(codes), _ptr(out))
-    return codes, out
+    assert x.shape == (T, D) and T <= PAGE
+    codes = np.zeros((T, D), np.uint8)
+    out = np.zeros((T, D), np.float64)
+    s = np.zeros(T, np.uint16)
+    z = np.zeros(T, np.uint16)
+    e = np.zeros(D, np.int32)
+    pres = None if present is None else _c(np.asarray(present, np.uint8), np.uint8)
+    rc = _load().kvqo_block_variant(_ptr(x.view(np.uint16)), None if pres is None else _ptr(pres), T, int(bits),
+                                    int(iters), _ptr(codes), _ptr(s), _ptr(z), _ptr(e), _ptr(out))
+    if rc != 0:
+        raise ValueError("block_variant: invalid arguments")
+    return codes, out, s, z, e
+
+
+# The page-balanced key preset (kvqo_quantize_append_pb): K4V2 regions followed
+# by 128 column-scale bytes.
+PB_REGION = 1792
+
+
+def pb_iters() -> int:
+    return int(_load().kvqo_pb_iters())
+
+
+def pb_region_bytes() -> int:
+    return int(_load().kvqo_pb_region_bytes())
+
+
+def quantize_append_pb(key_f16: np.ndarray, value_f16: np.ndarray, slot_mapping: np.ndarray, pool: np.ndarray) -> int:
+    """Whole-page append into a page-balanced pool u8 [num_pages][H][1792]:
+    call tokens 16b..16b+15 fill page slot_mapping[16b] / 16 from slot 0."""
+    k = _c(key_f16, np.float16)
+    v = _c(value_f16, np.float16)
+    T, H, _ = k.shape
+    assert v.shape == k.shape and pool.dtype == np.uint8 and pool.shape[1:] == (H, PB_REGION)
+    assert pool.flags.c_contiguous
+    sm = _c(slot_mapping, np.int64)
+    return int(_load().kvqo_quantize_append_pb(_ptr(k.view(np.uint16)), _ptr(v.view(np.uint16)), H * D, H * D,
+                                               _ptr(sm), T, H, _ptr(pool), pool.shape[0]))
+
+
+def dequant_slot_pb(region: np.ndarray, off: int):
+    assert region.dtype == np.uint8 and region.size == PB_REGION and region.flags.c_contiguous
+    k = np.empty(D, np.float64)
+    v = np.empty(D, np.float64)
+    _load().kvqo_dequant_slot_pb(_ptr(region), int(off), _ptr(k), _ptr(v))
+    return k, v
+
+
+def decode_attention_pb(pool, block_tables, seq_lens, query_f16, scale, head_mask=None):
+    """Plain fp64 decode over a page-balanced pool (16-token pages)."""
+    assert pool.dtype == np.uint8 and pool.shape[2] == PB_REGION and pool.flags.c_contiguous
+    bt = _c(block_tables, np.int32)
+    lens = _c(seq_lens, np.int32)
+    q = _c(query_f16, np.float16)
+    B, Hq, _ = q.shape
+    out = np.zeros((B, Hq, D), np.float64)
+    hm = None if head_mask is None else _c(head_mask, np.uint8)
+    rc = _load().kvqo_decode_attention_pb(_ptr(pool), pool.shape[0], pool.shape[1], _ptr(bt), bt.shape[1],
+                                          _ptr(lens), B, Hq, _ptr(q.view(np.uint16)), float(scale),
+                                          None if hm is None else _ptr(hm), _ptr(out))
+    if rc != 0:
+        raise ValueError("decode_attention_pb: invalid shape or page id")
+    return out

@@ -122,7 +122,7 @@ double kvqo_half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
-float kvqo_half_to_float(uint16_t h) { return (float)kvqo_half_to_double(h); }
+static float kvqo_half_to_float(uint16_t h) { return (float)kvqo_half_to_double(h); }
 
 /* Nearest binary16 to a binary32 value, ties to even.  |f| is scaled by the
  * binary16 unit in the last place of its binade (a power of two, so exact in
@@ -282,13 +282,6 @@ void kvqo_quantize_group_mode(const uint16_t *x, int bits, int offset_mode, uint
     *z_out = (z == 0x8000) ? 0 : z;
 }
 
-/* Keys: offset_mode 0 (zero z); values: offset_mode 1 (group mean). */
-void kvqo_quantize_group(const uint16_t *x, int bits, uint8_t *codes,
-                         uint16_t *s_out, uint16_t *z_out)
-{
-    kvqo_quantize_group_mode(x, bits, bits == 2 ? 1 : 0, codes, s_out, z_out);
-}
-
 /* ------------------------------------------------------------------------ */
 /* Byte layout of one (page, KV head) region.                                */
 /* ------------------------------------------------------------------------ */
@@ -433,19 +426,6 @@ void kvqo_load_token_fmt(int kbits, int vbits, const uint8_t *region, int off,
 }
 
 /* The 4-bit key / 2-bit value layout (KVarN's preset). */
-void kvqo_store_token(uint8_t *region, int off,
-                      const uint8_t *kc, uint16_t ks, uint16_t kz,
-                      const uint8_t *vc, uint16_t vs, uint16_t vz)
-{
-    kvqo_store_token_fmt(4, 2, region, off, kc, ks, kz, vc, vs, vz);
-}
-
-void kvqo_load_token(const uint8_t *region, int off,
-                     uint8_t *kc, uint16_t *ks, uint16_t *kz,
-                     uint8_t *vc, uint16_t *vs, uint16_t *vz)
-{
-    kvqo_load_token_fmt(4, 2, region, off, kc, ks, kz, vc, vs, vz);
-}
 
 /* ------------------------------------------------------------------------ */
 /* Quantise-on-write of cache blocks [KVARN-HN].                             */
@@ -483,24 +463,6 @@ int kvqo_quantize_append_paged(int kbits, int vbits, int page_tokens, const uint
     return rc;
 }
 
-int kvqo_quantize_append_fmt(int kbits, int vbits, const uint16_t *key, const uint16_t *value,
-                             int64_t key_token_stride, int64_t value_token_stride,
-                             const int64_t *slot_mapping, int64_t num_tokens,
-                             int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
-{
-    return kvqo_quantize_append_paged(kbits, vbits, KVQO_PAGE, key, value, key_token_stride, value_token_stride,
-                                      slot_mapping, num_tokens, num_kv_heads, pool, num_pages);
-}
-
-int kvqo_quantize_append(const uint16_t *key, const uint16_t *value,
-                         int64_t key_token_stride, int64_t value_token_stride,
-                         const int64_t *slot_mapping, int64_t num_tokens,
-                         int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
-{
-    return kvqo_quantize_append_fmt(4, 2, key, value, key_token_stride, value_token_stride, slot_mapping,
-                                    num_tokens, num_kv_heads, pool, num_pages);
-}
-
 /* ------------------------------------------------------------------------ */
 /* Decode attention over the quantised paged cache.                          */
 /* ------------------------------------------------------------------------ */
@@ -529,7 +491,7 @@ static void dequant_unrotate(const uint8_t *codes, uint16_t s16, uint16_t z16, i
         out[i] /= 128.0;
 }
 
-/* Public helper for tests: dequantised, un-rotated key and value of one slot. */
+/* Dequantised, un-rotated key and value of one slot (kbits, vbits layout). */
 void kvqo_dequant_slot_fmt(int kbits, int vbits, const uint8_t *region, int off, double *k_out, double *v_out)
 {
     uint8_t kc[KVQO_D], vc[KVQO_D];
@@ -537,11 +499,6 @@ void kvqo_dequant_slot_fmt(int kbits, int vbits, const uint8_t *region, int off,
     kvqo_load_token_fmt(kbits, vbits, region, off, kc, &ks, &kz, vc, &vs, &vz);
     dequant_unrotate(kc, ks, kz, 0, k_out);
     dequant_unrotate(vc, vs, vz, 1, v_out);
-}
-
-void kvqo_dequant_slot(const uint8_t *region, int off, double *k_out, double *v_out)
-{
-    kvqo_dequant_slot_fmt(4, 2, region, off, k_out, v_out);
 }
 
 /* Rotated-domain dequantised values of one slot (s*c + z per channel). */
@@ -556,11 +513,6 @@ void kvqo_dequant_slot_rotated_fmt(int kbits, int vbits, const uint8_t *region, 
         k_out[i] = kvqo_half_to_double(ks) * kc[i] + kzero;
         v_out[i] = kvqo_half_to_double(vs) * vc[i] + vzero;
     }
-}
-
-void kvqo_dequant_slot_rotated(const uint8_t *region, int off, double *k_out, double *v_out)
-{
-    kvqo_dequant_slot_rotated_fmt(4, 2, region, off, k_out, v_out);
 }
 
 /*
@@ -632,27 +584,6 @@ int kvqo_decode_attention_paged(int kbits, int vbits, int page_tokens, const uin
     return 0;
 }
 
-int kvqo_decode_attention_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
-                              int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
-                              const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                              const uint16_t *query, double scale,
-                              const uint8_t *head_mask, double *out)
-{
-    return kvqo_decode_attention_paged(kbits, vbits, KVQO_PAGE, pool, num_pages, num_kv_heads, block_tables,
-                                       max_pages_per_seq, seq_lens, num_seqs, num_q_heads, query, scale,
-                                       head_mask, out);
-}
-
-int kvqo_decode_attention(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
-                          const int32_t *block_tables, int32_t max_pages_per_seq,
-                          const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                          const uint16_t *query, double scale,
-                          const uint8_t *head_mask, double *out)
-{
-    return kvqo_decode_attention_fmt(4, 2, pool, num_pages, num_kv_heads, block_tables, max_pages_per_seq,
-                                     seq_lens, num_seqs, num_q_heads, query, scale, head_mask, out);
-}
-
 /*
  * Several query rows per sequence (the tokens of a speculative-decoding draft
  * or a prefill chunk): q_len rows, the last q_len tokens of the sequence, all
@@ -700,16 +631,6 @@ int kvqo_decode_attention_mq_paged(int kbits, int vbits, int page_tokens, const 
         }
     }
     return 0;
-}
-
-int kvqo_decode_attention_mq_fmt(int kbits, int vbits, const uint8_t *pool, int64_t num_pages,
-                                 int32_t num_kv_heads, const int32_t *block_tables, int32_t max_pages_per_seq,
-                                 const int32_t *seq_lens, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
-                                 const uint16_t *query, double scale, double *out)
-{
-    return kvqo_decode_attention_mq_paged(kbits, vbits, KVQO_PAGE, pool, num_pages, num_kv_heads, block_tables,
-                                          max_pages_per_seq, seq_lens, num_seqs, q_len, num_q_heads, query,
-                                          scale, out);
 }
 
 /*
@@ -780,16 +701,6 @@ int kvqo_decode_attention_folded_fmt(int kbits, int vbits, const uint8_t *pool, 
     return 0;
 }
 
-int kvqo_decode_attention_folded(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
-                                 const int32_t *block_tables, int32_t max_pages_per_seq,
-                                 const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                                 const uint16_t *query, double scale, double *out)
-{
-    return kvqo_decode_attention_folded_fmt(4, 2, pool, num_pages, num_kv_heads, block_tables,
-                                            max_pages_per_seq, seq_lens, num_seqs, num_q_heads, query,
-                                            scale, out);
-}
-
 /* ------------------------------------------------------------------------ */
 /* Uncompressed reference: attention over fp16 keys and values.              */
 /* ------------------------------------------------------------------------ */
@@ -848,64 +759,126 @@ void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const u
 }
 
 /* ------------------------------------------------------------------------ */
-/* Variance-normalisation variants (a study, not part of the format).        */
+/* Page-balanced keys: an active variance normalisation.                     */
 /* ------------------------------------------------------------------------ */
 
 /*
  * The pages name variance normalisation as stage 2 of the pipeline [KVARN-P
- * stage 2; KVARN-HN] without a formula; the Persian page's wording reads as
- * an iterative ("repeated") normalisation of the variance.  The format's
- * reading (divide each group by its RMS) is inert in exact arithmetic, since
- * min/max RTN is scale-equivariant.  These variants act on a block of T
- * tokens (a page of one KV head, keys or values) and do change the codes:
+ * stage 2; KVARN-HN] without a formula.  The Persian page's wording reads as
+ * an iterative ("repeated") normalisation of the variance, and its closing
+ * paragraph credits the method with removing fluctuations in logarithmic
+ * space.  The per-group reading of the v1 format (divide each group by its
+ * RMS) is inert in exact arithmetic, since min/max RTN is scale-equivariant.
+ * This reading acts on a block -- one page of one KV head, up to 16 tokens --
+ * and does change the codes:
  *
- *   Y = the rows' rotations (fp32 FWHT, as the encoder), r = 1, c = 1;
- *   iters rounds of   c_j = RMS over t of Y_tj / r_t   (per channel)
- *                     r_t = RMS over j of Y_tj / c_j   (per token)
- *   (a Sinkhorn-style balancing of the block's second moments, fp64);
- *   each row of Y / (r c) (fp32) then goes through the encoder's own steps
- *   (RMS, min/max, RTN with ties to even, clamp), its metadata folds r_t in,
- *   s_t = fp16(delta sigma r_t), z_t = fp16(m sigma r_t), and the column
- *   scales are stored as fp16(c_j);
- *   the block is rebuilt as  Y'_tj = c_j (s_t code_tj + z_t)  and returned
- *   in the original domain, H Y' / 128, in fp64.
+ *   Y_t = FWHT(x_t) for the present rows (fp32, the encoder's rotation);
+ *   absent rows are zero.  Row exponents f_t = 0.  For pass p = 1 .. iters:
+ *     column pass: ss_j = sum over the 16 row slots of (Y_tj 2^-f_t)^2 in
+ *       fp32, summed by the fixed tree h = 8, 4, 2, 1 (a[t] += a[t + h] for
+ *       t < h); e_j = floor(F_j / 2), where ss_j = m 2^F_j with m in [0.5, 1)
+ *       -- the nearest integer to log2 of the column's root mean square up
+ *       to a constant, halves rounded up; a zero column has no exponent;
+ *     row pass (between column passes only): ss_t = sum_j (Y_tj 2^-e_j)^2
+ *       by the encoder's tree (h = 64 .. 1), f_t = floor(F_t / 2) likewise
+ *       (0 for a zero row).
+ *   (Sinkhorn-style balancing of the block's second moments, with every
+ *   scale kept as a power of two: the log-space reading.)  The final column
+ *   exponents come from the last column pass's sums ss_j = m_j 2^F_j, in
+ *   integers: over the n non-zero columns, with S = sum of their F_j and
+ *   d_j = n F_j - S (n times the column's offset from the mean, in
+ *   half-octaves of its RMS),
+ *     e_j = 0                         if |d_j| < 2n  (within an octave),
+ *     e_j = floor((d_j + n) / (2n))   otherwise      (nearest octave),
+ *   clamped to [-6, 6]; a zero column takes -6.  A block whose columns the
+ *   rotation has already evened out thus keeps every e_j = 0 and is encoded
+ *   as the per-token encoder would; a column an octave or more louder than
+ *   the typical one is shrunk by 2^-e_j before RTN (and restored on read),
+ *   a quieter one amplified, so the rows' ranges stop being set by a few
+ *   columns.
+ *   Each present row of Yhat_tj = Y_tj 2^-e_j -- exact in fp32, since the
+ *   scales are powers of two -- goes through the encoder's own steps 2-4
+ *   (RMS, min/max, RTN with ties to even, fp16 s_t and z_t); the rotated
+ *   reconstruction is 2^e_j (s_t c_tj + z_t) and the original H (that)/128.
  *
- * iters = 0 is the per-token encoder (keys' zero offset): the same codes and
- * metadata, bit for bit.  x: fp16 [T][128]; codes (optional): u8 [T][128];
- * out: fp64 [T][128].
+ * iters = 0 leaves every e_j = 0: the per-token encoder, bit for bit.
+ *
+ * x: fp16 [T][128], T <= 16; present (optional, [T]): rows with 0 are
+ * absent (no codes, no metadata, zero in the sums).  Outputs (each optional):
+ * codes u8 [T][128], s, z fp16 bits [T], e int [128], out fp64 [T][128] (the
+ * original-domain reconstruction; absent rows zero).  Returns 0, or -1 when T
+ * is out of range.
  */
-void kvqo_block_variant(const uint16_t *x, int T, int bits, int iters, uint8_t *codes_out, double *out)
+static int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }   /* b > 0 */
+static int floor_half(int f) { return floor_div(f, 2); }
+#define KVQO_PB_EMAX 6
+
+int kvqo_block_variant(const uint16_t *x, const uint8_t *present, int T, int bits, int iters,
+                       uint8_t *codes_out, uint16_t *s_out, uint16_t *z_out, int *e_out, double *out)
 {
+    if (T < 0 || T > KVQO_PAGE || (bits != 2 && bits != 3 && bits != 4 && bits != 8) || iters < 0) return -1;
     const int L = (1 << bits) - 1;
-    float *Y = malloc(sizeof(float) * KVQO_D * (T > 0 ? T : 1));
-    double *r = malloc(sizeof(double) * (T > 0 ? T : 1));
-    double c[KVQO_D];
-    if (!Y || !r) { free(Y); free(r); return; }
+    float Y[KVQO_PAGE][KVQO_D];
+    int f[KVQO_PAGE], e[KVQO_D], has[KVQO_D];
+    memset(Y, 0, sizeof(Y));
     for (int t = 0; t < T; t++) {
-        for (int i = 0; i < KVQO_D; i++) Y[t * KVQO_D + i] = kvqo_half_to_float(x[t * KVQO_D + i]);
-        kvqo_fwht_f32(Y + t * KVQO_D);
-        r[t] = 1.0;
+        if (present && !present[t]) continue;
+        for (int j = 0; j < KVQO_D; j++) Y[t][j] = kvqo_half_to_float(x[t * KVQO_D + j]);
+        kvqo_fwht_f32(Y[t]);
     }
-    for (int i = 0; i < KVQO_D; i++) c[i] = 1.0;
-    for (int it = 0; it < iters; it++) {
+    for (int t = 0; t < KVQO_PAGE; t++) f[t] = 0;
+    for (int j = 0; j < KVQO_D; j++) { e[j] = 0; has[j] = 1; }
+    float css[KVQO_D];          /* the last column pass's sums */
+    for (int pass = 1; pass <= iters; pass++) {
         for (int j = 0; j < KVQO_D; j++) {
-            double ss = 0.0;
-            for (int t = 0; t < T; t++) { double v = Y[t * KVQO_D + j] / r[t]; ss += v * v; }
-            c[j] = ss > 0.0 ? sqrt(ss / T) : 1.0;
+            float a[KVQO_PAGE];
+            for (int t = 0; t < KVQO_PAGE; t++) {
+                float u = ldexpf(Y[t][j], -f[t]);
+                a[t] = u * u;
+            }
+            for (int h = KVQO_PAGE / 2; h >= 1; h >>= 1)
+                for (int t = 0; t < h; t++) a[t] = a[t] + a[t + h];
+            int F;
+            css[j] = a[0];
+            has[j] = a[0] != 0.0f;
+            (void)frexpf(a[0], &F);
+            e[j] = has[j] ? floor_half(F) : 0;
         }
-        for (int t = 0; t < T; t++) {
-            double ss = 0.0;
-            for (int j = 0; j < KVQO_D; j++) { double v = Y[t * KVQO_D + j] / c[j]; ss += v * v; }
-            r[t] = ss > 0.0 ? sqrt(ss / KVQO_D) : 1.0;
+        if (pass == iters) break;
+        for (int t = 0; t < KVQO_PAGE; t++) {
+            float a[KVQO_D];
+            for (int j = 0; j < KVQO_D; j++) {
+                float u = ldexpf(Y[t][j], -e[j]);
+                a[j] = u * u;
+            }
+            for (int h = KVQO_D / 2; h >= 1; h >>= 1)
+                for (int j = 0; j < h; j++) a[j] = a[j] + a[j + h];
+            int F;
+            (void)frexpf(a[0], &F);
+            f[t] = a[0] != 0.0f ? floor_half(F) : 0;
         }
     }
-    double cs[KVQO_D];
-    for (int j = 0; j < KVQO_D; j++) cs[j] = iters > 0 ? kvqo_half_to_double(kvqo_float_to_half((float)c[j])) : 1.0;
+    if (iters > 0) {
+        int n = 0, S = 0, F[KVQO_D];
+        for (int j = 0; j < KVQO_D; j++) {
+            (void)frexpf(css[j], &F[j]);
+            if (has[j]) { n++; S += F[j]; }
+        }
+        for (int j = 0; j < KVQO_D; j++) {
+            if (!has[j]) { e[j] = -KVQO_PB_EMAX; continue; }
+            const int d = n * F[j] - S;
+            int r = (d < 2 * n && d > -2 * n) ? 0 : floor_div(d + n, 2 * n);
+            e[j] = r < -KVQO_PB_EMAX ? -KVQO_PB_EMAX : r > KVQO_PB_EMAX ? KVQO_PB_EMAX : r;
+        }
+    }
     for (int t = 0; t < T; t++) {
+        if (present && !present[t]) {
+            if (out) memset(out + (int64_t)t * KVQO_D, 0, sizeof(double) * KVQO_D);
+            continue;
+        }
         float y[KVQO_D], p[KVQO_D];
-        for (int j = 0; j < KVQO_D; j++)
-            y[j] = iters > 0 ? (float)(Y[t * KVQO_D + j] / (r[t] * c[j])) : Y[t * KVQO_D + j];
-        /* the encoder's steps on the (scaled) rotated row */
+        for (int j = 0; j < KVQO_D; j++) y[j] = ldexpf(Y[t][j], -e[j]);
+        /* the encoder's steps 2-4 on the scaled rotated row (zero offset) */
         for (int j = 0; j < KVQO_D; j++) p[j] = y[j] * y[j];
         for (int h = KVQO_D / 2; h >= 1; h >>= 1)
             for (int j = 0; j < h; j++) p[j] = p[j] + p[j + h];
@@ -931,17 +904,144 @@ void kvqo_block_variant(const uint16_t *x, int T, int bits, int iters, uint8_t *
             sm = delta * sigma;
             zm = m * sigma;
         }
-        /* fold the row scale into the fp16 metadata (exactly as the encoder when r = 1) */
-        uint16_t s16 = kvqo_float_to_half(iters > 0 ? (float)(sm * r[t]) : sm);
-        uint16_t z16 = kvqo_float_to_half(iters > 0 ? (float)(zm * r[t]) : zm);
+        uint16_t s16 = kvqo_float_to_half(sm);
+        uint16_t z16 = kvqo_float_to_half(zm);
         if (z16 == 0x8000) z16 = 0;
-        double yt[KVQO_D];
-        for (int j = 0; j < KVQO_D; j++)
-            yt[j] = cs[j] * (kvqo_half_to_double(s16) * code[j] + kvqo_half_to_double(z16));
-        kvqo_hadamard_matvec_f64(yt, out + (int64_t)t * KVQO_D);
-        for (int j = 0; j < KVQO_D; j++) out[(int64_t)t * KVQO_D + j] /= 128.0;
         if (codes_out) memcpy(codes_out + (int64_t)t * KVQO_D, code, KVQO_D);
+        if (s_out) s_out[t] = s16;
+        if (z_out) z_out[t] = z16;
+        if (out) {
+            double yt[KVQO_D];
+            for (int j = 0; j < KVQO_D; j++)
+                yt[j] = ldexp(kvqo_half_to_double(s16) * code[j] + kvqo_half_to_double(z16), e[j]);
+            kvqo_hadamard_matvec_f64(yt, out + (int64_t)t * KVQO_D);
+            for (int j = 0; j < KVQO_D; j++) out[(int64_t)t * KVQO_D + j] /= 128.0;
+        }
     }
-    free(Y);
-    free(r);
+    if (e_out) memcpy(e_out, e, sizeof(e));
+    return 0;
+}
+
+/*
+ * The page-balanced key preset: the K4V2 layout of a 16-token region (1664
+ * bytes) followed by the keys' 128 column scales, one byte each: byte j at
+ * 1664 + j is the high byte of the fp16 bit pattern of 2^e_j (e_j in
+ * [-6, 6]; the low byte of a power of two is zero), i.e. (e_j + 15) * 4.
+ * 1792 bytes per (page, KV head), 112 per token.  Keys are balanced per page
+ * with KVQO_PB_ITERS column passes (kvqo_block_variant, 4 bits, zero offset);
+ * values are the v1 per-token groups (2 bits, group mean).
+ */
+#define KVQO_PB_REGION 1792
+#define KVQO_PB_ITERS 2
+
+int kvqo_pb_region_bytes(void) { return KVQO_PB_REGION; }
+int kvqo_pb_iters(void) { return KVQO_PB_ITERS; }
+
+/*
+ * Append whole pages.  Call tokens 16b .. 16b + 15 form block b: with
+ * base = slot_mapping[16b], the block fills page base / 16 from slot 0 and
+ * token 16b + r belongs to it iff 16b + r < num_tokens and slot_mapping[16b +
+ * r] == base + r (others are not written).  A block whose base is negative
+ * or not a multiple of 16 is skipped; one whose page is >= num_pages is
+ * skipped and makes the call return -1.  Slots of a page that no token of the
+ * block fills keep their bytes; the page's column scales are rewritten.
+ */
+int kvqo_quantize_append_pb(const uint16_t *key, const uint16_t *value, int64_t key_token_stride,
+                            int64_t value_token_stride, const int64_t *slot_mapping, int64_t num_tokens,
+                            int32_t num_kv_heads, uint8_t *pool, int64_t num_pages)
+{
+    int rc = 0;
+    for (int64_t b0 = 0; b0 < num_tokens; b0 += KVQO_PAGE) {
+        const int64_t base = slot_mapping[b0];
+        if (base < 0 || base % KVQO_PAGE) continue;
+        const int64_t page = base / KVQO_PAGE;
+        if (page >= num_pages) { rc = -1; continue; }
+        uint8_t present[KVQO_PAGE];
+        int T = 0;
+        for (int r = 0; r < KVQO_PAGE; r++) {
+            present[r] = b0 + r < num_tokens && slot_mapping[b0 + r] == base + r;
+            if (b0 + r < num_tokens) T = r + 1;
+        }
+        for (int h = 0; h < num_kv_heads; h++) {
+            uint16_t kx[KVQO_PAGE * KVQO_D];
+            memset(kx, 0, sizeof(kx));
+            for (int r = 0; r < T; r++)
+                if (present[r])
+                    memcpy(kx + r * KVQO_D, key + (b0 + r) * key_token_stride + (int64_t)h * KVQO_D,
+                           sizeof(uint16_t) * KVQO_D);
+            uint8_t kc[KVQO_PAGE * KVQO_D];
+            uint16_t ks[KVQO_PAGE], kz[KVQO_PAGE];
+            int e[KVQO_D];
+            kvqo_block_variant(kx, present, T, 4, KVQO_PB_ITERS, kc, ks, kz, e, NULL);
+            uint8_t *region = pool + (page * num_kv_heads + h) * KVQO_PB_REGION;
+            for (int r = 0; r < T; r++) {
+                if (!present[r]) continue;
+                uint8_t vc[KVQO_D];
+                uint16_t vs, vz;
+                kvqo_quantize_group_mode(value + (b0 + r) * value_token_stride + (int64_t)h * KVQO_D, 2, 1,
+                                         vc, &vs, &vz);
+                kvqo_store_token_fmt(4, 2, region, r, kc + r * KVQO_D, ks[r], kz[r], vc, vs, vz);
+            }
+            for (int j = 0; j < KVQO_D; j++) region[KVQO_REGION + j] = (uint8_t)((e[j] + 15) * 4);
+        }
+    }
+    return rc;
+}
+
+/* Dequantised, un-rotated key and value of token slot `off` of a
+ * page-balanced region: key 2^e_j (s c_j + z) (e_j from the column-scale
+ * byte), value as in v1; both through H / 128. */
+void kvqo_dequant_slot_pb(const uint8_t *region, int off, double *k_out, double *v_out)
+{
+    uint8_t kc[KVQO_D], vc[KVQO_D];
+    uint16_t ks, kz, vs, vz;
+    kvqo_load_token_fmt(4, 2, region, off, kc, &ks, &kz, vc, &vs, &vz);
+    double yt[KVQO_D];
+    for (int j = 0; j < KVQO_D; j++) {
+        const int e = region[KVQO_REGION + j] / 4 - 15;
+        yt[j] = ldexp(kvqo_half_to_double(ks) * kc[j] + kvqo_half_to_double(kz), e);
+    }
+    kvqo_hadamard_matvec_f64(yt, k_out);
+    for (int j = 0; j < KVQO_D; j++) k_out[j] /= 128.0;
+    dequant_unrotate(vc, vs, vz, 1, v_out);
+}
+
+/* Plain definition of a decode step over a page-balanced cache (16-token
+ * pages, u8 [num_pages][num_kv_heads][1792]): as kvqo_decode_attention, with
+ * the keys dequantised by kvqo_dequant_slot_pb.  Returns 0, or -1 on an
+ * invalid shape or page id. */
+int kvqo_decode_attention_pb(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                             const int32_t *block_tables, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, const uint16_t *query, double scale,
+                             const uint8_t *head_mask, double *out)
+{
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+    const int G = num_q_heads / num_kv_heads;
+    for (int b = 0; b < num_seqs; b++) {
+        const int64_t n = seq_lens[b];
+        if (n < 0 || n > (int64_t)max_pages_per_seq * KVQO_PAGE) return -1;
+        for (int kvh = 0; kvh < num_kv_heads; kvh++) {
+            int any = 0;
+            for (int g = 0; g < G; g++)
+                if (!head_mask || head_mask[b * num_q_heads + kvh * G + g]) any = 1;
+            if (!any) continue;
+            double *K = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
+            double *V = malloc(sizeof(double) * KVQO_D * (n > 0 ? n : 1));
+            if (!K || !V) { free(K); free(V); return -1; }
+            for (int64_t t = 0; t < n; t++) {
+                int32_t page = block_tables[(int64_t)b * max_pages_per_seq + t / KVQO_PAGE];
+                if (page < 0 || page >= num_pages) { free(K); free(V); return -1; }
+                kvqo_dequant_slot_pb(pool + ((int64_t)page * num_kv_heads + kvh) * KVQO_PB_REGION,
+                                     (int)(t % KVQO_PAGE), K + t * KVQO_D, V + t * KVQO_D);
+            }
+            for (int g = 0; g < G; g++) {
+                const int hq = kvh * G + g;
+                if (head_mask && !head_mask[b * num_q_heads + hq]) continue;
+                kvqo_attention_f64(K, V, n, query + ((int64_t)b * num_q_heads + hq) * KVQO_D, 1, scale,
+                                   out + ((int64_t)b * num_q_heads + hq) * KVQO_D);
+            }
+            free(K); free(V);
+        }
+    }
+    return 0;
 }

@@ -30,7 +30,15 @@ int kvqo_decode_attention_folded_fmt(int kbits, int vbits, const uint8_t *pool, 
                                      int32_t num_q_heads, const uint16_t *query, double scale, double *out);
 void kvqo_attention_f16(const uint16_t *k, const uint16_t *v, int64_t n, const uint16_t *q, int32_t G,
                         double scale, double *out);
-void kvqo_block_variant(const uint16_t *x, int T, int bits, int iters, uint8_t *codes_out, double *out);
+int kvqo_block_variant(const uint16_t *x, const uint8_t *present, int T, int bits, int iters,
+                       uint8_t *codes_out, uint16_t *s_out, uint16_t *z_out, int *e_out, double *out);
+int kvqo_quantize_append_pb(const uint16_t *key, const uint16_t *value, int64_t key_token_stride,
+                            int64_t value_token_stride, const int64_t *slot_mapping, int64_t num_tokens,
+                            int32_t num_kv_heads, uint8_t *pool, int64_t num_pages);
+int kvqo_decode_attention_pb(const uint8_t *pool, int64_t num_pages, int32_t num_kv_heads,
+                             const int32_t *block_tables, int32_t max_pages_per_seq, const int32_t *seq_lens,
+                             int32_t num_seqs, int32_t num_q_heads, const uint16_t *query, double scale,
+                             const uint8_t *head_mask, double *out);
 uint16_t kvqo_float_to_half(float f);
 
 static uint64_t state = 0x9E3779B97F4A7C15ull;
@@ -120,8 +128,32 @@ int main(void)
     uint8_t codes[16 * 128];
     kvqo_attention_f16(kx, vx, 64, qx, 3, 0.088, o);
     kvqo_attention_f16(kx, vx, 0, qx, 3, 0.088, o);
+    uint16_t ss[16], zz[16];
+    int ee[128];
+    uint8_t pres[16];
+    for (int t = 0; t < 16; t++) pres[t] = (uint8_t)(t % 5 != 3);
     for (int bits = 2; bits <= 8; bits *= 2)
-        for (int it = 0; it < 3; it++) kvqo_block_variant(kx, 16, bits, it, codes, rec);
+        for (int it = 0; it < 3; it++) {
+            if (kvqo_block_variant(kx, NULL, 16, bits, it, codes, ss, zz, ee, rec)) return 20;
+            if (kvqo_block_variant(kx, pres, 11, bits, it, codes, NULL, NULL, ee, rec)) return 21;
+        }
+    /* page-balanced keys: 2 pages (the second partial, with a hole) of 2 KV
+     * heads in a pool of 3, then a decode (30 tokens x 2 heads x 128 <= kx) */
+    {
+        const int64_t ntok = 30;
+        int64_t slots[30];
+        for (int t = 0; t < 30; t++) slots[t] = 16 * (t / 16 == 0 ? 2 : 0) + t % 16;
+        slots[20] = -1;
+        uint8_t *pool = calloc(3 * 2 * 1792, 1);
+        if (!pool) return 22;
+        if (kvqo_quantize_append_pb(kx, vx, 2 * 128, 2 * 128, slots, ntok, 2, pool, 3)) return 23;
+        const int32_t bt[3] = {2, 0, 1}, lens[1] = {30};
+        uint16_t q8[4 * 128];
+        for (int i = 0; i < 4 * 128; i++) q8[i] = rand_half(1.0);
+        double out8[4 * 128];
+        if (kvqo_decode_attention_pb(pool, 3, 2, bt, 3, lens, 1, 4, q8, 0.088, NULL, out8)) return 24;
+        free(pool);
+    }
     printf("selftest: ok\n");
     return 0;
 }

@@ -267,6 +267,88 @@ def test_value_mean_is_dequantised_channel_zero():
         assert abs(oracle.half_to_double(vmu) - float(x16[0])) <= s / 2 + 2.0 ** -10 * (3 * s + abs(float(x16[0]))) + 1e-7
 
 
+def _on_grid_loose_zero(rng, L, delta=2.0):
+    """fp16 group whose rotation y = z0 + delta * c lies exactly on an L-level
+    grid, but whose zero z0 is NOT representable in fp16, while the group mean
+    x_0 = z0 + delta * sum(c) / 128 (= original channel 0, since H 1 = 128 e_0)
+    is.  With delta = 2 every other channel x_j = delta (H c)_j / 128 is a
+    multiple of 2^-6 below 2^5 (fp16-exact), and the zero, between 16 and 32
+    in magnitude for typical codes, has more bits than fp16 keeps there."""
+    while True:
+        c = rng.integers(0, L + 1, D)
+        c[rng.integers(D)] = 0
+        c[rng.integers(D)] = L
+        if c.min() != 0 or c.max() != L:
+            continue
+        x0 = int(rng.integers(-1000, 1000)) * 2.0 ** -10
+        z0 = x0 - delta * c.sum() / 128.0
+        z16 = float(np.float16(z0))
+        if z16 == z0:
+            continue
+        # stay clear of fp16 rounding midpoints: the encoder's fp32 value of z0
+        # carries a rounding error of a few 2^-24 relative
+        ulp = 2.0 ** (math.floor(math.log2(abs(z0))) - 10)
+        if abs(abs(z16 - z0) - ulp / 2) < ulp / 64:
+            continue
+        y = z0 + delta * c
+        x = (H @ y) / 128.0
+        x16 = x.astype(np.float16)
+        if not np.array_equal(x16.astype(np.float64), x):
+            continue
+        return x16, c, delta, z0, x0
+
+
+def test_value_mean_reconstructs_channel_zero_exactly_where_the_zero_cannot():
+    """The reason values store the group mean mu instead of the zero z (the
+    fold of the zero-points into output channel 0 at read-back: dothoosh.com,
+    "KVarN vs TurboQuant", pipeline list, stage 4).  On-grid groups whose
+    rotated zero z0 is not fp16-representable: the same codes and scale come
+    out in both offset modes, but
+      - with mu stored, the dequantised rotated group is y exactly
+        (dequant_slot_rotated) and the un-rotated one is x exactly, channel 0
+        included (dequant_slot);
+      - with z stored, every channel j >= 1 is still exact (H 1 = 128 e_0 keeps
+        the zero out of them) but channel 0 is off by |fp16(z0) - z0| > 0.
+    k4v4 holds both modes at the same width: 4-bit keys store z, 4-bit values
+    mu.  The 2-bit values of K4V2 are checked the same way."""
+    rng = np.random.default_rng(4242)
+    err_z = []
+    for trial in range(60):
+        x16, c, delta, z0, x0 = _on_grid_loose_zero(rng, 15)
+        kc, ks, kz = oracle.quantize_group(x16, 4, offset_mode=0)
+        vc, vs, vmu = oracle.quantize_group(x16, 4, offset_mode=1)
+        assert np.array_equal(kc, c) and np.array_equal(vc, c)
+        assert oracle.half_to_double(ks) == delta == oracle.half_to_double(vs)
+        assert oracle.half_to_double(kz) == float(np.float16(z0)) != z0
+        assert oracle.half_to_double(vmu) == x0
+        region = np.zeros(oracle.region_bytes((4, 4)), np.uint8)
+        oracle.store_token(region, trial % 16, kc, ks, kz, vc, vs, vmu, fmt=(4, 4))
+        kr, vr = oracle.dequant_slot_rotated(region, trial % 16, fmt=(4, 4))
+        y = z0 + delta * c
+        assert np.array_equal(vr, y)
+        assert np.array_equal(kr, float(np.float16(z0)) + delta * c)
+        k, v = oracle.dequant_slot(region, trial % 16, fmt=(4, 4))
+        x = x16.astype(np.float64)
+        assert np.array_equal(v, x)
+        assert np.array_equal(k[1:], x[1:])
+        assert k[0] != x[0] and abs(k[0] - x[0]) == abs(float(np.float16(z0)) - z0)
+        err_z.append(abs(k[0] - x[0]))
+    assert min(err_z) > 0 and max(err_z) <= 2.0 ** -7     # half an fp16 ulp at |z0| < 32
+    # the K4V2 value layout (2-bit codes, mean stored): exact as well
+    for trial in range(30):
+        x16, c, delta, z0, x0 = _on_grid_loose_zero(rng, 3)
+        vc, vs, vmu = oracle.quantize_group(x16, 2)
+        assert np.array_equal(vc, c) and oracle.half_to_double(vs) == delta
+        assert oracle.half_to_double(vmu) == x0
+        region = np.zeros(1664, np.uint8)
+        zc = np.zeros(D, np.uint8)
+        oracle.store_token(region, 5, zc, 0, 0, vc, vs, vmu)
+        _, vr = oracle.dequant_slot_rotated(region, 5)
+        _, v = oracle.dequant_slot(region, 5)
+        assert np.array_equal(vr, z0 + delta * c)
+        assert np.array_equal(v, x16.astype(np.float64))
+
+
 # --------------------------------------------------------------------------
 # Byte layout
 # --------------------------------------------------------------------------
