@@ -291,8 +291,12 @@ FUSED = [
     (2, 8, 1, [16, 17], 0),
     (3, 16, 2, [400, 33, 777], 0),
     (3, 16, 2, [400, 32, 776], 2),      # new token fills a page inside the pair loop
-    (2, 32, 2, [300, 129], 0),          # G = 16: two head groups store the same bytes
+    (2, 32, 2, [300, 129], 0),          # G = 16: both head groups in one work-group
     (2, 64, 8, [513, 64], 4),
+    # G = 32: four head groups, two work-groups per (split, KV head), each of
+    # which encodes the new token into the same slot before reading the page
+    (2, 64, 2, [300, 129], 0),
+    (3, 64, 2, [40, 17, 1], 2),
 ]
 
 
@@ -882,6 +886,71 @@ def test_preset_decode_small_matches_oracle(dev, fmt, B, Hq, Hkv, lens):
         assert err <= TOL, f"pps={pps} err={err}"
     out16 = kvq.decode_attention(qd, cache, btd, ld, L, out_dtype=torch.float16, fmt=_kfmt(fmt))
     assert np.max(np.abs(out16.float().cpu().numpy() - ref)) <= TOL
+
+
+def test_bench_step_qwen3_32b_16k_k4v2(dev):
+    """The benchmark's timed step at full size: Qwen3-32B shape (8 x 16384
+    cached tokens, 64 q / 8 KV heads), the cache filled by the bulk append,
+    then kvq_append_decode_partials (the split kernel encodes each
+    sequence's token 16384 into its page) and kvq_decode_combine, with the
+    heuristic split and fp16 output, exactly as bench.py calls them.
+    Checked against the oracle: the new token's bytes of every (sequence, KV
+    head), all 16385 tokens' bytes of 2 sequences x 2 KV heads, and the
+    attention of their 8 query heads (2e-3)."""
+    w = inp.workload("qwen3_32b_16k")
+    B, Hq, Hkv, ctx = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.context
+    n = ctx + 1
+    log("bench step qwen3_32b_16k k4v2: fill")
+    bt, num_pages = inp.page_table(w)
+    cache = torch.zeros((num_pages, Hkv, 1664), dtype=torch.uint8, device=dev)
+    keep = (0, 5)
+    kept, new_k, new_v = {}, [], []
+    for b in range(B):
+        k, v = inp.sequence_kv(w, b, 0, n, device=dev)
+        gpu_append(k[:ctx], v[:ctx], torch.from_numpy(inp.slot_mapping(bt, b, 0, ctx)).to(dev), cache)
+        new_k.append(k[ctx:])
+        new_v.append(v[ctx:])
+        if b in keep:
+            kept[b] = (k.cpu().numpy(), v.cpu().numpy())
+        del k, v
+    nk, nv = torch.cat(new_k).contiguous(), torch.cat(new_v).contiguous()
+    q = inp.queries(w, 0, device=dev).contiguous()
+    lens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    btd = torch.from_numpy(bt).to(dev)
+    pps = kvq.decode_pages_per_split(B, Hq, Hkv, n)
+    log(f"bench step: fused partials + combine, {pps} pages per split")
+    ws = kvq.alloc_workspace(B, Hq, Hkv, n)
+    kvq.append_decode_partials(nk, nv, q, cache, btd, lens, n, ws)
+    out = kvq.decode_combine(ws, lens, Hq, Hkv, n, out_dtype=torch.float16).float().cpu().numpy()
+    torch.cuda.synchronize()
+    # the appended token of every sequence and KV head
+    nk_np, nv_np = nk.cpu().numpy(), nv.cpu().numpy()
+    page = bt[:, ctx // 16]
+    region_np = cache[torch.from_numpy(page.astype(np.int64)).to(dev)].cpu().numpy()      # [B][Hkv][1664]
+    for b in range(B):
+        pool = np.zeros((1, Hkv, 1664), np.uint8)
+        oracle.quantize_append(nk_np[b:b + 1], nv_np[b:b + 1], np.array([ctx % 16], np.int64), pool)
+        for kvh in range(Hkv):
+            got, ref = region_np[b, kvh], pool[0, kvh]
+            o = ctx % 16
+            for lo, hi in ((64 * o, 64 * o + 64), (1536 + 4 * o, 1540 + 4 * o), (1600 + 4 * o, 1604 + 4 * o)):
+                assert np.array_equal(got[lo:hi], ref[lo:hi]), f"new token of seq {b} head {kvh}"
+            for g4 in range(16):      # value words of slot o: u16 at 1024 + 128 (o/4) + 8 m + 2 (o%4)
+                a = 1024 + 128 * (o // 4) + 8 * g4 + 2 * (o % 4)
+                assert np.array_equal(got[a:a + 2], ref[a:a + 2])
+    pages = int(math.ceil(n / 16))
+    for b in keep:
+        k_seq, v_seq = kept[b]
+        for kvh in (2, 7):
+            pool = np.zeros((pages, 1, 1664), np.uint8)
+            oracle.quantize_append(k_seq[:, kvh:kvh + 1], v_seq[:, kvh:kvh + 1], np.arange(n, dtype=np.int64), pool)
+            got = cache[torch.from_numpy(bt[b, :pages].astype(np.int64)).to(dev), kvh].cpu().numpy()
+            assert np.array_equal(got, pool[:, 0]), f"codes differ: seq {b} head {kvh}"
+            qh = q.cpu().numpy()[b, kvh * w.gqa:(kvh + 1) * w.gqa][None]
+            ref = oracle.decode_attention(pool, np.arange(pages, dtype=np.int32)[None], np.array([n]), qh, SCALE)[0]
+            err = np.max(np.abs(out[b, kvh * w.gqa:(kvh + 1) * w.gqa] - ref))
+            log(f"  seq {b} kv {kvh}: err {err:.2e}")
+            assert err <= TOL
 
 
 @pytest.mark.parametrize("fmt", PRESET_FMTS)
