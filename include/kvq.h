@@ -335,6 +335,39 @@ kvq_status kvq_append_decode_partials(const kvq_format *fmt, const uint16_t *new
                                       void *stream);
 
 /*
+ * The decode step of kvq_append_decode_attention without a caller-supplied
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The split partials go to a fixed array of KVQ_NOALLOC_SCRATCH_BYTES in
+ * the library's device code, one per device, resolved on the first call on
+ * each device (with that device current) and held until the process ends.
+ * The call allocates nothing, on the host or the device.
+ *   Arguments, layouts, checks and results: as kvq_append_decode_attention
+ *   with workspace and workspace_bytes left out.
+ *   Errors: KVQ_ERR_WORKSPACE, before anything touches the device, when the
+ *   partials of these sizes (kvq_decode_workspace_bytes(fmt, num_seqs,
+ *   num_q_heads, num_kv_heads, max_seq_len, pages_per_split)) exceed
+ *   KVQ_NOALLOC_SCRATCH_BYTES; KVQ_ERR_UNSUPPORTED on a device index >= 64;
+ *   KVQ_ERR_HIP if the array's address cannot be resolved; otherwise the
+ *   statuses of kvq_append_decode_attention (invalid sizes included).
+ * Every call on a device shares that device's array, and it keeps the last
+ * call's contents (the partials are written before they are read, so
+ * nothing needs clearing).  Calls that overlap in time on one device --
+ * concurrent streams, or several host threads -- race on it: serialise
+ * them, e.g. on one stream.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+kvq_status kvq_append_decode_attention_noalloc(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                               const uint16_t *new_key, const uint16_t *new_value,
+                                               int64_t key_token_stride, int64_t value_token_stride,
+                                               const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                               const int32_t *block_tables, int32_t max_pages_per_seq,
+                                               const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                               int32_t pages_per_split, void *stream);
+
+/*
  * Several query rows per sequence: the q_len newest tokens of every sequence
  * (a speculative-decoding draft being verified, or a chunk of a prefill),
  * already appended to the cache, attend at once.  Row m of sequence b sits at

@@ -20,13 +20,15 @@ __all__ = [
     "KvqError", "Format", "load", "library_path", "format_from_string", "page_bytes",
     "cache_bytes", "alloc_cache", "quantize_append", "decode_workspace_bytes",
     "decode_pages_per_split", "alloc_workspace", "decode_attention", "decode_partials",
-    "decode_combine", "append_decode_attention", "append_decode_partials", "decode_split_slots",
+    "decode_combine", "append_decode_attention", "append_decode_partials", "append_decode_attention_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "decode_split_slots",
     "decode_partials_slots", "decode_combine_slots", "version",
     "HEAD_DIM", "PAGE", "REGION_BYTES",
 ]
 
 HEAD_DIM = 128
 PAGE = 16
+NOALLOC_SCRATCH_BYTES = 16 << 20     # KVQ_NOALLOC_SCRATCH_BYTES of include/kvq.h
 REGION_BYTES = 1664
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +90,8 @@ def load():
                                                        P, i32, i32, i32, i32, ctypes.c_float, P, sz, i32, P]),
         "kvq_append_decode_partials": (ctypes.c_int, [FP, P, P, i64, i64, P, P, i64, P, i32, P, i32, i32, i32,
                                                       i32, ctypes.c_float, P, sz, i32, P]),
+        "kvq_append_decode_attention_noalloc": (ctypes.c_int, [FP, P, ctypes.c_int, P, P, i64, i64, P, P, i64, P,
+                                                               i32, P, i32, i32, i32, i32, ctypes.c_float, i32, P]),
         "kvq_decode_workspace_bytes_mq": (sz, [FP, i32, i32, i32, i32, i32, i32]),
         "kvq_decode_attention_mq": (ctypes.c_int, [FP, P, ctypes.c_int, P, i32, P, i64, P, i32, P, i32, i32,
                                                    i32, i32, ctypes.c_float, P, sz, i32, P]),
@@ -381,6 +385,31 @@ def append_decode_attention(new_key: torch.Tensor, new_value: torch.Tensor, quer
         int(max_seq_len), float(softmax_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
         int(pages_per_split), _stream_ptr(stream))
     _check(st, "kvq_append_decode_attention")
+    return out
+
+
+def append_decode_attention_noalloc(new_key: torch.Tensor, new_value: torch.Tensor, query: torch.Tensor,
+                                    cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                    max_seq_len: int, out: torch.Tensor, softmax_scale: float | None = None,
+                                    pages_per_split: int = 0, stream=None, fmt: Format | None = None) -> torch.Tensor:
+    """``append_decode_attention`` with its split partials in the library's
+    fixed device array (kvq_append_decode_attention_noalloc): no workspace,
+    and nothing allocated -- ``out`` (fp32 or fp16 [B][Hq][128]) is
+    required.  Calls that overlap on one device race on the array."""
+    _decode_checks(query, cache, block_tables, seq_lens, fmt)
+    B, Hq, _ = query.shape
+    Hkv = cache.shape[1]
+    _new_token_checks(new_key, new_value, B, Hkv)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out.dtype not in (torch.float32, torch.float16) or not out.is_contiguous() or out.shape != (B, Hq, HEAD_DIM):
+        raise ValueError("out must be contiguous fp32/fp16 [B][Hq][128]")
+    st = load().kvq_append_decode_attention_noalloc(
+        ctypes.byref(_fmt(fmt)), _ptr(out), OUT_F32 if out.dtype == torch.float32 else OUT_F16,
+        _ptr(new_key), _ptr(new_value), new_key.stride(0), new_value.stride(0), _ptr(query), _ptr(cache),
+        cache.shape[0], _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), B, Hq, Hkv,
+        int(max_seq_len), float(softmax_scale), int(pages_per_split), _stream_ptr(stream))
+    _check(st, "kvq_append_decode_attention_noalloc")
     return out
 
 

@@ -3,6 +3,8 @@
 // include/kvq.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/kvq.h"
 #include "../../include/kvq_measure.h"
 #include "kvq_device.h"
@@ -59,6 +61,37 @@ kvq_status hip_status(hipError_t e) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split partials of kvq_append_decode_attention_noalloc, for callers that
+// cannot allocate: one fixed array per device, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the device address is resolved once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static_assert(kScratchBytes == KVQ_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];    // per device: the address of `scratch` there, once resolved
+
+// Device address of `scratch` on the current device (resolved on the first
+// call on each device, with that device current).
+kvq_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return KVQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return KVQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
 
 int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerGroup); }
 
@@ -357,6 +390,32 @@ kvq_status kvq_append_decode_attention(const kvq_format *fmt, void *out, kvq_out
     if (st == KVQ_OK) st = append_inputs(new_key, new_value, key_token_stride, value_token_stride, a);
     if (st != KVQ_OK) return st;
     return hip_status(launch_both(a, (hipStream_t)stream));
+}
+
+kvq_status kvq_append_decode_attention_noalloc(const kvq_format *fmt, void *out, kvq_out_dtype out_dtype,
+                                               const uint16_t *new_key, const uint16_t *new_value,
+                                               int64_t key_token_stride, int64_t value_token_stride,
+                                               const uint16_t *query, uint8_t *cache, int64_t num_pages,
+                                               const int32_t *block_tables, int32_t max_pages_per_seq,
+                                               const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t max_seq_len, float softmax_scale,
+                                               int32_t pages_per_split, void *stream) {
+    // the partials this call needs must fit the fixed array (checked before
+    // the device is touched); sizes the workspace query rejects are rejected
+    // the same way as by kvq_append_decode_attention
+    const size_t need = kvq_decode_workspace_bytes(fmt, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
+                                                   pages_per_split);
+    if (need > kScratchBytes) return KVQ_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const kvq_status st = scratch_address(&ws);
+        if (st != KVQ_OK) return st;
+    }
+    return kvq_append_decode_attention(fmt, out, out_dtype, new_key, new_value, key_token_stride,
+                                       value_token_stride, query, cache, num_pages, block_tables,
+                                       max_pages_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                                       max_seq_len, softmax_scale, ws, need ? kScratchBytes : 0,
+                                       pages_per_split, stream);
 }
 
 int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t num_q_heads,

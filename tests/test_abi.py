@@ -420,3 +420,26 @@ def test_binding_refuses_host_tensors():
     cache = torch.zeros((1, 1, 1664), dtype=torch.uint8)
     with pytest.raises(ValueError, match="GPU tensors"):
         kvq.quantize_append(k, k, slots, cache)
+
+
+def test_noalloc_step_rejects_partials_beyond_its_array_without_a_device():
+    """kvq_append_decode_attention_noalloc checks the partials' size against
+    its fixed array before it touches the device: sizes whose partials exceed
+    KVQ_NOALLOC_SCRATCH_BYTES give KVQ_ERR_WORKSPACE, a NULL format
+    KVQ_ERR_NULL, invalid sizes the workspace call's statuses."""
+    lib = kvq.load()
+    f = kvq.format_from_string("k4v2_g128")
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    g = P(0x10000)
+
+    def call(fmt, B, Hq, Hkv, L, pps=0):
+        return lib.kvq_append_decode_attention_noalloc(fmt, g, 1, g, g, i64(Hkv * 128), i64(Hkv * 128), g, g,
+                                                       i64(100), g, i32(-(-L // 16)), g, i32(B), i32(Hq), i32(Hkv),
+                                                       i32(L), ctypes.c_float(0.088), i32(pps), None)
+    assert kvq.decode_workspace_bytes(64, 64, 8, 131072) > kvq.NOALLOC_SCRATCH_BYTES
+    assert call(ctypes.byref(f), 64, 64, 8, 131072) == 5
+    assert call(None, 8, 64, 8, 1000) == 1
+    assert call(ctypes.byref(f), 8, 60, 8, 1000) == 2          # 60 % 8 != 0
+    header = open(HEADER).read()
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", header)
+    assert m and int(m.group(1)) << int(m.group(2)) == kvq.NOALLOC_SCRATCH_BYTES
