@@ -855,9 +855,45 @@ def mixed_window(torch, inp, kvq, lib, dev, stream, args, sink=4, recent=124):
             "kv_bytes": kv_bytes, "launches_per_step": 3}
 
 
+APPEND_COUNTERS_FILE = os.path.join(ROOT, "profiles", "append_staged_llama31_70b_128k_counters.txt")
+APPEND_SOURCES = [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "csrc", f)
+                  for f in ("kvq_append.hip", "kvq_device.h", "kvq_quant.h")] + \
+                 [os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "build.py")]
+# MI355X vector ALU: 256 CUs x 4 SIMDs x 16 lanes, one 32-bit lane-op per lane per clock
+# (fp32 add, mul, compare, integer, conversion) at 2.4 GHz
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def recorded_append_counters():
+    """(fields, note) from the committed append counter summary, or (None,
+    reason) when it is missing or the append sources changed since."""
+    if not os.path.exists(APPEND_COUNTERS_FILE):
+        return None, "no counter summary"
+    rec = {}
+    with open(APPEND_COUNTERS_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in APPEND_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if rec.get("kernel_source_sha256") != h.hexdigest():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return {k: int(rec[k]) for k in ("fetch_bytes_per_launch", "write_bytes_per_launch",
+                                         "valu_instructions_per_launch")}, "rocprofv3 counters (scaled bytes)"
+    except (KeyError, ValueError):
+        return None, "malformed counter summary"
+
+
 def append_bench(torch, inp, kvq, call, dev):
     """Bulk quantise-append of the Llama-3.1-70B-shaped 131072-token prompt
-    (8 KV heads) in one call; tokens/s of the prompt, timed with HIP events."""
+    (8 KV heads) in one call; tokens/s of the prompt.  Each of the timed
+    launches is bracketed by HIP events on the launch stream; the headline is
+    their mean, with the median and p10/p90 beside it (the encoder is
+    ALU-heavy and the shader clock falls over a run of launches)."""
     import numpy as np
     w = inp.workload("llama31_70b_128k")
     T = w.context
@@ -871,20 +907,39 @@ def append_bench(torch, inp, kvq, call, dev):
     for _ in range(3):
         fn(*args)
     reps = 20
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    hev = HipEvents(2 * reps)
     torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record(stream)
-        fn(*args)
-        e1.record(stream)
+    for r in range(reps):
+        hev.record(2 * r, stream.cuda_stream)
+        if fn(*args):
+            raise RuntimeError("kvq_quantize_append failed")
+        hev.record(2 * r + 1, stream.cuda_stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms_all = np.array([hev.elapsed_ms(2 * r, 2 * r + 1) for r in range(reps)])
+    hev.close()
+    ms = float(ms_all.mean())
     moved = T * w.num_kv_heads * APPEND_BYTES_PER_TOKEN_HEAD
+    counters, note = recorded_append_counters()
+    roof = {"kernel": "quantize_append_staged", "bound": "alu", "unit": "lane-op/s",
+            "peak": VALU_PEAK_LANE_OPS, "achieved": None, "frac": None,
+            "hbm_bytes_per_launch": moved, "hbm_GBps": round(moved / (ms * 1e-3) / 1e9, 2),
+            "hbm_frac": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None, "counters_note": note}
+    if counters:
+        lane_ops = counters["valu_instructions_per_launch"] * 64
+        roof.update({"valu_instructions_per_launch": counters["valu_instructions_per_launch"],
+                     "achieved": round(lane_ops / (ms * 1e-3), 1),
+                     "frac": round(lane_ops / (ms * 1e-3) / VALU_PEAK_LANE_OPS, 4),
+                     "traffic": counters["fetch_bytes_per_launch"] + counters["write_bytes_per_launch"]})
     return {"append_tokens_per_s": round(T / (ms * 1e-3), 1),
             "append_config": {"workload": "llama31_70b_128k prefill", "tokens": T,
                               "num_kv_heads": w.num_kv_heads, "kernel_ms": round(ms, 5),
+                              "kernel_ms_median": round(float(np.median(ms_all)), 5),
+                              "kernel_ms_p10": round(float(np.percentile(ms_all, 10)), 5),
+                              "kernel_ms_p90": round(float(np.percentile(ms_all, 90)), 5),
+                              "launches": reps,
                               "GBps": round(moved / (ms * 1e-3) / 1e9, 2),
-                              "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}}
+                              "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                              "roofline": roof}}
 
 
 if __name__ == "__main__":

@@ -147,6 +147,48 @@ def test_append_mixed_regimes_strided_and_skips(dev, H, T, num_pages, seed):
     assert diff.size == 0, f"{len(diff)} bytes differ, first at {diff[:5].tolist()}"
 
 
+# Bulk appends (65536 (token, KV head) rows and more) take the LDS-staged
+# kernel for power-of-two head counts -- with separate address forms below 4
+# heads, from 4 to 32, and 64 or more -- and the lane-per-row kernel
+# otherwise.  (H, T, token-stride padding in elements, format)
+BULK = [(1, 65600, 0, (4, 2)), (2, 33000, 8, (4, 2)), (4, 17000, 0, (4, 2)), (8, 8193, 24, (4, 2)),
+        (16, 4200, 0, (8, 4)), (64, 1100, 0, (4, 2)), (128, 520, 16, (4, 4)), (3, 22000, 0, (4, 2)),
+        (8, 8300, 0, (3, 3)), (8, 8300, 8, (8, 2))]
+
+
+@pytest.mark.parametrize("H,T,pad,fmt", BULK)
+def test_bulk_append_kernels_bit_exact(dev, H, T, pad, fmt):
+    """Bulk appends against the oracle, bit for bit, over the whole pool:
+    random page placement, strided token rows, skipped slots (negative) and
+    slots outside the pool (not written), and a ragged last batch."""
+    log(f"bulk append H={H} T={T} pad={pad} fmt={fmt}")
+    rng = np.random.default_rng(H * 1000 + T + pad)
+    region, kf = oracle.region_bytes(fmt), _kfmt(fmt)
+    num_pages = -(-T // 16) + 3
+    perm = rng.permutation(num_pages).astype(np.int64)
+    t = np.arange(T)
+    slots = perm[t // 16] * 16 + t % 16
+    slots[rng.choice(T, 37, replace=False)] = -1
+    slots[rng.choice(T, 11, replace=False)] = (num_pages + 2) * 16 + 3       # outside the pool
+    width = H * D + pad
+    kbuf = (rng.standard_normal((T, width)) * rng.choice([0.05, 1, 30], (T, 1))).astype(np.float16)
+    vbuf = rng.standard_normal((T, width)).astype(np.float16)
+    kbuf[:, 5::97] *= 12
+    kt, vt = torch.from_numpy(kbuf).to(dev), torch.from_numpy(vbuf).to(dev)
+    k = kt[:, :H * D].view(T, H, D) if pad == 0 else torch.as_strided(kt, (T, H, D), (width, D, 1))
+    v = vt[:, :H * D].view(T, H, D) if pad == 0 else torch.as_strided(vt, (T, H, D), (width, D, 1))
+    cache = torch.full((num_pages, H, region), 0xA5, dtype=torch.uint8, device=dev)
+    gpu_append(k, v, torch.from_numpy(slots).to(dev), cache, fmt=kf)
+    pool = np.full((num_pages, H, region), 0xA5, np.uint8)
+    in_pool = np.where(slots < num_pages * 16, slots, -1)        # the oracle skips them the same way
+    oracle.quantize_append(np.ascontiguousarray(kbuf[:, :H * D].reshape(T, H, D)),
+                           np.ascontiguousarray(vbuf[:, :H * D].reshape(T, H, D)), in_pool, pool, fmt=fmt)
+    got = cache.cpu().numpy()
+    if not np.array_equal(got, pool):
+        bad = np.argwhere(got != pool)
+        raise AssertionError(f"{len(bad)} bytes differ, first at (page, head, byte) {bad[0].tolist()}")
+
+
 def test_append_one_token_at_a_time_matches_bulk(dev):
     w = inp.workload("qwen3_32b_16k", context=64, new_tokens=0, num_seqs=2)
     bt, num_pages = inp.page_table(w)
