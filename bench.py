@@ -70,6 +70,9 @@ def parse():
                     help="skip the fp16 sink + recent window beside the K4V2 history")
     ap.add_argument("--no-presets", action="store_true",
                     help="skip the k4v4 / k8v2 / k8v4 / k3v3 presets on the same workload")
+    ap.add_argument("--preset-list", default="",
+                    help="comma-separated preset:page_tokens legs to run instead of the default list "
+                         "(e.g. k4v2_g128:64)")
     ap.add_argument("--no-multi-query", action="store_true",
                     help="skip the multi-row (speculative draft) decode on the same cache")
     ap.add_argument("--no-warm", action="store_true",
@@ -544,10 +547,12 @@ def main():
         result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
 
     if not args.no_presets:
-        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt)
-                             for p, pt in (("k4v4_g128", 16), ("k8v2_g128", 16), ("k8v4_g128", 16),
-                                           ("k3v3_g128", 16), ("k4v2_g128", 32), ("k4v2_g128", 64),
-                                           ("k4v2_g128", 128))]
+        legs = (("k4v4_g128", 16), ("k8v2_g128", 16), ("k8v4_g128", 16), ("k3v3_g128", 16),
+                ("k4v2_g128", 32), ("k4v2_g128", 64), ("k4v2_g128", 128))
+        if args.preset_list:
+            legs = [(x.split(":")[0], int(x.split(":")[1]) if ":" in x else 16)
+                    for x in args.preset_list.split(",")]
+        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt) for p, pt in legs]
 
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))

@@ -74,6 +74,8 @@
 namespace kvq {
 namespace {
 
+constexpr int kDecodeWaves = 4;    // waves per work-group of decode_kernel
+
 
 // One page of one lane, for KB-bit keys and VB-bit values.
 template <int KB, int VB>
@@ -398,23 +400,17 @@ __device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const Pag
     return __builtin_bit_cast(v8h, bwu);
 }
 
-// One page pair for kG head groups of 8 query heads (kG = 2: 16 heads, when
-// a KV head has more than 8 query heads or query rows): the key and value
-// operands are unpacked once and feed every group's MFMAs; each group keeps
-// its own softmax state.  lim[h]: group h's token limit (kMasked).
-template <int KB, int VB, int kG, bool kMasked, bool kFirst>
-__device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
-                                             int tokB, const int (&lim)[kG], const v8h (&bq)[kG][4],
-                                             const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
-    v8h bw[kG];
+// Code-domain dot products of one page pair for kG head groups: the score
+// MFMAs (4 per page and group).  With kG = 2 each k-step's key operands feed
+// both groups' MFMAs as they are unpacked, so that only one operand per page
+// is live at a time.
+template <int KB, int VB, int kG>
+__device__ __forceinline__ void pair_dots(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B,
+                                          const v8h (&bq)[kG][4], v4f (&dA)[kG], v4f (&dB)[kG]) {
     if constexpr (kG == 1) {
-        const v4f dA = page_dots<KB, VB>(A, bq[0]);
-        const v4f dB = page_dots<KB, VB>(B, bq[0]);
-        bw[0] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim[0], lc[0], g, st[0]);
+        dA[0] = page_dots<KB, VB>(A, bq[0]);
+        dB[0] = page_dots<KB, VB>(B, bq[0]);
     } else {
-        // each k-step's key operands feed every group's MFMAs as they are
-        // unpacked, so that only one operand per page is live at a time
-        v4f dA[kG], dB[kG];
 #pragma unroll
         for (int h = 0; h < kG; h++) dA[h] = dB[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -427,10 +423,22 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
                 dB[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, bq[h][q], dB[h], 0, 0, 0);
             }
         }
-#pragma unroll
-        for (int h = 0; h < kG; h++)
-            bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], g, st[h]);
     }
+}
+
+// The rest of a page pair once its dot products dA, dB are known: softmax
+// weights, then the P.V MFMAs (8 per group); the value operands are unpacked
+// once and feed every group.  Each group keeps its own softmax state.
+// lim[h]: group h's token limit (kMasked).
+template <int KB, int VB, int kG, bool kMasked, bool kFirst>
+__device__ __forceinline__ void pair_finish(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B,
+                                            const v4f (&dA)[kG], const v4f (&dB)[kG], int tokA, int tokB,
+                                            const int (&lim)[kG], const LaneConsts (&lc)[kG], int g,
+                                            State (&st)[kG]) {
+    v8h bw[kG];
+#pragma unroll
+    for (int h = 0; h < kG; h++)
+        bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], g, st[h]);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         const v8h av = value_operand<KB, VB>(A, B, j);
@@ -440,10 +448,22 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
     }
 }
 
+// One page pair for kG head groups of 8 query heads (kG = 2: 16 heads, when
+// a KV head has more than 8 query heads or query rows): the key and value
+// operands are unpacked once and feed every group's MFMAs.
+template <int KB, int VB, int kG, bool kMasked, bool kFirst>
+__device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, int tokA,
+                                             int tokB, const int (&lim)[kG], const v8h (&bq)[kG][4],
+                                             const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
+    v4f dA[kG], dB[kG];
+    pair_dots<KB, VB, kG>(A, B, bq, dA, dB);
+    pair_finish<KB, VB, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, g, st);
+}
+
 // kG: head groups (of 8 query heads, or (row, head) pairs) per work-group;
 // 2 when a KV head has more than 8, so that they share the page unpack.
 template <int KB, int VB, bool kMQ, bool kPaged, int kG>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs a) {
     using Lay = Layout<KB, VB>;
     const int sgroups = (a.head_groups + kG - 1) / kG;   // work-groups per (split, KV head, sequence)
     int split, kvh, sg, b;
@@ -473,8 +493,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // Page ids of this wave's page pairs, one pair per lane: lane j holds the
-    // block-table entries of pages 2k and 2k + 1 of the split, k = wave + 4j
-    // (a split has at most 512 pages, so j < 64; indices are clamped into the
+    // block-table entries of pages 2k and 2k + 1 of the split, k = wave + W j
+    // with W = kDecodeWaves (a split has at most 512 pages, so j < 64 for
+    // W >= 4; indices are clamped into the
     // row, and entries past the split or the sequence are never used).  One
     // vector load at the start replaces a scalar load and wait per pair; the
     // pair loop reads the ids with v_readlane.
@@ -482,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     int32_t bt_a, bt_b;
     {
         const int last = a.bt_stride - 1;
-        const int pa = split * a.pages_per_split + 2 * (wave + kWaves * lane);
+        const int pa = split * a.pages_per_split + 2 * (wave + kDecodeWaves * lane);
         // with pages of several 16-token regions, entry pa >> log2s holds region pa
         const int ea = kPaged ? pa >> a.page_log2s : pa;
         const int eb = kPaged ? (pa + 1) >> a.page_log2s : pa + 1;
@@ -530,7 +551,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 
     __shared__ _Float16 s_qb[kG][16][kHeadDim];   // [group][column][slot], slot = 32g + 8d + e
     __shared__ float s_c1[kG][kHeadsPerGroup], s_c2[kG][kHeadsPerGroup];
-    __shared__ MergeLds s_merge;
+    __shared__ MergeLdsT<kDecodeWaves> s_merge;
 
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
@@ -560,7 +581,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // loaded and processed afterwards with per-token masking.
     const int full_end = min(p_end, n_min / kPage);       // pages below: full
     const int nfull = full_end > p_begin ? (full_end - p_begin) >> 1 : 0;
-    const int nk = nfull > wave ? (nfull - wave + kWaves - 1) / kWaves : 0;
+    const int nk = nfull > wave ? (nfull - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
 
     // The scheduling barrier keeps the compiler from sinking the prefetch
     // loads into the next pair's arithmetic (which it otherwise does to save
@@ -571,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // last pair, and ~14 MB less cache traffic per launch.
     auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, int i) {
         const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
-        const int pa = kPaged ? p_begin + 2 * (wave + kWaves * j) : 0;
+        const int pa = kPaged ? p_begin + 2 * (wave + kDecodeWaves * j) : 0;
         const bool live = i < nk;
         load_page(region_of(__builtin_amdgcn_readlane(bt_a, j), pa), lo, A, live);
         load_page(region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1), lo, B, live);
@@ -624,9 +645,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 of each group ----
     // q' = H q in fp32, scaled by a power of two so that max |q'| lies in
     // [2^13, 2^14), then written as q_hi = fp16(q'), q_lo = fp16(q' - q_hi):
-    // the two-term query carries q' to about 2^-22 of each element.
+    // the two-term query carries q' to about 2^-22 of each element.  (Waves
+    // past the fourth have no heads to rotate.)
 #pragma unroll
-    for (int hq = 0; hq < kG; hq++) {
+    for (int hq = 0; hq < kG && 2 * wave < kHeadsPerGroup; hq++) {
         const int hh = 2 * wave + (lane >> 5);
         const int l32 = lane & 31;
         const int c0 = 4 * l32;
@@ -713,21 +735,24 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     }
 
     if (nk > 0) {
-        // the wave's first pair sets the running maximum; the loop then
-        // rotates the three buffers (pair i in r1, i + 1 in r2, i + 2 in r0)
+        // The wave's first pair sets the running maximum; the loop then
+        // rotates the three buffers (pair i in r1, i + 1 in r2, i + 2 in r0).
+        // Three is the measured best depth: two left the arithmetic waiting
+        // for loads, four made the split kernel slower (more random reads in
+        // flight lower the HBM's efficiency on 1664-byte regions; the
+        // page-walk probe alone slows the same way with depth), and so did a
+        // four-buffer variant that issued each pair's score MFMAs one pair
+        // ahead of its softmax.
         process_pair<KB, VB, kG, false, true>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
-        if (nk > 1) {
-            for (int i = 1;; i += 3) {
-                issue(r0A, r0B, i + 2);
-                process_pair<KB, VB, kG, false, false>(r1A, r1B, 0, 0, lim0, bq, lc, g, st);
-                if (i + 1 >= nk) break;
-                issue(r1A, r1B, i + 3);
-                process_pair<KB, VB, kG, false, false>(r2A, r2B, 0, 0, lim0, bq, lc, g, st);
-                if (i + 2 >= nk) break;
-                issue(r2A, r2B, i + 4);
-                process_pair<KB, VB, kG, false, false>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
-                if (i + 3 >= nk) break;
-            }
+        for (int i = 1; i < nk; i += 3) {
+            issue(r0A, r0B, i + 2);
+            process_pair<KB, VB, kG, false, false>(r1A, r1B, 0, 0, lim0, bq, lc, g, st);
+            if (i + 1 >= nk) break;
+            issue(r1A, r1B, i + 3);
+            process_pair<KB, VB, kG, false, false>(r2A, r2B, 0, 0, lim0, bq, lc, g, st);
+            if (i + 2 >= nk) break;
+            issue(r2A, r2B, i + 4);
+            process_pair<KB, VB, kG, false, false>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
         }
     }
     // Masked pairs: the last pair, and with several query rows possibly the
@@ -746,7 +771,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         PageRegs<KB, VB> tA, tB;
         const int pa = p_begin + 2 * i;
         const bool has_b = pa + 1 < p_end;
-        const int j = i / kWaves;               // the pair's lane in bt_a / bt_b
+        const int j = i / kDecodeWaves;         // the pair's lane in bt_a / bt_b
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
         load_page(region_of(id_a, pa), lo, tA);
         load_page(has_b ? region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1) : region_of(id_a, pa), lo, tB);
@@ -756,8 +781,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
         else
             process_pair<KB, VB, kG, true, false>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
     };
-    if (nfull < npairs && wave == (npairs - 1) % kWaves) masked_pair(npairs - 1);
-    if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kWaves) masked_pair(npairs - 2);
+    if (nfull < npairs && wave == (npairs - 1) % kDecodeWaves) masked_pair(npairs - 1);
+    if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kDecodeWaves) masked_pair(npairs - 2);
 
     // ---- merge the 4 waves; write the partial (or the output) ----
 #pragma unroll
@@ -936,7 +961,7 @@ int resident_workgroups() {
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1>, 256, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1>, 64 * kDecodeWaves, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -962,10 +987,10 @@ hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const La
         grid = dim3((unsigned)blocks, 1, 1);
     }
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(256), 0, stream, ev.start,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start,
                               ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
     return hipGetLastError();
 }
 

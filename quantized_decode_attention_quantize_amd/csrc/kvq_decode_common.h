@@ -80,23 +80,26 @@ __device__ __forceinline__ int64_t io_row(const DecodeArgs &a, int b, int kvh, i
     return ((int64_t)b * a.q_len + m) * (a.num_q_heads / a.q_len) + kvh * G + (v - m * G);
 }
 
-// LDS of the wave merge.
-struct MergeLds {
-    float m[kWaves][kHeadsPerGroup];
-    float l[kWaves][kHeadsPerGroup];
-    float z[kWaves][kHeadsPerGroup];
-    float acc[kWaves][kHeadsPerGroup][kHeadDim];
+// LDS of the merge of the W waves of a work-group.
+template <int W>
+struct MergeLdsT {
+    float m[W][kHeadsPerGroup];
+    float l[W][kHeadsPerGroup];
+    float z[W][kHeadsPerGroup];
+    float acc[W][kHeadsPerGroup][kHeadDim];
 };
+using MergeLds = MergeLdsT<kWaves>;
 
-// Merge the 4 waves' states of a work-group (head indices v0 .. v0 + nh - 1
+// Merge the W waves' states of a work-group (head indices v0 .. v0 + nh - 1
 // of KV head kvh of sequence b) and write the split's partial, or the output
 // when the launch has a single split (then no combine runs).  unscale(j) is
-// the factor of channel block j.  Every thread of the work-group must call it.
+// the factor of channel block j.  Every thread of the work-group must call it;
+// the first 256 (32 per head) merge and store.
 // (rotate_out: the partial is stored in the K4V2 Hadamard domain, acc' = H acc
 // and zacc = acc_0, so that it merges with K4V2 partials in one combine:
 // (H acc')_j / 128 = acc_j for j >= 1 and channel 0 comes from zacc.)
-template <bool kMQ = false, typename Unscale>
-__device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const DecodeArgs &a, int rotated,
+template <bool kMQ = false, int W, typename Unscale>
+__device__ __forceinline__ void merge_and_store(State &st, MergeLdsT<W> &s, const DecodeArgs &a, int rotated,
                                                 Unscale unscale, int wave, int tid, int b, int kvh, int v0,
                                                 int nh, int split, int rotate_out = 0) {
     const int hq0 = kvh * a.gqa + v0;
@@ -128,14 +131,15 @@ __device__ __forceinline__ void merge_and_store(State &st, MergeLds &s, const De
     __syncthreads();
 
     const int hh = tid >> 5;          // head of this thread in the merge
+    if (hh >= kHeadsPerGroup) return;
     const int l32 = tid & 31;
     const int c0 = 4 * l32;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) M = fmaxf(M, s.m[w][hh]);
+    for (int w = 0; w < W; w++) M = fmaxf(M, s.m[w][hh]);
     float lt = 0.0f, zt = 0.0f, acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) {
+    for (int w = 0; w < W; w++) {
         const float mw = s.m[w][hh];
         const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
         lt += f * s.l[w][hh];
@@ -183,7 +187,7 @@ __device__ __forceinline__ void write_empty(const DecodeArgs &a, int tid, int b,
         return;
     }
     constexpr int kQuads = kPartialFloats / 4;   // 33 float4 per partial
-    for (int i = tid; i < nh * kQuads; i += 256) {
+    for (int i = tid; i < nh * kQuads; i += (int)blockDim.x) {
         const int hh = i / kQuads, qd = i % kQuads;
         const int64_t row = (int64_t)b * a.num_q_heads + hq0 + hh;
         float *mine = a.partials + (row * a.slot_stride + a.slot_offset + split) * kPartialFloats;
