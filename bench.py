@@ -480,6 +480,12 @@ def main():
             raise RuntimeError("kvq call failed in the warm launches")
         warm_ms = hw.elapsed_ms(0, 1) / nl
         hw.close()
+    # output quality of the benchmark step: relative MSE against exact
+    # attention over the unquantised keys and values (sampled sequences)
+    quality_ref = attention_reference(torch, inp, w, q, QUALITY_SEQS)
+    step(0)
+    torch.cuda.synchronize()
+    out_rel_mse = rel_mse(out, quality_ref)
     traffic, traffic_note = recorded_traffic()
     ceiling = walk = None
     if not args.no_read_ceiling:
@@ -501,6 +507,9 @@ def main():
                    "pool_replicas": len(pools),
                    "pages_per_split": pps or kvq.decode_pages_per_split(B, Hq, Hkv, n)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "output_rel_mse": float(f"{out_rel_mse:.4e}"),
+        "output_rel_mse_note": f"sum |out - exact|^2 / sum |exact|^2, sequences {list(QUALITY_SEQS)}, all heads; "
+                               "exact = fp32 attention over the unquantised fp16 keys and values",
         "ms_per_step_median": None if dist is None else dist["median_ms"],
         "ms_per_step_p10": None if dist is None else dist["p10_ms"],
         "ms_per_step_p90": None if dist is None else dist["p90_ms"],
@@ -547,12 +556,13 @@ def main():
         result["mixed_window"] = mixed_window(torch, inp, kvq, lib, dev, stream, args)
 
     if not args.no_presets:
-        legs = (("k4v4_g128", 16), ("k8v2_g128", 16), ("k8v4_g128", 16), ("k3v3_g128", 16),
-                ("k4v2_g128", 32), ("k4v2_g128", 64), ("k4v2_g128", 128))
+        legs = (("k4v4_g128", 16), ("k4v2_g128_pb", 16), ("k8v2_g128", 16), ("k8v4_g128", 16),
+                ("k3v3_g128", 16), ("k4v2_g128", 32), ("k4v2_g128", 64), ("k4v2_g128", 128))
         if args.preset_list:
             legs = [(x.split(":")[0], int(x.split(":")[1]) if ":" in x else 16)
                     for x in args.preset_list.split(",")]
-        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt) for p, pt in legs]
+        result["presets"] = [preset_bench(torch, inp, kvq, lib, dev, stream, args, p, pt,
+                                          ref=quality_ref if pt == 16 else None) for p, pt in legs]
 
     if not args.no_append_bench:
         result.update(append_bench(torch, inp, kvq, call, dev))
@@ -721,16 +731,48 @@ def multi_query_bench(torch, inp, kvq, lib, dev, stream, args, pools, bt, lens, 
     return res
 
 
-def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16):
+def attention_reference(torch, inp, w, q, seqs):
+    """Exact attention of the sampled sequences over their unquantised fp16
+    keys and values (fp32 matmuls; a quality measure, not a timed step):
+    {b: [Hq][128] float32}.  q: fp16 [B][Hq][128] on the device."""
+    ref = {}
+    n = w.context + 1
+    G = w.num_q_heads // w.num_kv_heads
+    for b in seqs:
+        k, v = inp.sequence_kv(w, b, 0, n, device=q.device)
+        kf = k.float().permute(1, 0, 2).contiguous()          # [Hkv][n][128]
+        vf = v.float().permute(1, 0, 2).contiguous()
+        qb = q[b].float().view(w.num_kv_heads, G, 128)
+        p = torch.softmax(torch.matmul(qb, kf.transpose(1, 2).contiguous()) / math.sqrt(128), dim=-1)
+        ref[b] = torch.matmul(p, vf).reshape(w.num_q_heads, 128)
+        del k, v, kf, vf, p
+    return ref
+
+
+def rel_mse(out, ref):
+    """sum |out - ref|^2 / sum |ref|^2 over the sampled sequences."""
+    num = sum(float(((out[b].float() - r) ** 2).sum()) for b, r in ref.items())
+    den = sum(float((r ** 2).sum()) for r in ref.values())
+    return num / den
+
+
+QUALITY_SEQS = (0, 5)
+
+
+def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16, ref=None):
     """The benchmark step (fused append + decode split kernel, then the
     combine) on the same workload with another preset's bit widths or page
     size; the split kernel alone is then timed back to back between two
-    events."""
+    events.  Page-balanced keys take no fused append: every sequence's
+    16385 tokens are written with its pages (whole-page blocks), and the
+    step is the split kernel + combine.  With ref, the output's relative MSE
+    against exact attention on the sampled sequences."""
     import numpy as np
     w = inp.workload("qwen3_32b_16k")
     B, Hq, Hkv = w.num_seqs, w.num_q_heads, w.num_kv_heads
     ctx, n = w.context, w.context + 1
     fmt = kvq.format_from_string(preset, page_tokens=page_tokens)
+    balanced = fmt.key_norm == kvq.KEY_NORM_PAGE
     region = kvq.page_bytes(fmt)
     if page_tokens == 16:
         bt_np, num_pages = inp.page_table(w)
@@ -745,9 +787,10 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
     nk, nv = [], []
     for b in range(B):
         k, v = inp.sequence_kv(w, b, 0, n, device=dev)
-        t = np.arange(ctx)
+        m = n if balanced else ctx
+        t = np.arange(m)
         slots = bt_np[b, t // page_tokens].astype(np.int64) * page_tokens + t % page_tokens
-        kvq.quantize_append(k[:ctx], v[:ctx], torch.from_numpy(slots).to(dev), base, fmt=fmt)
+        kvq.quantize_append(k[:m], v[:m], torch.from_numpy(slots).to(dev), base, fmt=fmt)
         nk.append(k[ctx:])
         nv.append(v[ctx:])
         del k, v
@@ -760,9 +803,14 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
     ws = kvq.alloc_workspace(B, Hq, Hkv, n, fmt=fmt)
     call = DecodeCall(kvq, lib, fmt, stream.cuda_stream)
-    part = [call.fused_args(nk, nv, q, p, bt, lens, n, ws, 0) for p in pools]
+    if balanced:
+        part = [call.partials_args(q, p, bt, lens, n, ws, 0) for p in pools]
+        pf = lib.kvq_decode_partials
+    else:
+        part = [call.fused_args(nk, nv, q, p, bt, lens, n, ws, 0) for p in pools]
+        pf = lib.kvq_append_decode_partials
     comb = call.combine_args(out, lens, Hq, Hkv, n, ws, 0)
-    pf, cfn = lib.kvq_append_decode_partials, lib.kvq_decode_combine
+    cfn = lib.kvq_decode_combine
     steps = max(20, args.steps // 2)
     for i in range(5):
         pf(*part[i % len(part)]); cfn(*comb)
@@ -785,14 +833,24 @@ def preset_bench(torch, inp, kvq, lib, dev, stream, args, preset, page_tokens=16
         raise RuntimeError(f"{preset} decode call failed")
     kern = hev.elapsed_ms(0, 1) / nl
     hev.close()
-    per_token_head = 16 * (fmt.k_bits + fmt.v_bits) + 8
+    quality = None
+    if ref is not None:
+        pf(*part[0])
+        cfn(*comb)
+        torch.cuda.synchronize()
+        quality = rel_mse(out, ref)
+    per_token_head = region // page_tokens       # bytes per (token, KV head)
     kv_bytes = B * n * Hkv * per_token_head
     del pools, base
-    return {"preset": preset, "page_tokens": page_tokens, "bytes_per_token_head": per_token_head,
-            "ms_per_step": round(ms, 5),
-            "step_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "split_kernel_ms": round(kern, 5),
-            "kernel_GBps": round(kv_bytes / (kern * 1e-3) / 1e9, 2),
-            "kernel_pct_hbm_peak": round(100 * kv_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    r = {"preset": preset, "page_tokens": page_tokens, "bytes_per_token_head": per_token_head,
+         "ms_per_step": round(ms, 5),
+         "step_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "split_kernel_ms": round(kern, 5),
+         "kernel_GBps": round(kv_bytes / (kern * 1e-3) / 1e9, 2),
+         "kernel_pct_hbm_peak": round(100 * kv_bytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+         "output_rel_mse": None if quality is None else float(f"{quality:.4e}")}
+    if balanced:
+        r["step"] = "decode split kernel + combine (the new token written with its page; no fused append)"
+    return r
 
 
 def mixed_window(torch, inp, kvq, lib, dev, stream, args, sink=4, recent=124):

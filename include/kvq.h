@@ -80,6 +80,25 @@
  *                     code
  *       key (s, z)    at 1536 + 4*o; value (s, mu) at 1600 + 4*o
  *
+ * Page-balanced keys ("k4v2_g128_pb", also "kvarn_k4v2_g128_pb"; key_norm =
+ * KVQ_KEY_NORM_PAGE): an active reading of the variance normalisation
+ * [KVARN-P stage 2, worded there as repeated; its closing paragraph on
+ * removing fluctuations in log space].  The rotated keys of one page of one
+ * KV head (up to 16 tokens) are balanced as a block: two column passes of
+ * second-moment balancing with a row pass between them, every scale a power
+ * of two, give each channel j an exponent e_j in [-6, 6] (a channel within an
+ * octave of the block's typical RMS keeps e_j = 0, a zero channel takes -6);
+ * each token's scaled row Y_tj 2^-e_j is then encoded by the K4V2 steps
+ * (RMS, asymmetric 4-bit round-to-nearest, fp16 s and z), and the rotated key
+ * is 2^e_j (s c_j + z).  Values are the K4V2 per-token groups.  Region of
+ * 1792 bytes: the K4V2 region (1664 bytes, same offsets) followed by 128
+ * bytes, byte j at 1664 + j the high byte of the fp16 bit pattern of 2^e_j,
+ * i.e. (e_j + 15) * 4; 112 bytes per token per KV head.  Pages of 16 tokens
+ * only.  The block is a whole page, so kvq_quantize_append writes whole pages
+ * (see there), and the fused append-and-decode and multi-row decode calls
+ * return KVQ_ERR_UNSUPPORTED; the recent, partly filled page belongs in an
+ * fp16 window merged by the mixed-cache calls below.
+ *
  * Baseline format "fp16" (k_bits = v_bits = 16): the uncompressed cache the
  * K4V2 format is measured against (the pages compare KVarN with fp16 on
  * accuracy, capacity and throughput [KVARN-HN lede; KVARN-P results]).  The
@@ -135,36 +154,47 @@ typedef enum kvq_status {
     KVQ_ERR_HIP = 6           /* the HIP runtime reported an error             */
 } kvq_status;
 
-/* Format descriptor: {128, 128, k_bits, v_bits, block_size} with k_bits in
- * {4, 8} and v_bits in {2, 4}, or k_bits = v_bits = 3, and block_size in
- * {16, 32, 64, 128} tokens per page ({128, 128, 4, 2, 16} is K4V2 v1), or
- * {128, 128, 16, 16, 16} (the fp16 baseline).  A page of block_size tokens holds, per KV head, block_size / 16
- * consecutive 16-token regions of the layout above: the pool is u8
+/* Format descriptor: {128, 128, k_bits, v_bits, block_size, key_norm} with
+ * k_bits in {4, 8} and v_bits in {2, 4}, or k_bits = v_bits = 3, and
+ * block_size in {16, 32, 64, 128} tokens per page ({128, 128, 4, 2, 16, 0}
+ * is K4V2 v1), or {128, 128, 16, 16, 16, 0} (the fp16 baseline), or
+ * {128, 128, 4, 2, 16, KVQ_KEY_NORM_PAGE} (page-balanced keys).  A page of
+ * block_size tokens holds, per KV head, block_size / 16 consecutive 16-token
+ * regions of the layout above: the pool is u8
  * [num_pages][num_kv_heads][block_size / 16][region], and token r of a page
  * (slot = page * block_size + r) sits in region r / 16, slot r % 16 (the
  * variable page size [KVARN-P] announces, read this way).  Block tables index
- * pages of block_size tokens. */
+ * pages of block_size tokens.  key_norm is KVQ_KEY_NORM_GROUP (0: each
+ * token's key group normalised on its own) unless set; an initialiser that
+ * names only the first five fields leaves it 0. */
+#define KVQ_KEY_NORM_GROUP 0
+#define KVQ_KEY_NORM_PAGE 1
+
 typedef struct kvq_format {
     int32_t head_dim;    /* channels per head                    */
     int32_t group_size;  /* channels per quantisation group      */
     int32_t k_bits;      /* key code width                       */
     int32_t v_bits;      /* value code width                     */
     int32_t block_size;  /* tokens per page                      */
+    int32_t key_norm;    /* KVQ_KEY_NORM_GROUP or KVQ_KEY_NORM_PAGE */
 } kvq_format;
 
 typedef enum kvq_out_dtype { KVQ_OUT_F16 = 0, KVQ_OUT_F32 = 1 } kvq_out_dtype;
 
 /* Parse a preset name ([KVARN-HN] flag value; [KVARN-P] kv_cache_dtype string).
- * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16}); "k4v4_g128",
+ * Accepts "k4v2_g128" and "kvarn_k4v2_g128" ({128, 128, 4, 2, 16, 0}); "k4v4_g128",
  * "k8v2_g128", "k8v4_g128" and "k3v3_g128" (each with or without the "kvarn_"
- * prefix); and the baseline "fp16" ({128, 128, 16, 16, 16}).  Every preset
- * has 16-token pages; set block_size afterwards for larger ones.  preset, out: (host).
+ * prefix); "k4v2_g128_pb" and "kvarn_k4v2_g128_pb" (page-balanced keys,
+ * {128, 128, 4, 2, 16, KVQ_KEY_NORM_PAGE}); and the baseline "fp16"
+ * ({128, 128, 16, 16, 16, 0}).  Every preset has 16-token pages; set
+ * block_size afterwards for larger ones (not with page-balanced keys).
+ * preset, out: (host).
  * Returns KVQ_ERR_NULL, KVQ_ERR_UNSUPPORTED for any other name, else KVQ_OK. */
 kvq_status kvq_format_from_string(const char *preset, kvq_format *out);
 
 /* Bytes of one (page, KV head): block_size / 16 regions of 256 * (k_bits +
- * v_bits) + 128 bytes for a quantised format (1664 for K4V2 v1), 8192 for
- * fp16; 0 for an unsupported format or NULL. */
+ * v_bits) + 128 bytes for a quantised format (1664 for K4V2 v1), 1792 with
+ * page-balanced keys, 8192 for fp16; 0 for an unsupported format or NULL. */
 size_t kvq_page_bytes(const kvq_format *fmt);
 
 /* Bytes of a pool of num_pages pages and num_kv_heads heads; 0 on invalid input. */
@@ -184,6 +214,14 @@ size_t kvq_cache_bytes(const kvq_format *fmt, int64_t num_pages, int32_t num_kv_
  *                     Only the addressed token slots change.
  * The codes depend only on the token's own 128 values (no calibration), so
  * appends are order-independent and idempotent.
+ * Page-balanced keys encode whole pages instead: call tokens 16b .. 16b + 15
+ * form block b, which fills page p = slot_mapping[16b] / 16 from its slot 0;
+ * token 16b + r belongs to it iff 16b + r < num_tokens and
+ * slot_mapping[16b + r] == 16p + r.  A block whose first slot is negative or
+ * not a multiple of 16, or whose page is >= num_pages, is skipped.  The
+ * block's tokens are balanced together (absent rows count as zeros); the
+ * page's slots that no token of the block fills keep their bytes, and its
+ * 128 column-scale bytes are rewritten.  Blocks must name distinct pages.
  * num_tokens == 0 is a no-op returning KVQ_OK.
  */
 kvq_status kvq_quantize_append(const kvq_format *fmt,

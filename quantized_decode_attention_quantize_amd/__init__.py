@@ -23,7 +23,7 @@ __all__ = [
     "decode_combine", "append_decode_attention", "append_decode_partials", "append_decode_attention_noalloc",
     "NOALLOC_SCRATCH_BYTES", "decode_split_slots",
     "decode_partials_slots", "decode_combine_slots", "version",
-    "HEAD_DIM", "PAGE", "REGION_BYTES",
+    "HEAD_DIM", "PAGE", "REGION_BYTES", "KEY_NORM_GROUP", "KEY_NORM_PAGE",
 ]
 
 HEAD_DIM = 128
@@ -51,10 +51,14 @@ class KvqError(RuntimeError):
         super().__init__(msg)
 
 
+KEY_NORM_GROUP = 0      # each token's key group normalised on its own (v1)
+KEY_NORM_PAGE = 1       # page-balanced keys: per-page column scales
+
+
 class Format(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("block_size", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("key_norm", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -188,7 +192,9 @@ def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
 def quantize_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
                     cache: torch.Tensor, stream=None, fmt: Format | None = None) -> None:
     """Quantise fp16 key/value [T][num_kv_heads][128] into the pool at the given
-    slots (int64 [T]; page*16 + offset; negative = skip)."""
+    slots (int64 [T]; page*16 + offset; negative = skip).  With page-balanced
+    keys (fmt.key_norm == KEY_NORM_PAGE) tokens 16b .. 16b + 15 form one
+    whole-page block, written together (see kvq_quantize_append)."""
     if key.dtype != torch.float16 or value.dtype != torch.float16:
         raise TypeError("key/value must be float16")
     if slot_mapping.dtype != torch.int64 or cache.dtype != torch.uint8:

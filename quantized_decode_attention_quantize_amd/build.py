@@ -36,6 +36,7 @@ COMMON = [
 MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 SOURCES = {
     "kvq_append.hip": ["-ffp-contract=off"],
+    "kvq_balance.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": MFMA_VGPR,
     "kvq_fp16.hip": MFMA_VGPR,
     "kvq_api.hip": [],

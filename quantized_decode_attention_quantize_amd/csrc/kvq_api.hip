@@ -28,26 +28,35 @@ int page_log2s(const kvq_format *f) {
     }
 }
 
+// Page-balanced keys: K4V2 with 16-token pages and per-page column scales.
+bool is_pb(const kvq_format *f) {
+    return is_g128(f) && f->key_norm == KVQ_KEY_NORM_PAGE && f->k_bits == 4 && f->v_bits == 2 &&
+           f->block_size == 16;
+}
+
 // A quantised cache: 4- or 8-bit keys with 2- or 4-bit values (4/2 is
-// KVarN's), or 3 bits both; pages of 16 to 128 tokens.
+// KVarN's), or 3 bits both; pages of 16 to 128 tokens; or page-balanced keys.
 bool is_quant(const kvq_format *f) {
-    return is_g128(f) &&
-           (((f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4)) ||
-            (f->k_bits == 3 && f->v_bits == 3)) &&
-           page_log2s(f) >= 0;
+    return (is_g128(f) && f->key_norm == KVQ_KEY_NORM_GROUP &&
+            (((f->k_bits == 4 || f->k_bits == 8) && (f->v_bits == 2 || f->v_bits == 4)) ||
+             (f->k_bits == 3 && f->v_bits == 3)) &&
+            page_log2s(f) >= 0) ||
+           is_pb(f);
 }
 
 // The uncompressed fp16 baseline cache (16-token pages).
 bool is_fp16(const kvq_format *f) {
-    return is_g128(f) && f->k_bits == 16 && f->v_bits == 16 && f->block_size == 16;
+    return is_g128(f) && f->key_norm == KVQ_KEY_NORM_GROUP && f->k_bits == 16 && f->v_bits == 16 &&
+           f->block_size == 16;
 }
 
 bool is_known(const kvq_format *f) { return is_quant(f) || is_fp16(f); }
 
 // Bytes of one (page, KV head): its 16-token regions.
 size_t region_bytes(const kvq_format *f) {
-    return is_quant(f) ? (size_t)(256 * (f->k_bits + f->v_bits) + 128) << page_log2s(f)
-                       : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
+    return is_pb(f) ? (size_t)kvq::kRegionPB
+                    : is_quant(f) ? (size_t)(256 * (f->k_bits + f->v_bits) + 128) << page_log2s(f)
+                                  : is_fp16(f) ? (size_t)kvq::kRegionF16 : 0;
 }
 
 int32_t max_pps(bool fp16) { return fp16 ? kvq::kMaxPagesPerSplitF16 : kvq::kMaxPagesPerSplit; }
@@ -101,7 +110,7 @@ int32_t head_groups(int32_t gqa) { return (int32_t)ceil_div(gqa, kvq::kHeadsPerG
 // carries the same work, and pays its fixed cost (query rotation, wave merge,
 // partial write) once.
 int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
-                      int32_t k_bits = 4, int32_t v_bits = 2) {
+                      int32_t k_bits = 4, int32_t v_bits = 2, bool page_balanced = false) {
     const bool fp16 = k_bits == 16;
     // work-groups per (sequence, KV head): the quantised kernel takes two head
     // groups per work-group when there are several; the fp16 kernel one
@@ -110,7 +119,7 @@ int32_t heuristic_pps(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
     const int64_t units = (int64_t)num_seqs * num_kv_heads * wgs;
     const int64_t max_pages = ceil_div(max_seq_len, kvq::kPage);
     const int64_t resident = fp16 ? kvq::decode_fp16_resident_workgroups()
-                                  : kvq::decode_resident_workgroups(k_bits, v_bits);
+                                  : kvq::decode_resident_workgroups(k_bits, v_bits, page_balanced);
     int64_t splits = resident / units;
     if (splits < 1) splits = 1;
     int64_t pps = ceil_div(max_pages, splits);
@@ -160,7 +169,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     if ((uintptr_t)seq_lens & 3u) return KVQ_ERR_ALIGN;
     const int32_t pps = pages_per_split ? pages_per_split
                                         : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len,
-                                                        fmt->k_bits, fmt->v_bits);
+                                                        fmt->k_bits, fmt->v_bits, is_pb(fmt));
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     if (!workspace || workspace_bytes < w.total) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
@@ -170,6 +179,7 @@ kvq_status decode_common(const kvq_format *fmt, const int32_t *seq_lens, int32_t
     a.rotated = fp16 ? 0 : 1;
     a.k_bits = fmt->k_bits;
     a.v_bits = fmt->v_bits;
+    a.key_norm = is_pb(fmt) ? 1 : 0;
     a.page_log2s = fp16 ? 0 : page_log2s(fmt);
     a.max_seq_len = max_seq_len;
     a.seq_lens = seq_lens;
@@ -205,7 +215,9 @@ kvq_status decode_inputs(const uint16_t *query, const uint8_t *cache, int64_t nu
 
 kvq_status append_inputs(const uint16_t *new_key, const uint16_t *new_value, int64_t key_token_stride,
                          int64_t value_token_stride, kvq::DecodeArgs &a) {
-    if (!a.rotated) return KVQ_ERR_UNSUPPORTED;   // the fused append exists for quantised caches only
+    // the fused append exists for quantised caches with per-token key groups
+    // only (page-balanced keys are encoded a whole page at a time)
+    if (!a.rotated || a.key_norm) return KVQ_ERR_UNSUPPORTED;
     if (!new_key || !new_value) return KVQ_ERR_NULL;
     const int64_t row = (int64_t)a.num_kv_heads * kvq::kHeadDim;
     if (key_token_stride < row || value_token_stride < row) return KVQ_ERR_SHAPE;
@@ -249,12 +261,13 @@ kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
     if (!preset || !out) return KVQ_ERR_NULL;
     static const struct {
         const char *name;
-        int32_t k_bits, v_bits;
+        int32_t k_bits, v_bits, key_norm;
     } presets[] = {
-        {"k4v2_g128", 4, 2}, {"kvarn_k4v2_g128", 4, 2}, {"k4v4_g128", 4, 4}, {"kvarn_k4v4_g128", 4, 4},
-        {"k8v2_g128", 8, 2}, {"kvarn_k8v2_g128", 8, 2}, {"k8v4_g128", 8, 4}, {"kvarn_k8v4_g128", 8, 4},
-        {"k3v3_g128", 3, 3}, {"kvarn_k3v3_g128", 3, 3},
-        {"fp16", 16, 16},
+        {"k4v2_g128", 4, 2, 0}, {"kvarn_k4v2_g128", 4, 2, 0}, {"k4v4_g128", 4, 4, 0}, {"kvarn_k4v4_g128", 4, 4, 0},
+        {"k8v2_g128", 8, 2, 0}, {"kvarn_k8v2_g128", 8, 2, 0}, {"k8v4_g128", 8, 4, 0}, {"kvarn_k8v4_g128", 8, 4, 0},
+        {"k3v3_g128", 3, 3, 0}, {"kvarn_k3v3_g128", 3, 3, 0},
+        {"k4v2_g128_pb", 4, 2, KVQ_KEY_NORM_PAGE}, {"kvarn_k4v2_g128_pb", 4, 2, KVQ_KEY_NORM_PAGE},
+        {"fp16", 16, 16, 0},
     };
     for (const auto &p : presets) {
         if (strcmp(preset, p.name) == 0) {
@@ -263,6 +276,7 @@ kvq_status kvq_format_from_string(const char *preset, kvq_format *out) {
             out->k_bits = p.k_bits;
             out->v_bits = p.v_bits;
             out->block_size = 16;
+            out->key_norm = p.key_norm;
             return KVQ_OK;
         }
     }
@@ -304,6 +318,10 @@ kvq_status kvq_quantize_append(const kvq_format *fmt, const uint16_t *key, const
     a.k_bits = fmt->k_bits;
     a.v_bits = fmt->v_bits;
     a.page_log2s = is_fp16(fmt) ? 0 : page_log2s(fmt);
+    if (is_pb(fmt)) {
+        if (num_kv_heads > 65535) return KVQ_ERR_SHAPE;
+        return hip_status(kvq::launch_balance_append(a, (hipStream_t)stream));
+    }
     return hip_status(is_fp16(fmt) ? kvq::launch_fp16_append(a, (hipStream_t)stream)
                                    : kvq::launch_append(a, (hipStream_t)stream));
 }
@@ -320,7 +338,8 @@ size_t kvq_decode_workspace_bytes(const kvq_format *fmt, int32_t num_seqs, int32
     const bool fp16 = is_fp16(fmt);
     if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits,
+                                                        is_pb(fmt));
     return layout(num_seqs, num_q_heads, max_seq_len, pps).total;
 }
 
@@ -402,7 +421,10 @@ kvq_status kvq_append_decode_attention_noalloc(const kvq_format *fmt, void *out,
                                                int32_t pages_per_split, void *stream) {
     // the partials this call needs must fit the fixed array (checked before
     // the device is touched); sizes the workspace query rejects are rejected
-    // the same way as by kvq_append_decode_attention
+    // the same way as by kvq_append_decode_attention, and so are the formats
+    // without a fused append (the fp16 baseline, page-balanced keys)
+    if (!fmt) return KVQ_ERR_NULL;
+    if (!is_quant(fmt) || is_pb(fmt)) return KVQ_ERR_UNSUPPORTED;
     const size_t need = kvq_decode_workspace_bytes(fmt, num_seqs, num_q_heads, num_kv_heads, max_seq_len,
                                                    pages_per_split);
     if (need > kScratchBytes) return KVQ_ERR_WORKSPACE;
@@ -424,7 +446,8 @@ int32_t kvq_decode_split_slots(const kvq_format *fmt, int32_t num_seqs, int32_t 
     const bool fp16 = is_fp16(fmt);
     if (pages_per_split < 0 || (pages_per_split % 2) || pages_per_split > max_pps(fp16)) return 0;
     const int32_t pps = pages_per_split ? pages_per_split
-                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits);
+                                        : heuristic_pps(num_seqs, num_q_heads, num_kv_heads, max_seq_len, fmt->k_bits, fmt->v_bits,
+                                                        is_pb(fmt));
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, max_seq_len, pps);
     return w.splits > 65535 ? 0 : w.splits;
 }
@@ -515,7 +538,8 @@ kvq_status kvq_decode_attention_mq(const kvq_format *fmt, void *out, kvq_out_dty
     if (q_len < 1 || q_len > 16 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
         (int64_t)num_q_heads * q_len > 65535)
         return KVQ_ERR_SHAPE;
-    if (q_len > 1 && !is_quant(fmt)) return KVQ_ERR_UNSUPPORTED;   // the fp16 baseline decodes one row
+    // the fp16 baseline and page-balanced keys decode one row
+    if (q_len > 1 && (!is_quant(fmt) || is_pb(fmt))) return KVQ_ERR_UNSUPPORTED;
     // (row, head) pairs take the place of query heads: q_len * num_q_heads of them
     kvq::DecodeArgs a;
     kvq_status st = decode_common(fmt, seq_lens, num_seqs, q_len * num_q_heads, num_kv_heads, max_seq_len,

@@ -66,6 +66,7 @@
 
 #include <atomic>
 #include <math.h>
+#include <type_traits>
 
 #include "kvq_decode_common.h"
 #include "kvq_device.h"
@@ -324,7 +325,7 @@ __device__ __forceinline__ v8h value_operand(const PageRegs<KB, VB> &A, const Pa
 // added across the pair before the merge.
 template <int KB, int VB, bool kMasked, bool kFirst>
 __device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, const v4f &dA,
-                                            const v4f &dB, int tokA, int tokB, int lim, const LaneConsts &lc,
+                                            const v4f &dB, int tokA, int tokB, int lim, const LaneConsts &lc, float c2,
                                             int g, State &st) {
     constexpr bool first = kFirst;
     const bool hb = lc.hb;
@@ -341,7 +342,7 @@ __device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const Pag
         const uint32_t km = hb ? kmB[i] : kmA[i];
         const float ks = half_bits_to_float(km & 0xffffu);
         const float kz = half_bits_to_float(km >> 16);
-        lg[i] = __builtin_fmaf(dot * lc.c1, ks, __builtin_fmaf(lc.c2, kz, -mref));
+        lg[i] = __builtin_fmaf(dot * lc.c1, ks, __builtin_fmaf(c2, kz, -mref));
         if (kMasked) {
             valid[i] = (hb ? tokB : tokA) + 4 * g + i < lim;
             lg[i] = valid[i] ? lg[i] : -INFINITY;
@@ -430,15 +431,17 @@ __device__ __forceinline__ void pair_dots(const PageRegs<KB, VB> &A, const PageR
 // weights, then the P.V MFMAs (8 per group); the value operands are unpacked
 // once and feed every group.  Each group keeps its own softmax state.
 // lim[h]: group h's token limit (kMasked).
+// c2[h]: the coefficient of the key offset z in group h's scores for this
+// lane's page (the query sum times the score scale).
 template <int KB, int VB, int kG, bool kMasked, bool kFirst>
 __device__ __forceinline__ void pair_finish(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B,
                                             const v4f (&dA)[kG], const v4f (&dB)[kG], int tokA, int tokB,
-                                            const int (&lim)[kG], const LaneConsts (&lc)[kG], int g,
-                                            State (&st)[kG]) {
+                                            const int (&lim)[kG], const LaneConsts (&lc)[kG], const float (&c2)[kG],
+                                            int g, State (&st)[kG]) {
     v8h bw[kG];
 #pragma unroll
     for (int h = 0; h < kG; h++)
-        bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], g, st[h]);
+        bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], c2[h], g, st[h]);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         const v8h av = value_operand<KB, VB>(A, B, j);
@@ -457,14 +460,144 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
                                              const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
     v4f dA[kG], dB[kG];
     pair_dots<KB, VB, kG>(A, B, bq, dA, dB);
-    pair_finish<KB, VB, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, g, st);
+    float c2[kG];
+#pragma unroll
+    for (int h = 0; h < kG; h++) c2[h] = lc[h].c2;
+    pair_finish<KB, VB, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, g, st);
+}
+
+// ---- page-balanced keys ----
+// A page's key channel j carries the column scale 2^e_j, stored as the high
+// byte of its fp16 bit pattern at 1664 + j.  The scale is folded into the
+// query per page: the score of token t is c1 (s_t D + z_t W) with
+// D = sum_j (q'_j 2^e_j) c_tj and W = sum_j q'_j 2^e_j, both in the MFMA's
+// units (the query operand, scaled by the page's 2^e_j, against the codes
+// and against an operand of unit codes).
+
+// The 32 scale bytes of lane group g (channels 32g .. 32g + 31), as loaded.
+struct PageScales {
+    uint32_t w[8];
+};
+struct NoScales {};
+
+__device__ __forceinline__ void load_scales(const uint8_t *region, int g, PageScales &s, bool live) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(region), (short)0, live ? kRegionPB : 0, 0x00020000);
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rs, kScalesPB + 32 * g, 0, 0);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rs, kScalesPB + 32 * g + 16, 0, 0);
+    s.w[0] = lo.x; s.w[1] = lo.y; s.w[2] = lo.z; s.w[3] = lo.w;
+    s.w[4] = hi.x; s.w[5] = hi.y; s.w[6] = hi.z; s.w[7] = hi.w;
+}
+
+// fp16 multipliers 2^e in the key operand's slot order: slot pair k of
+// block d (k = 0..3) holds channels 8d + k and 8d + 4 + k (see key_codes),
+// i.e. byte k of dword 2d and of dword 2d + 1 of the scale bytes, each moved
+// to the high byte of its half by one byte permute.
+__device__ __forceinline__ void scale_multipliers(const PageScales &s, v8h (&m)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        const uint32_t lo = s.w[2 * d], hi = s.w[2 * d + 1];
+        const uint4 u = {__builtin_amdgcn_perm(hi, lo, 0x040c000cu), __builtin_amdgcn_perm(hi, lo, 0x050c010cu),
+                         __builtin_amdgcn_perm(hi, lo, 0x060c020cu), __builtin_amdgcn_perm(hi, lo, 0x070c030cu)};
+        m[d] = __builtin_bit_cast(v8h, u);
+    }
+}
+
+// Key-code A operand of one 8-channel dword w for page-balanced keys: the
+// slot order of key_codes, but every code at mantissa bits 6-9 (the fp16
+// subnormal c * 2^-18), one shift and one AND per pair of channels.  The
+// page's column scales can shrink query elements by up to 2^-6; with the
+// codes 2^6 higher than key_codes' low slots the MFMA's products keep the
+// magnitudes of the per-token format (measured: with codes at bits 0-3 and
+// 4-7 and the query 2^6 lower, the decode's error against the fp64
+// definition was up to ~40x that format's on the same keys; the MFMA keeps
+// fewer bits of very small products).
+__device__ __forceinline__ v8h key_codes_pb(uint32_t w) {
+    constexpr uint32_t kBits69 = 0x03C003C0u;
+    const uint4 u = {(w << 6) & kBits69, (w << 2) & kBits69, (w >> 2) & kBits69, (w >> 6) & kBits69};
+    return __builtin_bit_cast(v8h, u);
+}
+
+__device__ __forceinline__ v4f page_dots_pb(const PageRegs<4, 2> &r, const v8h (&bq)[4]) {
+    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; q++) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes_pb(r.k[q]), bq[q], d, 0, 0, 0);
+    return d;
+}
+
+// Sum over the 32 channels of each k-step of the query operand q (unit codes
+// in key_codes_pb's scaling, 2^-18 in every slot): every row of the result
+// holds W of column n.
+__device__ __forceinline__ float page_query_sum(const v8h (&q)[4]) {
+    const v8h ones = __builtin_bit_cast(v8h, make_uint4(0x00400040u, 0x00400040u, 0x00400040u, 0x00400040u));
+    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; k++) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, q[k], d, 0, 0, 0);
+    return d[0] + row_swap8(d[0]);            // the query's two fp16 terms
+}
+
+// One page pair with page-balanced keys (K4V2): the query operand of each
+// group is scaled per page, and the z coefficient is the scaled query's sum.
+template <int kG, bool kMasked, bool kFirst>
+__device__ __forceinline__ void process_pair_pb(const PageRegs<4, 2> &A, const PageRegs<4, 2> &B,
+                                                const PageScales &SA, const PageScales &SB, int tokA, int tokB,
+                                                const int (&lim)[kG], const v8h (&bq)[kG][4],
+                                                const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
+    v4f dA[kG], dB[kG];
+    float wa[kG], wb[kG], c2[kG];
+    // one page at a time, so that one page's multipliers are live at once
+    {
+        v8h m[4];
+        scale_multipliers(SA, m);
+#pragma unroll
+        for (int h = 0; h < kG; h++) {
+            v8h qs[4];
+#pragma unroll
+            for (int d = 0; d < 4; d++) qs[d] = bq[h][d] * m[d];
+            dA[h] = page_dots_pb(A, qs);
+            wa[h] = page_query_sum(qs);
+        }
+    }
+    {
+        v8h m[4];
+        scale_multipliers(SB, m);
+#pragma unroll
+        for (int h = 0; h < kG; h++) {
+            v8h qs[4];
+#pragma unroll
+            for (int d = 0; d < 4; d++) qs[d] = bq[h][d] * m[d];
+            dB[h] = page_dots_pb(B, qs);
+            wb[h] = page_query_sum(qs);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < kG; h++) c2[h] = lc[h].c1 * (lc[h].hb ? wb[h] : wa[h]);
+    pair_finish<4, 2, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, g, st);
+}
+
+// One page pair of either key normalisation (Scales: PageScales with
+// page-balanced keys, else NoScales, unused).
+template <int KB, int VB, int kG, bool kMasked, bool kFirst, bool kPB, typename Scales>
+__device__ __forceinline__ void run_pair(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, const Scales &SA,
+                                         const Scales &SB, int tokA, int tokB, const int (&lim)[kG],
+                                         const v8h (&bq)[kG][4], const LaneConsts (&lc)[kG], int g,
+                                         State (&st)[kG]) {
+    if constexpr (kPB)
+        process_pair_pb<kG, kMasked, kFirst>(A, B, SA, SB, tokA, tokB, lim, bq, lc, g, st);
+    else
+        process_pair<KB, VB, kG, kMasked, kFirst>(A, B, tokA, tokB, lim, bq, lc, g, st);
 }
 
 // kG: head groups (of 8 query heads, or (row, head) pairs) per work-group;
 // 2 when a KV head has more than 8, so that they share the page unpack.
-template <int KB, int VB, bool kMQ, bool kPaged, int kG>
+// kPB: page-balanced keys (K4V2, one query row, 16-token pages; 1792-byte
+// regions whose column scales are folded into the query per page).
+template <int KB, int VB, bool kMQ, bool kPaged, int kG, bool kPB = false>
 __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs a) {
+    static_assert(!kPB || (KB == 4 && VB == 2 && !kMQ && !kPaged), "page-balanced keys: K4V2, one row, 16-token pages");
     using Lay = Layout<KB, VB>;
+    using Scales = typename std::conditional<kPB, PageScales, NoScales>::type;
+    constexpr int kRegion = kPB ? kRegionPB : Lay::kBytes;   // bytes of one (16-token page, KV head)
     const int sgroups = (a.head_groups + kG - 1) / kG;   // work-groups per (split, KV head, sequence)
     int split, kvh, sg, b;
     if (!kMQ) {
@@ -556,8 +689,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     // ---- page-pair loop ----
     const int npairs = (p_end - p_begin + 1) >> 1;
     const int log2s = kPaged ? a.page_log2s : 0;
-    const int64_t head_off = ((int64_t)kvh * Lay::kBytes) << log2s;
-    const int64_t page_stride = ((int64_t)a.num_kv_heads * Lay::kBytes) << log2s;
+    const int64_t head_off = ((int64_t)kvh * kRegion) << log2s;
+    const int64_t page_stride = ((int64_t)a.num_kv_heads * kRegion) << log2s;
     const int sub_mask = (1 << log2s) - 1;
 
     // A page id outside the pool is read as page 0: never an out-of-bounds
@@ -590,12 +723,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     // that every wait count in the loop is the same on every path) but read
     // nothing: measured, 0.2 us per launch at 16K against re-reading the
     // last pair, and ~14 MB less cache traffic per launch.
-    auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, int i) {
+    auto issue = [&](PageRegs<KB, VB> &A, PageRegs<KB, VB> &B, Scales &SA, Scales &SB, int i) {
         const int j = i < nk ? i : nk - 1;      // the wave's j-th pair: lane j of bt_a / bt_b
         const int pa = kPaged ? p_begin + 2 * (wave + kDecodeWaves * j) : 0;
         const bool live = i < nk;
-        load_page(region_of(__builtin_amdgcn_readlane(bt_a, j), pa), lo, A, live);
-        load_page(region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1), lo, B, live);
+        const uint8_t *ra = region_of(__builtin_amdgcn_readlane(bt_a, j), pa);
+        const uint8_t *rb = region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1);
+        load_page(ra, lo, A, live);
+        load_page(rb, lo, B, live);
+        if constexpr (kPB) {
+            load_scales(ra, lane >> 4, SA, live);
+            load_scales(rb, lane >> 4, SB, live);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
     // Fused append: a work-group whose split holds the sequence's last token
@@ -603,7 +742,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     // the cache before any of its waves reads the page.  With more than one
     // head group per KV head, every such work-group stores the same bytes; each
     // reads the page only after its own stores have completed.
-    if (a.append) {
+    if (!kPB && a.append) {             // (no fused append with page-balanced keys)
         const int pos = n_tokens - 1;
         const int pnew = pos / kPage;
         if (pnew >= p_begin && pnew < p_end) {
@@ -636,10 +775,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     // flight) inside the pair loop.
     asm volatile("" ::"v"(bt_a), "v"(bt_b));
     PageRegs<KB, VB> r0A, r0B, r1A, r1B, r2A, r2B;
+    Scales s0A, s0B, s1A, s1B, s2A, s2B;
     if (nk > 0) {
-        issue(r0A, r0B, 0);
-        issue(r1A, r1B, 1);
-        issue(r2A, r2B, 2);
+        issue(r0A, r0B, s0A, s0B, 0);
+        issue(r1A, r1B, s1A, s1B, 1);
+        issue(r2A, r2B, s2A, s2B, 2);
     }
 
     // ---- query prologue: wave w rotates and splits heads 2w and 2w+1 of each group ----
@@ -681,7 +821,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
         }
         int ex = 0;
         if (am > 0.0f) (void)frexpf(am, &ex);          // am in [2^(ex-1), 2^ex)
-        const int shift = 14 - ex;                       // q' * 2^shift: max in [2^13, 2^14)
+        // q' * 2^shift: max in [2^13, 2^14); with page-balanced keys in
+        // [2^7, 2^8), so that a page's column scales (up to 2^6) keep the
+        // scaled query inside fp16
+        const int shift = (kPB ? 8 : 14) - ex;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int ch = c0 + e;
@@ -693,7 +836,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
             int slot, down = 0;
             if (KB == 4) {
                 slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
-                down = 4 * ((slot >> 1) & 1);
+                down = kPB ? 0 : 4 * ((slot >> 1) & 1);   // page-balanced keys: every code at 2^-18
             } else if (KB == 3) {
                 const int x = ch & 31, r16 = x & 15;   // channel 32g + x; x = 16 hi + r16
                 slot = (ch & ~31) + 8 * (2 * (r16 >> 3) + ((r16 >> 2) & 1)) + 2 * (r16 & 3) + (x >> 4);
@@ -708,7 +851,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
         }
         if (l32 == 0) {
             // dot(q', c) = D * 2^(24 - shift), D the MFMA sum with codes c * 2^-24
-            s_c1[hq][hh] = a.alpha * __builtin_ldexpf(1.0f, 24 - shift);
+            // (c * 2^-18 with page-balanced keys)
+            s_c1[hq][hh] = a.alpha * __builtin_ldexpf(1.0f, (kPB ? 18 : 24) - shift);
             s_c2[hq][hh] = a.alpha * qs;
         }
     }
@@ -743,16 +887,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
         // page-walk probe alone slows the same way with depth), and so did a
         // four-buffer variant that issued each pair's score MFMAs one pair
         // ahead of its softmax.
-        process_pair<KB, VB, kG, false, true>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
+        run_pair<KB, VB, kG, false, true, kPB>(r0A, r0B, s0A, s0B, 0, 0, lim0, bq, lc, g, st);
         for (int i = 1; i < nk; i += 3) {
-            issue(r0A, r0B, i + 2);
-            process_pair<KB, VB, kG, false, false>(r1A, r1B, 0, 0, lim0, bq, lc, g, st);
+            issue(r0A, r0B, s0A, s0B, i + 2);
+            run_pair<KB, VB, kG, false, false, kPB>(r1A, r1B, s1A, s1B, 0, 0, lim0, bq, lc, g, st);
             if (i + 1 >= nk) break;
-            issue(r1A, r1B, i + 3);
-            process_pair<KB, VB, kG, false, false>(r2A, r2B, 0, 0, lim0, bq, lc, g, st);
+            issue(r1A, r1B, s1A, s1B, i + 3);
+            run_pair<KB, VB, kG, false, false, kPB>(r2A, r2B, s2A, s2B, 0, 0, lim0, bq, lc, g, st);
             if (i + 2 >= nk) break;
-            issue(r2A, r2B, i + 4);
-            process_pair<KB, VB, kG, false, false>(r0A, r0B, 0, 0, lim0, bq, lc, g, st);
+            issue(r2A, r2B, s2A, s2B, i + 4);
+            run_pair<KB, VB, kG, false, false, kPB>(r0A, r0B, s0A, s0B, 0, 0, lim0, bq, lc, g, st);
         }
     }
     // Masked pairs: the last pair, and with several query rows possibly the
@@ -769,17 +913,24 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
             }
         }
         PageRegs<KB, VB> tA, tB;
+        Scales tsA, tsB;
         const int pa = p_begin + 2 * i;
         const bool has_b = pa + 1 < p_end;
         const int j = i / kDecodeWaves;         // the pair's lane in bt_a / bt_b
         const int32_t id_a = __builtin_amdgcn_readlane(bt_a, j);
-        load_page(region_of(id_a, pa), lo, tA);
-        load_page(has_b ? region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1) : region_of(id_a, pa), lo, tB);
+        const uint8_t *ra = region_of(id_a, pa);
+        const uint8_t *rb = has_b ? region_of(__builtin_amdgcn_readlane(bt_b, j), pa + 1) : ra;
+        load_page(ra, lo, tA);
+        load_page(rb, lo, tB);
+        if constexpr (kPB) {
+            load_scales(ra, g, tsA, true);
+            load_scales(rb, g, tsB, true);
+        }
         const int tok_b = has_b ? (pa + 1) * kPage : n_tokens;
         if (nk == 0)
-            process_pair<KB, VB, kG, true, true>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
+            run_pair<KB, VB, kG, true, true, kPB>(tA, tB, tsA, tsB, pa * kPage, tok_b, lim, bq, lc, g, st);
         else
-            process_pair<KB, VB, kG, true, false>(tA, tB, pa * kPage, tok_b, lim, bq, lc, g, st);
+            run_pair<KB, VB, kG, true, false, kPB>(tA, tB, tsA, tsB, pa * kPage, tok_b, lim, bq, lc, g, st);
     };
     if (nfull < npairs && wave == (npairs - 1) % kDecodeWaves) masked_pair(npairs - 1);
     if (kMQ && nfull + 1 < npairs && wave == (npairs - 2) % kDecodeWaves) masked_pair(npairs - 2);
@@ -947,7 +1098,7 @@ __global__ __launch_bounds__(256) void combine_wide_kernel(DecodeArgs a) {
 
 // Work-groups of decode_kernel<KB, VB> the current device holds at once
 // (compute units x occupancy), queried once per device; 512 without a device.
-template <int KB, int VB>
+template <int KB, int VB, bool kPB = false>
 int resident_workgroups() {
     // one entry per device; several host threads may fill an entry at once,
     // and they all store the same value
@@ -961,7 +1112,7 @@ int resident_workgroups() {
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1>, 64 * kDecodeWaves, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<KB, VB, false, false, 1, kPB>, 64 * kDecodeWaves, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         return 512;
@@ -975,7 +1126,7 @@ int resident_workgroups() {
     return cus * per_cu;
 }
 
-template <int KB, int VB, bool kMQ, bool kPaged, int kG>
+template <int KB, int VB, bool kMQ, bool kPaged, int kG, bool kPB = false>
 hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
     const int sgroups = (a.head_groups + kG - 1) / kG;
     dim3 grid((unsigned)a.splits, (unsigned)(a.num_kv_heads * sgroups), (unsigned)a.num_seqs);
@@ -987,10 +1138,10 @@ hipError_t launch_split_kernel(const DecodeArgs &a, hipStream_t stream, const La
         grid = dim3((unsigned)blocks, 1, 1);
     }
     if (ev.start || ev.stop)
-        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start,
+        hipExtLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG, kPB>), grid, dim3(64 * kDecodeWaves), 0, stream, ev.start,
                               ev.stop, 0, a);
     else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(decode_kernel<KB, VB, kMQ, kPaged, kG, kPB>), grid, dim3(64 * kDecodeWaves), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1014,7 +1165,8 @@ hipError_t launch_split_fmt(const DecodeArgs &a, hipStream_t stream, const Launc
 
 }  // namespace
 
-int decode_resident_workgroups(int k_bits, int v_bits) {
+int decode_resident_workgroups(int k_bits, int v_bits, bool page_balanced) {
+    if (page_balanced) return k_bits == 4 && v_bits == 2 ? resident_workgroups<4, 2, true>() : 512;
     if (k_bits == 4 && v_bits == 2) return resident_workgroups<4, 2>();
     if (k_bits == 4 && v_bits == 4) return resident_workgroups<4, 4>();
     if (k_bits == 8 && v_bits == 2) return resident_workgroups<8, 2>();
@@ -1024,6 +1176,12 @@ int decode_resident_workgroups(int k_bits, int v_bits) {
 }
 
 hipError_t launch_decode_split(const DecodeArgs &a, hipStream_t stream, const LaunchEvents &ev) {
+    if (a.key_norm) {          // page-balanced keys: K4V2, one query row, 16-token pages
+        if (a.k_bits != 4 || a.v_bits != 2 || a.q_len > 1 || a.page_log2s != 0 || a.append)
+            return hipErrorInvalidValue;
+        return a.head_groups >= 2 ? launch_split_kernel<4, 2, false, false, 2, true>(a, stream, ev)
+                                  : launch_split_kernel<4, 2, false, false, 1, true>(a, stream, ev);
+    }
     if (a.k_bits == 4 && a.v_bits == 2) return launch_split_fmt<4, 2>(a, stream, ev);
     if (a.k_bits == 4 && a.v_bits == 4) return launch_split_fmt<4, 4>(a, stream, ev);
     if (a.k_bits == 8 && a.v_bits == 2) return launch_split_fmt<8, 2>(a, stream, ev);

@@ -35,6 +35,11 @@ static_assert(Layout<4, 2>::kVCodes == 1024 && Layout<4, 2>::kKMeta == 1536 && L
                   Layout<4, 2>::kBytes == 1664,
               "the K4V2 region");
 
+// Page-balanced keys: the K4V2 region followed by 128 column-scale bytes
+// (byte j = the high byte of fp16 2^e_j), 1792 bytes per (page, KV head).
+constexpr int kScalesPB = 1664;
+constexpr int kRegionPB = 1792;
+
 // Decode work decomposition.
 constexpr int kWaves = 4;           // waves per work-group
 constexpr int kHeadsPerGroup = 8;   // query heads per MFMA column block (hi + lo = 16 columns)
@@ -111,6 +116,8 @@ struct AppendArgs {
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+// Page-balanced keys (K4V2, 16-token pages): whole-page blocks of 16 call tokens.
+hipError_t launch_balance_append(const AppendArgs &a, hipStream_t stream);
 
 struct DecodeArgs {
     void *out;
@@ -140,6 +147,7 @@ struct DecodeArgs {
     int32_t page_log2s;       // block-table pages of 16 << page_log2s tokens, each a run of
                               // 2^page_log2s 16-token regions per KV head (0: 16-token pages)
     int32_t rotated;          // 1: quantised (Hadamard epilogue); 0: fp16 baseline
+    int32_t key_norm;         // 1: page-balanced keys (K4V2, 16-token pages, 1792-byte regions)
     int32_t slot_offset;      // partial of split s goes to slot slot_offset + s ...
     int32_t slot_stride;      // ... of rows holding slot_stride slots each
     int32_t rotate_partials;  // fp16: store partials in the Hadamard domain
@@ -171,7 +179,7 @@ hipError_t launch_decode_combine(const DecodeArgs &a, hipStream_t stream);
 
 // Work-groups of the decode kernel for these bit widths that the current
 // device runs at once.
-int decode_resident_workgroups(int k_bits, int v_bits);
+int decode_resident_workgroups(int k_bits, int v_bits, bool page_balanced = false);
 
 // fp16 baseline cache: append, decode split kernel (the combine is shared,
 // with a.rotated = 0), resident work-groups of its split kernel.

@@ -38,25 +38,19 @@ __device__ __forceinline__ float materialize(float x) {
     return x;
 }
 
-// Encode the 128 fp16 values at `src` (16-byte aligned) with the 16 lanes of
-// one row (r = lane within the row; all 16 lanes must be active and share the
-// arguments) and store codes and metadata of token slot `off` (0..15) in the
-// (page, KV head) region `region` of the KB-bit key / VB-bit value layout.
-template <int KB, int VB>
-__device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, int r, uint8_t *region,
-                                                 int off) {
+// Step 1, the Hadamard rotation, of the group whose channels 8r..8r+7 are
+// the four words of `raw` (fp16 pairs, low half first), on the 16 lanes of
+// one row (r = lane within the row; all 16 must be active): y[e] receives
+// rotated channel 8r + e in fp32.
+__device__ __forceinline__ void rotate_row(const uint4 raw, int r, float (&y)[8]) {
 #pragma clang fp contract(off)
-    using Lay = Layout<KB, VB>;
-    const uint4 raw = *reinterpret_cast<const uint4 *>(src + 8 * r);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float y[8];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
         y[2 * e] = half_bits_to_float(w[e] & 0xffffu);
         y[2 * e + 1] = half_bits_to_float(w[e] >> 16);
     }
-
-    // 1. Hadamard rotation: in-lane stages h = 1, 2, 4 ...
+    // in-lane stages h = 1, 2, 4 ...
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -78,8 +72,12 @@ __device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, 
             y[e] = upper ? (other - y[e]) : (y[e] + other);
         }
     }
+}
 
-    // 2. Variance normalisation: RMS over the group, fixed pairwise tree.
+// Sum of squares of the row's 128 values (y[e] = channel 8r + e, 16 lanes)
+// by the format's fixed pairwise tree; every lane of the row gets the sum.
+__device__ __forceinline__ float row_sum_squares(const float (&y)[8]) {
+#pragma clang fp contract(off)
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) p[e] = y[e] * y[e];
@@ -90,7 +88,19 @@ __device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, 
     }
     p[0] = p[0] + p[4]; p[1] = p[1] + p[5]; p[2] = p[2] + p[6]; p[3] = p[3] + p[7];
     p[0] = p[0] + p[2]; p[1] = p[1] + p[3];
-    const float ss = p[0] + p[1];
+    return p[0] + p[1];
+}
+
+// Steps 2-4 of the group held rotated in y (channel 8r + e in y[e], 16 lanes
+// of one row, all active, sharing the arguments), and the store of its codes
+// and metadata in token slot `off` (0..15) of the (page, KV head) region
+// `region` of the KB-bit key / VB-bit value layout.
+template <int KB, int VB>
+__device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int r, uint8_t *region, int off) {
+#pragma clang fp contract(off)
+    using Lay = Layout<KB, VB>;
+    // 2. Variance normalisation: RMS over the group, fixed pairwise tree.
+    const float ss = row_sum_squares(y);
 
     const int L = is_v ? Lay::kVL : Lay::kKL;
     uint32_t code[8];
@@ -274,6 +284,18 @@ __device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, 
         if (r == 0)
             *reinterpret_cast<uint32_t *>(region + Lay::kVMeta + 4 * off) = s16 | (z16 << 16);
     }
+}
+
+// Encode the 128 fp16 values at `src` (16-byte aligned) with the 16 lanes of
+// one row (r = lane within the row; all 16 lanes must be active and share the
+// arguments) and store codes and metadata of token slot `off` (0..15) in the
+// (page, KV head) region `region` of the KB-bit key / VB-bit value layout.
+template <int KB, int VB>
+__device__ __forceinline__ void encode_group_fmt(const uint16_t *src, int is_v, int r, uint8_t *region,
+                                                 int off) {
+    float y[8];
+    rotate_row(*reinterpret_cast<const uint4 *>(src + 8 * r), r, y);
+    encode_rotated_fmt<KB, VB>(y, is_v, r, region, off);
 }
 
 // The K4V2 layout.

@@ -443,3 +443,39 @@ def test_noalloc_step_rejects_partials_beyond_its_array_without_a_device():
     header = open(HEADER).read()
     m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", header)
     assert m and int(m.group(1)) << int(m.group(2)) == kvq.NOALLOC_SCRATCH_BYTES
+
+
+def test_page_balanced_format_and_unsupported_calls_launch_nothing():
+    """The page-balanced preset: 1792-byte regions, 16-token pages only, and
+    the calls it lacks (fused append-and-decode, several query rows) refused
+    before anything is launched."""
+    lib = kvq.load()
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    g = P(0x10000)
+    for name in ("k4v2_g128_pb", "kvarn_k4v2_g128_pb"):
+        f = kvq.format_from_string(name)
+        assert (f.k_bits, f.v_bits, f.block_size, f.key_norm) == (4, 2, 16, kvq.KEY_NORM_PAGE)
+        assert kvq.page_bytes(f) == 1792 and kvq.cache_bytes(10, 8, f) == 10 * 8 * 1792
+    with pytest.raises(kvq.KvqError):
+        kvq.format_from_string("k4v2_g128_pb", page_tokens=64)
+    f = kvq.format_from_string("k4v2_g128")
+    assert f.key_norm == kvq.KEY_NORM_GROUP
+    bad = kvq.Format(128, 128, 8, 4, 16, kvq.KEY_NORM_PAGE)      # page-balanced keys are K4V2 only
+    assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
+    bad = kvq.Format(128, 128, 4, 2, 16, 2)
+    assert lib.kvq_page_bytes(ctypes.byref(bad)) == 0
+    pb = ctypes.byref(kvq.format_from_string("k4v2_g128_pb"))
+    ws = lib.kvq_decode_workspace_bytes(pb, 2, 8, 2, 100, 0)
+    assert ws > 0
+    st = lib.kvq_append_decode_attention(pb, g, 1, g, g, i64(256), i64(256), g, g, i64(10), g, i32(7), g, i32(2),
+                                         i32(8), i32(2), i32(100), ctypes.c_float(0.088), g, ctypes.c_size_t(ws),
+                                         i32(0), None)
+    assert st == 3
+    st = lib.kvq_append_decode_attention_noalloc(pb, g, 1, g, g, i64(256), i64(256), g, g, i64(10), g, i32(7), g,
+                                                 i32(2), i32(8), i32(2), i32(100), ctypes.c_float(0.088), i32(0),
+                                                 None)
+    assert st == 3
+    wsm = lib.kvq_decode_workspace_bytes_mq(pb, 2, 4, 8, 2, 100, 0)
+    st = lib.kvq_decode_attention_mq(pb, g, 1, g, i32(4), g, i64(10), g, i32(7), g, i32(2), i32(8), i32(2),
+                                     i32(100), ctypes.c_float(0.088), g, ctypes.c_size_t(wsm), i32(0), None)
+    assert st == 3
