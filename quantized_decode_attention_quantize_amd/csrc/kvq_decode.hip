@@ -326,7 +326,7 @@ __device__ __forceinline__ v8h value_operand(const PageRegs<KB, VB> &A, const Pa
 template <int KB, int VB, bool kMasked, bool kFirst>
 __device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B, const v4f &dA,
                                             const v4f &dB, int tokA, int tokB, int lim, const LaneConsts &lc, float c2,
-                                            int g, State &st) {
+                                            float woff, int g, State &st) {
     constexpr bool first = kFirst;
     const bool hb = lc.hb;
     const float mref = first ? 0.0f : st.m + kLazyThreshold;
@@ -338,7 +338,7 @@ __device__ __forceinline__ v8h pair_weights(const PageRegs<KB, VB> &A, const Pag
     for (int i = 0; i < 4; i++) {
         const float sA = dA[i] + row_swap8(dA[i]);     // q_hi . c + q_lo . c
         const float sB = dB[i] + row_swap8(dB[i]);
-        const float dot = hb ? sB : sA;
+        const float dot = (hb ? sB : sA) - woff;
         const uint32_t km = hb ? kmB[i] : kmA[i];
         const float ks = half_bits_to_float(km & 0xffffu);
         const float kz = half_bits_to_float(km >> 16);
@@ -432,16 +432,18 @@ __device__ __forceinline__ void pair_dots(const PageRegs<KB, VB> &A, const PageR
 // once and feed every group.  Each group keeps its own softmax state.
 // lim[h]: group h's token limit (kMasked).
 // c2[h]: the coefficient of the key offset z in group h's scores for this
-// lane's page (the query sum times the score scale).
+// lane's page (the query sum times the score scale); woff[h]: subtracted
+// from the lane's dot products first (0 but for page-balanced keys).
 template <int KB, int VB, int kG, bool kMasked, bool kFirst>
 __device__ __forceinline__ void pair_finish(const PageRegs<KB, VB> &A, const PageRegs<KB, VB> &B,
                                             const v4f (&dA)[kG], const v4f (&dB)[kG], int tokA, int tokB,
                                             const int (&lim)[kG], const LaneConsts (&lc)[kG], const float (&c2)[kG],
-                                            int g, State (&st)[kG]) {
+                                            const float (&woff)[kG], int g, State (&st)[kG]) {
     v8h bw[kG];
 #pragma unroll
     for (int h = 0; h < kG; h++)
-        bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], c2[h], g, st[h]);
+        bw[h] = pair_weights<KB, VB, kMasked, kFirst>(A, B, dA[h], dB[h], tokA, tokB, lim[h], lc[h], c2[h], woff[h],
+                                                      g, st[h]);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         const v8h av = value_operand<KB, VB>(A, B, j);
@@ -460,19 +462,29 @@ __device__ __forceinline__ void process_pair(const PageRegs<KB, VB> &A, const Pa
                                              const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
     v4f dA[kG], dB[kG];
     pair_dots<KB, VB, kG>(A, B, bq, dA, dB);
-    float c2[kG];
+    float c2[kG], woff[kG];
 #pragma unroll
-    for (int h = 0; h < kG; h++) c2[h] = lc[h].c2;
-    pair_finish<KB, VB, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, g, st);
+    for (int h = 0; h < kG; h++) {
+        c2[h] = lc[h].c2;
+        woff[h] = 0.0f;
+    }
+    pair_finish<KB, VB, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, woff, g, st);
 }
 
 // ---- page-balanced keys ----
 // A page's key channel j carries the column scale 2^e_j, stored as the high
-// byte of its fp16 bit pattern at 1664 + j.  The scale is folded into the
-// query per page: the score of token t is c1 (s_t D + z_t W) with
-// D = sum_j (q'_j 2^e_j) c_tj and W = sum_j q'_j 2^e_j, both in the MFMA's
-// units (the query operand, scaled by the page's 2^e_j, against the codes
-// and against an operand of unit codes).
+// byte of its fp16 bit pattern at 1664 + j.  The key operand carries it: the
+// A element of (token t, channel j) is the fp16 number 2^e_j (1 + c_tj / 16),
+// its bits the scale's bits OR the code at mantissa bits 6-9 (one shift and
+// one AND-OR per pair of channels, as many instructions as key_codes).  With
+// D'_t = sum_j a_tj q''_j and W = sum_j 2^e_j q''_j (the same MFMA against the
+// scales alone), sum_j q''_j 2^e_j c_tj = 16 (D'_t - W): the score of token t
+// is c1 (s_t (D'_t - W) + z_t W / 16), c1 = alpha 2^(4 - shift).  The products
+// are normal fp16 products, so the MFMA keeps the precision of the per-token
+// format (an earlier form that scaled the query by 2^e_j per page and kept the
+// codes as subnormals lost up to 40x more against the fp64 definition: the
+// MFMA keeps fewer bits of very small products), and the query needs no
+// per-page scaling.
 
 // The 32 scale bytes of lane group g (channels 32g .. 32g + 31), as loaded.
 struct PageScales {
@@ -489,90 +501,57 @@ __device__ __forceinline__ void load_scales(const uint8_t *region, int g, PageSc
     s.w[4] = hi.x; s.w[5] = hi.y; s.w[6] = hi.z; s.w[7] = hi.w;
 }
 
-// fp16 multipliers 2^e in the key operand's slot order: slot pair k of
-// block d (k = 0..3) holds channels 8d + k and 8d + 4 + k (see key_codes),
+// The scales 2^e as fp16 in the key operand's slot order: slot pair k of
+// k-step d (k = 0..3) holds channels 8d + k and 8d + 4 + k (see key_codes),
 // i.e. byte k of dword 2d and of dword 2d + 1 of the scale bytes, each moved
 // to the high byte of its half by one byte permute.
-__device__ __forceinline__ void scale_multipliers(const PageScales &s, v8h (&m)[4]) {
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-        const uint32_t lo = s.w[2 * d], hi = s.w[2 * d + 1];
-        const uint4 u = {__builtin_amdgcn_perm(hi, lo, 0x040c000cu), __builtin_amdgcn_perm(hi, lo, 0x050c010cu),
-                         __builtin_amdgcn_perm(hi, lo, 0x060c020cu), __builtin_amdgcn_perm(hi, lo, 0x070c030cu)};
-        m[d] = __builtin_bit_cast(v8h, u);
-    }
+__device__ __forceinline__ uint4 scale_words(const PageScales &s, int d) {
+    const uint32_t lo = s.w[2 * d], hi = s.w[2 * d + 1];
+    return uint4{__builtin_amdgcn_perm(hi, lo, 0x040c000cu), __builtin_amdgcn_perm(hi, lo, 0x050c010cu),
+                 __builtin_amdgcn_perm(hi, lo, 0x060c020cu), __builtin_amdgcn_perm(hi, lo, 0x070c030cu)};
 }
 
-// Key-code A operand of one 8-channel dword w for page-balanced keys: the
-// slot order of key_codes, but every code at mantissa bits 6-9 (the fp16
-// subnormal c * 2^-18), one shift and one AND per pair of channels.  The
-// page's column scales can shrink query elements by up to 2^-6; with the
-// codes 2^6 higher than key_codes' low slots the MFMA's products keep the
-// magnitudes of the per-token format (measured: with codes at bits 0-3 and
-// 4-7 and the query 2^6 lower, the decode's error against the fp64
-// definition was up to ~40x that format's on the same keys; the MFMA keeps
-// fewer bits of very small products).
-__device__ __forceinline__ v8h key_codes_pb(uint32_t w) {
+// D' (rows: tokens 4g..4g+3 of column n) and W (of column n's head, both
+// query terms) of one page for kG head groups.
+template <int kG>
+__device__ __forceinline__ void page_dots_pb(const PageRegs<4, 2> &r, const PageScales &sc, const v8h (&bq)[kG][4],
+                                             v4f (&d)[kG], float (&w)[kG]) {
     constexpr uint32_t kBits69 = 0x03C003C0u;
-    const uint4 u = {(w << 6) & kBits69, (w << 2) & kBits69, (w >> 2) & kBits69, (w >> 6) & kBits69};
-    return __builtin_bit_cast(v8h, u);
-}
-
-__device__ __forceinline__ v4f page_dots_pb(const PageRegs<4, 2> &r, const v8h (&bq)[4]) {
-    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f wv[kG];
 #pragma unroll
-    for (int q = 0; q < 4; q++) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes_pb(r.k[q]), bq[q], d, 0, 0, 0);
-    return d;
-}
-
-// Sum over the 32 channels of each k-step of the query operand q (unit codes
-// in key_codes_pb's scaling, 2^-18 in every slot): every row of the result
-// holds W of column n.
-__device__ __forceinline__ float page_query_sum(const v8h (&q)[4]) {
-    const v8h ones = __builtin_bit_cast(v8h, make_uint4(0x00400040u, 0x00400040u, 0x00400040u, 0x00400040u));
-    v4f d = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h = 0; h < kG; h++) d[h] = wv[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < 4; k++) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, q[k], d, 0, 0, 0);
-    return d[0] + row_swap8(d[0]);            // the query's two fp16 terms
+    for (int q = 0; q < 4; q++) {
+        const uint4 m = scale_words(sc, q);
+        const uint32_t x = r.k[q];
+        const uint4 a = {((x << 6) & kBits69) | m.x, ((x << 2) & kBits69) | m.y, ((x >> 2) & kBits69) | m.z,
+                         ((x >> 6) & kBits69) | m.w};
+#pragma unroll
+        for (int h = 0; h < kG; h++) {
+            d[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), bq[h][q], d[h], 0, 0, 0);
+            wv[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, m), bq[h][q], wv[h], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < kG; h++) w[h] = wv[h][0] + row_swap8(wv[h][0]);   // every row holds W
 }
 
-// One page pair with page-balanced keys (K4V2): the query operand of each
-// group is scaled per page, and the z coefficient is the scaled query's sum.
+// One page pair with page-balanced keys (K4V2).
 template <int kG, bool kMasked, bool kFirst>
 __device__ __forceinline__ void process_pair_pb(const PageRegs<4, 2> &A, const PageRegs<4, 2> &B,
                                                 const PageScales &SA, const PageScales &SB, int tokA, int tokB,
                                                 const int (&lim)[kG], const v8h (&bq)[kG][4],
                                                 const LaneConsts (&lc)[kG], int g, State (&st)[kG]) {
     v4f dA[kG], dB[kG];
-    float wa[kG], wb[kG], c2[kG];
-    // one page at a time, so that one page's multipliers are live at once
-    {
-        v8h m[4];
-        scale_multipliers(SA, m);
+    float wa[kG], wb[kG], c2[kG], woff[kG];
+    page_dots_pb<kG>(A, SA, bq, dA, wa);
+    page_dots_pb<kG>(B, SB, bq, dB, wb);
 #pragma unroll
-        for (int h = 0; h < kG; h++) {
-            v8h qs[4];
-#pragma unroll
-            for (int d = 0; d < 4; d++) qs[d] = bq[h][d] * m[d];
-            dA[h] = page_dots_pb(A, qs);
-            wa[h] = page_query_sum(qs);
-        }
+    for (int h = 0; h < kG; h++) {
+        woff[h] = lc[h].hb ? wb[h] : wa[h];
+        c2[h] = lc[h].c1 * 0.0625f * woff[h];
     }
-    {
-        v8h m[4];
-        scale_multipliers(SB, m);
-#pragma unroll
-        for (int h = 0; h < kG; h++) {
-            v8h qs[4];
-#pragma unroll
-            for (int d = 0; d < 4; d++) qs[d] = bq[h][d] * m[d];
-            dB[h] = page_dots_pb(B, qs);
-            wb[h] = page_query_sum(qs);
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < kG; h++) c2[h] = lc[h].c1 * (lc[h].hb ? wb[h] : wa[h]);
-    pair_finish<4, 2, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, g, st);
+    pair_finish<4, 2, kG, kMasked, kFirst>(A, B, dA, dB, tokA, tokB, lim, lc, c2, woff, g, st);
 }
 
 // One page pair of either key normalisation (Scales: PageScales with
@@ -821,10 +800,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
         }
         int ex = 0;
         if (am > 0.0f) (void)frexpf(am, &ex);          // am in [2^(ex-1), 2^ex)
-        // q' * 2^shift: max in [2^13, 2^14); with page-balanced keys in
-        // [2^7, 2^8), so that a page's column scales (up to 2^6) keep the
-        // scaled query inside fp16
-        const int shift = (kPB ? 8 : 14) - ex;
+        const int shift = 14 - ex;                       // q' * 2^shift: max in [2^13, 2^14)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             const int ch = c0 + e;
@@ -836,7 +812,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
             int slot, down = 0;
             if (KB == 4) {
                 slot = (ch & ~7) + (r8 < 4 ? 2 * r8 : 2 * (r8 - 4) + 1);
-                down = kPB ? 0 : 4 * ((slot >> 1) & 1);   // page-balanced keys: every code at 2^-18
+                down = kPB ? 0 : 4 * ((slot >> 1) & 1);   // (page-balanced keys: normal fp16 operands)
             } else if (KB == 3) {
                 const int x = ch & 31, r16 = x & 15;   // channel 32g + x; x = 16 hi + r16
                 slot = (ch & ~31) + 8 * (2 * (r16 >> 3) + ((r16 >> 2) & 1)) + 2 * (r16 & 3) + (x >> 4);
@@ -850,9 +826,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
             s_qb[hq][8 + hh][slot] = (_Float16)(v - (float)vh);
         }
         if (l32 == 0) {
-            // dot(q', c) = D * 2^(24 - shift), D the MFMA sum with codes c * 2^-24
-            // (c * 2^-18 with page-balanced keys)
-            s_c1[hq][hh] = a.alpha * __builtin_ldexpf(1.0f, (kPB ? 18 : 24) - shift);
+            // dot(q', c) = D * 2^(24 - shift), D the MFMA sum with codes c * 2^-24;
+            // page-balanced keys: 16 (D' - W) 2^-shift (see page_dots_pb)
+            s_c1[hq][hh] = a.alpha * __builtin_ldexpf(1.0f, (kPB ? 4 : 24) - shift);
             s_c2[hq][hh] = a.alpha * qs;
         }
     }

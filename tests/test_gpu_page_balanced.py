@@ -305,3 +305,49 @@ def test_pb_workload_qwen3_32b_16k_sampled(dev, pb):
             err = np.max(np.abs(out[b, kvh * w.gqa:(kvh + 1) * w.gqa] - ref))
             log(f"  seq {b} kv {kvh}: err {err:.2e}")
             assert err <= TOL
+
+
+@pytest.mark.parametrize("sink,window,hist", [(4, 44, [300, 1000, 0]), (0, 16, [512, 80, 16])])
+def test_pb_history_with_fp16_window(dev, pb, sink, window, hist):
+    """The serving layout for page-balanced keys: whole pages of history in
+    the page-balanced cache, the sink and the recent (partly filled) page's
+    tokens uncompressed in an fp16 cache; both caches' partials merged by one
+    combine equal the oracle's attention over the union (history dequantised
+    by kvqo_dequant_slot_pb, window raw)."""
+    B, Hq, Hkv = len(hist), 16, 2
+    G = Hq // Hkv
+    log(f"pb history sink={sink} window={window} hist={hist}")
+    rng = np.random.default_rng(sink * 7 + window + sum(hist))
+    cache_h, pool_h, bt_h, lens_h, q = _build_pb_case(dev, pb, B, Hq, Hkv, hist, seed=sum(hist) + 11)
+    f16 = kvq.format_from_string("fp16")
+    nf = sink + window
+    pages_f = -(-max(nf, 1) // 16)
+    bt_f = np.arange(B * pages_f, dtype=np.int32).reshape(B, pages_f)
+    cache_f = torch.full((B * pages_f, Hkv, 8192), 0xFF, dtype=torch.uint8, device=dev)
+    kf = (rng.standard_normal((B, nf, Hkv, D)) * 0.8).astype(np.float16)
+    vf = rng.standard_normal((B, nf, Hkv, D)).astype(np.float16)
+    for b in range(B):
+        kvq.quantize_append(torch.from_numpy(kf[b]).to(dev), torch.from_numpy(vf[b]).to(dev),
+                            torch.from_numpy(inp.slot_mapping(bt_f, b, 0, nf)).to(dev), cache_f, fmt=f16)
+    qd = torch.from_numpy(q).to(dev)
+    Lh, Lf = max(int(lens_h.max()), 1), max(nf, 1)
+    s_h = kvq.decode_split_slots(B, Hq, Hkv, Lh, fmt=pb)
+    s_f = kvq.decode_split_slots(B, Hq, Hkv, Lf, fmt=f16)
+    total = s_h + s_f
+    ws = torch.full((kvq.slots_workspace_bytes(B, Hq, total),), 0xFF, dtype=torch.uint8, device=dev)
+    kvq.decode_partials_slots(qd, cache_h, torch.from_numpy(bt_h).to(dev),
+                              torch.from_numpy(lens_h.astype(np.int32)).to(dev), Lh, ws, 0, total, fmt=pb)
+    kvq.decode_partials_slots(qd, cache_f, torch.from_numpy(bt_f).to(dev),
+                              torch.full((B,), nf, dtype=torch.int32, device=dev), Lf, ws, s_h, total,
+                              rotated=True, fmt=f16)
+    out = kvq.decode_combine_slots(ws, B, Hq, total).cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv):
+            kh = np.zeros((hist[b], D)); vh = np.zeros((hist[b], D))
+            for t in range(hist[b]):
+                kh[t], vh[t] = oracle.dequant_slot_pb(np.ascontiguousarray(pool_h[bt_h[b, t // 16], h]), t % 16)
+            k_all = np.concatenate([kf[b, :, h].astype(np.float64), kh])
+            v_all = np.concatenate([vf[b, :, h].astype(np.float64), vh])
+            ref = oracle.attention_f64(k_all, v_all, q[b, h * G:(h + 1) * G], SCALE)
+            err = np.max(np.abs(out[b, h * G:(h + 1) * G] - ref))
+            assert err <= TOL, f"b={b} h={h} err={err}"
