@@ -50,7 +50,7 @@ __device__ __forceinline__ int frexp_exponent(float x) {
 // Sum of the 64 lanes' values of one wave.
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
-    for (int x = 1; x < 64; x <<= 1) v += (int)xor_lane_u((uint32_t)v, x);
+    for (int x = 1; x < 64; x <<= 1) v += (int)xor_lane_u_dpp((uint32_t)v, x);
     return v;
 }
 
@@ -73,13 +73,14 @@ __global__ __launch_bounds__(256) void balance_append_kernel(AppendArgs a) {
     __shared__ int s_e[kHeadDim];             // column exponents
     __shared__ int s_red[2][2];               // (non-zero columns, sum of their F) per wave
 
-    float y[8];
-    {
-        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-        if (present)
-            raw = *reinterpret_cast<const uint4 *>(a.key + tok * a.key_stride + (int64_t)head * kHeadDim + 8 * r);
-        rotate_row(raw, r, y);                 // an absent row stays zero
+    // the row's key and value words, both requested before any arithmetic
+    uint4 raw = make_uint4(0u, 0u, 0u, 0u), raw_v = make_uint4(0u, 0u, 0u, 0u);
+    if (present) {
+        raw = *reinterpret_cast<const uint4 *>(a.key + tok * a.key_stride + (int64_t)head * kHeadDim + 8 * r);
+        raw_v = *reinterpret_cast<const uint4 *>(a.value + tok * a.value_stride + (int64_t)head * kHeadDim + 8 * r);
     }
+    float y[8];
+    rotate_row(raw, r, y);                     // an absent row stays zero
 
     int f = 0;                 // this row's exponent f_t
     float css = 0.0f;          // lanes < 128: the last column pass's sum of column tid
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(256) void balance_append_kernel(AppendArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e++) ys[e] = __builtin_ldexpf(y[e], -s_e[8 * r + e]);
         encode_rotated_fmt<4, 2>(ys, 0, r, region, t);
-        encode_group_fmt<4, 2>(a.value + tok * a.value_stride + (int64_t)head * kHeadDim, 1, r, region, t);
+        float yv[8];
+        rotate_row(raw_v, r, yv);
+        encode_rotated_fmt<4, 2>(yv, 1, r, region, t);
     }
 }
 

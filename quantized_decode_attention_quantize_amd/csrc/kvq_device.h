@@ -91,6 +91,15 @@ __device__ __forceinline__ float xor_lane_dpp(float v, int x) {
                     : xor_lane(v, x);
 }
 
+// The same for 32-bit integers.
+__device__ __forceinline__ uint32_t xor_lane_u_dpp(uint32_t v, int x) {
+    const int b = (int)v;
+    return x == 1   ? (uint32_t)__builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false)
+           : x == 2 ? (uint32_t)__builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false)
+           : x == 8 ? (uint32_t)__builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false)
+                    : xor_lane_u(v, x);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
 }

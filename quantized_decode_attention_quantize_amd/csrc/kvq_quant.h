@@ -12,7 +12,10 @@
 // holds channels 8r..8r+7 in registers.  The FWHT runs stages h = 1, 2, 4
 // inside a lane and h = 8, 16, 32, 64 across lanes r^1, r^2, r^4, r^8, so
 // every butterfly is the same fp32 a+b / a-b, in the same stage order, as the
-// format's definition.  The sum of squares uses the format's fixed pairwise
+// format's definition.  Partners 1, 2 and 8 lanes apart are read with DPP
+// moves, 4 apart through the LDS crossbar (the values are the same either
+// way); a row is always active or inactive as a whole, so every partner
+// lane is active.  The sum of squares uses the format's fixed pairwise
 // tree (lanes ^8, ^4, ^2, ^1, then in-lane 4, 2, 1); IEEE addition is
 // commutative, so both lanes of a pair hold identical bits.  Codes are
 // therefore bit-identical to any correct implementation of the format.  No
@@ -68,7 +71,7 @@ __device__ __forceinline__ void rotate_row(const uint4 raw, int r, float (&y)[8]
         const bool upper = (r & x) != 0;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-            const float other = xor_lane(y[e], x);
+            const float other = xor_lane_dpp(y[e], x);
             y[e] = upper ? (other - y[e]) : (y[e] + other);
         }
     }
@@ -84,7 +87,7 @@ __device__ __forceinline__ float row_sum_squares(const float (&y)[8]) {
 #pragma unroll
     for (int x = 8; x >= 1; x >>= 1) {
 #pragma unroll
-        for (int e = 0; e < 8; e++) p[e] = p[e] + xor_lane(p[e], x);
+        for (int e = 0; e < 8; e++) p[e] = p[e] + xor_lane_dpp(p[e], x);
     }
     p[0] = p[0] + p[4]; p[1] = p[1] + p[5]; p[2] = p[2] + p[6]; p[3] = p[3] + p[7];
     p[0] = p[0] + p[2]; p[1] = p[1] + p[3];
@@ -120,8 +123,8 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
         }
 #pragma unroll
         for (int x = 1; x < 16; x <<= 1) {
-            lo = fminf(lo, xor_lane(lo, x));
-            hi = fmaxf(hi, xor_lane(hi, x));
+            lo = fminf(lo, xor_lane_dpp(lo, x));
+            hi = fmaxf(hi, xor_lane_dpp(hi, x));
         }
         // 3. Asymmetric round-to-nearest (ties to even), clamp to [0, L].
         float delta = 0.0f;
@@ -147,7 +150,7 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
 #pragma unroll
             for (int e = 0; e < 8; e++) csum += code[e];
 #pragma unroll
-            for (int x = 1; x < 16; x <<= 1) csum += xor_lane_u(csum, x);
+            for (int x = 1; x < 16; x <<= 1) csum += xor_lane_u_dpp(csum, x);
             float t = delta * (float)csum;
             t = t * 0x1p-7f;
             t = lo + t;
@@ -204,18 +207,18 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
         for (int k = 0; k < 4; k++) {
             const uint32_t send = b1 ? v8[k] : v8[4 + k];
             const uint32_t keep = b1 ? v8[4 + k] : v8[k];
-            v4[k] = keep | xor_lane_u(send, 2);
+            v4[k] = keep | xor_lane_u_dpp(send, 2);
         }
         uint32_t v2[2];
 #pragma unroll
         for (int k = 0; k < 2; k++) {
             const uint32_t send = b2 ? v4[k] : v4[2 + k];
             const uint32_t keep = b2 ? v4[2 + k] : v4[k];
-            v2[k] = keep | xor_lane_u(send, 4);
+            v2[k] = keep | xor_lane_u_dpp(send, 4);
         }
         const uint32_t send = b3 ? v2[0] : v2[1];
         const uint32_t keep = b3 ? v2[1] : v2[0];
-        const uint32_t word = keep | xor_lane_u(send, 8);
+        const uint32_t word = keep | xor_lane_u_dpp(send, 8);
         const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + (int)b3;
         const int g = off >> 2, i = off & 3;
         uint8_t *vb = region + Lay::kVCodes + 12 * (16 * g + m) + (((i & 1) << 1) | (i >> 1));
@@ -238,7 +241,7 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
         for (int k = 0; k < 4; k++) {
             const uint32_t send = b1 ? v8[k] : v8[4 + k];
             const uint32_t keep = b1 ? v8[4 + k] : v8[k];
-            v4[k] = keep | xor_lane_u(send, 2);
+            v4[k] = keep | xor_lane_u_dpp(send, 2);
         }
         const int g = off >> 2, i = off & 3, h = r >> 3;
         uint8_t *base = region + Lay::kVCodes + 256 * g + 8 * (i >> 1) + 4 * h + 2 * (i & 1);
@@ -246,7 +249,7 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
         for (int u = 0; u < 2; u++) {
             const uint32_t send = b2 ? v4[u] : v4[2 + u];
             const uint32_t keep = b2 ? v4[2 + u] : v4[u];
-            const uint32_t word = keep | xor_lane_u(send, 4);
+            const uint32_t word = keep | xor_lane_u_dpp(send, 4);
             const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + u;
             *reinterpret_cast<uint16_t *>(base + 16 * m) = (uint16_t)word;
         }
@@ -266,18 +269,18 @@ __device__ __forceinline__ void encode_rotated_fmt(float (&y)[8], int is_v, int 
         for (int k = 0; k < 4; k++) {
             const uint32_t send = b1 ? v8[k] : v8[4 + k];
             const uint32_t keep = b1 ? v8[4 + k] : v8[k];
-            v4[k] = keep | xor_lane_u(send, 2);
+            v4[k] = keep | xor_lane_u_dpp(send, 2);
         }
         uint32_t v2[2];
 #pragma unroll
         for (int k = 0; k < 2; k++) {
             const uint32_t send = b2 ? v4[k] : v4[2 + k];
             const uint32_t keep = b2 ? v4[2 + k] : v4[k];
-            v2[k] = keep | xor_lane_u(send, 4);
+            v2[k] = keep | xor_lane_u_dpp(send, 4);
         }
         const uint32_t send = b3 ? v2[0] : v2[1];
         const uint32_t keep = b3 ? v2[1] : v2[0];
-        const uint32_t word = keep | xor_lane_u(send, 8);
+        const uint32_t word = keep | xor_lane_u_dpp(send, 8);
         const int m = 8 * (r & 1) + 4 * (int)b1 + 2 * (int)b2 + (int)b3;
         const int g = off >> 2, i = off & 3;
         *reinterpret_cast<uint16_t *>(region + Lay::kVCodes + 128 * g + 8 * m + 2 * i) = (uint16_t)word;
