@@ -273,6 +273,30 @@ def test_decode_small_matches_oracle(dev, B, Hq, Hkv, lens):
     assert err16 <= TOL, f"fp16 out err={err16}"
 
 
+# Sequence lengths whose waves run 4 to 16 page pairs per split at 128 pages per
+# split (64 pairs over 4 waves): whole unguarded rounds of three pairs, every
+# length (1 to 4 pairs) of the guarded last stretch, the work-left priority steps
+# and a masked last pair.  With 16 query heads per KV head (two head groups) the
+# guarded loop runs throughout.
+LOOP_LENS = [600, 700, 800, 900, 1000, 1100, 1300, 2049, 4000]
+
+
+@pytest.mark.parametrize("Hq,Hkv,fmt", [(8, 1, (4, 2)), (32, 2, (4, 2)), (16, 2, (4, 4))])
+def test_decode_pair_loop_lengths_match_oracle(dev, Hq, Hkv, fmt):
+    B = len(LOOP_LENS)
+    log(f"decode pair-loop lengths Hq={Hq} Hkv={Hkv} fmt={fmt} lens={LOOP_LENS}")
+    cache, pool, bt, lens_np, q = _build_case(dev, B, Hq, Hkv, LOOP_LENS, seed=4099 + Hq + fmt[1], fmt=fmt)
+    assert np.array_equal(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention(pool, bt, lens_np, q, SCALE, fmt=fmt)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (128, 64, 0):
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=_kfmt(fmt))
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+
+
 def test_decode_deterministic_split_invariant_and_page_placement(dev):
     B, Hq, Hkv, lens = 3, 16, 2, [400, 1, 777]
     log("decode determinism / split / placement")
