@@ -14,10 +14,12 @@ stream: kvq_append_decode_partials (the split kernel, which also encodes each
 sequence's new token into its page before reading it; the dominant kernel)
 and kvq_decode_combine.  The timed steps carry no events.
 
-roofline.achieved: after the timed steps, --kernel-launches back-to-back
-launches of the split kernel alone (same arguments, same pool rotation) run
-between two HIP events recorded on the launch stream; their elapsed time over
-the launch count is the kernel's average launch duration.  Per-launch kernel
+roofline.achieved: after the timed steps and --kernel-warmup untimed
+launches (the shader clock ramps back up for ~10 ms after the idle gap of a
+sync), --kernel-launches back-to-back launches of the split kernel alone
+(same arguments, same pool rotation) run between two HIP events recorded on
+the launch stream; their elapsed time over the launch count is the kernel's
+average launch duration.  Per-launch kernel
 events (kvq_set_split_kernel_events, hipExtLaunchKernel's start/stop events)
 are available with --event-every N, but each timed launch then runs a few
 microseconds longer than an untimed one, so they are not the default.
@@ -84,6 +86,8 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=200,
                     help="back-to-back split-kernel launches timed for roofline.achieved")
+    ap.add_argument("--kernel-warmup", type=int, default=400,
+                    help="untimed split-kernel launches right before the timed ones (shader clock ramp)")
     ap.add_argument("--dist-blocks", type=int, default=100,
                     help="blocks timed for the per-step median and p10/p90 (0: skip)")
     ap.add_argument("--dist-block-steps", type=int, default=10,
@@ -422,12 +426,19 @@ def main():
         raise RuntimeError("kvq call failed in the timed region")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the split kernel alone, back to back, between two events on its stream
+    # the split kernel alone, back to back, between two events on its stream,
+    # after --kernel-warmup untimed launches: after an idle gap (the sync
+    # above) the shader clock ramps back up over ~10 ms, and the first ~400
+    # launches measured ~8% slower than the ones after them
     nl = max(1, args.kernel_launches)
+    nw = max(0, args.kernel_warmup)
+    k0 = args.warmup + args.steps
+    for i in range(nw):
+        bad |= part_fn(*part_args[(k0 + i) % len(pools)])
     kl0 = 2 * len(sampled)
     hev.record(kl0, stream.cuda_stream)
     for i in range(nl):
-        bad |= part_fn(*part_args[(args.warmup + args.steps + i) % len(pools)])
+        bad |= part_fn(*part_args[(k0 + nw + i) % len(pools)])
     hev.record(kl0 + 1, stream.cuda_stream)
     torch.cuda.synchronize()
     if bad:
@@ -461,7 +472,7 @@ def main():
                     "p90_ms": round(float(np.percentile(per, 90)), 5),
                     "mean_ms": round(float(per.mean()), 5), "blocks": nb, "steps_per_block": bs}
 
-        base_i = args.warmup + args.steps + nl
+        base_i = args.warmup + args.steps + nw + nl
         dist = blocks(lambda k: sum(step(base_i + k * bs + j) for j in range(bs)))
         kdist = blocks(lambda k: sum(part_fn(*part_args[(base_i + k * bs + j) % len(pools)]) for j in range(bs)))
     # labelled warm figure: the same launches on one pool copy, whose 109 MB
@@ -517,6 +528,7 @@ def main():
         "decode_kernel_ms": round(dec_avg_ms, 5),
         "decode_kernel_distribution": kdist,
         "decode_kernel_launches_timed": nl,
+        "decode_kernel_launches_warmup": nw,
         "warm_cache_decode_kernel_ms": None if warm_ms is None else round(warm_ms, 5),
         "warm_cache_note": "one pool copy re-read back to back (resident in the 256 MB Infinity Cache); "
                            "not HBM-bound, not the roofline figure",
