@@ -239,6 +239,26 @@ def test_pb_decode_matches_oracle(dev, pb, B, Hq, Hkv, lens):
     assert err16 <= TOL, f"fp16 out err={err16}"
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (32, 2)])
+def test_pb_decode_pair_loop_lengths_match_oracle(dev, pb, Hq, Hkv):
+    # waves of 4 to 16 page pairs per split at 128 and 64 pages per split: the
+    # unguarded rounds of three pairs, every length of the guarded last stretch
+    # and a masked last pair (two head groups: the guarded loop throughout)
+    lens = [600, 700, 800, 900, 1000, 1100, 1300, 2049, 4000]
+    B = len(lens)
+    log(f"pb decode pair-loop lengths Hq={Hq} Hkv={Hkv}")
+    cache, pool, bt, lens_np, q = _build_pb_case(dev, pb, B, Hq, Hkv, lens, seed=7001 + Hq)
+    _assert_same(cache.cpu().numpy(), pool)
+    ref = oracle.decode_attention_pb(pool, bt, lens_np, q, SCALE)
+    qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
+    ld = torch.from_numpy(lens_np.astype(np.int32)).to(dev)
+    L = int(lens_np.max())
+    for pps in (128, 64, 0):
+        out = kvq.decode_attention(qd, cache, btd, ld, L, pages_per_split=pps, fmt=pb)
+        err = np.max(np.abs(out.cpu().numpy() - ref))
+        assert err <= TOL, f"pps={pps} err={err}"
+
+
 def test_pb_decode_two_phase_matches_one_call(dev, pb):
     cache, pool, bt, lens_np, q = _build_pb_case(dev, pb, 3, 16, 2, [400, 1, 777], seed=31)
     qd, btd = torch.from_numpy(q).to(dev), torch.from_numpy(bt).to(dev)
